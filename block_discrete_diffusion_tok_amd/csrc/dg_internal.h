@@ -1,0 +1,165 @@
+// Internal declarations shared by the libdg kernels and the host runtime.
+// gfx950 (CDNA4) only: wave64, bf16 MFMA 16x16x32, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg.h"
+
+namespace dg {
+
+// ------------------------------------------------------------------ types
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// OCP E4M3 byte -> bf16 bits (exact: 3 mantissa bits and exponents 2^-9..2^8
+// all fit in bfloat16).  Exponent field 0 is subnormal m * 2^-9; the code
+// S.1111.111 is NaN.
+__device__ __forceinline__ uint16_t e4m3_to_bf(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 8;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t m = c & 0x7u;
+  if (e == 0xFu && m == 0x7u) return (uint16_t)(s | 0x7fc0u);
+  if (e != 0) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
+  if (m == 0) return (uint16_t)s;
+  // subnormal: m * 2^-9 with m in 1..7 -> normalise
+  float v = (float)m * 0.001953125f;  // 2^-9
+  return (uint16_t)(s | (__float_as_uint(v) >> 16));
+}
+
+// One bf16 MFMA: D(16x16) += A(16x32) * B(32x16).  Lane l supplies row
+// (A) / column (B) l % 16 and the 8 k-slots 8*(l/16)..+7; the result holds
+// column l % 16, rows 4*(l/16)+i in element i.  Any assignment of real k
+// indices to k-slots works as long as A and B use the same one.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b,
+                                                f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+
+// ------------------------------------------------------------------ launches
+// Every launcher returns hipSuccess or the launch error; shapes were checked
+// by the caller.
+
+enum GemmEpi : int {
+  EPI_STORE_BF16 = 0,  // C bf16 [M, N]
+  EPI_STORE_F32 = 1,   // C fp32 [M, N]
+  EPI_ADD_F32 = 2,     // C fp32 [M, N] += acc
+  EPI_SWIGLU = 3,      // act bf16 [rows, F] = silu(gate) * up
+  EPI_DOWN = 4,        // y fp32 [pair, N] = w_pair * acc (scattered rows)
+  EPI_LMSTATS = 5      // per-row (max, sum exp, sum exp*(z-max), argmax)
+};
+
+struct GemmArgs {
+  const uint16_t* A;       // bf16 [rows, K]
+  int lda;
+  const int32_t* a_map;    // optional: A row = a_map[row] / a_map_div
+  int a_map_div;
+  const void* B;           // weights [N, K] (bf16 or e4m3), per group stride
+  long long b_group_stride;  // elements between groups
+  const float* b_scale;    // e4m3 per-row scales, [groups][scale_rows]
+  int scale_rows;
+  int M;                   // rows (dense)
+  const int32_t* M_dev;    // optional device row count (dense)
+  int N, K;
+  int n_groups;                  // grouped mode when group_offsets != null
+  const int32_t* group_offsets;  // [G+1] row offsets
+  const int32_t* tile_offsets;   // [G+1] m-tile offsets
+  void* C;                 // output
+  int ldc;
+  const int32_t* c_map;    // EPI_DOWN: pair index of each row
+  const float* row_scale;  // EPI_DOWN: gate weight per pair
+  int ffn;                 // EPI_SWIGLU: F
+  float4* part;            // EPI_LMSTATS: [rows][n_tiles]
+  int n_tiles;
+  float* logits;           // EPI_LMSTATS: optional [rows, N] (row_map placed)
+  const int32_t* row_map;  // EPI_LMSTATS: logits row of each A row
+};
+
+// Tile sizes of the grouped GEMMs (rows of one expert are tiled by this).
+constexpr int kGroupBM = 64;
+
+hipError_t launch_gemm(int epi, bool w_e4m3, const GemmArgs& a, int grid_m,
+                       hipStream_t s);
+int gemm_bn(int epi);   // BN of the instance used for an epilogue
+int gemm_bm(int epi);   // BM of the instance used for an epilogue
+
+struct AttnArgs {
+  const uint16_t* qkv;  // [n*C, ldqkv]
+  int ldqkv;
+  int C, Hq, Hkv, D;
+  const uint16_t* kc;   // layer base of the K cache
+  const uint16_t* vc;
+  long long req_stride;   // elements between request slots
+  long long head_stride;  // elements between KV heads (= max_kv_len * D)
+  int req[DG_MAX_BATCH];
+  int plen[DG_MAX_BATCH];
+  int n;
+  int splits;
+  int causal;
+  uint16_t* out;        // [n*C, Hq*D]
+  float* opart;         // [splits][n*Hq*C][D]
+  float* lpart;         // [splits][n*Hq*C]
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+int attention_auto_splits(int n, int C, int Hq, int Hkv);
+
+hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
+                        int V, int H, float* x, hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
+                          float eps, uint16_t* out, const int32_t* row_map,
+                          const int32_t* m_dev, float* copy_f32,
+                          hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx,
+                       float* w, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
+                          int32_t* chunk_counts, int32_t* local_rank,
+                          int32_t* chunk_base, int32_t* offsets,
+                          int32_t* tile_offsets, int32_t* counts,
+                          int32_t* perm, hipStream_t s);
+int permute_chunks(int n_pairs);
+hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
+                            float* moe_out, hipStream_t s);
+hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
+                          int32_t* m_dev, hipStream_t s);
+hipError_t launch_lm_merge(const float4* part, int n_tiles,
+                           const int32_t* m_dev, int m_max,
+                           const int32_t* row_map, float* entropy, float* lse,
+                           int32_t* argmax, hipStream_t s);
+hipError_t launch_eb_select(int n, const float* entropy, const int32_t* argmax,
+                            uint8_t* committed, int32_t* tokens, int32_t* step,
+                            const float* gamma, int step_cap, int refine,
+                            int32_t* n_new, uint8_t* done, hipStream_t s);
+hipError_t launch_kv_append(const uint16_t* qkv, int ldqkv, int col0_k,
+                            int col0_v, int n, int C, int Hkv, int D,
+                            uint16_t* kc, uint16_t* vc, long long req_stride,
+                            long long head_stride, const int* req,
+                            const int* row0, hipStream_t s);
+hipError_t launch_kv_install(const uint16_t* src, int Hkv, int n, int D,
+                             uint16_t* dst, long long head_stride,
+                             hipStream_t s);
+
+}  // namespace dg

@@ -1,0 +1,526 @@
+// Latency-scale kernels of the denoising step: embedding gather, RMSNorm,
+// router top-k, the stable expert permutation, un-permute + residual,
+// uncommitted-row compaction, the vocabulary-statistics merge, the
+// entropy-bounded selection and the KV-cache copies.
+#include <math.h>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+// ---------------------------------------------------------------- embedding
+// x[t, :] = E[tok_t, :] (bf16 -> fp32).  One workgroup per token.  Token ids
+// outside [0, V) are clamped into range so that a bad id cannot read outside
+// the embedding.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok,
+                                                    const uint16_t* E, int V,
+                                                    int H, float* x) {
+  const int t = blockIdx.x;
+  const int id = min(max(tok[t], 0), V - 1);
+  const uint16_t* src = E + (long long)id * H;
+  float* dst = x + (long long)t * H;
+  for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
+    const uint4 v = *(const uint4*)(src + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dst[i + 2 * q] = bf2f((uint16_t)(w[q] & 0xffff));
+      dst[i + 2 * q + 1] = bf2f((uint16_t)(w[q] >> 16));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// out[r, :] = bf16(x[src, :] / sqrt(mean(x^2) + eps) * g), one wave per row;
+// src = row_map[r] when given, rows beyond *m_dev skipped.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(
+    const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
+    const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  const int n = m_dev ? *m_dev : rows;
+  if (r >= n) return;
+  const int src = row_map ? row_map[r] : r;
+  const float* xr = x + (long long)src * H;
+  float ss = 0.f;
+  for (int i = lane * 4; i < H; i += 256) {
+    const float4 v = *(const float4*)(xr + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  uint16_t* o = out + (long long)r * H;
+  for (int i = lane * 4; i < H; i += 256) {
+    const float4 v = *(const float4*)(xr + i);
+    const float4 gg = *(const float4*)(g + i);
+    const uint16_t b0 = f2bf(v.x * inv * gg.x), b1 = f2bf(v.y * inv * gg.y);
+    const uint16_t b2 = f2bf(v.z * inv * gg.z), b3 = f2bf(v.w * inv * gg.w);
+    *(uint2*)(o + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
+                                  (uint32_t)b2 | ((uint32_t)b3 << 16));
+    if (copy_f32)
+      *(float4*)(copy_f32 + (long long)r * H + i) =
+          make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+// One wave per token: k rounds of (max value, lowest index) over the E
+// logits (up to 4 per lane), then softmax over the k selected.
+__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T,
+                                                   int E, int k, int32_t* idx,
+                                                   float* w) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  float v[4];
+  bool taken[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? logits[(long long)t * E + e] : -INFINITY;
+    taken[j] = e >= E;
+  }
+  float sel_v[16];
+  int sel_i[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r >= k) break;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = shfl_xor(bv, off);
+      const int oi = shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (bi == lane + 64 * j) taken[j] = true;
+    sel_v[r] = bv;
+    sel_i[r] = bi;
+  }
+  const float mx = sel_v[0];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (r < k) sum += __expf(sel_v[r] - mx);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r < k && lane == r) {
+      idx[(long long)t * k + r] = sel_i[r];
+      w[(long long)t * k + r] = __expf(sel_v[r] - mx) / sum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- permute
+// Stable counting sort of the T*k (token, rank) pairs by expert, in three
+// passes over chunks of 256 pairs: per-chunk histogram and in-chunk rank,
+// scan over (expert, chunk), scatter.  Pair p = t*k + j lands at
+// perm[offsets[e] + #{pairs p' < p with expert e}].
+constexpr int kChunk = 256;
+
+__global__ __launch_bounds__(kChunk) void moe_count_kernel(
+    const int32_t* idx, int n_pairs, int E, int32_t* chunk_counts,
+    int32_t* local_rank) {
+  __shared__ int ex[kChunk];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x * kChunk + tid;
+  const int e = p < n_pairs ? idx[p] : -1;
+  ex[tid] = e;
+  if (tid < E) hist[tid] = 0;
+  __syncthreads();
+  if (e >= 0) {
+    int rank = 0;
+    for (int q = 0; q < tid; ++q) rank += (ex[q] == e);
+    local_rank[p] = rank;
+    atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) chunk_counts[(long long)blockIdx.x * E + tid] = hist[tid];
+}
+
+__global__ __launch_bounds__(256) void moe_scan_kernel(
+    int n_chunks, int E, int bm, const int32_t* chunk_counts,
+    int32_t* chunk_base, int32_t* offsets, int32_t* tile_offsets,
+    int32_t* counts) {
+  __shared__ int s_tot[256];
+  __shared__ int s_tiles[256];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int c = 0; c < n_chunks; ++c) tot += chunk_counts[(long long)c * E + e];
+  s_tot[e] = e < E ? tot : 0;
+  s_tiles[e] = e < E ? (tot + bm - 1) / bm : 0;
+  __syncthreads();
+  if (e == 0) {
+    int run = 0, runt = 0;
+    for (int q = 0; q < E; ++q) {
+      const int o = s_tot[q];
+      s_tot[q] = run;
+      run += o;
+      const int ot = s_tiles[q];
+      s_tiles[q] = runt;
+      runt += ot;
+    }
+    offsets[E] = run;
+    tile_offsets[E] = runt;
+  }
+  __syncthreads();
+  if (e < E) {
+    offsets[e] = s_tot[e];
+    tile_offsets[e] = s_tiles[e];
+    if (counts) counts[e] = tot;
+    int base = s_tot[e];
+    for (int c = 0; c < n_chunks; ++c) {
+      chunk_base[(long long)c * E + e] = base;
+      base += chunk_counts[(long long)c * E + e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kChunk) void moe_scatter_kernel(
+    const int32_t* idx, int n_pairs, int E, const int32_t* chunk_base,
+    const int32_t* local_rank, int32_t* perm) {
+  const int p = blockIdx.x * kChunk + threadIdx.x;
+  if (p >= n_pairs) return;
+  const int e = idx[p];
+  perm[chunk_base[(long long)blockIdx.x * E + e] + local_rank[p]] = p;
+}
+
+// ---------------------------------------------------------------- un-permute
+// x[t, :] += sum_j y[t*k + j, :] in rank order (no atomics); optionally the
+// sum alone is written to moe_out.  x may be null (store only).
+__global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
+                                                        int H, float* x,
+                                                        float* moe_out) {
+  const int t = blockIdx.x;
+  for (int i = threadIdx.x * 4; i < H; i += 1024) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 v = *(const float4*)(y + ((long long)t * k + j) * H + i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    if (x) {
+      float4* xp = (float4*)(x + (long long)t * H + i);
+      float4 o = *xp;
+      o.x += s.x; o.y += s.y; o.z += s.z; o.w += s.w;
+      *xp = o;
+    }
+    if (moe_out) *(float4*)(moe_out + (long long)t * H + i) = s;
+  }
+}
+
+// ---------------------------------------------------------------- compaction
+// row_map[0..M) = indices t with committed[t] == 0 in increasing order;
+// *m_dev = M.  One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
+                                                       int T, int32_t* row_map,
+                                                       int32_t* m_dev) {
+  __shared__ int s[1024];
+  __shared__ int run;
+  const int tid = threadIdx.x;
+  if (tid == 0) run = 0;
+  __syncthreads();
+  for (int base = 0; base < T; base += 1024) {
+    const int t = base + tid;
+    const int f = (t < T && committed[t] == 0) ? 1 : 0;
+    s[tid] = f;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = tid >= off ? s[tid - off] : 0;
+      __syncthreads();
+      s[tid] += v;
+      __syncthreads();
+    }
+    if (f) row_map[run + s[tid] - 1] = t;
+    const int total = s[1023];
+    __syncthreads();
+    if (tid == 0) run += total;
+    __syncthreads();
+  }
+  if (tid == 0) *m_dev = run;
+}
+
+// ---------------------------------------------------------------- LM merge
+// Reduce the per-tile (max, sum e^(z-max), sum e^(z-max)(z-max), argmax)
+// partials of a row in a fixed order: lse = max + ln s, entropy =
+// ln s - t / s (clamped at 0), argmax lowest id among maxima.
+__device__ __forceinline__ void merge_stats(float& m, float& s, float& t,
+                                            int& am, float m2, float s2,
+                                            float t2, int am2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  const bool take2 = (m2 > m) || (m2 == m && am2 < am);
+  const float d1 = (m == -INFINITY) ? 0.f : (m - mn);
+  const float d2 = (m2 == -INFINITY) ? 0.f : (m2 - mn);
+  const float e1 = (m == -INFINITY) ? 0.f : __expf(d1);
+  const float e2 = (m2 == -INFINITY) ? 0.f : __expf(d2);
+  t = e1 * (t + s * d1) + e2 * (t2 + s2 * d2);
+  s = s * e1 + s2 * e2;
+  if (take2) am = am2;
+  m = mn;
+}
+
+__global__ __launch_bounds__(256) void lm_merge_kernel(
+    const float4* part, int n_tiles, const int32_t* m_dev, int m_max,
+    const int32_t* row_map, float* entropy, float* lse, int32_t* argmax) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  const int n = m_dev ? *m_dev : m_max;
+  if (r >= n) return;
+  float m = -INFINITY, s = 0.f, t = 0.f;
+  int am = 0x7fffffff;
+  for (int i = lane; i < n_tiles; i += 64) {
+    const float4 p = part[(long long)r * n_tiles + i];
+    merge_stats(m, s, t, am, p.x, p.y, p.z, __float_as_int(p.w));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = shfl_xor(m, off), s2 = shfl_xor(s, off);
+    const float t2 = shfl_xor(t, off);
+    const int am2 = shfl_xor(am, off);
+    merge_stats(m, s, t, am, m2, s2, t2, am2);
+  }
+  if (lane == 0) {
+    const int pos = row_map ? row_map[r] : r;
+    const float ls = logf(s);
+    lse[pos] = m + ls;
+    entropy[pos] = fmaxf(ls - t / s, 0.f);
+    argmax[pos] = am;
+  }
+}
+
+// ---------------------------------------------------------------- EB select
+// One workgroup of 256 threads per canvas, thread j = position j.
+// Rank of each uncommitted position under the total order (entropy,
+// position); the fp64 running sum is taken in that order by one thread,
+// exactly as the rule defines it.
+__global__ __launch_bounds__(256) void eb_kernel(
+    const float* entropy, const int32_t* argmax, uint8_t* committed,
+    int32_t* tokens, int32_t* step, const float* gamma, int cap, int refine,
+    int32_t* n_new, uint8_t* done) {
+  __shared__ unsigned long long keys[DG_CANVAS];
+  __shared__ float sorted_h[DG_CANVAS];
+  __shared__ int s_nstar;
+  const int b = blockIdx.x, j = threadIdx.x;
+  const long long base = (long long)b * DG_CANVAS;
+  const bool unc = committed[base + j] == 0;
+  float h = unc ? entropy[base + j] : 0.f;
+  if (h == 0.f) h = 0.f;  // -0 -> +0
+  uint32_t u = __float_as_uint(h);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving
+  const unsigned long long key =
+      unc ? (((unsigned long long)u << 32) | (unsigned)j) : ~0ull;
+  keys[j] = key;
+  const int n_unc = __syncthreads_count(unc);
+  int rank = 0;
+  if (unc) {
+    for (int i = 0; i < DG_CANVAS; ++i) rank += keys[i] < key;
+    sorted_h[rank] = h;
+  }
+  __syncthreads();
+  if (j == 0) {
+    int n = 0;
+    if (n_unc > 0) {
+      const double lim = (double)gamma[b];
+      double tot = 0.0;
+      for (int r = 0; r < n_unc; ++r) {
+        tot += (double)sorted_h[r];
+        if (tot <= lim) ++n;
+        else break;
+      }
+      if (n < 1) n = 1;
+      if (step[b] + 1 >= cap) n = n_unc;
+    }
+    s_nstar = n;
+  }
+  __syncthreads();
+  const int n = s_nstar;
+  if (n_unc == 0) {
+    if (j == 0) {
+      n_new[b] = 0;
+      done[b] = 1;
+    }
+    return;
+  }
+  if (unc) {
+    if (rank < n) {
+      committed[base + j] = 1;
+      tokens[base + j] = argmax[base + j];
+    } else if (refine) {
+      tokens[base + j] = argmax[base + j];
+    }
+  }
+  if (j == 0) {
+    step[b] += 1;
+    n_new[b] = n;
+    done[b] = (n == n_unc) ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- KV copies
+struct KvAppendArgs {
+  const uint16_t* qkv;
+  int ldqkv, col0_k, col0_v, C, Hkv, D;
+  uint16_t* kc;
+  uint16_t* vc;
+  long long req_stride, head_stride;
+  int req[DG_MAX_BATCH];
+  int row0[DG_MAX_BATCH];
+};
+
+__global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
+  const int b = blockIdx.y;
+  const int per_row = a.Hkv * (a.D / 8);
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.C * per_row) return;
+  const int j = c / per_row, rem = c % per_row;
+  const int g = rem / (a.D / 8), dc = rem % (a.D / 8);
+  const uint16_t* src = a.qkv + (long long)(b * a.C + j) * a.ldqkv + g * a.D + dc * 8;
+  const long long dst = (long long)a.req[b] * a.req_stride +
+                        (long long)g * a.head_stride +
+                        (long long)(a.row0[b] + j) * a.D + dc * 8;
+  *(uint4*)(a.kc + dst) = *(const uint4*)(src + a.col0_k);
+  *(uint4*)(a.vc + dst) = *(const uint4*)(src + a.col0_v);
+}
+
+// src [Hkv][n][D] -> dst [Hkv][max_kv_len][D] rows [0, n)
+__global__ __launch_bounds__(256) void kv_install_kernel(const uint16_t* src,
+                                                         int Hkv, int n, int D,
+                                                         uint16_t* dst,
+                                                         long long head_stride) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long per_head = (long long)n * (D / 8);
+  if (c >= Hkv * per_head) return;
+  const int g = (int)(c / per_head);
+  const long long rem = c % per_head;
+  const long long row = rem / (D / 8);
+  const int dc = (int)(rem % (D / 8));
+  *(uint4*)(dst + g * head_stride + row * D + dc * 8) =
+      *(const uint4*)(src + ((long long)g * n + row) * D + dc * 8);
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
+                        int V, int H, float* x, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, s, tokens, embed, V,
+                     H, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
+                          float eps, uint16_t* out, const int32_t* row_map,
+                          const int32_t* m_dev, float* copy_f32,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x,
+                     rows, H, g, eps, out, row_map, m_dev, copy_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx,
+                       float* w, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
+                     T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+int permute_chunks(int n_pairs) { return (n_pairs + kChunk - 1) / kChunk; }
+
+hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
+                          int32_t* chunk_counts, int32_t* local_rank,
+                          int32_t* chunk_base, int32_t* offsets,
+                          int32_t* tile_offsets, int32_t* counts,
+                          int32_t* perm, hipStream_t s) {
+  const int nc = permute_chunks(n_pairs);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(nc), dim3(kChunk), 0, s, idx,
+                     n_pairs, E, chunk_counts, local_rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), 0, s, nc, E, bm,
+                     chunk_counts, chunk_base, offsets, tile_offsets, counts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(nc), dim3(kChunk), 0, s, idx,
+                     n_pairs, E, chunk_base, local_rank, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
+                            float* moe_out, hipStream_t s) {
+  hipLaunchKernelGGL(unpermute_kernel, dim3(T), dim3(256), 0, s, y, k, H, x,
+                     moe_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
+                          int32_t* m_dev, hipStream_t s) {
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, committed, T,
+                     row_map, m_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_merge(const float4* part, int n_tiles,
+                           const int32_t* m_dev, int m_max,
+                           const int32_t* row_map, float* entropy, float* lse,
+                           int32_t* argmax, hipStream_t s) {
+  if (m_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lm_merge_kernel, dim3((m_max + 3) / 4), dim3(256), 0, s,
+                     part, n_tiles, m_dev, m_max, row_map, entropy, lse,
+                     argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_eb_select(int n, const float* entropy, const int32_t* argmax,
+                            uint8_t* committed, int32_t* tokens, int32_t* step,
+                            const float* gamma, int step_cap, int refine,
+                            int32_t* n_new, uint8_t* done, hipStream_t s) {
+  hipLaunchKernelGGL(eb_kernel, dim3(n), dim3(DG_CANVAS), 0, s, entropy, argmax,
+                     committed, tokens, step, gamma, step_cap, refine, n_new,
+                     done);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const uint16_t* qkv, int ldqkv, int col0_k,
+                            int col0_v, int n, int C, int Hkv, int D,
+                            uint16_t* kc, uint16_t* vc, long long req_stride,
+                            long long head_stride, const int* req,
+                            const int* row0, hipStream_t s) {
+  KvAppendArgs a;
+  a.qkv = qkv; a.ldqkv = ldqkv; a.col0_k = col0_k; a.col0_v = col0_v;
+  a.C = C; a.Hkv = Hkv; a.D = D; a.kc = kc; a.vc = vc;
+  a.req_stride = req_stride; a.head_stride = head_stride;
+  for (int b = 0; b < n; ++b) { a.req[b] = req[b]; a.row0[b] = row0[b]; }
+  const int total = C * Hkv * (D / 8);
+  hipLaunchKernelGGL(kv_append_kernel, dim3((total + 255) / 256, n), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_install(const uint16_t* src, int Hkv, int n, int D,
+                             uint16_t* dst, long long head_stride,
+                             hipStream_t s) {
+  const long long total = (long long)Hkv * n * (D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_install_kernel, dim3((unsigned)((total + 255) / 256)),
+                     dim3(256), 0, s, src, Hkv, n, D, dst, head_stride);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,339 @@
+"""ctypes binding of libdg (include/dg.h, include/dg_ops.h).
+
+Argument marshalling only: every function below checks nothing that the C
+library does not check itself and computes nothing; torch tensors are used
+for device memory and streams.  Importing this module does not load the
+library; the first call does, and it raises if libdg.so has not been built.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "libdg.so")
+_lib = None
+
+CANVAS = 256
+MAX_BATCH = 64
+BF16, FP8_E4M3 = 0, 1
+
+STATUS = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_SHAPE",
+          3: "DG_ERR_CAPACITY", 4: "DG_ERR_STATE", 5: "DG_ERR_HIP",
+          6: "DG_ERR_UNSUPPORTED"}
+
+
+class DgError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("expert_dtype", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up",
+        "w_down", "gate_up_scale", "down_scale")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights))]
+
+
+class CanvasBatch(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("req", ctypes.POINTER(ctypes.c_int32)),
+                ("tokens", ctypes.c_void_p), ("committed", ctypes.c_void_p),
+                ("step", ctypes.c_void_p)]
+
+
+class Capture(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "attn_out", "moe_out", "route_idx", "route_w", "router_logits",
+        "final_xhat")]
+
+
+class StepOut(ctypes.Structure):
+    _fields_ = [("entropy", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("argmax", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("capture", ctypes.POINTER(Capture))]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "dg_status_string": (ctypes.c_char_p, [_I]),
+    "dg_last_error": (ctypes.c_char_p, [_P]),
+    "dg_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ModelDesc), _I]),
+    "dg_kv_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(ModelDesc), _I, _I]),
+    "dg_create": (_I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(Weights), _I,
+                       _I, _I, _P, _P, _P, ctypes.c_size_t, _P,
+                       ctypes.POINTER(_P)]),
+    "dg_destroy": (None, [_P]),
+    "dg_prefill_kv": (_I, [_P, _I, _I, _P, _P, _P]),
+    "dg_denoise_step": (_I, [_P, ctypes.POINTER(CanvasBatch),
+                             ctypes.POINTER(StepOut)]),
+    "dg_eb_select": (_I, [_P, ctypes.POINTER(CanvasBatch), _P, _P, _P, _I, _I,
+                          _P, _P]),
+    "dg_commit_block": (_I, [_P, ctypes.POINTER(CanvasBatch)]),
+    "dg_set_kv_len": (_I, [_P, _I, _I]),
+    "dg_kv_len": (_I, [_P, _I]),
+    "dg_op_rmsnorm": (_I, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
+    "dg_op_linear": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
+    "dg_op_canvas_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+                                    ctypes.POINTER(_I), ctypes.POINTER(_I), _I,
+                                    _I, _P, _P, ctypes.c_size_t, _P]),
+    "dg_op_attention_workspace_bytes": (ctypes.c_size_t, [_I] * 6),
+    "dg_op_router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "dg_op_moe": (_I, [ctypes.POINTER(ModelDesc), ctypes.POINTER(LayerWeights),
+                       _P, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "dg_op_moe_workspace_bytes": (ctypes.c_size_t,
+                                  [ctypes.POINTER(ModelDesc), _I]),
+    "dg_op_lmhead_entropy": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]),
+    "dg_op_lmhead_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "dg_op_eb_select": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+                             ctypes.POINTER(_I), ctypes.POINTER(_I), _P]),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """Load libdg.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; run "
+                "`python -m block_discrete_diffusion_tok_amd.build`")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status, ctx=None):
+    if status != 0:
+        msg = lib().dg_last_error(ctx)
+        raise DgError(status, msg.decode() if msg else "")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def model_desc(shape):
+    return ModelDesc(shape.n_layers, shape.hidden, shape.n_q_heads,
+                     shape.n_kv_heads, shape.head_dim, shape.n_experts,
+                     shape.top_k, shape.expert_ffn, shape.vocab,
+                     shape.rms_eps,
+                     FP8_E4M3 if shape.expert_dtype == "fp8_e4m3" else BF16)
+
+
+def layer_weights(lw):
+    return LayerWeights(*[(lw[k].data_ptr() if lw.get(k) is not None else None)
+                          for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm",
+                                    "w_router", "w_gate_up", "w_down",
+                                    "gate_up_scale", "down_scale")])
+
+
+def _i32_array(values):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+class Engine:
+    """Owner of one libdg context and the device buffers it runs on.
+
+    weights: dict as produced by ``synth.make_weights`` (device tensors).
+    The KV caches and the workspace are allocated here with torch (the
+    library itself never allocates)."""
+
+    def __init__(self, shape, weights, max_requests, max_kv_len,
+                 max_canvases=1, device="cuda"):
+        L = lib()
+        self.shape = shape
+        self.weights = weights  # keep alive
+        self.desc = model_desc(shape)
+        self._layers = (LayerWeights * shape.n_layers)(
+            *[layer_weights(lw) for lw in weights["layers"]])
+        self._w = Weights(weights["embed"].data_ptr(),
+                          weights["final_norm"].data_ptr(), self._layers)
+        kv_bytes = L.dg_kv_cache_bytes(ctypes.byref(self.desc), max_requests,
+                                       max_kv_len)
+        ws_bytes = L.dg_workspace_bytes(ctypes.byref(self.desc), max_canvases)
+        if kv_bytes == 0 or ws_bytes == 0:
+            raise DgError(2, "unsupported model shape")
+        self.k_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
+                                   device=device)
+        self.v_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
+                                   device=device)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8,
+                                     device=device)
+        self.max_requests, self.max_kv_len = max_requests, max_kv_len
+        ctx = ctypes.c_void_p()
+        _check(L.dg_create(ctypes.byref(self.desc), ctypes.byref(self._w),
+                           max_requests, max_kv_len, max_canvases,
+                           _ptr(self.k_cache), _ptr(self.v_cache),
+                           _ptr(self.workspace), ws_bytes, _stream(),
+                           ctypes.byref(ctx)))
+        self.ctx = ctx
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            lib().dg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cache_view(self, which="k"):
+        s = self.shape
+        t = self.k_cache if which == "k" else self.v_cache
+        return t.view(s.n_layers, self.max_requests, s.n_kv_heads,
+                      self.max_kv_len, s.head_dim)
+
+    def prefill_kv(self, req, k, v):
+        """k, v: [L, Hkv, n, D] bf16 device tensors (contiguous)."""
+        n = k.shape[2]
+        _check(lib().dg_prefill_kv(self.ctx, req, n, None, _ptr(k), _ptr(v)),
+               self.ctx)
+
+    def set_kv_len(self, req, n):
+        _check(lib().dg_set_kv_len(self.ctx, req, n), self.ctx)
+
+    def kv_len(self, req):
+        return lib().dg_kv_len(self.ctx, req)
+
+    @staticmethod
+    def _batch(req, tokens, committed, step):
+        reqs = _i32_array(req)
+        b = CanvasBatch(len(req), reqs, tokens.data_ptr(),
+                        committed.data_ptr(), step.data_ptr())
+        b._keep = reqs
+        return b
+
+    def denoise_step(self, req, tokens, committed, step, entropy, lse, argmax,
+                     logits=None, capture=None):
+        b = self._batch(req, tokens, committed, step)
+        cap = None
+        if capture is not None:
+            cap = Capture(*[(capture[k].data_ptr() if capture.get(k)
+                             is not None else None) for k in (
+                "attn_out", "moe_out", "route_idx", "route_w",
+                "router_logits", "final_xhat")])
+        out = StepOut(entropy.data_ptr(), lse.data_ptr(), argmax.data_ptr(),
+                      None if logits is None else logits.data_ptr(),
+                      ctypes.pointer(cap) if cap is not None else None)
+        _check(lib().dg_denoise_step(self.ctx, ctypes.byref(b),
+                                     ctypes.byref(out)), self.ctx)
+
+    def eb_select(self, req, tokens, committed, step, entropy, argmax, gamma,
+                  step_cap, refine, n_new, done):
+        b = self._batch(req, tokens, committed, step)
+        _check(lib().dg_eb_select(self.ctx, ctypes.byref(b), _ptr(entropy),
+                                  _ptr(argmax), _ptr(gamma), step_cap,
+                                  int(refine), _ptr(n_new), _ptr(done)),
+               self.ctx)
+
+    def commit_block(self, req, tokens, committed, step):
+        b = self._batch(req, tokens, committed, step)
+        _check(lib().dg_commit_block(self.ctx, ctypes.byref(b)), self.ctx)
+
+
+# ------------------------------------------------------------------ dg_ops.h
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def op_rmsnorm(x, g, eps, out):
+    _check(lib().dg_op_rmsnorm(_ptr(x), x.shape[0], x.shape[1], _ptr(g),
+                               eps, _ptr(out), _stream()))
+
+
+def op_linear(x, w, out, mode):
+    _check(lib().dg_op_linear(_ptr(x), x.shape[0], x.shape[1], _ptr(w),
+                              w.shape[0], mode, _ptr(out), _stream()))
+
+
+def op_canvas_attention(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,
+                        k_cache, v_cache, max_requests, max_kv_len, req,
+                        prefix_len, causal, kv_splits, out):
+    L = lib()
+    nb = L.dg_op_attention_workspace_bytes(n, canvas_len, n_q_heads,
+                                           n_kv_heads, head_dim, kv_splits)
+    ws = _ws(nb, qkv.device)
+    _check(L.dg_op_canvas_attention(
+        _ptr(qkv), n, canvas_len, n_q_heads, n_kv_heads, head_dim,
+        _ptr(k_cache), _ptr(v_cache), max_requests, max_kv_len,
+        _i32_array(req), _i32_array(prefix_len), int(causal), kv_splits,
+        _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def op_router_topk(logits, top_k, idx, w):
+    _check(lib().dg_op_router_topk(_ptr(logits), logits.shape[0],
+                                   logits.shape[1], top_k, _ptr(idx), _ptr(w),
+                                   _stream()))
+
+
+def op_moe(shape, lw, xhat, y, route_idx=None, route_w=None, counts=None):
+    L = lib()
+    desc = model_desc(shape)
+    w = layer_weights(lw)
+    nb = L.dg_op_moe_workspace_bytes(ctypes.byref(desc), xhat.shape[0])
+    ws = _ws(nb, xhat.device)
+    _check(L.dg_op_moe(ctypes.byref(desc), ctypes.byref(w), _ptr(xhat),
+                       xhat.shape[0], _ptr(y), _ptr(route_idx), _ptr(route_w),
+                       _ptr(counts), _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def op_lmhead_entropy(xhat, embed, entropy, lse, argmax, logits=None):
+    L = lib()
+    nb = L.dg_op_lmhead_workspace_bytes(xhat.shape[0], embed.shape[0])
+    ws = _ws(nb, xhat.device)
+    _check(L.dg_op_lmhead_entropy(_ptr(xhat), xhat.shape[0], xhat.shape[1],
+                                  _ptr(embed), embed.shape[0], _ptr(entropy),
+                                  _ptr(lse), _ptr(argmax), _ptr(logits),
+                                  _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def op_eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,
+                 refine, n_new, done):
+    _check(lib().dg_op_eb_select(entropy.shape[0], _ptr(entropy),
+                                 _ptr(argmax), _ptr(committed), _ptr(tokens),
+                                 _ptr(step), _ptr(gamma), step_cap,
+                                 int(refine), _ptr(n_new), _ptr(done),
+                                 _stream()))
+
+
+def op_kv_append(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,
+                 k_cache, v_cache, max_requests, max_kv_len, req, row0):
+    _check(lib().dg_op_kv_append(_ptr(qkv), n, canvas_len, n_q_heads,
+                                 n_kv_heads, head_dim, _ptr(k_cache),
+                                 _ptr(v_cache), max_requests, max_kv_len,
+                                 _i32_array(req), _i32_array(row0),
+                                 _stream()))

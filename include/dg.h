@@ -1,0 +1,203 @@
+/*
+ * libdg -- one block-diffusion denoising step over a 256-token canvas on
+ * MI355X (gfx950), behind a plain C ABI.
+ *
+ * The calls follow the generation pipeline of the "DiffusionGemma Technical
+ * Report" (write-up of the paper), Figure 4:
+ *   1. context encoding: the prompt's K/V fill a per-request cache
+ *      (dg_prefill_kv);
+ *   2. denoising loop: a noisy canvas is refined by the decoder, which
+ *      attends bidirectionally over the canvas and to the cache
+ *      (dg_denoise_step), and the entropy-bounded sampler with adaptive
+ *      stopping commits confident positions (dg_eb_select; write-up "What
+ *      they did", model card "Benchmark Results");
+ *   3. encode & append: the finished canvas is encoded causally and its K/V
+ *      appended to the cache (dg_commit_block; write-up Figure 4 stage 3,
+ *      model card "Model Overview").
+ *
+ * Conventions for every function in this header and in dg_ops.h:
+ *   - Pointers are DEVICE pointers unless marked (host).
+ *   - The caller owns every buffer (weights, caches, workspace, canvas state,
+ *     outputs).  The library never allocates or frees device memory; a
+ *     context owns host metadata only.
+ *   - Calls enqueue work on the context's (or the given) HIP stream and
+ *     return without synchronising; results are valid after that stream is
+ *     synchronised.  A context is single-stream and not thread-safe.
+ *   - Arguments, shapes and capacities are validated on the host before any
+ *     launch; a failed validation returns an error status and enqueues
+ *     nothing.  A failed launch returns DG_ERR_HIP.  Faults inside kernels
+ *     surface at the caller's next synchronisation.  Nothing aborts, exits or
+ *     throws across the ABI.
+ *   - bf16 means IEEE bfloat16 stored as 16-bit words; e4m3 means OCP FP8
+ *     E4M3 ("fn": no infinities, max 448) bytes.
+ *   - Matrices are row-major [rows, cols] with cols contiguous; a weight
+ *     matrix is [out, in] so that y = W x.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_CANVAS 256     /* positions per canvas (write-up: 256-token blocks) */
+#define DG_MAX_BATCH 64   /* canvases per call */
+
+typedef struct dg_ctx dg_ctx;
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1, /* null pointer, bad enum, out-of-range scalar */
+  DG_ERR_SHAPE = 2,       /* model shape the kernels do not support */
+  DG_ERR_CAPACITY = 3,    /* KV cache, batch or workspace too small */
+  DG_ERR_STATE = 4,       /* request slot in the wrong state */
+  DG_ERR_HIP = 5,         /* a HIP runtime call or launch failed */
+  DG_ERR_UNSUPPORTED = 6
+} dg_status;
+
+typedef enum { DG_BF16 = 0, DG_FP8_E4M3 = 1 } dg_dtype;
+
+/* Model shape.  Mixture-of-experts transformer (write-up Table 1: 8 of 128
+ * experts active, 262k vocabulary; the layer internals are the reading the
+ * library implements: pre-norm RMSNorm blocks, grouped-query attention
+ * without positional encoding, top-k softmax router over SwiGLU experts,
+ * LM head tied to the embedding).
+ * Supported: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
+ * hidden, n_q_heads*head_dim and expert_ffn multiples of 64;
+ * n_experts <= 256; 1 <= top_k <= min(n_experts, 16); vocab >= 1. */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t expert_ffn;
+  int32_t vocab;
+  float rms_eps;          /* e.g. 1e-6 */
+  int32_t expert_dtype;   /* dg_dtype of w_gate_up / w_down */
+} dg_model_desc;
+
+/* Weights of one layer (all device pointers, read-only, must outlive the
+ * context). */
+typedef struct {
+  const float* attn_norm;     /* [H] fp32 RMSNorm gain before attention */
+  const void* w_qkv;          /* [(Hq + 2 Hkv) D, H] bf16: Q rows, K rows, V rows */
+  const void* w_o;            /* [H, Hq D] bf16 */
+  const float* ffn_norm;      /* [H] fp32 RMSNorm gain before the MoE */
+  const void* w_router;       /* [E, H] bf16 */
+  const void* w_gate_up;      /* [E, 2F, H] bf16 or e4m3: F gate rows, then F up rows */
+  const void* w_down;         /* [E, H, F] bf16 or e4m3 */
+  const float* gate_up_scale; /* [E, 2F] fp32 per-row scale (e4m3 only, else NULL) */
+  const float* down_scale;    /* [E, H] fp32 per-row scale (e4m3 only, else NULL) */
+} dg_layer_weights;
+
+typedef struct {
+  const void* embed;               /* [V, H] bf16; also the tied LM head */
+  const float* final_norm;         /* [H] fp32 */
+  const dg_layer_weights* layers;  /* (host) array of n_layers entries, copied */
+} dg_weights;
+
+/* Bytes of device workspace a context needs for up to max_canvases canvases
+ * per call (0 if the shape is unsupported). */
+size_t dg_workspace_bytes(const dg_model_desc* desc, int32_t max_canvases);
+
+/* Bytes of ONE of the two caches (K or V): layout
+ * [n_layers][max_requests][n_kv_heads][max_kv_len][head_dim] bf16. */
+size_t dg_kv_cache_bytes(const dg_model_desc* desc, int32_t max_requests,
+                         int32_t max_kv_len);
+
+/* Create a context over caller-owned memory.  k_cache / v_cache hold
+ * dg_kv_cache_bytes each; workspace holds dg_workspace_bytes(desc,
+ * max_canvases).  stream is a hipStream_t (NULL: the null stream).  All
+ * request slots start with kv_len 0.  On error *out is set to NULL. */
+dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
+                    int32_t max_requests, int32_t max_kv_len,
+                    int32_t max_canvases, void* k_cache, void* v_cache,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    dg_ctx** out);
+void dg_destroy(dg_ctx* ctx); /* frees host state only; NULL is a no-op */
+
+/* Stage 1 (write-up Figure 4, "context encoding").  Install mode: k and v
+ * are [n_layers][n_kv_heads][n][head_dim] bf16 (already encoded prompt K/V)
+ * and are copied into cache rows [0, n) of slot req; tokens must be NULL.
+ * The slot's kv_len becomes n.  Token mode (tokens non-NULL, k = v = NULL)
+ * is not provided: it returns DG_ERR_UNSUPPORTED. */
+dg_status dg_prefill_kv(dg_ctx* ctx, int32_t req, int32_t n,
+                        const int32_t* tokens, const void* k, const void* v);
+
+/* Canvas state of a batch of n canvases, one per request slot. */
+typedef struct {
+  int32_t n;               /* 1..max_canvases */
+  const int32_t* req;      /* (host) [n] request slot of each canvas, distinct */
+  int32_t* tokens;         /* [n, 256] int32 current canvas tokens in [0, V),
+                              in/out (ids outside are clamped when embedded) */
+  uint8_t* committed;      /* [n, 256] 1 = committed (frozen), in/out */
+  int32_t* step;           /* [n] denoise steps taken in this block, in/out */
+} dg_canvas_batch;
+
+/* Optional per-layer captures for parity checks (each NULL to skip). */
+typedef struct {
+  void* attn_out;       /* [L, n*256, Hq*D] bf16 attention output before W_o */
+  float* moe_out;       /* [L, n*256, H] fp32 MoE mixture added to the residual */
+  int32_t* route_idx;   /* [L, n*256, top_k] selected experts, rank order */
+  float* route_w;       /* [L, n*256, top_k] gate weights */
+  float* router_logits; /* [L, n*256, E] fp32 */
+  float* final_xhat;    /* [n*256, H] fp32 copy of the bf16 final-norm rows,
+                           compacted in the order of the uncommitted rows */
+} dg_capture;
+
+typedef struct {
+  float* entropy;        /* [n, 256] nats, >= 0 (uncommitted positions only) */
+  float* lse;            /* [n, 256] log-sum-exp of the logits */
+  int32_t* argmax;       /* [n, 256] lowest vocab id of the largest logit */
+  float* logits;         /* NULL or [n*256, V] fp32 (uncommitted rows only) */
+  dg_capture* capture;   /* (host) NULL or capture pointers */
+} dg_step_out;
+
+/* Stage 2 forward (write-up Figure 4, "denoising loop"): embed the n
+ * canvases, run every layer (canvas attention over prefix + canvas, MoE),
+ * final RMSNorm of the uncommitted rows, tied LM head with a fused
+ * log-sum-exp / entropy / argmax epilogue.  Values at committed positions of
+ * the outputs are left untouched. */
+dg_status dg_denoise_step(dg_ctx* ctx, const dg_canvas_batch* batch,
+                          const dg_step_out* out);
+
+/* Entropy-bounded selection (write-up "What they did"; model card "Entropy
+ * Bound (EB) sampler"), per canvas over its uncommitted positions U: sort by
+ * (entropy, position) ascending; n* = the length of the longest prefix whose
+ * fp64 running entropy sum is <= gamma[b], at least 1; all of U when
+ * step[b] + 1 >= step_cap (the step budget).  The first n* positions are
+ * committed with token = argmax; with refine != 0 the other positions of U
+ * take their argmax token too, otherwise they keep theirs.  step[b] += 1,
+ * n_new[b] = n*, done[b] = (U now empty).  A canvas whose U is already empty
+ * is left unchanged with n_new = 0, done = 1.
+ * entropy / argmax: [n, 256] as written by dg_denoise_step; gamma: [n] fp32
+ * (device); step_cap in 1..65535; n_new, done: [n] device outputs. */
+dg_status dg_eb_select(dg_ctx* ctx, const dg_canvas_batch* batch,
+                       const float* entropy, const int32_t* argmax,
+                       const float* gamma, int32_t step_cap, int32_t refine,
+                       int32_t* n_new, uint8_t* done);
+
+/* Stage 3 (write-up Figure 4, "encode & append"): run the canvas tokens
+ * causally (position i sees the cache and canvas positions <= i) through the
+ * layers and write each layer's K/V of the 256 positions into cache rows
+ * [kv_len, kv_len + 256) of each canvas's slot; kv_len += 256.
+ * DG_ERR_CAPACITY if kv_len + 256 > max_kv_len. */
+dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
+
+dg_status dg_set_kv_len(dg_ctx* ctx, int32_t req, int32_t len);
+int32_t dg_kv_len(const dg_ctx* ctx, int32_t req); /* -1 on a bad slot */
+
+const char* dg_status_string(dg_status s);
+const char* dg_last_error(const dg_ctx* ctx); /* "" if none; NULL ctx: last
+                                                  global error */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

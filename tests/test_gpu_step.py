@@ -1,0 +1,268 @@
+"""Step-level parity through the context API (dg_prefill_kv, dg_denoise_step,
+dg_eb_select, dg_commit_block) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_discrete_diffusion_tok_amd import dg, synth
+from gpu_common import (DEV, MARGIN, TOL, log, np32, oshape, rel_err,
+                        routing_margin, step_outputs, to_dev, top2_margin)
+
+pytestmark = pytest.mark.gpu
+
+TINY_WL = synth.WORKLOADS["tiny_l1_h256_p512"]
+GEMMA_WL = synth.WORKLOADS["moe_layer_h2048_v262k_p2048"]
+
+
+def _setup(shape, prefix_lens, max_kv, gain_std=0.1, seed=0, device="cpu"):
+    """Weights, engine with prefilled slots 0..n-1, host copies for the
+    oracle."""
+    w = synth.make_weights(shape, seed=seed, gain_std=gain_std, device=device)
+    wd = to_dev(w) if device == "cpu" else w
+    n = len(prefix_lens)
+    eng = dg.Engine(shape, wd, max_requests=n, max_kv_len=max_kv,
+                    max_canvases=n)
+    prefix = []
+    for r, p in enumerate(prefix_lens):
+        k, v = synth.make_prefix_kv(shape, p, r, seed=seed, device=device)
+        if p > 0:
+            eng.prefill_kv(r, k.to(DEV).contiguous(), v.to(DEV).contiguous())
+        else:
+            eng.set_kv_len(r, 0)
+        prefix.append((np32(k), np32(v)))
+    return eng, synth.to_numpy_weights(w), prefix
+
+
+def _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, n):
+    """Oracle step in mirror mode vs the GPU outputs; decisions compared
+    where the oracle's margin is at least MARGIN."""
+    cap_o = []
+    ref = oracle.denoise_step(oshape(shape), wn, cv["tokens"].numpy(),
+                              cv["committed"].numpy(), prefix, mirror=True,
+                              want_logits=logits is not None, capture=cap_o)
+    rows = ref["rows"]
+    T = n * 256
+    # routing agreement per layer; rows after a clear-margin flip would fail
+    flipped = np.zeros(T, bool)
+    for li, c in enumerate(cap_o):
+        g_idx = cap["route_idx"][li].cpu().numpy()
+        diff = np.any(g_idx != c["idx"], axis=1)
+        marg = routing_margin(c["router_logits"], shape.top_k)
+        assert np.all(marg[diff] < MARGIN), f"layer {li}: routing differs"
+        flipped |= diff
+        e_att = rel_err(np32(cap["attn_out"][li]), c["attn"])
+        e_moe = rel_err(cap["moe_out"][li].cpu().numpy()[~flipped],
+                        c["moe"][~flipped])
+        log(f"  layer {li}: attn rel err {e_att:.2e}, moe rel err {e_moe:.2e},"
+            f" {int(diff.sum())} low-margin routing flips")
+        assert e_att < TOL and e_moe < TOL
+    ok_rows = ~flipped.reshape(-1)[rows] if flipped.any() else np.ones(len(rows), bool)
+    g_ent = ent.cpu().numpy().reshape(-1)[rows]
+    g_lse = lse.cpu().numpy().reshape(-1)[rows]
+    g_am = am.cpu().numpy().reshape(-1)[rows]
+    o_ent = ref["entropy"].reshape(-1)[rows]
+    o_lse = ref["lse"].reshape(-1)[rows]
+    o_am = ref["argmax"].reshape(-1)[rows]
+    e_ent = rel_err(g_ent[ok_rows], o_ent[ok_rows])
+    e_lse = rel_err(g_lse[ok_rows], o_lse[ok_rows])
+    msg = f"  entropy rel err {e_ent:.2e}, lse rel err {e_lse:.2e}"
+    if logits is not None:
+        z = ref["logits"]
+        e_z = rel_err(logits.cpu().numpy()[rows][ok_rows], z[ok_rows])
+        marg = top2_margin(z)
+        msg += f", logits rel err {e_z:.2e}"
+        assert e_z < TOL
+        bad = (g_am != o_am) & (marg >= MARGIN) & ok_rows
+        low = int(((g_am != o_am) & (marg < MARGIN)).sum())
+        msg += f", argmax low-margin diffs {low}"
+        assert not bad.any(), "argmax differs at a clear margin"
+    log(msg)
+    assert e_ent < TOL and e_lse < TOL
+    return ref
+
+
+def _capture(shape, n, L):
+    T = n * 256
+    return {
+        "attn_out": torch.zeros((L, T, shape.n_q_heads * shape.head_dim),
+                                dtype=torch.bfloat16, device=DEV),
+        "moe_out": torch.zeros((L, T, shape.hidden), dtype=torch.float32,
+                               device=DEV),
+        "route_idx": torch.zeros((L, T, shape.top_k), dtype=torch.int32,
+                                 device=DEV),
+        "route_w": torch.zeros((L, T, shape.top_k), dtype=torch.float32,
+                               device=DEV),
+    }
+
+
+@pytest.mark.parametrize("uncommitted", [256, 128])
+def test_denoise_step_tiny_elementwise(uncommitted):
+    shape = TINY_WL.shape
+    log(f"tiny step, {uncommitted} uncommitted")
+    eng, wn, prefix = _setup(shape, [512], 1024)
+    cv = synth.make_canvas(shape, 1, uncommitted, seed=5)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    ent, lse, am, logits = step_outputs(1, shape.vocab)
+    cap = _capture(shape, 1, 1)
+    eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
+    torch.cuda.synchronize()
+    _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, 1)
+    # committed positions are left untouched
+    committed = cv["committed"].numpy()[0] == 1
+    assert np.all(np.isnan(ent.cpu().numpy()[0, committed]))
+
+
+def test_denoise_step_two_layers_three_canvases():
+    shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096)
+    log("two layers, three canvases with prefixes 512 / 0 / 77")
+    eng, wn, prefix = _setup(shape, [512, 0, 77], 2048, seed=2)
+    cv = synth.make_canvas(shape, 3, 180, seed=6)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    ent, lse, am, logits = step_outputs(3, shape.vocab)
+    cap = _capture(shape, 3, 2)
+    eng.denoise_step([0, 1, 2], tok, com, step, ent, lse, am, logits, cap)
+    torch.cuda.synchronize()
+    _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, 3)
+    # batch invariance: canvas 1 alone in slot 1 gives the same decisions
+    ent1, lse1, am1, _ = step_outputs(1)
+    eng.denoise_step([1], tok[1:2].contiguous(), com[1:2].contiguous(),
+                     step[1:2].contiguous(), ent1, lse1, am1)
+    torch.cuda.synchronize()
+    rows = cv["committed"].numpy()[1] == 0
+    assert rel_err(ent1.cpu().numpy()[0, rows], ent.cpu().numpy()[1, rows]) < 1e-4
+    assert np.mean(am1.cpu().numpy()[0, rows] == am.cpu().numpy()[1, rows]) > 0.99
+
+
+def test_denoise_step_is_deterministic():
+    shape = TINY_WL.shape
+    eng, _, _ = _setup(shape, [512], 1024)
+    cv = synth.make_canvas(shape, 1, 256, seed=8)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    outs = []
+    for _ in range(3):
+        ent, lse, am, logits = step_outputs(1, shape.vocab)
+        eng.denoise_step([0], tok, com, step, ent, lse, am, logits)
+        torch.cuda.synchronize()
+        outs.append((ent.cpu(), lse.cpu(), am.cpu(), logits.cpu()))
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert torch.equal(a, b)
+
+
+def test_commit_block_two_layers_against_oracle():
+    shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096)
+    log("commit: two layers, prefixes 300 / 512")
+    eng, wn, prefix = _setup(shape, [300, 512], 2048, seed=4)
+    cv = synth.make_canvas(shape, 2, 0, seed=9)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    eng.commit_block([0, 1], tok, com, step)
+    torch.cuda.synchronize()
+    assert eng.kv_len(0) == 556 and eng.kv_len(1) == 768
+    ref = oracle.commit_block(oshape(shape), wn, cv["tokens"].numpy(), prefix,
+                              mirror=True)
+    kc, vc = eng.cache_view("k"), eng.cache_view("v")
+    for b, p in enumerate((300, 512)):
+        for li in range(2):
+            gk = np32(kc[li, b, :, p:p + 256])
+            gv = np32(vc[li, b, :, p:p + 256])
+            ek = rel_err(gk, ref[b][0][li])
+            ev = rel_err(gv, ref[b][1][li])
+            log(f"  canvas {b} layer {li}: K rel err {ek:.2e}, V {ev:.2e}")
+            assert ek < TOL and ev < TOL
+        # the prefix rows are untouched
+        assert np.array_equal(np32(kc[0, b, :, :p]), prefix[b][0][0])
+
+
+def test_eb_decode_tiny_block_to_completion():
+    """Tiny workload: gamma 0.5, EB until every position is committed.  GPU
+    and oracle run the whole block independently from the same start; the
+    committed set of every step is compared until the first step whose EB
+    decision the oracle calls low-margin (after which the trajectories may
+    legitimately part)."""
+    wl = TINY_WL
+    shape = wl.shape
+    eng, wn, prefix = _setup(shape, [wl.prefix_len], 1024)
+    cv = synth.make_canvas(shape, 1, 256, seed=1)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    gamma = torch.full((1,), wl.gamma, dtype=torch.float32, device=DEV)
+    n_new = torch.zeros(1, dtype=torch.int32, device=DEV)
+    done = torch.zeros(1, dtype=torch.uint8, device=DEV)
+    ent, lse, am, _ = step_outputs(1)
+    o_tok = cv["tokens"].numpy().astype(np.int64)
+    o_com = cv["committed"].numpy()
+    o_step = np.zeros(1, np.int64)
+    agree_until = None
+    steps = 0
+    osh = oshape(shape)
+    while True:
+        eng.denoise_step([0], tok, com, step, ent, lse, am)
+        eng.eb_select([0], tok, com, step, ent, am, gamma, wl.step_cap, True,
+                      n_new, done)
+        g_done = int(done.item())
+        steps += 1
+        if agree_until is None:
+            ref = oracle.denoise_step(osh, wn, o_tok, o_com, prefix,
+                                      mirror=True)
+            o_ent = ref["entropy"].astype(np.float32)
+            unc = np.nonzero(o_com[0] == 0)[0]
+            hs = np.sort(o_ent[0, unc])
+            eb_margin = hs[1] - hs[0] if len(hs) > 1 else np.inf
+            o_com, o_tok, o_step, o_new, o_done = oracle.eb_select(
+                o_ent, ref["argmax"], o_com, o_tok, o_step,
+                np.array([wl.gamma], np.float32), wl.step_cap)
+            same = np.array_equal(com.cpu().numpy(), o_com)
+            if not same:
+                assert eb_margin < MARGIN, f"step {steps}: EB set differs"
+                agree_until = steps
+        assert int(n_new.item()) == 1  # every entropy exceeds gamma = 0.5
+        if g_done:
+            break
+        assert steps < 256
+    log(f"  block finished in {steps} steps; oracle agreed "
+        f"{'throughout' if agree_until is None else f'until step {agree_until}'}")
+    assert steps == 256
+    assert int(step.item()) == 256 and bool(com.cpu().numpy().all())
+
+
+def test_full_size_layer_step_elementwise():
+    """One 2048-hidden / 128-expert layer plus the 262144-vocab LM head,
+    128 uncommitted positions, prefix 2048: every output of the step
+    against the oracle, then one EB selection with gamma 1."""
+    wl = GEMMA_WL
+    shape = wl.shape
+    log("full-size layer step")
+    eng, wn, prefix = _setup(shape, [wl.prefix_len], 4096, gain_std=0.0,
+                             device=DEV)
+    cv = synth.make_canvas(shape, 1, wl.uncommitted, seed=0)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    ent, lse, am, logits = step_outputs(1, shape.vocab)
+    cap = _capture(shape, 1, 1)
+    eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
+    torch.cuda.synchronize()
+    log("  gpu done; oracle running")
+    ref = _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, 1)
+    gamma = torch.full((1,), wl.gamma, dtype=torch.float32, device=DEV)
+    n_new = torch.zeros(1, dtype=torch.int32, device=DEV)
+    done = torch.zeros(1, dtype=torch.uint8, device=DEV)
+    eng.eb_select([0], tok, com, step, ent, am, gamma, wl.step_cap, True,
+                  n_new, done)
+    torch.cuda.synchronize()
+    # the oracle's own selection from its own entropies
+    o_ent = ref["entropy"].astype(np.float32)
+    o = oracle.eb_select(o_ent, ref["argmax"], cv["committed"].numpy(),
+                         cv["tokens"].numpy(), cv["step"].numpy(),
+                         np.array([wl.gamma], np.float32), wl.step_cap)
+    assert int(n_new.item()) == o[3][0] == 1
+    unc = np.nonzero(cv["committed"].numpy()[0] == 0)[0]
+    hs = np.sort(o_ent[0, unc])
+    if hs[1] - hs[0] >= MARGIN:
+        np.testing.assert_array_equal(com.cpu().numpy(), o[0])
+    else:
+        log(f"  EB choice is low-margin ({hs[1] - hs[0]:.2e}); not compared")
