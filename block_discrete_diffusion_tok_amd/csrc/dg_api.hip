@@ -16,6 +16,62 @@ using namespace dg;
 // ------------------------------------------------------------------ errors
 static thread_local std::string g_last_error;
 
+// ------------------------------------------------------------------ timing
+// Optional per-kernel timing: hipEvents recorded on the context's stream
+// around every launch, accumulated per kernel kind when read back.
+namespace {
+const char* const kKindNames[DG_PROF_KINDS] = {
+    "embed",      "rmsnorm",    "qkv_proj", "attention", "o_proj",
+    "router",     "topk",       "permute",  "moe_gate_up", "moe_down",
+    "unpermute",  "compact",    "lm_head",  "lm_merge",  "eb_select",
+    "kv_append",  "kv_install"};
+constexpr size_t kMaxEvents = 1 << 20;
+
+struct Profiler {
+  bool on = false;
+  bool overflow = false;
+  hipStream_t s = nullptr;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, size_t>> marks;
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+  ~Profiler() {
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+struct ProfScope {
+  Profiler* p;
+  int kind;
+  size_t idx = 0;
+  ProfScope(Profiler* prof, int k) : p(nullptr), kind(k) {
+    if (prof && prof->on && prof->used + 2 <= kMaxEvents) {
+      p = prof;
+      idx = p->used;
+      hipEvent_t e = p->next();
+      if (!e) { p = nullptr; return; }
+      (void)hipEventRecord(e, p->s);
+    } else if (prof && prof->on) {
+      prof->overflow = true;
+    }
+  }
+  ~ProfScope() {
+    if (!p) return;
+    hipEvent_t e = p->next();
+    if (!e) return;
+    (void)hipEventRecord(e, p->s);
+    p->marks.push_back({kind, idx});
+  }
+};
+}  // namespace
+
 struct dg_ctx {
   dg_model_desc d;
   const uint16_t* embed;
@@ -29,6 +85,7 @@ struct dg_ctx {
   hipStream_t stream;
   std::vector<int32_t> kv_len;
   std::string last_error;
+  Profiler prof;
   // workspace carve-up
   float* x;
   uint16_t* xh;
@@ -64,6 +121,13 @@ static dg_status fail(dg_ctx* c, dg_status s, const std::string& msg) {
     if (e_ != hipSuccess)                                                    \
       return fail(ctx, DG_ERR_HIP, std::string(#expr ": ") +                 \
                                        hipGetErrorString(e_));               \
+  } while (0)
+
+// HIPCHK plus a timing scope of the given kernel kind.
+#define KRUN(ctx, kind, expr)                                                \
+  do {                                                                       \
+    ProfScope ps_(&(ctx)->prof, kind);                                       \
+    HIPCHK(ctx, expr);                                                       \
   } while (0)
 
 // ------------------------------------------------------------------ layout
@@ -235,18 +299,28 @@ int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi);
 // into moe_out (if moe_out).
 hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
                    const uint16_t* xh, int T, const MoeBufs& b, float* x,
-                   float* moe_out, int32_t* counts, hipStream_t s) {
+                   float* moe_out, int32_t* counts, hipStream_t s,
+                   Profiler* prof = nullptr) {
   const int H = d.hidden, E = d.n_experts, k = d.top_k, F = d.expert_ffn;
   const bool w8 = d.expert_dtype == DG_FP8_E4M3;
   const int pairs = T * k;
   hipError_t e;
   GemmArgs r = gemm_dense(xh, T, H, w.w_router, E, b.rlogits, E);
-  if ((e = launch_gemm(EPI_STORE_F32, false, r, grid_m_dense(T, EPI_STORE_F32), s)) != hipSuccess) return e;
-  if ((e = launch_topk(b.rlogits, T, E, k, b.ridx, b.rw, s)) != hipSuccess) return e;
-  if ((e = launch_permute(b.ridx, pairs, E, kGroupBM, b.chunk_counts,
-                          b.local_rank, b.chunk_base, b.offsets,
-                          b.tile_offsets, counts, b.perm, s)) != hipSuccess)
-    return e;
+  {
+    ProfScope ps(prof, 5);
+    if ((e = launch_gemm(EPI_STORE_F32, false, r, grid_m_dense(T, EPI_STORE_F32), s)) != hipSuccess) return e;
+  }
+  {
+    ProfScope ps(prof, 6);
+    if ((e = launch_topk(b.rlogits, T, E, k, b.ridx, b.rw, s)) != hipSuccess) return e;
+  }
+  {
+    ProfScope ps(prof, 7);
+    if ((e = launch_permute(b.ridx, pairs, E, kGroupBM, b.chunk_counts,
+                            b.local_rank, b.chunk_base, b.offsets,
+                            b.tile_offsets, counts, b.perm, s)) != hipSuccess)
+      return e;
+  }
   const int grid_m = (pairs + kGroupBM - 1) / kGroupBM + std::min(E, pairs);
   GemmArgs gu = gemm_dense(xh, pairs, H, w.w_gate_up, 2 * F, b.act, F);
   gu.a_map = b.perm;
@@ -258,7 +332,10 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   gu.group_offsets = b.offsets;
   gu.tile_offsets = b.tile_offsets;
   gu.ffn = F;
-  if ((e = launch_gemm(EPI_SWIGLU, w8, gu, grid_m, s)) != hipSuccess) return e;
+  {
+    ProfScope ps(prof, 8);
+    if ((e = launch_gemm(EPI_SWIGLU, w8, gu, grid_m, s)) != hipSuccess) return e;
+  }
   GemmArgs dn = gemm_dense(b.act, pairs, F, w.w_down, H, b.y, H);
   dn.b_group_stride = (long long)H * F;
   dn.b_scale = w.down_scale;
@@ -268,7 +345,11 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   dn.tile_offsets = b.tile_offsets;
   dn.c_map = b.perm;
   dn.row_scale = b.rw;
-  if ((e = launch_gemm(EPI_DOWN, w8, dn, grid_m, s)) != hipSuccess) return e;
+  {
+    ProfScope ps(prof, 9);
+    if ((e = launch_gemm(EPI_DOWN, w8, dn, grid_m, s)) != hipSuccess) return e;
+  }
+  ProfScope ps10(prof, 10);
   return launch_unpermute(b.y, T, k, H, x, moe_out, s);
 }
 
@@ -320,14 +401,14 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   const long long req_stride = (long long)Hkv * head_stride;
   const long long layer_stride = (long long)c->max_requests * req_stride;
   hipStream_t s = c->stream;
-  HIPCHK(c, launch_rmsnorm(c->x, T, H, w.attn_norm, d.rms_eps, c->xh, nullptr,
+  KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.attn_norm, d.rms_eps, c->xh, nullptr,
                            nullptr, nullptr, s));
   GemmArgs g = gemm_dense(c->xh, T, H, w.w_qkv, qkvN, c->qkv, qkvN);
-  HIPCHK(c, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
+  KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
   uint16_t* kc = c->k_cache + l * layer_stride;
   uint16_t* vc = c->v_cache + l * layer_stride;
   if (commit) {
-    HIPCHK(c, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
+    KRUN(c, 15, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
                                DG_CANVAS, Hkv, D, kc, vc, req_stride,
                                head_stride, req, plen, s));
     if (l == d.n_layers - 1) return DG_OK;
@@ -354,17 +435,18 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   aa.out = c->attn;
   aa.opart = c->opart;
   aa.lpart = c->lpart;
-  HIPCHK(c, launch_attention(aa, s));
+  KRUN(c, 3, launch_attention(aa, s));
   if (cap && cap->attn_out)
     HIPCHK(c, hipMemcpyAsync((char*)cap->attn_out + (size_t)l * T * Hq * D * 2,
                              c->attn, (size_t)T * Hq * D * 2,
                              hipMemcpyDeviceToDevice, s));
   GemmArgs o = gemm_dense(c->attn, T, Hq * D, w.w_o, H, c->x, H);
-  HIPCHK(c, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
-  HIPCHK(c, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
+  KRUN(c, 4, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
+  KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
                            nullptr, nullptr, s));
   float* moe_out = (cap && cap->moe_out) ? cap->moe_out + (size_t)l * T * H : nullptr;
-  HIPCHK(c, run_moe(d, w, c->xh, T, ctx_moe_bufs(c), c->x, moe_out, nullptr, s));
+  HIPCHK(c, run_moe(d, w, c->xh, T, ctx_moe_bufs(c), c->x, moe_out, nullptr, s,
+                    &c->prof));
   if (cap) {
     const size_t tk = (size_t)T * d.top_k;
     if (cap->route_idx)
@@ -459,12 +541,48 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   c->ws_bytes = workspace_bytes;
   c->stream = (hipStream_t)stream;
   c->kv_len.assign(max_requests, 0);
+  c->prof.s = c->stream;
   ctx_layout(*desc, max_canvases, c);
   *out = c;
   return DG_OK;
 }
 
 void dg_destroy(dg_ctx* c) { delete c; }
+
+dg_status dg_profile_enable(dg_ctx* c, int32_t on) {
+  if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  c->prof.on = on != 0;
+  return DG_OK;
+}
+
+int32_t dg_profile_read(dg_ctx* c, float* ms, int32_t* launches) {
+  if (!c || !ms || !launches) return -1;
+  for (int k = 0; k < DG_PROF_KINDS; ++k) {
+    ms[k] = 0.f;
+    launches[k] = 0;
+  }
+  Profiler& p = c->prof;
+  if (p.used > 0 && hipEventSynchronize(p.pool[p.used - 1]) != hipSuccess) {
+    fail(c, DG_ERR_HIP, "hipEventSynchronize failed in dg_profile_read");
+    return -1;
+  }
+  for (const auto& m : p.marks) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p.pool[m.second], p.pool[m.second + 1]) == hipSuccess) {
+      ms[m.first] += t;
+      launches[m.first] += 1;
+    }
+  }
+  const int32_t overflow = p.overflow ? 1 : 0;
+  p.used = 0;
+  p.marks.clear();
+  p.overflow = false;
+  return overflow;
+}
+
+const char* dg_profile_kind_name(int32_t kind) {
+  return (kind >= 0 && kind < DG_PROF_KINDS) ? kKindNames[kind] : "";
+}
 
 dg_status dg_set_kv_len(dg_ctx* c, int32_t req, int32_t len) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
@@ -500,10 +618,10 @@ dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
   const long long src_layer = (long long)d.n_kv_heads * n * d.head_dim;
   for (int l = 0; l < d.n_layers; ++l) {
     const long long dst = l * layer_stride + req * req_stride;
-    HIPCHK(c, launch_kv_install((const uint16_t*)k + l * src_layer,
+    KRUN(c, 16, launch_kv_install((const uint16_t*)k + l * src_layer,
                                 d.n_kv_heads, n, d.head_dim, c->k_cache + dst,
                                 head_stride, c->stream));
-    HIPCHK(c, launch_kv_install((const uint16_t*)v + l * src_layer,
+    KRUN(c, 16, launch_kv_install((const uint16_t*)v + l * src_layer,
                                 d.n_kv_heads, n, d.head_dim, c->v_cache + dst,
                                 head_stride, c->stream));
   }
@@ -526,14 +644,14 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     plen[b] = c->kv_len[req[b]];
   }
   hipStream_t s = c->stream;
-  HIPCHK(c, launch_embed(bt->tokens, T, c->embed, d.vocab, H, c->x, s));
+  KRUN(c, 0, launch_embed(bt->tokens, T, c->embed, d.vocab, H, c->x, s));
   for (int l = 0; l < d.n_layers; ++l) {
     st = run_layer(c, l, n, req, plen, false, out->capture);
     if (st != DG_OK) return st;
   }
-  HIPCHK(c, launch_compact(bt->committed, T, c->row_map, c->m_dev, s));
+  KRUN(c, 11, launch_compact(bt->committed, T, c->row_map, c->m_dev, s));
   float* fx = (out->capture && out->capture->final_xhat) ? out->capture->final_xhat : nullptr;
-  HIPCHK(c, launch_rmsnorm(c->x, T, H, c->final_norm, d.rms_eps, c->xh,
+  KRUN(c, 1, launch_rmsnorm(c->x, T, H, c->final_norm, d.rms_eps, c->xh,
                            c->row_map, c->m_dev, fx, s));
   GemmArgs g = gemm_dense(c->xh, T, H, c->embed, d.vocab, nullptr, 0);
   g.M_dev = c->m_dev;
@@ -541,8 +659,8 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
   g.n_tiles = lm_tiles(d.vocab);
   g.logits = out->logits;
   g.row_map = c->row_map;
-  HIPCHK(c, launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(T, EPI_LMSTATS), s));
-  HIPCHK(c, launch_lm_merge(c->lm_part, g.n_tiles, c->m_dev, T, c->row_map,
+  KRUN(c, 12, launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(T, EPI_LMSTATS), s));
+  KRUN(c, 13, launch_lm_merge(c->lm_part, g.n_tiles, c->m_dev, T, c->row_map,
                             out->entropy, out->lse, out->argmax, s));
   return DG_OK;
 }
@@ -558,7 +676,7 @@ dg_status dg_eb_select(dg_ctx* c, const dg_canvas_batch* bt,
     return fail(c, DG_ERR_INVALID_ARG, "sampler pointers must not be NULL");
   if (step_cap < 1 || step_cap > 65535)
     return fail(c, DG_ERR_INVALID_ARG, "step_cap must be in 1..65535");
-  HIPCHK(c, launch_eb_select(bt->n, entropy, argmax, bt->committed, bt->tokens,
+  KRUN(c, 14, launch_eb_select(bt->n, entropy, argmax, bt->committed, bt->tokens,
                              bt->step, gamma, step_cap, refine, n_new, done,
                              c->stream));
   return DG_OK;
@@ -576,7 +694,7 @@ dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
     if (plen[b] + DG_CANVAS > c->max_kv_len)
       return fail(c, DG_ERR_CAPACITY, "KV cache full: kv_len + 256 > max_kv_len");
   }
-  HIPCHK(c, launch_embed(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x, c->stream));
+  KRUN(c, 0, launch_embed(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x, c->stream));
   for (int l = 0; l < c->d.n_layers; ++l) {
     st = run_layer(c, l, n, req, plen, true, nullptr);
     if (st != DG_OK) return st;

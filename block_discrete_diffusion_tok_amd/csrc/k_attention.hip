@@ -12,8 +12,13 @@
 // and the rescale of the output accumulator is a per-lane multiply.  P^T is
 // taken straight from the S^T accumulators as the B operand of O^T = V^T P^T;
 // V is stored in LDS as key quads ([key/4][d][4]) so that the matching A
-// operand is two 8-byte reads.  Splits write (O / l, log2 l + max) partials
-// that a second kernel merges with log-sum-exp weights.
+// operand is two 8-byte reads.  P enters the MFMA as two bf16 terms,
+// P = hi + lo with hi = bf16(P) and lo = bf16(P - hi), so the probabilities
+// keep ~16 significant bits instead of 8: rounding P to a single bf16 adds a
+// relative error of ~2^-9 per weight, which survives the averaging over keys
+// at full size and moves router logits downstream by more than 1e-3.
+// Splits write (O / l, log2 l + max) partials that a second kernel merges
+// with log-sum-exp weights.
 #include <math.h>
 
 #include "dg_internal.h"
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 
     // ---- online softmax per query column
-    uint4 pf[2][2];
+    uint4 pf[2][2], pl[2][2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       float sv[4][4];
@@ -178,11 +183,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt][ct] *= alpha;
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        pf[ct][kc] = make_uint4(pack_bf2(p[2 * kc][0], p[2 * kc][1]),
-                                pack_bf2(p[2 * kc][2], p[2 * kc][3]),
-                                pack_bf2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
-                                pack_bf2(p[2 * kc + 1][2], p[2 * kc + 1][3]));
+      for (int kc = 0; kc < 2; ++kc) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 4; ++h2) {
+          const float a0 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1)];
+          const float a1 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1) + 1];
+          const uint16_t b0 = f2bf(a0), b1 = f2bf(a1);
+          hi[h2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+          lo[h2] = pack_bf2(a0 - bf2f(b0), a1 - bf2f(b1));
+        }
+        pf[ct][kc] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        pl[ct][kc] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
     }
 
     // ---- O^T += V^T P^T
@@ -196,6 +209,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
         oacc[dt][0] = mfma16x16x32(vf, pf[0][kc], oacc[dt][0]);
         oacc[dt][1] = mfma16x16x32(vf, pf[1][kc], oacc[dt][1]);
+        oacc[dt][0] = mfma16x16x32(vf, pl[0][kc], oacc[dt][0]);
+        oacc[dt][1] = mfma16x16x32(vf, pl[1][kc], oacc[dt][1]);
       }
     }
   }

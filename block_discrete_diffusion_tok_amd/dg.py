@@ -17,6 +17,7 @@ _lib = None
 CANVAS = 256
 MAX_BATCH = 64
 BF16, FP8_E4M3 = 0, 1
+PROF_KINDS = 17
 
 STATUS = {0: "DG_OK", 1: "DG_ERR_INVALID_ARG", 2: "DG_ERR_SHAPE",
           3: "DG_ERR_CAPACITY", 4: "DG_ERR_STATE", 5: "DG_ERR_HIP",
@@ -85,6 +86,9 @@ _SIGS = {
                           _P, _P]),
     "dg_commit_block": (_I, [_P, ctypes.POINTER(CanvasBatch)]),
     "dg_set_kv_len": (_I, [_P, _I, _I]),
+    "dg_profile_enable": (_I, [_P, _I]),
+    "dg_profile_read": (_I, [_P, _P, _P]),
+    "dg_profile_kind_name": (ctypes.c_char_p, [_I]),
     "dg_kv_len": (_I, [_P, _I]),
     "dg_op_rmsnorm": (_I, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
     "dg_op_linear": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
@@ -217,6 +221,19 @@ class Engine:
         n = k.shape[2]
         _check(lib().dg_prefill_kv(self.ctx, req, n, None, _ptr(k), _ptr(v)),
                self.ctx)
+
+    def profile_enable(self, on=True):
+        _check(lib().dg_profile_enable(self.ctx, int(on)), self.ctx)
+
+    def profile_read(self):
+        """{kernel kind: (total ms, launches)} since the last read."""
+        L = lib()
+        ms = (ctypes.c_float * PROF_KINDS)()
+        n = (ctypes.c_int32 * PROF_KINDS)()
+        if L.dg_profile_read(self.ctx, ms, n) < 0:
+            _check(5, self.ctx)
+        return {L.dg_profile_kind_name(k).decode(): (ms[k], n[k])
+                for k in range(PROF_KINDS) if n[k] > 0}
 
     def set_kv_len(self, req, n):
         _check(lib().dg_set_kv_len(self.ctx, req, n), self.ctx)

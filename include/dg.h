@@ -193,6 +193,20 @@ dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
 dg_status dg_set_kv_len(dg_ctx* ctx, int32_t req, int32_t len);
 int32_t dg_kv_len(const dg_ctx* ctx, int32_t req); /* -1 on a bad slot */
 
+/* Instrumentation (not part of the method): per-kernel timing of the
+ * context's launches with hipEvents recorded on its stream around every
+ * kernel.  dg_profile_enable turns recording on or off (off by default;
+ * recording adds a few microseconds per launch).  dg_profile_read waits for
+ * the recorded events, writes the summed milliseconds and launch counts per
+ * kernel kind into ms[DG_PROF_KINDS] and launches[DG_PROF_KINDS] (host
+ * arrays), clears the record and returns 0, 1 if events were dropped
+ * because more than 2^20 were recorded between reads, or -1 on error.
+ * Kind k is named by dg_profile_kind_name(k). */
+#define DG_PROF_KINDS 17
+dg_status dg_profile_enable(dg_ctx* ctx, int32_t on);
+int32_t dg_profile_read(dg_ctx* ctx, float* ms, int32_t* launches);
+const char* dg_profile_kind_name(int32_t kind);
+
 const char* dg_status_string(dg_status s);
 const char* dg_last_error(const dg_ctx* ctx); /* "" if none; NULL ctx: last
                                                   global error */

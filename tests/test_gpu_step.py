@@ -35,51 +35,58 @@ def _setup(shape, prefix_lens, max_kv, gain_std=0.1, seed=0, device="cpu"):
 
 
 def _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, n):
-    """Oracle step in mirror mode vs the GPU outputs; decisions compared
-    where the oracle's margin is at least MARGIN."""
+    """Oracle step in mirror mode vs the GPU outputs.
+
+    Layer by layer: attention output on every row, MoE output on the rows
+    whose routing agrees, routing bit-exact except where the oracle's margin
+    is below MARGIN.  A (low-margin) routing flip in layer l changes that
+    token's residual, and through attention every row of the later layers, so
+    the comparison stops after that layer and the flip is reported.  Without
+    a flip the final entropy / lse / logits / argmax are compared too."""
     cap_o = []
     ref = oracle.denoise_step(oshape(shape), wn, cv["tokens"].numpy(),
                               cv["committed"].numpy(), prefix, mirror=True,
                               want_logits=logits is not None, capture=cap_o)
     rows = ref["rows"]
-    T = n * 256
-    # routing agreement per layer; rows after a clear-margin flip would fail
-    flipped = np.zeros(T, bool)
     for li, c in enumerate(cap_o):
         g_idx = cap["route_idx"][li].cpu().numpy()
         diff = np.any(g_idx != c["idx"], axis=1)
         marg = routing_margin(c["router_logits"], shape.top_k)
         assert np.all(marg[diff] < MARGIN), f"layer {li}: routing differs"
-        flipped |= diff
         e_att = rel_err(np32(cap["attn_out"][li]), c["attn"])
-        e_moe = rel_err(cap["moe_out"][li].cpu().numpy()[~flipped],
-                        c["moe"][~flipped])
+        e_moe = rel_err(cap["moe_out"][li].cpu().numpy()[~diff], c["moe"][~diff])
         log(f"  layer {li}: attn rel err {e_att:.2e}, moe rel err {e_moe:.2e},"
-            f" {int(diff.sum())} low-margin routing flips")
+            f" routing flips {int(diff.sum())} (margins "
+            f"{np.sort(marg[diff]).tolist()}), tokens with margin < {MARGIN}: "
+            f"{int((marg < MARGIN).sum())}")
         assert e_att < TOL and e_moe < TOL
-    ok_rows = ~flipped.reshape(-1)[rows] if flipped.any() else np.ones(len(rows), bool)
+        if diff.any():
+            log(f"  low-margin routing flip in layer {li}: later layers and "
+                "the LM head are not compared")
+            return ref, False
     g_ent = ent.cpu().numpy().reshape(-1)[rows]
     g_lse = lse.cpu().numpy().reshape(-1)[rows]
     g_am = am.cpu().numpy().reshape(-1)[rows]
     o_ent = ref["entropy"].reshape(-1)[rows]
     o_lse = ref["lse"].reshape(-1)[rows]
     o_am = ref["argmax"].reshape(-1)[rows]
-    e_ent = rel_err(g_ent[ok_rows], o_ent[ok_rows])
-    e_lse = rel_err(g_lse[ok_rows], o_lse[ok_rows])
+    e_ent = rel_err(g_ent, o_ent)
+    e_lse = rel_err(g_lse, o_lse)
     msg = f"  entropy rel err {e_ent:.2e}, lse rel err {e_lse:.2e}"
     if logits is not None:
         z = ref["logits"]
-        e_z = rel_err(logits.cpu().numpy()[rows][ok_rows], z[ok_rows])
+        e_z = rel_err(logits.cpu().numpy()[rows], z)
         marg = top2_margin(z)
         msg += f", logits rel err {e_z:.2e}"
         assert e_z < TOL
-        bad = (g_am != o_am) & (marg >= MARGIN) & ok_rows
+        bad = (g_am != o_am) & (marg >= MARGIN)
         low = int(((g_am != o_am) & (marg < MARGIN)).sum())
-        msg += f", argmax low-margin diffs {low}"
+        msg += (f", argmax diffs at margin < {MARGIN}: {low} "
+                f"(rows with such margins: {int((marg < MARGIN).sum())})")
         assert not bad.any(), "argmax differs at a clear margin"
     log(msg)
     assert e_ent < TOL and e_lse < TOL
-    return ref
+    return ref, True
 
 
 def _capture(shape, n, L):
@@ -163,15 +170,24 @@ def test_commit_block_two_layers_against_oracle():
     eng.commit_block([0, 1], tok, com, step)
     torch.cuda.synchronize()
     assert eng.kv_len(0) == 556 and eng.kv_len(1) == 768
-    ref = oracle.commit_block(oshape(shape), wn, cv["tokens"].numpy(), prefix,
-                              mirror=True)
+    kv_o, cap_o = [], []
+    oracle.model._layers_forward(oshape(shape), wn, cv["tokens"].numpy(),
+                                 prefix, True, True, cap_o, kv_out=kv_o)
     kc, vc = eng.cache_view("k"), eng.cache_view("v")
     for b, p in enumerate((300, 512)):
+        rows = slice(b * 256, (b + 1) * 256)
         for li in range(2):
+            if li > 0:
+                m = routing_margin(cap_o[li - 1]["router_logits"][rows],
+                                   shape.top_k)
+                if m.min() < MARGIN:
+                    log(f"  canvas {b}: layer {li - 1} has a routing margin "
+                        f"{m.min():.2e} < {MARGIN}; layer {li} not compared")
+                    break
             gk = np32(kc[li, b, :, p:p + 256])
             gv = np32(vc[li, b, :, p:p + 256])
-            ek = rel_err(gk, ref[b][0][li])
-            ev = rel_err(gv, ref[b][1][li])
+            ek = rel_err(gk, kv_o[li][0][:, rows])
+            ev = rel_err(gv, kv_o[li][1][:, rows])
             log(f"  canvas {b} layer {li}: K rel err {ek:.2e}, V {ev:.2e}")
             assert ek < TOL and ev < TOL
         # the prefix rows are untouched
@@ -247,7 +263,8 @@ def test_full_size_layer_step_elementwise():
     eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
     torch.cuda.synchronize()
     log("  gpu done; oracle running")
-    ref = _compare_step(shape, wn, prefix, cv, ent, lse, am, logits, cap, 1)
+    ref, full = _compare_step(shape, wn, prefix, cv, ent, lse, am, logits,
+                              cap, 1)
     gamma = torch.full((1,), wl.gamma, dtype=torch.float32, device=DEV)
     n_new = torch.zeros(1, dtype=torch.int32, device=DEV)
     done = torch.zeros(1, dtype=torch.uint8, device=DEV)
@@ -262,7 +279,9 @@ def test_full_size_layer_step_elementwise():
     assert int(n_new.item()) == o[3][0] == 1
     unc = np.nonzero(cv["committed"].numpy()[0] == 0)[0]
     hs = np.sort(o_ent[0, unc])
-    if hs[1] - hs[0] >= MARGIN:
+    if not full:
+        log("  EB set not compared (routing diverged upstream)")
+    elif hs[1] - hs[0] >= MARGIN:
         np.testing.assert_array_equal(com.cpu().numpy(), o[0])
     else:
         log(f"  EB choice is low-margin ({hs[1] - hs[0]:.2e}); not compared")
