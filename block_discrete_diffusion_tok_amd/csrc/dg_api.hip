@@ -295,6 +295,54 @@ GemmArgs gemm_dense(const uint16_t* A, int M, int K, const void* W, int N,
 
 int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi); }
 
+// Weight-streaming kernels when the expert matrices see few rows each (a
+// batch of a few canvases): on average at most 32 (token, expert) pairs per
+// expert, and K dimensions that are multiples of the streaming K chunk.
+bool use_stream_moe(const dg_model_desc& d, int T) {
+  const long long pairs = (long long)T * d.top_k;
+  return pairs <= 32LL * d.n_experts && d.hidden % stream_k_chunk() == 0 &&
+         d.expert_ffn % stream_k_chunk() == 0;
+}
+
+// The LM head streams the tied embedding once per 128 rows; beyond 256 rows
+// the tiled kernel reuses it better.
+bool use_stream_lm(int rows, int hidden) {
+  return rows <= 256 && hidden % stream_k_chunk() == 0;
+}
+
+// Run the LM head with the vocabulary statistics epilogue; returns the
+// number of partials per row written to part.
+hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
+                       int hidden, const void* embed, int vocab, float4* part,
+                       float* logits, const int32_t* row_map, int* n_tiles,
+                       hipStream_t s) {
+  if (use_stream_lm(rows_max, hidden)) {
+    StreamArgs a;
+    memset(&a, 0, sizeof(a));
+    a.X = xh;
+    a.ldx = hidden;
+    a.W = embed;
+    a.M = rows_max;
+    a.M_dev = m_dev;
+    a.N = vocab;
+    a.K = hidden;
+    a.part = part;
+    a.n_tiles = (vocab + stream_rows_per_wg() - 1) / stream_rows_per_wg();
+    a.logits = logits;
+    a.row_map = row_map;
+    *n_tiles = a.n_tiles;
+    return launch_stream(EPI_LMSTATS, false, 8, a, 1, s);
+  }
+  GemmArgs g = gemm_dense(xh, rows_max, hidden, embed, vocab, nullptr, 0);
+  g.M_dev = m_dev;
+  g.part = part;
+  g.n_tiles = (vocab + gemm_bn(EPI_LMSTATS) - 1) / gemm_bn(EPI_LMSTATS);
+  g.logits = logits;
+  g.row_map = row_map;
+  *n_tiles = g.n_tiles;
+  return launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(rows_max, EPI_LMSTATS), s);
+}
+
 // MoE FFN on xh [T, H] bf16: y mixture added into x (if x) and/or stored
 // into moe_out (if moe_out).
 hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
@@ -320,6 +368,49 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
                             b.local_rank, b.chunk_base, b.offsets,
                             b.tile_offsets, counts, b.perm, s)) != hipSuccess)
       return e;
+  }
+  if (use_stream_moe(d, T)) {
+    StreamArgs gu;
+    memset(&gu, 0, sizeof(gu));
+    gu.X = xh;
+    gu.ldx = H;
+    gu.x_map = b.perm;
+    gu.x_map_div = k;
+    gu.W = w.w_gate_up;
+    gu.w_group_stride = (long long)2 * F * H;
+    gu.w_scale = w.gate_up_scale;
+    gu.scale_rows = 2 * F;
+    gu.N = 2 * F;
+    gu.K = H;
+    gu.group_offsets = b.offsets;
+    gu.C = b.act;
+    gu.ldc = F;
+    gu.ffn = F;
+    {
+      ProfScope ps(prof, 8);
+      if ((e = launch_stream(EPI_SWIGLU, w8, 2, gu, E, s)) != hipSuccess) return e;
+    }
+    StreamArgs dn;
+    memset(&dn, 0, sizeof(dn));
+    dn.X = b.act;
+    dn.ldx = F;
+    dn.W = w.w_down;
+    dn.w_group_stride = (long long)H * F;
+    dn.w_scale = w.down_scale;
+    dn.scale_rows = H;
+    dn.N = H;
+    dn.K = F;
+    dn.group_offsets = b.offsets;
+    dn.C = b.y;
+    dn.ldc = H;
+    dn.c_map = b.perm;
+    dn.row_scale = b.rw;
+    {
+      ProfScope ps(prof, 9);
+      if ((e = launch_stream(EPI_DOWN, w8, 2, dn, E, s)) != hipSuccess) return e;
+    }
+    ProfScope ps10(prof, 10);
+    return launch_unpermute(b.y, T, k, H, x, moe_out, s);
   }
   const int grid_m = (pairs + kGroupBM - 1) / kGroupBM + std::min(E, pairs);
   GemmArgs gu = gemm_dense(xh, pairs, H, w.w_gate_up, 2 * F, b.act, F);
@@ -653,14 +744,10 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
   float* fx = (out->capture && out->capture->final_xhat) ? out->capture->final_xhat : nullptr;
   KRUN(c, 1, launch_rmsnorm(c->x, T, H, c->final_norm, d.rms_eps, c->xh,
                            c->row_map, c->m_dev, fx, s));
-  GemmArgs g = gemm_dense(c->xh, T, H, c->embed, d.vocab, nullptr, 0);
-  g.M_dev = c->m_dev;
-  g.part = c->lm_part;
-  g.n_tiles = lm_tiles(d.vocab);
-  g.logits = out->logits;
-  g.row_map = c->row_map;
-  KRUN(c, 12, launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(T, EPI_LMSTATS), s));
-  KRUN(c, 13, launch_lm_merge(c->lm_part, g.n_tiles, c->m_dev, T, c->row_map,
+  int n_tiles = 0;
+  KRUN(c, 12, run_lm_head(c->xh, T, c->m_dev, H, c->embed, d.vocab, c->lm_part,
+                          out->logits, c->row_map, &n_tiles, s));
+  KRUN(c, 13, launch_lm_merge(c->lm_part, n_tiles, c->m_dev, T, c->row_map,
                             out->entropy, out->lse, out->argmax, s));
   return DG_OK;
 }
@@ -864,14 +951,13 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
     return fail(nullptr, DG_ERR_SHAPE, "need m >= 1, vocab >= 1, hidden a multiple of 64");
   if (workspace_bytes < dg_op_lmhead_workspace_bytes(m, vocab))
     return fail(nullptr, DG_ERR_CAPACITY, "workspace too small");
-  GemmArgs g = gemm_dense((const uint16_t*)xhat, m, hidden, embed, vocab, nullptr, 0);
-  g.part = (float4*)workspace;
-  g.n_tiles = lm_tiles(vocab);
-  g.logits = logits;
   hipStream_t s = (hipStream_t)stream;
-  HIPCHK(nullptr, launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(m, EPI_LMSTATS), s));
-  HIPCHK(nullptr, launch_lm_merge(g.part, g.n_tiles, nullptr, m, nullptr,
-                                  entropy, lse, argmax, s));
+  int n_tiles = 0;
+  HIPCHK(nullptr, run_lm_head((const uint16_t*)xhat, m, nullptr, hidden, embed,
+                              vocab, (float4*)workspace, logits, nullptr,
+                              &n_tiles, s));
+  HIPCHK(nullptr, launch_lm_merge((const float4*)workspace, n_tiles, nullptr, m,
+                                  nullptr, entropy, lse, argmax, s));
   return DG_OK;
 }
 

@@ -107,6 +107,36 @@ hipError_t launch_gemm(int epi, bool w_e4m3, const GemmArgs& a, int grid_m,
 int gemm_bn(int epi);   // BN of the instance used for an epilogue
 int gemm_bm(int epi);   // BM of the instance used for an epilogue
 
+// Weight-streaming GEMM (few token rows per weight matrix); see k_stream.hip.
+struct StreamArgs {
+  const uint16_t* X;       // bf16 token rows [rows, K]
+  int ldx;
+  const int32_t* x_map;    // optional: X row = x_map[row] / x_map_div
+  int x_map_div;
+  const void* W;           // weights [N, K] per group (bf16 or e4m3)
+  long long w_group_stride;  // elements between groups
+  const float* w_scale;    // e4m3 per-row scales [groups][scale_rows]
+  int scale_rows;
+  int M;                   // token rows (dense)
+  const int32_t* M_dev;    // optional device token count (dense)
+  int N, K;                // K a multiple of stream_k_chunk()
+  const int32_t* group_offsets;  // grouped: [G+1] token-row offsets
+  void* C;
+  int ldc;
+  const int32_t* c_map;    // EPI_DOWN: pair index of each token row
+  const float* row_scale;  // EPI_DOWN: gate weight per pair
+  int ffn;                 // EPI_SWIGLU: F
+  float4* part;            // EPI_LMSTATS: [rows][n_tiles]
+  int n_tiles;
+  float* logits;           // EPI_LMSTATS: optional [rows, N]
+  const int32_t* row_map;  // EPI_LMSTATS: logits row of each token row
+};
+// nt: 16-token tiles held per pass (8: LM head and dense, 2: experts).
+hipError_t launch_stream(int epi, bool w_e4m3, int nt, const StreamArgs& a,
+                         int groups, hipStream_t s);
+int stream_rows_per_wg();  // weight rows per workgroup
+int stream_k_chunk();      // K chunk; K must be a multiple of it
+
 struct AttnArgs {
   const uint16_t* qkv;  // [n*C, ldqkv]
   int ldqkv;
