@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "dg.h"
 
 namespace dg {
@@ -12,6 +14,9 @@ namespace dg {
 // ------------------------------------------------------------------ types
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Native 128-bit vector: copies of it are plain register moves (a uint4
+// struct copy goes through memcpy, which can pin it in private memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -53,6 +58,19 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b,
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
       0, 0);
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0..N-1.
+// Register arrays indexed through it get constant indices in the IR, so they
+// are split into registers before any pass could place them in memory.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f,
+                                                std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <typename T>

@@ -64,17 +64,79 @@ __device__ __forceinline__ void widen_e4m3(const uint4 q, uint4& lo, uint4& hi) 
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Loads of one K chunk.  Every address is a valid one: rows outside the
+// matrix or the token set read a clamped row whose results are never stored,
+// so the loads stay plain global loads with no null test (a select between a
+// global and a private "zero" would turn them into flat loads, which the
+// waitcnt pass can only wait for all at once).
+template <int RT, int WREGS, int ESZ, int KC>
+__device__ __forceinline__ void load_w(uint4 (&w)[RT][WREGS],
+                                       const char* const (&src)[RT], int kc) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < WREGS; ++q)
+      w[rt][q] = *(const uint4*)(src[rt] + (long long)kc * KC * ESZ + 16 * q);
+}
+
+// Token loads of one K chunk into xr[0..XPT) and their store into an LDS
+// buffer, with compile-time indices so that xr stays in registers.
+#define DG_LOAD_X(kc)                                                      \
+  static_for<XPT>([&](auto j) {                                            \
+    xr[j] = *(const u32x4_t*)(xsrc[j] + (kc) * KC);                          \
+  });
+#define DG_STORE_X(xs)                                                     \
+  static_for<XPT>([&](auto j) {                                            \
+    const int it = tid + 256 * j;                                          \
+    const int row = it / (KC / 8), kc8 = it % (KC / 8);                    \
+    *(u32x4_t*)&(xs)[row * XP + kc8 * 8] = xr[j];                            \
+  });
+
+template <int RT, int NT, int KC, int XP, int WREGS, bool W8>
+__device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
+                                           const uint4 (&w)[RT][WREGS],
+                                           const uint16_t* xs,
+                                           int l16, int lg) {
+#pragma unroll
+  for (int j = 0; j < KC / 32; ++j) {
+    uint4 af[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (W8) {
+        uint4 lo, hi;
+        widen_e4m3(w[rt][j >> 1], lo, hi);
+        af[rt] = (j & 1) ? hi : lo;
+      } else {
+        af[rt] = w[rt][j];
+      }
+    }
+    // Every token tile is computed: tiles past the last token hold clamped
+    // (valid) rows whose results the epilogues drop, and a uniform branch
+    // here would serialise the LDS reads behind one wait each.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint4 bx = *(const uint4*)&xs[(nt * 16 + l16) * XP + (KC / 4) * lg + 8 * j];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma16x16x32(af[rt], bx, acc[rt][nt]);
+    }
+  }
+}
+
 template <int RT, int NT, int KC, int EPI, bool W8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_kernel(StreamArgs a) {
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
   static_assert(KC == 64 || KC == 128, "K chunk");
   constexpr int XP = KC + 8;          // LDS token-row pitch (elements)
-  constexpr int KS = KC / 32;         // MFMA k sub-steps per chunk
   constexpr int WROWS = 4 * RT * 16;  // weight rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][NT * 16 * XP];
+  constexpr int ESZ = W8 ? 1 : 2;     // bytes per weight element
   // uint4 per row tile per chunk: a lane's KC/4 contiguous k values
-  constexpr int WREGS = W8 ? (KC / 4) / 16 : (KC / 4) / 8;
+  constexpr int WREGS = (KC / 4) * ESZ / 16;
+  constexpr int XITEMS = NT * 16 * (KC / 8);  // 16-byte token items per chunk
+  static_assert(XITEMS % 256 == 0, "token items per thread");
+  constexpr int XPT = XITEMS / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][NT * 16 * XP];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int group = blockIdx.y;
@@ -86,83 +148,51 @@ void stream_kernel(StreamArgs a) {
     t_end = a.group_offsets[group + 1];
   } else {
     t_begin = 0;
-    t_end = a.M_dev ? *a.M_dev : a.M;
+    t_end = a.M;
+    if (a.M_dev) t_end = min(t_end, a.M_dev[0]);
   }
   if (t_end <= t_begin) return;
 
-  // ---- weight rows of this workgroup / wave
-  const int n_base = blockIdx.x * WROWS;  // in "row space" of the epilogue
-  // row index r of tile rt for this lane -> weight matrix row
-  auto wrow = [&](int rt, bool& ok) -> int {
-    const int r = n_base + (wave * RT + rt) * 16 + l16;
-    if (EPI == EPI_SWIGLU) {
-      // per wave: tiles [0, RT/2) are gate rows of channels c0 + 16*rt + l16,
-      // tiles [RT/2, RT) the up rows of the same channels
-      const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT);
-      const int ch = c0 + (rt % (RT / 2)) * 16 + l16;
-      ok = ch < a.ffn;
-      return (rt < RT / 2) ? ch : a.ffn + ch;
-    }
-    ok = r < a.N;
-    return r;
-  };
+  // ---- this lane's weight rows (r < n_valid) and their source pointers
+  const int n_base = blockIdx.x * WROWS;
+  const char* wgroup = (const char*)a.W + (long long)group * a.w_group_stride * ESZ;
   const char* wsrc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
+    int r;
     bool ok;
-    const int r = wrow(rt, ok);
-    wsrc[rt] = ok ? (const char*)a.W +
-                        ((long long)group * a.w_group_stride + (long long)r * a.K +
-                         (KC / 4) * lg) * (W8 ? 1 : 2)
-                  : nullptr;
+    if (EPI == EPI_SWIGLU) {
+      // tiles [0, RT/2) are gate rows of channels c0 + 16*rt + l16, tiles
+      // [RT/2, RT) the up rows of the same channels
+      const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT);
+      const int ch = c0 + (rt % (RT / 2)) * 16 + l16;
+      ok = ch < a.ffn;
+      r = (rt < RT / 2) ? ch : a.ffn + ch;
+    } else {
+      r = n_base + (wave * RT + rt) * 16 + l16;
+      ok = r < a.N;
+    }
+    wsrc[rt] = wgroup + ((long long)(ok ? r : 0) * a.K + (KC / 4) * lg) * ESZ;
   }
   const int nk = a.K / KC;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
 
   for (int t0 = t_begin; t0 < t_end; t0 += NT * 16) {
     const int nt_rows = min(NT * 16, t_end - t0);
     const int nt_act = (nt_rows + 15) >> 4;
 
-    // token fill: NT*16 rows x KC, 16 B per item, KC/8 items per row
-    constexpr int XITEMS = NT * 16 * (KC / 8);
-    constexpr int XPT = (XITEMS + 255) / 256;
     const uint16_t* xsrc[XPT];
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
+    const uint16_t* const xbase = a.X;
+    const int32_t* const xmap = a.x_map;
+    const int xdiv = a.x_map_div, ldx = a.ldx;
+    static_for<XPT>([&](auto j) {
       const int it = tid + 256 * j;
       const int row = it / (KC / 8), kc8 = it % (KC / 8);
-      xsrc[j] = nullptr;
-      if (it < XITEMS && row < nt_rows) {
-        const int trow = t0 + row;
-        const int src = a.x_map ? a.x_map[trow] / a.x_map_div : trow;
-        xsrc[j] = a.X + (long long)src * a.ldx + kc8 * 8;
-      }
-    }
-    uint4 xr[XPT];
-    auto xload = [&](int kc) {
-#pragma unroll
-      for (int j = 0; j < XPT; ++j)
-        xr[j] = xsrc[j] ? *(const uint4*)(xsrc[j] + kc * KC) : zero;
-    };
-    auto xstore = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < XPT; ++j) {
-        const int it = tid + 256 * j;
-        if (it < XITEMS) {
-          const int row = it / (KC / 8), kc8 = it % (KC / 8);
-          *(uint4*)&Xs[buf][row * XP + kc8 * 8] = xr[j];
-        }
-      }
-    };
+      const int trow = t0 + (row < nt_rows ? row : 0);
+      const int src = xmap ? xmap[trow] / xdiv : trow;
+      xsrc[j] = xbase + (long long)src * ldx + kc8 * 8;
+    });
+    u32x4_t xr[XPT];
     uint4 wa[RT][WREGS], wb[RT][WREGS];
-    auto wload = [&](uint4 (&w)[RT][WREGS], int kc) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int q = 0; q < WREGS; ++q)
-          w[rt][q] = wsrc[rt] ? *(const uint4*)(wsrc[rt] + (long long)kc * KC * (W8 ? 1 : 2) + 16 * q)
-                              : zero;
-    };
 
     f32x4_t acc[RT][NT];
 #pragma unroll
@@ -170,51 +200,39 @@ void stream_kernel(StreamArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const uint4 (&w)[RT][WREGS], int buf) {
-#pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        uint4 af[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          if (W8) {
-            uint4 lo, hi;
-            widen_e4m3(w[rt][j >> 1], lo, hi);
-            af[rt] = (j & 1) ? hi : lo;
-          } else {
-            af[rt] = w[rt][j];
-          }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (nt < nt_act) {
-            const uint4 bx = *(const uint4*)&Xs[buf][(nt * 16 + l16) * XP + (KC / 4) * lg + 8 * j];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma16x16x32(af[rt], bx, acc[rt][nt]);
-          }
-        }
-      }
-    };
-
-    // prologue
-    __syncthreads();  // previous pass done with Xs
-    wload(wa, 0);
-    xload(0);
-    xstore(0);
-    if (nk > 1) wload(wb, 1);
+    // prologue: chunk 0 in wa / Xs[0], chunk 1 in wb
+    __syncthreads();  // the previous pass is done with Xs
+    load_w<RT, WREGS, ESZ, KC>(wa, wsrc, 0);
+    DG_LOAD_X(0);
+    DG_STORE_X(Xs[0]);
+    load_w<RT, WREGS, ESZ, KC>(wb, wsrc, min(1, nk - 1));
     __syncthreads();
+    // Issue order per half step: next token chunk (L2), MFMAs of this
+    // chunk, weight chunk two ahead (HBM), then the LDS store of the next
+    // token chunk, so that the store waits only for the token loads and the
+    // weight loads stay in flight across the next MFMAs.  Chunk indices past
+    // the end are clamped to the last chunk (a redundant, valid load) so that
+    // the body is straight-line code the compiler cannot regroup.
+    const int last = nk - 1;
     for (int kc = 0; kc < nk; kc += 2) {
-      // even chunk kc in wa / Xs[0]
-      if (kc + 1 < nk) xload(kc + 1);
-      compute(wa, 0);
-      if (kc + 2 < nk) wload(wa, kc + 2);
-      if (kc + 1 < nk) xstore(1);
+      // even chunk kc: weights in wa, tokens in Xs[0]
+      DG_LOAD_X(min(kc + 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk<RT, NT, KC, XP, WREGS, W8>(acc, wa, Xs[0], l16, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w<RT, WREGS, ESZ, KC>(wa, wsrc, min(kc + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      DG_STORE_X(Xs[1]);
       __syncthreads();
       if (kc + 1 >= nk) break;
-      // odd chunk kc+1 in wb / Xs[1]
-      if (kc + 2 < nk) xload(kc + 2);
-      compute(wb, 1);
-      if (kc + 3 < nk) wload(wb, kc + 3);
-      if (kc + 2 < nk) xstore(0);
+      // odd chunk kc + 1: weights in wb, tokens in Xs[1]
+      DG_LOAD_X(min(kc + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_chunk<RT, NT, KC, XP, WREGS, W8>(acc, wb, Xs[1], l16, lg);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w<RT, WREGS, ESZ, KC>(wb, wsrc, min(kc + 3, last));
+      __builtin_amdgcn_sched_barrier(0);
+      DG_STORE_X(Xs[0]);
       __syncthreads();
     }
 
@@ -364,6 +382,9 @@ constexpr int kDenseRT = 2, kMoeRT = 2;
 constexpr int kDenseKC = 64, kMoeKC = 128;
 int stream_rows_per_wg() { return 4 * kDenseRT * 16; }
 int stream_k_chunk() { return kMoeKC > kDenseKC ? kMoeKC : kDenseKC; }
+
+#undef DG_LOAD_X
+#undef DG_STORE_X
 
 hipError_t launch_stream(int epi, bool w8, int nt, const StreamArgs& a,
                          int groups, hipStream_t s) {
