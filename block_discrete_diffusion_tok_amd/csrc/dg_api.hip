@@ -300,14 +300,13 @@ int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi);
 // expert, and K dimensions that are multiples of the streaming K chunk.
 bool use_stream_moe(const dg_model_desc& d, int T) {
   const long long pairs = (long long)T * d.top_k;
-  return pairs <= 32LL * d.n_experts && d.hidden % stream_k_chunk() == 0 &&
-         d.expert_ffn % stream_k_chunk() == 0;
+  return pairs <= 32LL * d.n_experts && stream_moe_ok(d.hidden, d.expert_ffn);
 }
 
 // The LM head streams the tied embedding once per 128 rows; beyond 256 rows
 // the tiled kernel reuses it better.
 bool use_stream_lm(int rows, int hidden) {
-  return rows <= 256 && hidden % stream_k_chunk() == 0;
+  return rows <= 256 && stream_lm_ok(hidden);
 }
 
 // Run the LM head with the vocabulary statistics epilogue; returns the
@@ -331,7 +330,7 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
     a.logits = logits;
     a.row_map = row_map;
     *n_tiles = a.n_tiles;
-    return launch_stream(EPI_LMSTATS, false, 8, a, 1, s);
+    return launch_stream(EPI_LMSTATS, false, a, 1, s);
   }
   GemmArgs g = gemm_dense(xh, rows_max, hidden, embed, vocab, nullptr, 0);
   g.M_dev = m_dev;
@@ -388,7 +387,7 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     gu.ffn = F;
     {
       ProfScope ps(prof, 8);
-      if ((e = launch_stream(EPI_SWIGLU, w8, 2, gu, E, s)) != hipSuccess) return e;
+      if ((e = launch_stream(EPI_SWIGLU, w8, gu, E, s)) != hipSuccess) return e;
     }
     StreamArgs dn;
     memset(&dn, 0, sizeof(dn));
@@ -407,7 +406,7 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     dn.row_scale = b.rw;
     {
       ProfScope ps(prof, 9);
-      if ((e = launch_stream(EPI_DOWN, w8, 2, dn, E, s)) != hipSuccess) return e;
+      if ((e = launch_stream(EPI_DOWN, w8, dn, E, s)) != hipSuccess) return e;
     }
     ProfScope ps10(prof, 10);
     return launch_unpermute(b.y, T, k, H, x, moe_out, s);

@@ -137,7 +137,7 @@ struct StreamArgs {
   int scale_rows;
   int M;                   // token rows (dense)
   const int32_t* M_dev;    // optional device token count (dense)
-  int N, K;                // K a multiple of stream_k_chunk()
+  int N, K;                // K as stream_lm_ok / stream_moe_ok require
   const int32_t* group_offsets;  // grouped: [G+1] token-row offsets
   void* C;
   int ldc;
@@ -149,11 +149,13 @@ struct StreamArgs {
   float* logits;           // EPI_LMSTATS: optional [rows, N]
   const int32_t* row_map;  // EPI_LMSTATS: logits row of each token row
 };
-// nt: 16-token tiles held per pass (8: LM head and dense, 2: experts).
-hipError_t launch_stream(int epi, bool w_e4m3, int nt, const StreamArgs& a,
-                         int groups, hipStream_t s);
+// Epilogues EPI_LMSTATS (128 token columns per pass) and EPI_SWIGLU /
+// EPI_DOWN (32 per pass).  K must satisfy stream_lm_ok / stream_moe_ok.
+hipError_t launch_stream(int epi, bool w_e4m3, const StreamArgs& a, int groups,
+                         hipStream_t s);
+bool stream_lm_ok(int hidden);
+bool stream_moe_ok(int hidden, int ffn);
 int stream_rows_per_wg();  // weight rows per workgroup
-int stream_k_chunk();      // K chunk; K must be a multiple of it
 
 struct AttnArgs {
   const uint16_t* qkv;  // [n*C, ldqkv]

@@ -1,4 +1,4 @@
-// Tiled bf16 MFMA GEMM  C = A W^T  (A: activations [rows, K]; W: weights
+// Tiled bf16 MFMA GEMM  C = A W^T  (A: token rows [rows, K]; W: weights
 // [N, K]), fp32 accumulation, with the epilogues the denoising step needs:
 //   - Q/K/V projection (bf16 out), router logits (fp32 out), output
 //     projection added into the fp32 residual stream;
@@ -12,10 +12,18 @@
 // Expert weights may be OCP E4M3 bytes: they are widened to bf16 exactly on
 // their way into LDS and the per-row scale is applied in the epilogue.
 //
-// Workgroup: 256 threads = 4 waves in a 2x2 grid over a BM x BN tile; each
-// wave owns (BM/2) x (BN/2) as (BM/32) x (BN/32) MFMA 16x16x32 tiles.
-// K is walked in steps of 64 with the next step's global loads issued before
-// the current step's MFMAs.
+// Workgroup: 256 threads = 4 waves in a 2x2 grid over a BM (tokens) x BN
+// (weight rows) tile; each wave owns (BM/2) x (BN/2) as MFMA 16x16x32 tiles
+// with the weights as the A operand, so a lane's accumulators hold one token
+// and 4 consecutive output columns (vector stores in every epilogue).
+// K is walked in steps of 64 through double-buffered LDS: later steps'
+// global loads are issued before the current step's MFMAs and the next
+// step is stored into the other buffer after them, one barrier per step.  Every load address is
+// valid (rows past the end are clamped and their results dropped), so the
+// loads stay plain global loads with per-load waits.
+// The loop keeps P K steps of global loads in flight in registers (4 for
+// 64x64 tiles, 2 for 128x128), so a workgroup waits about a quarter of a
+// memory latency per step instead of a whole one.
 #include <math.h>
 
 #include "dg_internal.h"
@@ -44,13 +52,62 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float& t,
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
+// 16 e4m3 bytes -> 16 bf16 (exact).
+__device__ __forceinline__ void widen16(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = q[i];
+    o[2 * i] = (uint32_t)e4m3_to_bf(w & 0xff) | ((uint32_t)e4m3_to_bf((w >> 8) & 0xff) << 16);
+    o[2 * i + 1] = (uint32_t)e4m3_to_bf((w >> 16) & 0xff) | ((uint32_t)e4m3_to_bf(w >> 24) << 16);
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
+__device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Global loads of K step kt into staging register set p, and the store of
+// set p into LDS buffer b (token chunk j of thread tid covers row c/8, 8 k
+// values at (c%8)*8 with c = tid + 256 j; weight chunks likewise, or 16
+// bytes of e4m3 covering row c/4 and k values (c%4)*16..+15).
+#define DG_GLOAD(p, kt)                                                       \
+  static_for<XA>([&](auto j) {                                                \
+    tr[p][j] = *(const u32x4_t*)(tsrc[j] + (long long)(kt) * BK);             \
+  });                                                                         \
+  static_for<XB>([&](auto j) {                                                \
+    wr[p][j] = *(const u32x4_t*)(wsrc[j] + (long long)(kt) * BK * ESZ);       \
+  });
+#define DG_LSTORE(b, p)                                                       \
+  static_for<XA>([&](auto j) {                                                \
+    const int c = tid + 256 * j;                                              \
+    *(u32x4_t*)&Ts[b][(c >> 3) * LDK + (c & 7) * 8] = tr[p][j];               \
+  });                                                                         \
+  static_for<XB>([&](auto j) {                                                \
+    const int c = tid + 256 * j;                                              \
+    if (W8) {                                                                 \
+      u32x4_t lo, hi;                                                         \
+      widen16(wr[p][j], lo, hi);                                              \
+      *(u32x4_t*)&Ws[b][(c >> 2) * LDK + (c & 3) * 16] = lo;                  \
+      *(u32x4_t*)&Ws[b][(c >> 2) * LDK + (c & 3) * 16 + 8] = hi;              \
+    } else {                                                                  \
+      *(u32x4_t*)&Ws[b][(c >> 3) * LDK + (c & 7) * 8] = wr[p][j];             \
+    }                                                                         \
+  });
+
 template <int BM, int BN, int EPI, bool W8>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
-  constexpr int TM = BM / 32;  // MFMA row tiles per wave (= A chunks/thread)
-  constexpr int TN = BN / 32;  // MFMA col tiles per wave (= B chunks/thread)
-  constexpr int NB8 = BN / 64; // e4m3 B chunks (16 bytes) per thread
+  constexpr int TM = BM / 32;                 // token tiles per wave
+  constexpr int TN = BN / 32;                 // weight-row tiles per wave
+  constexpr int XA = BM / 32;                 // token 16-byte loads per thread
+  constexpr int XB = W8 ? BN / 64 : BN / 32;  // weight 16-byte loads per thread
+  constexpr int ESZ = W8 ? 1 : 2;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  __shared__ __attribute__((aligned(16))) uint16_t Ts[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -77,85 +134,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     row_end = m_rows;
   }
 
-  // ---- per-thread global source pointers (fixed over K)
-  const uint16_t* a_src[TM];
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-    const int row = row_begin + r;
-    a_src[j] = nullptr;
-    if (row < row_end) {
-      const int src = a.a_map ? a.a_map[row] / a.a_map_div : row;
-      a_src[j] = a.A + (long long)src * a.lda + kc * 8;
-    }
-  }
-  auto weight_row = [&](int r, bool& ok) -> int {
-    if (EPI == EPI_SWIGLU) {
-      const int grp = r >> 5, half = (r >> 4) & 1;
-      const int ch = nt * (BN / 2) + grp * 16 + (r & 15);
-      ok = ch < a.ffn;
-      return half ? a.ffn + ch : ch;
-    }
-    const int wr = nt * BN + r;
-    ok = wr < a.N;
-    return wr;
-  };
-  constexpr int NBL = W8 ? NB8 : TN;
-  const char* b_src[NBL];
-#pragma unroll
-  for (int j = 0; j < NBL; ++j) {
+  // ---- per-thread source addresses
+  const int nk = a.K / BK;
+  const uint16_t* tsrc[XA];
+  const int32_t* const amap = a.a_map;
+  static_for<XA>([&](auto j) {
+    const int c = tid + 256 * j;
+    const int row = min(row_begin + (c >> 3), row_end - 1);
+    const int src = amap ? amap[row] / a.a_map_div : row;
+    tsrc[j] = a.A + (long long)src * a.lda + (c & 7) * 8;
+  });
+  const char* wsrc[XB];
+  static_for<XB>([&](auto j) {
     const int c = tid + 256 * j;
     const int r = W8 ? (c >> 2) : (c >> 3);
-    const int kc = W8 ? (c & 3) : (c & 7);
-    bool ok;
-    const int wr = weight_row(r, ok);
-    b_src[j] = nullptr;
-    if (ok) {
-      const long long elem = (long long)group * a.b_group_stride +
-                             (long long)wr * a.K + (W8 ? kc * 16 : kc * 8);
-      b_src[j] = (const char*)a.B + elem * (W8 ? 1 : 2);
+    int wrow;
+    if (EPI == EPI_SWIGLU) {
+      // 16 gate rows then the 16 matching up rows, per 32-row block
+      const int ch = min(nt * (BN / 2) + (r >> 5) * 16 + (r & 15), a.ffn - 1);
+      wrow = ((r >> 4) & 1) ? a.ffn + ch : ch;
+    } else {
+      wrow = min(nt * BN + r, a.N - 1);
     }
-  }
-
-  uint4 ra[TM], rb[NBL];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-      ra[j] = a_src[j] ? *(const uint4*)(a_src[j] + k0) : zero;
-#pragma unroll
-    for (int j = 0; j < NBL; ++j)
-      rb[j] = b_src[j] ? *(const uint4*)(b_src[j] + (long long)k0 * (W8 ? 1 : 2))
-                       : zero;
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int c = tid + 256 * j, r = c >> 3, kc = c & 7;
-      *(uint4*)&As[r * LDK + kc * 8] = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NBL; ++j) {
-      const int c = tid + 256 * j;
-      if (W8) {
-        const int r = c >> 2, kc = c & 3;
-        const uint32_t w[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[2 * q] = (uint32_t)e4m3_to_bf(w[q] & 0xff) |
-                     ((uint32_t)e4m3_to_bf((w[q] >> 8) & 0xff) << 16);
-          o[2 * q + 1] = (uint32_t)e4m3_to_bf((w[q] >> 16) & 0xff) |
-                         ((uint32_t)e4m3_to_bf(w[q] >> 24) << 16);
-        }
-        *(uint4*)&Bs[r * LDK + kc * 16] = make_uint4(o[0], o[1], o[2], o[3]);
-        *(uint4*)&Bs[r * LDK + kc * 16 + 8] = make_uint4(o[4], o[5], o[6], o[7]);
-      } else {
-        const int r = c >> 3, kc = c & 7;
-        *(uint4*)&Bs[r * LDK + kc * 8] = rb[j];
-      }
-    }
-  };
+    const long long elem = (long long)group * a.b_group_stride +
+                           (long long)wrow * a.K +
+                           (W8 ? (c & 3) * 16 : (c & 7) * 8);
+    wsrc[j] = (const char*)a.B + elem * ESZ;
+  });
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -163,61 +168,82 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.K / BK;
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  // P register sets keep the global loads of P K steps in flight (one
+  // step's loads alone would leave the loop waiting a full memory latency
+  // per step).  Invariant at step k: set (k+1) % P holds step k+1.
+  constexpr int P = BM == 64 ? 4 : 2;
+  static_assert(P % 2 == 0, "LDS buffer parity follows the step parity");
+  u32x4_t tr[P][XA], wr[P][XB];
+  const uint16_t* const tfrag = &Ts[0][(wm * (BM / 2) + l16) * LDK + lg * 8];
+  const uint16_t* const wfrag = &Ws[0][(wn * (BN / 2) + l16) * LDK + lg * 8];
+  auto compute = [&](int b) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *(const uint4*)&As[(wm * (BM / 2) + i * 16 + l16) * LDK +
-                                   ks * 32 + lg * 8];
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      u32x4_t wf[TN], tf[TM];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *(const uint4*)&Bs[(wn * (BN / 2) + j * 16 + l16) * LDK +
-                                    ks * 32 + lg * 8];
+        wf[j] = *(const u32x4_t*)(wfrag + b * BN * LDK + j * 16 * LDK + ks * 32);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        tf[i] = *(const u32x4_t*)(tfrag + b * BM * LDK + i * 16 * LDK + ks * 32);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_v(wf[j], tf[i], acc[i][j]);
     }
-    __syncthreads();
-    if (kt + 1 < nk) {
-      lstore();
-      __syncthreads();
-    }
-  }
+  };
 
-  // ---- epilogues.  Lane holds column l16 of each 16x16 tile, rows 4*lg+i.
+  // Step indices past the end are clamped to the last step (a redundant,
+  // valid load) so that the body stays straight-line code.
+  const int last = nk - 1;
+  static_for<P>([&](auto p) { DG_GLOAD(p, min((int)p, last)); });
+  DG_LSTORE(0, 0);
+  DG_GLOAD(0, min(P, last));
+  __syncthreads();
+  // Main loop over whole groups of P steps (straight-line, so the waits
+  // before each LDS store cover only the oldest register set), then the
+  // remaining nk % P steps.
+  auto step = [&](auto p, int kt) {
+    constexpr int q = (p + 1) % P;
+    __builtin_amdgcn_sched_barrier(0);
+    compute(p & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    DG_LSTORE((p + 1) & 1, q);
+    DG_GLOAD(q, min(kt + p + 1 + P, last));
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + P <= nk; kt += P)
+    static_for<P>([&](auto p) { step(p, kt); });
+  if (kt < nk)
+    static_for<P - 1>([&](auto p) {
+      if (kt + p < nk) step(p, kt);
+    });
+
+  // ---- epilogues.  acc[i][j][e]: token row_begin + wm*BM/2 + 16 i + l16,
+  // weight row (output column) wn*BN/2 + 16 j + 4 lg + e of the tile.
   if (EPI == EPI_LMSTATS) {
-    float4* red = (float4*)As;  // [2][BM]; the loop ended with a barrier
+    float4* red = (float4*)&Ts[0][0];  // [2 (wn)][BM]; the loop ended with a barrier
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      const int t_loc = wm * (BM / 2) + i * 16 + l16;
+      const int row = row_begin + t_loc;
+      float m = -INFINITY, s = 0.f, t = 0.f;
+      int am = 0x7fffffff;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r_loc = wm * (BM / 2) + i * 16 + lg * 4 + e;
-        const int row = row_begin + r_loc;
-        float m = -INFINITY;
-        int am = 0x7fffffff;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = nt * BN + wn * (BN / 2) + j * 16 + l16;
+        for (int e = 0; e < 4; ++e) {
+          const int col = nt * BN + wn * (BN / 2) + j * 16 + 4 * lg + e;
           const float v = acc[i][j][e];
           if (col < a.N && v > m) { m = v; am = col; }
-          if (a.logits && col < a.N && row < row_end) {
-            const int lrow = a.row_map ? a.row_map[row] : row;
-            a.logits[(long long)lrow * a.N + col] = v;
-          }
         }
-        float s = 0.f, t = 0.f;
-        if (m != -INFINITY) {
+      if (m != -INFINITY) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int col = nt * BN + wn * (BN / 2) + j * 16 + l16;
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int col = nt * BN + wn * (BN / 2) + j * 16 + 4 * lg + e;
             if (col < a.N) {
               const float d = acc[i][j][e] - m;
               const float ex = __expf(d);
@@ -225,76 +251,116 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
               t += ex * d;
             }
           }
-        }
+      }
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float m2 = shfl_xor(m, off), s2 = shfl_xor(s, off);
-          const float t2 = shfl_xor(t, off);
-          const int am2 = shfl_xor(am, off);
-          stats_merge(m, s, t, am, m2, s2, t2, am2);
+      for (int off = 16; off < 64; off <<= 1) {
+        const float m2 = shfl_xor(m, off), s2 = shfl_xor(s, off);
+        const float t2 = shfl_xor(t, off);
+        const int am2 = shfl_xor(am, off);
+        stats_merge(m, s, t, am, m2, s2, t2, am2);
+      }
+      if (lg == 0) red[wn * BM + t_loc] = make_float4(m, s, t, __int_as_float(am));
+      if (a.logits && row < row_end) {
+        const int lrow = a.row_map ? a.row_map[row] : row;
+        float* lp = a.logits + (long long)lrow * a.N;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + wn * (BN / 2) + j * 16 + 4 * lg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < a.N) lp[col + e] = acc[i][j][e];
         }
-        if (l16 == 0) red[wn * BM + r_loc] = make_float4(m, s, t, __int_as_float(am));
       }
     }
     __syncthreads();
     if (tid < BM) {
       const int row = row_begin + tid;
       if (row < row_end) {
-        float4 p = red[tid];
+        const float4 p = red[tid];
         const float4 q = red[BM + tid];
         float m = p.x, s = p.y, t = p.z;
         int am = __float_as_int(p.w);
         stats_merge(m, s, t, am, q.x, q.y, q.z, __float_as_int(q.w));
-        a.part[(long long)row * a.n_tiles + nt] =
-            make_float4(m, s, t, __int_as_float(am));
+        a.part[(long long)row * a.n_tiles + nt] = make_float4(m, s, t, __int_as_float(am));
       }
     }
     return;
   }
 
+  const bool vec = ((a.ldc | a.N) & 3) == 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    const int row = row_begin + wm * (BM / 2) + i * 16 + l16;
+    if (row >= row_end) continue;
+    if (EPI == EPI_SWIGLU) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = row_begin + wm * (BM / 2) + i * 16 + lg * 4 + e;
-      if (row >= row_end) continue;
-      if (EPI == EPI_SWIGLU) {
+      for (int j = 0; j < TN; j += 2) {
+        // tiles j (gate) and j+1 (up) cover the same 16 channels
+        const int ch = nt * (BN / 2) + ((wn * (BN / 2) + j * 16) >> 5) * 16 + 4 * lg;
+        if (ch >= a.ffn) continue;  // ffn is a multiple of 64
+        float g[4], u[4];
 #pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int grp = (wn * (BN / 2) + j * 16) >> 5;
-          const int ch = nt * (BN / 2) + grp * 16 + l16;
-          if (ch >= a.ffn) continue;
-          float gate = acc[i][j][e], up = acc[i][j + 1][e];
+        for (int e = 0; e < 4; ++e) {
+          g[e] = acc[i][j][e];
+          u[e] = acc[i][j + 1][e];
           if (W8) {
             const float* sc = a.b_scale + (long long)group * a.scale_rows;
-            gate *= sc[ch];
-            up *= sc[a.ffn + ch];
+            g[e] *= sc[ch + e];
+            u[e] *= sc[a.ffn + ch + e];
           }
-          ((uint16_t*)a.C)[(long long)row * a.ldc + ch] = f2bf(silu(gate) * up);
         }
-      } else {
+        *(uint2*)((uint16_t*)a.C + (long long)row * a.ldc + ch) =
+            make_uint2(pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
+                       pack_bf2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = nt * BN + wn * (BN / 2) + j * 16 + l16;
-          if (col >= a.N) continue;
-          const float v = acc[i][j][e];
+      for (int j = 0; j < TN; ++j) {
+        const int n = nt * BN + wn * (BN / 2) + j * 16 + 4 * lg;
+        if (n >= a.N) continue;
+        const f32x4_t v = acc[i][j];
+        if (EPI == EPI_DOWN) {
+          // N (hidden) is a multiple of 64 on this path
+          const int pair = a.c_map[row];
+          const float wgt = a.row_scale[pair];
+          float sc4[4] = {1.f, 1.f, 1.f, 1.f};
+          if (W8) {
+            const float* sc = a.b_scale + (long long)group * a.scale_rows + n;
+            sc4[0] = sc[0]; sc4[1] = sc[1]; sc4[2] = sc[2]; sc4[3] = sc[3];
+          }
+          *(float4*)((float*)a.C + (long long)pair * a.ldc + n) =
+              make_float4(v[0] * wgt * sc4[0], v[1] * wgt * sc4[1],
+                          v[2] * wgt * sc4[2], v[3] * wgt * sc4[3]);
+        } else if (vec) {
           if (EPI == EPI_STORE_BF16) {
-            ((uint16_t*)a.C)[(long long)row * a.ldc + col] = f2bf(v);
+            *(uint2*)((uint16_t*)a.C + (long long)row * a.ldc + n) =
+                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
           } else if (EPI == EPI_STORE_F32) {
-            ((float*)a.C)[(long long)row * a.ldc + col] = v;
+            *(float4*)((float*)a.C + (long long)row * a.ldc + n) =
+                make_float4(v[0], v[1], v[2], v[3]);
           } else if (EPI == EPI_ADD_F32) {
-            ((float*)a.C)[(long long)row * a.ldc + col] += v;
-          } else if (EPI == EPI_DOWN) {
-            const int pair = a.c_map[row];
-            float y = v * a.row_scale[pair];
-            if (W8) y *= a.b_scale[(long long)group * a.scale_rows + col];
-            ((float*)a.C)[(long long)pair * a.ldc + col] = y;
+            float4* cp = (float4*)((float*)a.C + (long long)row * a.ldc + n);
+            float4 o = *cp;
+            o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
+            *cp = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= a.N) break;
+            const long long o = (long long)row * a.ldc + n + e;
+            if (EPI == EPI_STORE_BF16) ((uint16_t*)a.C)[o] = f2bf(v[e]);
+            else if (EPI == EPI_STORE_F32) ((float*)a.C)[o] = v[e];
+            else if (EPI == EPI_ADD_F32) ((float*)a.C)[o] += v[e];
           }
         }
       }
     }
   }
 }
+
+#undef DG_GLOAD
+#undef DG_LSTORE
 
 template <int BM, int BN, int EPI, bool W8>
 hipError_t launch_one(const GemmArgs& a, int grid_m, hipStream_t s) {

@@ -11,19 +11,25 @@
 //     K chunk, two chunks ahead of the MFMAs (weights are used once, so they
 //     never pass through LDS);
 //   * the group's token rows (gathered through the expert permutation when
-//     needed) are staged per K chunk in double-buffered LDS and shared by the
-//     4 waves;
+//     needed) go HBM/L2 -> LDS directly (LDS-DMA loads, no registers) into
+//     a ring of D+1 chunk stages shared by the 4 waves.  Each chunk's token
+//     DMA and weight loads are issued together D chunks ahead, so the wait
+//     for a chunk covers exactly the loads issued D chunks earlier (the
+//     load counter completes in issue order: a token load issued after
+//     younger weight loads would force those to land first);
 //   * MFMA 16x16x32 bf16 with the weights as the A operand, so a lane's
 //     accumulators hold one token column and 4 consecutive weight rows: the
 //     epilogues (SwiGLU of paired gate/up rows, gate-weight scaling with the
 //     scatter back to (token, rank) slots, vocabulary statistics) work on
 //     contiguous outputs.
 //
-// The K-slot permutation: in a K chunk of KC starting at k0, lane group lg
-// (lanes 16*lg..16*lg+15) feeds k = k0 + (KC/4)*lg + 8*j + [0, 8) to MFMA
-// sub-step j (j = 0..KC/32-1) for both operands, so a lane's weight bytes for
-// the chunk are one contiguous run of KC/4 values.  The dot product is the
-// same sum in a different order.
+// K-slot map: in a K chunk starting at k0, MFMA sub-step j takes from lane
+// group lg (lanes 16*lg..16*lg+15) the 8 values k0 + 32*j + 8*lg + [0, 8)
+// for bf16 weights, and k0 + 64*(j/2) + 16*lg + 8*(j%2) + [0, 8) for e4m3
+// weights (both operands alike; the dot product is the same sum in another
+// order).  Either way a lane's q-th 16-byte weight load of the chunk starts
+// at byte 64*q + 16*lg of its row, so the 4 lanes of a row read 64
+// contiguous bytes per load instruction.
 #include <math.h>
 
 #include "dg_internal.h"
@@ -49,93 +55,106 @@ __device__ __forceinline__ void smerge(float& m, float& s, float& t, int& am,
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
-// Widen 16 e4m3 bytes (one uint4) to 16 bf16 (two uint4).
-__device__ __forceinline__ void widen_e4m3(const uint4 q, uint4& lo, uint4& hi) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o[2 * i] = (uint32_t)e4m3_to_bf(w[i] & 0xff) |
-               ((uint32_t)e4m3_to_bf((w[i] >> 8) & 0xff) << 16);
-    o[2 * i + 1] = (uint32_t)e4m3_to_bf((w[i] >> 16) & 0xff) |
-                   ((uint32_t)e4m3_to_bf(w[i] >> 24) << 16);
-  }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
-// Loads of one K chunk.  Every address is a valid one: rows outside the
-// matrix or the token set read a clamped row whose results are never stored,
-// so the loads stay plain global loads with no null test (a select between a
-// global and a private "zero" would turn them into flat loads, which the
-// waitcnt pass can only wait for all at once).
+// Weight loads of one K chunk into register set w.  Every address is a
+// valid one: rows outside the matrix read a clamped row whose results are
+// never stored, so the loads stay plain global loads with no null test (a
+// select between a global and a private "zero" would turn them into flat
+// loads, which the waitcnt pass can only wait for all at once).
 template <int RT, int WREGS, int ESZ, int KC>
-__device__ __forceinline__ void load_w(uint4 (&w)[RT][WREGS],
+__device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
                                        const char* const (&src)[RT], int kc) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int q = 0; q < WREGS; ++q)
-      w[rt][q] = *(const uint4*)(src[rt] + (long long)kc * KC * ESZ + 16 * q);
+      w[rt][q] = *(const u32x4_t*)(src[rt] + (long long)kc * KC * ESZ + 64 * q);
 }
 
-// Token loads of one K chunk into xr[0..XPT) and their store into an LDS
-// buffer, with compile-time indices so that xr stays in registers.
-#define DG_LOAD_X(kc)                                                      \
-  static_for<XPT>([&](auto j) {                                            \
-    xr[j] = *(const u32x4_t*)(xsrc[j] + (kc) * KC);                          \
-  });
-#define DG_STORE_X(xs)                                                     \
-  static_for<XPT>([&](auto j) {                                            \
-    const int it = tid + 256 * j;                                          \
-    const int row = it / (KC / 8), kc8 = it % (KC / 8);                    \
-    *(u32x4_t*)&(xs)[row * XP + kc8 * 8] = xr[j];                            \
-  });
+// LDS-DMA of 16 bytes per lane: lane l's bytes land at lds_wave_base +
+// 16*l (the base is uniform over the wave).
+#ifndef DG_LDS_PTR
+#define DG_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+#endif
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, DG_LDS_PTR(lds_wave_base), 16, 0, 0);
+}
 
-template <int RT, int NT, int KC, int XP, int WREGS, bool W8>
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (other counters untouched).
+constexpr int vm_wait(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+__device__ __forceinline__ void widen_e4m3(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = q[i];
+    o[2 * i] = (uint32_t)e4m3_to_bf(w & 0xff) | ((uint32_t)e4m3_to_bf((w >> 8) & 0xff) << 16);
+    o[2 * i + 1] = (uint32_t)e4m3_to_bf((w >> 16) & 0xff) | ((uint32_t)e4m3_to_bf(w >> 24) << 16);
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
+__device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// One K chunk of MFMAs.  Stage layout: token row r's 16-byte unit c
+// (k values 8c..8c+7 of the chunk) sits at unit r*(KC/8) + (c ^ (r & 7)),
+// so the 8 rows a ds_read_b128 phase touches fall in distinct banks.
+template <int RT, int NT, int KC, int WREGS, bool W8>
 __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
-                                           const uint4 (&w)[RT][WREGS],
-                                           const uint16_t* xs,
+                                           const u32x4_t (&w)[RT][WREGS],
+                                           const uint16_t* stage,
                                            int l16, int lg) {
 #pragma unroll
   for (int j = 0; j < KC / 32; ++j) {
-    uint4 af[RT];
+    u32x4_t af[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if (W8) {
-        uint4 lo, hi;
+        u32x4_t lo, hi;
         widen_e4m3(w[rt][j >> 1], lo, hi);
         af[rt] = (j & 1) ? hi : lo;
       } else {
         af[rt] = w[rt][j];
       }
     }
+    const int koff = W8 ? 64 * (j >> 1) + 16 * lg + 8 * (j & 1) : 32 * j + 8 * lg;
+    const int unit = (koff >> 3) ^ (l16 & 7);
     // Every token tile is computed: tiles past the last token hold clamped
     // (valid) rows whose results the epilogues drop, and a uniform branch
     // here would serialise the LDS reads behind one wait each.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint4 bx = *(const uint4*)&xs[(nt * 16 + l16) * XP + (KC / 4) * lg + 8 * j];
+      const u32x4_t bx = *(const u32x4_t*)&stage[((nt * 16 + l16) * (KC / 8) + unit) * 8];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma16x16x32(af[rt], bx, acc[rt][nt]);
+      for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma_v(af[rt], bx, acc[rt][nt]);
     }
   }
 }
 
-template <int RT, int NT, int KC, int EPI, bool W8>
+template <int RT, int NT, int KC, int D, int EPI, bool W8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void stream_kernel(StreamArgs a) {
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
   static_assert(KC == 64 || KC == 128, "K chunk");
-  constexpr int XP = KC + 8;          // LDS token-row pitch (elements)
   constexpr int WROWS = 4 * RT * 16;  // weight rows per workgroup
   constexpr int ESZ = W8 ? 1 : 2;     // bytes per weight element
-  // uint4 per row tile per chunk: a lane's KC/4 contiguous k values
+  // 16-byte weight loads per row tile per chunk (KC/4 k values per lane)
   constexpr int WREGS = (KC / 4) * ESZ / 16;
-  constexpr int XITEMS = NT * 16 * (KC / 8);  // 16-byte token items per chunk
-  static_assert(XITEMS % 256 == 0, "token items per thread");
-  constexpr int XPT = XITEMS / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][NT * 16 * XP];
+  static_assert(D >= 2, "chunks in flight");
+  constexpr int S = D + 1;                     // token stages
+  constexpr int STAGE = NT * 16 * KC;          // elements per stage
+  constexpr int UNITS = STAGE / 8;             // 16-byte units per stage
+  static_assert(UNITS % 256 == 0, "token units per thread");
+  constexpr int IPW = UNITS / 256;             // token DMAs per wave per chunk
+  constexpr int LOADS = IPW + RT * WREGS;      // loads per wave per chunk
+  static_assert((D - 1) * LOADS <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -172,7 +191,7 @@ void stream_kernel(StreamArgs a) {
       r = n_base + (wave * RT + rt) * 16 + l16;
       ok = r < a.N;
     }
-    wsrc[rt] = wgroup + ((long long)(ok ? r : 0) * a.K + (KC / 4) * lg) * ESZ;
+    wsrc[rt] = wgroup + (long long)(ok ? r : 0) * a.K * ESZ + 16 * lg;
   }
   const int nk = a.K / KC;
 
@@ -180,19 +199,22 @@ void stream_kernel(StreamArgs a) {
     const int nt_rows = min(NT * 16, t_end - t0);
     const int nt_act = (nt_rows + 15) >> 4;
 
-    const uint16_t* xsrc[XPT];
+    // token unit u = 64*(wave*IPW + i) + lane of a stage holds row
+    // u / (KC/8), logical unit (u % (KC/8)) ^ (row & 7)
+    const uint16_t* xsrc[IPW];
     const uint16_t* const xbase = a.X;
     const int32_t* const xmap = a.x_map;
     const int xdiv = a.x_map_div, ldx = a.ldx;
-    static_for<XPT>([&](auto j) {
-      const int it = tid + 256 * j;
-      const int row = it / (KC / 8), kc8 = it % (KC / 8);
+    static_for<IPW>([&](auto i) {
+      const int u = 64 * (wave * IPW + i) + lane;
+      const int row = u / (KC / 8);
+      const int c = (u % (KC / 8)) ^ (row & 7);
       const int trow = t0 + (row < nt_rows ? row : 0);
       const int src = xmap ? xmap[trow] / xdiv : trow;
-      xsrc[j] = xbase + (long long)src * ldx + kc8 * 8;
+      xsrc[i] = xbase + (long long)src * ldx + c * 8;
     });
-    u32x4_t xr[XPT];
-    uint4 wa[RT][WREGS], wb[RT][WREGS];
+    // D weight register sets; chunk k uses set k % D and stage k % S.
+    u32x4_t w[D][RT][WREGS];
 
     f32x4_t acc[RT][NT];
 #pragma unroll
@@ -200,47 +222,56 @@ void stream_kernel(StreamArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: chunk 0 in wa / Xs[0], chunk 1 in wb
-    __syncthreads();  // the previous pass is done with Xs
-    load_w<RT, WREGS, ESZ, KC>(wa, wsrc, 0);
-    DG_LOAD_X(0);
-    DG_STORE_X(Xs[0]);
-    load_w<RT, WREGS, ESZ, KC>(wb, wsrc, min(1, nk - 1));
-    __syncthreads();
-    // Issue order per half step: next token chunk (L2), MFMAs of this
-    // chunk, weight chunk two ahead (HBM), then the LDS store of the next
-    // token chunk, so that the store waits only for the token loads and the
-    // weight loads stay in flight across the next MFMAs.  Chunk indices past
-    // the end are clamped to the last chunk (a redundant, valid load) so that
-    // the body is straight-line code the compiler cannot regroup.
     const int last = nk - 1;
-    for (int kc = 0; kc < nk; kc += 2) {
-      // even chunk kc: weights in wa, tokens in Xs[0]
-      DG_LOAD_X(min(kc + 1, last));
+    // Loads of chunk k (clamped to the last chunk: a redundant, valid load
+    // into a stage and a register set whose chunk is already consumed).
+    auto issue = [&](auto p, int k) {
+      const int kk = min(k, last);
+      uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
+      static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)kk * KC, st + i * 64 * 8); });
+      load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, kk);
+    };
+    // Chunk k: wait for its loads (all but the (D-1) younger chunks'),
+    // barrier (every wave's token DMA has landed; every wave is past chunk
+    // k-1, whose stage the chunk k+D DMA reuses), MFMAs, then issue chunk
+    // k+D.  The barrier is the bare instruction: a workgroup fence here
+    // would wait for every DMA in flight.
+    auto step = [&](auto p, int k) {
+      __builtin_amdgcn_s_waitcnt(vm_wait((D - 1) * LOADS));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk<RT, NT, KC, XP, WREGS, W8>(acc, wa, Xs[0], l16, lg);
+      mfma_chunk<RT, NT, KC, WREGS, W8>(acc, w[p], &Xs[(k % S) * STAGE], l16, lg);
       __builtin_amdgcn_sched_barrier(0);
-      load_w<RT, WREGS, ESZ, KC>(wa, wsrc, min(kc + 2, last));
+      issue(p, k + D);
       __builtin_amdgcn_sched_barrier(0);
-      DG_STORE_X(Xs[1]);
-      __syncthreads();
-      if (kc + 1 >= nk) break;
-      // odd chunk kc + 1: weights in wb, tokens in Xs[1]
-      DG_LOAD_X(min(kc + 2, last));
+    };
+
+    __syncthreads();  // the previous pass is done with Xs
+    static_for<D>([&](auto p) {
+      issue(p, (int)p);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk<RT, NT, KC, XP, WREGS, W8>(acc, wb, Xs[1], l16, lg);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w<RT, WREGS, ESZ, KC>(wb, wsrc, min(kc + 3, last));
-      __builtin_amdgcn_sched_barrier(0);
-      DG_STORE_X(Xs[0]);
-      __syncthreads();
-    }
+    });
+    // Whole groups of D chunks as straight-line code in a loop entered
+    // unconditionally (nk >= D is a launch precondition), so the issue
+    // order is the same on entry and on the back edge and every wait stays
+    // exact; then the remaining nk % D chunks.
+    int kc = 0;
+    do {
+      static_for<D>([&](auto p) { step(p, kc + p); });
+      kc += D;
+    } while (kc + D <= nk);
+    static_for<D - 1>([&](auto p) {
+      if (kc + p < nk) step(p, kc + p);
+    });
+    __syncthreads();  // drains the redundant DMAs before LDS is reused
 
     // ---- epilogues: lane holds token column t0 + 16*nt + l16 and weight
     // rows 4*lg + e of each row tile
     if (EPI == EPI_LMSTATS) {
-      float4* red = (float4*)&Xs[0][0];  // [4 waves][NT*16]
-      static_assert(4 * NT * 16 * 16 <= 2 * NT * 16 * XP * 2, "LDS reuse");
+      float4* red = (float4*)&Xs[0];  // [4 waves][NT*16]
+      static_assert(4 * NT * 16 * 16 <= S * STAGE * 2, "LDS reuse");
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float m = -INFINITY, s = 0.f, t = 0.f;
@@ -364,46 +395,50 @@ void stream_kernel(StreamArgs a) {
   }
 }
 
-template <int RT, int NT, int KC, int EPI, bool W8>
+template <int RT, int NT, int KC, int D, int EPI, bool W8>
 hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
   constexpr int WROWS = 4 * RT * 16;
   int grid_x;
   if (EPI == EPI_SWIGLU) grid_x = (a.ffn + WROWS / 2 - 1) / (WROWS / 2);
   else grid_x = (a.N + WROWS - 1) / WROWS;
   if (grid_x <= 0 || groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, EPI, W8>), dim3(grid_x, groups),
+  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, D, EPI, W8>), dim3(grid_x, groups),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-constexpr int kDenseRT = 2, kMoeRT = 2;
-constexpr int kDenseKC = 64, kMoeKC = 128;
-int stream_rows_per_wg() { return 4 * kDenseRT * 16; }
-int stream_k_chunk() { return kMoeKC > kDenseKC ? kMoeKC : kDenseKC; }
+// LM head: 2 row tiles per wave (128 vocabulary rows per workgroup), 128
+// token columns per pass, K chunks of 64, 4 chunks in flight (5 stages of
+// 16 KB).  Experts: 2 row tiles, 32 token columns, K chunks of 128, 3 in
+// flight (4 stages of 8 KB).
+constexpr int kLmRT = 2, kLmKC = 64, kLmD = 4;
+constexpr int kMoeRT = 2, kMoeKC = 128, kMoeD = 3;
 
-#undef DG_LOAD_X
-#undef DG_STORE_X
+int stream_rows_per_wg() { return 4 * kLmRT * 16; }
+bool stream_lm_ok(int hidden) {
+  return hidden % kLmKC == 0 && hidden / kLmKC >= kLmD;
+}
+bool stream_moe_ok(int hidden, int ffn) {
+  return hidden % kMoeKC == 0 && ffn % kMoeKC == 0 && hidden / kMoeKC >= kMoeD &&
+         ffn / kMoeKC >= kMoeD;
+}
 
-hipError_t launch_stream(int epi, bool w8, int nt, const StreamArgs& a,
-                         int groups, hipStream_t s) {
-  if (nt == 8) {
-    switch (epi) {
-      case EPI_LMSTATS: return launch_s<kDenseRT, 8, kDenseKC, EPI_LMSTATS, false>(a, groups, s);
-      case EPI_STORE_BF16: return launch_s<kDenseRT, 8, kDenseKC, EPI_STORE_BF16, false>(a, groups, s);
-      case EPI_STORE_F32: return launch_s<kDenseRT, 8, kDenseKC, EPI_STORE_F32, false>(a, groups, s);
-      case EPI_ADD_F32: return launch_s<kDenseRT, 8, kDenseKC, EPI_ADD_F32, false>(a, groups, s);
-    }
-  } else if (nt == 2) {
-    switch (epi) {
-      case EPI_SWIGLU:
-        return w8 ? launch_s<kMoeRT, 2, kMoeKC, EPI_SWIGLU, true>(a, groups, s)
-                  : launch_s<kMoeRT, 2, kMoeKC, EPI_SWIGLU, false>(a, groups, s);
-      case EPI_DOWN:
-        return w8 ? launch_s<kMoeRT, 2, kMoeKC, EPI_DOWN, true>(a, groups, s)
-                  : launch_s<kMoeRT, 2, kMoeKC, EPI_DOWN, false>(a, groups, s);
-    }
+hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
+                         hipStream_t s) {
+  switch (epi) {
+    case EPI_LMSTATS:
+      if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
+      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false>(a, groups, s);
+    case EPI_SWIGLU:
+      if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false>(a, groups, s);
+    case EPI_DOWN:
+      if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false>(a, groups, s);
   }
   return hipErrorInvalidValue;
 }

@@ -26,8 +26,13 @@ def _randn(shape, std, name, dtype=torch.bfloat16, seed=7):
 
 # ------------------------------------------------------------------ linear
 
+# Projection shapes of one 2048-hidden layer (Q/K/V, output, router) at 256
+# rows, plus ragged rows/columns (90 columns: scalar stores) and K not a
+# multiple of the 4-step pipeline (K = 448, 320).
 @pytest.mark.parametrize("m,k,n", [(300, 256, 200), (1, 128, 64),
-                                   (256, 2048, 4096)])
+                                   (256, 2048, 4096), (256, 2048, 2048),
+                                   (256, 2048, 128), (200, 448, 96),
+                                   (200, 320, 90)])
 def test_linear_three_modes(m, k, n):
     log(f"linear m={m} k={k} n={n}")
     x = _randn((m, k), 1.0, f"lin.x{m}")
