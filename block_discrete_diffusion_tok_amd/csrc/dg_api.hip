@@ -153,7 +153,7 @@ long long attn_split_rows(const dg_model_desc& d, int max_canvases) {
   for (int n = 1; n <= max_canvases; ++n)
     best = std::max<long long>(
         best, (long long)attention_auto_splits(n, DG_CANVAS, d.n_q_heads,
-                                               d.n_kv_heads) * n);
+                                               d.n_kv_heads, 0) * n);
   return best;
 }
 
@@ -520,7 +520,9 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
     aa.plen[b] = plen[b];
   }
   aa.n = n;
-  aa.splits = attention_auto_splits(n, DG_CANVAS, Hq, Hkv);
+  int max_keys = 0;
+  for (int b = 0; b < n; ++b) max_keys = std::max(max_keys, plen[b] + DG_CANVAS);
+  aa.splits = attention_auto_splits(n, DG_CANVAS, Hq, Hkv, max_keys);
   aa.causal = commit ? 1 : 0;
   aa.out = c->attn;
   aa.opart = c->opart;
@@ -822,7 +824,7 @@ size_t dg_op_attention_workspace_bytes(int32_t n, int32_t canvas_len,
   if (n < 1 || canvas_len < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1)
     return 0;
   const int s = kv_splits > 0 ? kv_splits
-                              : attention_auto_splits(n, canvas_len, n_q_heads, n_kv_heads);
+                              : attention_auto_splits(n, canvas_len, n_q_heads, n_kv_heads, 0);
   if (s == 1) return kAlign;
   const long long rows = (long long)s * n * n_q_heads * canvas_len;
   return align_up(rows * head_dim * 4) + align_up(rows * 4);
@@ -874,8 +876,11 @@ dg_status dg_op_canvas_attention(const void* qkv, int32_t n, int32_t canvas_len,
     aa.plen[b] = prefix_len[b];
   }
   aa.n = n;
+  int max_keys = 0;
+  for (int b = 0; b < n; ++b) max_keys = std::max(max_keys, prefix_len[b] + canvas_len);
   aa.splits = kv_splits > 0 ? kv_splits
-                            : attention_auto_splits(n, canvas_len, n_q_heads, n_kv_heads);
+                            : attention_auto_splits(n, canvas_len, n_q_heads, n_kv_heads,
+                                                    max_keys);
   aa.causal = causal ? 1 : 0;
   aa.out = (uint16_t*)out;
   if (aa.splits > 1) {

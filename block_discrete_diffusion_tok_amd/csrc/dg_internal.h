@@ -175,7 +175,9 @@ struct AttnArgs {
   float* lpart;         // [splits][n*Hq*C]
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-int attention_auto_splits(int n, int C, int Hq, int Hkv);
+// KV splits for n canvases; max_keys = longest prefix + C (0: the upper
+// bound over all prefix lengths, used to size workspaces).
+int attention_auto_splits(int n, int C, int Hq, int Hkv, int max_keys);
 
 hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
                         int V, int H, float* x, hipStream_t s);

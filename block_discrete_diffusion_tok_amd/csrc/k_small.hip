@@ -34,9 +34,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok,
 // ---------------------------------------------------------------- RMSNorm
 // out[r, :] = bf16(x[src, :] / sqrt(mean(x^2) + eps) * g), one wave per row;
 // src = row_map[r] when given, rows beyond *m_dev skipped.
+// One wave per row.  Each pass keeps 8 float4 loads in flight per lane
+// (2048 floats per round), so a row costs a couple of memory latencies.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(
     const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
     const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
+  constexpr int U = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
   const int n = m_dev ? *m_dev : rows;
@@ -44,30 +47,46 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
   const int src = row_map ? row_map[r] : r;
   const float* xr = x + (long long)src * H;
   float ss = 0.f;
-  for (int i = lane * 4; i < H; i += 256) {
-    const float4 v = *(const float4*)(xr + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  for (int base = 0; base < H; base += 256 * U) {
+    float4 v[U];
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = base + 256 * c + lane * 4;
+      v[c] = i < H ? *(const float4*)(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int c = 0; c < U; ++c)
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
   const float inv = rsqrtf(ss / (float)H + eps);
   uint16_t* o = out + (long long)r * H;
-  for (int i = lane * 4; i < H; i += 256) {
-    const float4 v = *(const float4*)(xr + i);
-    const float4 gg = *(const float4*)(g + i);
-    const uint16_t b0 = f2bf(v.x * inv * gg.x), b1 = f2bf(v.y * inv * gg.y);
-    const uint16_t b2 = f2bf(v.z * inv * gg.z), b3 = f2bf(v.w * inv * gg.w);
-    *(uint2*)(o + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
-                                  (uint32_t)b2 | ((uint32_t)b3 << 16));
-    if (copy_f32)
-      *(float4*)(copy_f32 + (long long)r * H + i) =
-          make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
+  for (int base = 0; base < H; base += 256 * U) {
+    float4 v[U], gg[U];
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = base + 256 * c + lane * 4;
+      if (i < H) {
+        v[c] = *(const float4*)(xr + i);
+        gg[c] = *(const float4*)(g + i);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = base + 256 * c + lane * 4;
+      if (i >= H) continue;
+      const uint16_t b0 = f2bf(v[c].x * inv * gg[c].x), b1 = f2bf(v[c].y * inv * gg[c].y);
+      const uint16_t b2 = f2bf(v[c].z * inv * gg[c].z), b3 = f2bf(v[c].w * inv * gg[c].w);
+      *(uint2*)(o + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
+                                    (uint32_t)b2 | ((uint32_t)b3 << 16));
+      if (copy_f32)
+        *(float4*)(copy_f32 + (long long)r * H + i) =
+            make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
+    }
   }
 }
 
-// ---------------------------------------------------------------- top-k
-// One wave per token: k rounds of (max value, lowest index) over the E
-// logits (up to 4 per lane), then softmax over the k selected.
 __global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T,
                                                    int E, int k, int32_t* idx,
                                                    float* w) {
@@ -276,18 +295,29 @@ __device__ __forceinline__ void merge_stats(float& m, float& s, float& t,
   m = mn;
 }
 
+// One workgroup per row: each thread merges 8 tiles' partials at a time
+// (loads issued together), then the wave and the 4 waves are merged.
 __global__ __launch_bounds__(256) void lm_merge_kernel(
     const float4* part, int n_tiles, const int32_t* m_dev, int m_max,
     const int32_t* row_map, float* entropy, float* lse, int32_t* argmax) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
+  constexpr int U = 8;
+  __shared__ float4 red[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = blockIdx.x;
   const int n = m_dev ? *m_dev : m_max;
   if (r >= n) return;
   float m = -INFINITY, s = 0.f, t = 0.f;
   int am = 0x7fffffff;
-  for (int i = lane; i < n_tiles; i += 64) {
-    const float4 p = part[(long long)r * n_tiles + i];
-    merge_stats(m, s, t, am, p.x, p.y, p.z, __float_as_int(p.w));
+  const float4* pr = part + (long long)r * n_tiles;
+  for (int base = 0; base < n_tiles; base += 256 * U) {
+    float4 p[U];
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = base + 256 * c + tid;
+      p[c] = i < n_tiles ? pr[i] : make_float4(-INFINITY, 0.f, 0.f, __int_as_float(0x7fffffff));
+    }
+#pragma unroll
+    for (int c = 0; c < U; ++c) merge_stats(m, s, t, am, p[c].x, p[c].y, p[c].z, __float_as_int(p[c].w));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -296,7 +326,12 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(
     const int am2 = shfl_xor(am, off);
     merge_stats(m, s, t, am, m2, s2, t2, am2);
   }
-  if (lane == 0) {
+  if (lane == 0) red[wave] = make_float4(m, s, t, __int_as_float(am));
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      merge_stats(m, s, t, am, red[w].x, red[w].y, red[w].z, __float_as_int(red[w].w));
     const int pos = row_map ? row_map[r] : r;
     const float ls = logf(s);
     lse[pos] = m + ls;
@@ -305,11 +340,6 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(
   }
 }
 
-// ---------------------------------------------------------------- EB select
-// One workgroup of 256 threads per canvas, thread j = position j.
-// Rank of each uncommitted position under the total order (entropy,
-// position); the fp64 running sum is taken in that order by one thread,
-// exactly as the rule defines it.
 __global__ __launch_bounds__(256) void eb_kernel(
     const float* entropy, const int32_t* argmax, uint8_t* committed,
     int32_t* tokens, int32_t* step, const float* gamma, int cap, int refine,
@@ -481,7 +511,7 @@ hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* row_map, float* entropy, float* lse,
                            int32_t* argmax, hipStream_t s) {
   if (m_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lm_merge_kernel, dim3((m_max + 3) / 4), dim3(256), 0, s,
+  hipLaunchKernelGGL(lm_merge_kernel, dim3(m_max), dim3(256), 0, s,
                      part, n_tiles, m_dev, m_max, row_map, entropy, lse,
                      argmax);
   return hipGetLastError();
