@@ -78,6 +78,26 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
+// ------------------------------------------------------------------ packed weights
+// Every weight matrix the kernels read ([R, K] row-major per group: Q/K/V,
+// output, router, gate/up, down, the tied embedding) is stored in an
+// MFMA-tiled layout: R/16 x K/kPackK blocks of 1024 bytes, block (rb, kb)
+// at byte (rb * K/kPackK + kb) * 1024, kPackK = 64 / element bytes (32 bf16
+// or 64 e4m3 values).  Inside a block, the 16 bytes at 16 * l (l = r + 16 q,
+// r < 16, q < 4) hold row 16 rb + r, values kb * kPackK + q * kPackK/4 ..
+// +kPackK/4 - 1: exactly what lane l feeds to a 16x16x32 MFMA as the A
+// operand, so one wave load instruction reads one contiguous kilobyte.
+// Rows are zero-padded to a multiple of 16; with several groups (experts)
+// the row count per group must already be a multiple of 16.
+constexpr int kPackBlock = 1024;
+__host__ __device__ constexpr int pack_k(int esz) { return 64 / esz; }
+// byte offset of block (rb, kb) in a matrix with K columns
+__host__ __device__ inline long long pack_block_offset(int rb, int kb, int K, int esz) {
+  return ((long long)rb * (K / pack_k(esz)) + kb) * kPackBlock;
+}
+hipError_t launch_pack(const void* src, int groups, int rows, int cols, int esz,
+                       void* dst, hipStream_t s);
+
 // ------------------------------------------------------------------ launches
 // Every launcher returns hipSuccess or the launch error; shapes were checked
 // by the caller.

@@ -9,8 +9,10 @@
 //   - tied LM head with the vocabulary statistics fused: per row and tile of
 //     vocabulary columns the partial (max, sum e^(z-max), sum e^(z-max)(z-max),
 //     argmax), so that logits never have to be written.
-// Expert weights may be OCP E4M3 bytes: they are widened to bf16 exactly on
-// their way into LDS and the per-row scale is applied in the epilogue.
+// Weights are in the packed (MFMA-tiled) layout of 1 KB blocks, so every
+// weight load instruction reads contiguous kilobytes.  Expert weights may be
+// OCP E4M3 bytes: they are widened to bf16 exactly on their way into LDS and
+// the per-row scale is applied in the epilogue.
 //
 // Workgroup: 256 threads = 4 waves in a 2x2 grid over a BM (tokens) x BN
 // (weight rows) tile; each wave owns (BM/2) x (BN/2) as MFMA 16x16x32 tiles
@@ -71,15 +73,18 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
 }
 
 // Global loads of K step kt into staging register set p, and the store of
-// set p into LDS buffer b (token chunk j of thread tid covers row c/8, 8 k
-// values at (c%8)*8 with c = tid + 256 j; weight chunks likewise, or 16
-// bytes of e4m3 covering row c/4 and k values (c%4)*16..+15).
+// set p into LDS buffer b.  Token chunk j of thread tid covers row c/8, 8 k
+// values at (c%8)*8 with c = tid + 256 j.  Weight piece c of a K step is
+// lane c%64 of packed block c/64: for bf16 the BN/16 row tiles x 2 blocks of
+// 32 k values (block b: row tile b/2, k values 32*(b%2) + 8*(lane/16)), for
+// e4m3 BN/16 row tiles x 1 block of 64 (k values 16*(lane/16), widened to
+// bf16 on the way into LDS); the piece's row is 16 * tile + lane % 16.
 #define DG_GLOAD(p, kt)                                                       \
   static_for<XA>([&](auto j) {                                                \
     tr[p][j] = *(const u32x4_t*)(tsrc[j] + (long long)(kt) * BK);             \
   });                                                                         \
   static_for<XB>([&](auto j) {                                                \
-    wr[p][j] = *(const u32x4_t*)(wsrc[j] + (long long)(kt) * BK * ESZ);       \
+    wr[p][j] = *(const u32x4_t*)(wsrc[j] + (long long)(kt) * ESZ * kPackBlock); \
   });
 #define DG_LSTORE(b, p)                                                       \
   static_for<XA>([&](auto j) {                                                \
@@ -87,14 +92,16 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
     *(u32x4_t*)&Ts[b][(c >> 3) * LDK + (c & 7) * 8] = tr[p][j];               \
   });                                                                         \
   static_for<XB>([&](auto j) {                                                \
-    const int c = tid + 256 * j;                                              \
+    const int c = tid + 256 * j, blk = c >> 6, ln = c & 63;                   \
     if (W8) {                                                                 \
       u32x4_t lo, hi;                                                         \
       widen16(wr[p][j], lo, hi);                                              \
-      *(u32x4_t*)&Ws[b][(c >> 2) * LDK + (c & 3) * 16] = lo;                  \
-      *(u32x4_t*)&Ws[b][(c >> 2) * LDK + (c & 3) * 16 + 8] = hi;              \
+      const int o = (blk * 16 + (ln & 15)) * LDK + (ln >> 4) * 16;            \
+      *(u32x4_t*)&Ws[b][o] = lo;                                              \
+      *(u32x4_t*)&Ws[b][o + 8] = hi;                                          \
     } else {                                                                  \
-      *(u32x4_t*)&Ws[b][(c >> 3) * LDK + (c & 7) * 8] = wr[p][j];             \
+      const int o = ((blk >> 1) * 16 + (ln & 15)) * LDK + (blk & 1) * 32 + (ln >> 4) * 8; \
+      *(u32x4_t*)&Ws[b][o] = wr[p][j];                                        \
     }                                                                         \
   });
 
@@ -145,21 +152,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     tsrc[j] = a.A + (long long)src * a.lda + (c & 7) * 8;
   });
   const char* wsrc[XB];
+  const char* const wgroup = (const char*)a.B + (long long)group * a.b_group_stride * ESZ;
   static_for<XB>([&](auto j) {
-    const int c = tid + 256 * j;
-    const int r = W8 ? (c >> 2) : (c >> 3);
-    int wrow;
+    const int c = tid + 256 * j, blk = c >> 6, ln = c & 63;
+    const int tile = W8 ? blk : (blk >> 1);     // 16-row tile within the BN rows
+    const int kb = W8 ? 0 : (blk & 1);          // k block within the K step
+    int rb;                                     // global 16-row tile
     if (EPI == EPI_SWIGLU) {
       // 16 gate rows then the 16 matching up rows, per 32-row block
-      const int ch = min(nt * (BN / 2) + (r >> 5) * 16 + (r & 15), a.ffn - 1);
-      wrow = ((r >> 4) & 1) ? a.ffn + ch : ch;
+      const int cb = min(nt * (BN / 32) + (tile >> 1), a.ffn / 16 - 1);
+      rb = (tile & 1) ? a.ffn / 16 + cb : cb;
     } else {
-      wrow = min(nt * BN + r, a.N - 1);
+      rb = min(nt * (BN / 16) + tile, (a.N + 15) / 16 - 1);  // zero-padded last tile
     }
-    const long long elem = (long long)group * a.b_group_stride +
-                           (long long)wrow * a.K +
-                           (W8 ? (c & 3) * 16 : (c & 7) * 8);
-    wsrc[j] = (const char*)a.B + elem * ESZ;
+    wsrc[j] = wgroup + pack_block_offset(rb, kb, a.K, ESZ) + 16 * ln;
   });
 
   f32x4_t acc[TM][TN];

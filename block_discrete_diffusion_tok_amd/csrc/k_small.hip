@@ -13,21 +13,52 @@ namespace {
 // x[t, :] = E[tok_t, :] (bf16 -> fp32).  One workgroup per token.  Token ids
 // outside [0, V) are clamped into range so that a bad id cannot read outside
 // the embedding.
+// Embedding rows gathered from the packed (MFMA-tiled) table: value k of
+// row id sits in block (id / 16, k / 32), piece (id % 16) + 16 * (k % 32 / 8).
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok,
                                                     const uint16_t* E, int V,
                                                     int H, float* x) {
   const int t = blockIdx.x;
   const int id = min(max(tok[t], 0), V - 1);
-  const uint16_t* src = E + (long long)id * H;
+  const char* base = (const char*)E;
   float* dst = x + (long long)t * H;
   for (int i = threadIdx.x * 8; i < H; i += 256 * 8) {
-    const uint4 v = *(const uint4*)(src + i);
+    const long long off = pack_block_offset(id >> 4, i >> 5, H, 2) +
+                          16 * ((id & 15) + 16 * ((i & 31) >> 3));
+    const uint4 v = *(const uint4*)(base + off);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dst[i + 2 * q] = bf2f((uint16_t)(w[q] & 0xffff));
-      dst[i + 2 * q + 1] = bf2f((uint16_t)(w[q] >> 16));
-    }
+    float4 lo, hi;
+    lo.x = bf2f((uint16_t)(w[0] & 0xffff)); lo.y = bf2f((uint16_t)(w[0] >> 16));
+    lo.z = bf2f((uint16_t)(w[1] & 0xffff)); lo.w = bf2f((uint16_t)(w[1] >> 16));
+    hi.x = bf2f((uint16_t)(w[2] & 0xffff)); hi.y = bf2f((uint16_t)(w[2] >> 16));
+    hi.z = bf2f((uint16_t)(w[3] & 0xffff)); hi.w = bf2f((uint16_t)(w[3] >> 16));
+    *(float4*)(dst + i) = lo;
+    *(float4*)(dst + i + 4) = hi;
+  }
+}
+
+// Row-major [groups][rows][cols] -> packed layout, one 16-byte piece per
+// thread (grid-stride); rows are padded with zeros up to a multiple of 16.
+__global__ __launch_bounds__(256) void pack_kernel(const char* src, int rows,
+                                                   long long pieces_per_group,
+                                                   int groups, int cols, int esz,
+                                                   char* dst) {
+  const long long total = pieces_per_group * groups;
+  const int kb_n = cols / pack_k(esz);
+  const int per_piece = 16 / esz;  // values per piece
+  const long long src_group = (long long)rows * cols * esz;
+  for (long long p = (long long)blockIdx.x * 256 + threadIdx.x; p < total;
+       p += (long long)gridDim.x * 256) {
+    const long long g = p / pieces_per_group, pin = p % pieces_per_group;
+    const long long block = pin >> 6;
+    const int lane = (int)(pin & 63);
+    const long long rb = block / kb_n;
+    const int kb = (int)(block % kb_n);
+    const long long row = rb * 16 + (lane & 15);
+    const long long col = (long long)kb * pack_k(esz) + (lane >> 4) * per_piece;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < rows) v = *(const uint4*)(src + g * src_group + (row * cols + col) * esz);
+    *(uint4*)(dst + p * 16) = v;
   }
 }
 
@@ -446,6 +477,16 @@ __global__ __launch_bounds__(256) void kv_install_kernel(const uint16_t* src,
 }
 
 }  // namespace
+
+hipError_t launch_pack(const void* src, int groups, int rows, int cols, int esz,
+                       void* dst, hipStream_t s) {
+  const long long ppg = (long long)((rows + 15) / 16 * 16) * cols * esz / 16;
+  if (ppg * groups <= 0) return hipSuccess;
+  const long long blocks = std::min<long long>((ppg * groups + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const char*)src, rows, ppg, groups, cols, esz, (char*)dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
                         int V, int H, float* x, hipStream_t s) {

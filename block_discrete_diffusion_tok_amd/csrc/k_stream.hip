@@ -7,9 +7,12 @@
 // in the LM head), so the kernel is organised around HBM streaming:
 //
 //   * each wave owns RT x 16 weight rows and reads them straight from HBM
-//     into registers, 64 contiguous bytes per lane per row tile and 128-wide
-//     K chunk, two chunks ahead of the MFMAs (weights are used once, so they
-//     never pass through LDS);
+//     into registers, D chunks ahead of the MFMAs (weights are used once, so
+//     they never pass through LDS).  The weights are in the packed
+//     (MFMA-tiled) layout, so every wave load instruction reads one
+//     contiguous kilobyte of full cache lines: with a row-major layout each
+//     instruction would touch 16 lines and use half of each, and the L1's
+//     outstanding-miss capacity, not HBM, would bound the stream;
 //   * the group's token rows (gathered through the expert permutation when
 //     needed) go HBM/L2 -> LDS directly (LDS-DMA loads, no registers) into
 //     a ring of D+1 chunk stages shared by the 4 waves.  Each chunk's token
@@ -27,9 +30,8 @@
 // group lg (lanes 16*lg..16*lg+15) the 8 values k0 + 32*j + 8*lg + [0, 8)
 // for bf16 weights, and k0 + 64*(j/2) + 16*lg + 8*(j%2) + [0, 8) for e4m3
 // weights (both operands alike; the dot product is the same sum in another
-// order).  Either way a lane's q-th 16-byte weight load of the chunk starts
-// at byte 64*q + 16*lg of its row, so the 4 lanes of a row read 64
-// contiguous bytes per load instruction.
+// order).  This is the order of the packed layout's blocks: a lane's q-th
+// 16-byte weight load of chunk kc is block kc * KC/(32 or 64) + q.
 #include <math.h>
 
 #include "dg_internal.h"
@@ -60,6 +62,8 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 // never stored, so the loads stay plain global loads with no null test (a
 // select between a global and a private "zero" would turn them into flat
 // loads, which the waitcnt pass can only wait for all at once).
+// In the packed layout the q-th load of chunk kc is block kc * WREGS + q of
+// the row tile: one contiguous kilobyte per wave load.
 template <int RT, int WREGS, int ESZ, int KC>
 __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
                                        const char* const (&src)[RT], int kc) {
@@ -67,7 +71,7 @@ __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int q = 0; q < WREGS; ++q)
-      w[rt][q] = *(const u32x4_t*)(src[rt] + (long long)kc * KC * ESZ + 64 * q);
+      w[rt][q] = *(const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackBlock);
 }
 
 // LDS-DMA of 16 bytes per lane: lane l's bytes land at lds_wave_base +
@@ -172,26 +176,27 @@ void stream_kernel(StreamArgs a) {
   }
   if (t_end <= t_begin) return;
 
-  // ---- this lane's weight rows (r < n_valid) and their source pointers
+  // ---- this wave's weight row tiles (16 rows each) and the packed address
+  // of this lane's piece of their first block; tiles past the matrix read
+  // tile 0 (valid addresses, results never stored)
   const int n_base = blockIdx.x * WROWS;
   const char* wgroup = (const char*)a.W + (long long)group * a.w_group_stride * ESZ;
   const char* wsrc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    int r;
+    int r0;
     bool ok;
     if (EPI == EPI_SWIGLU) {
-      // tiles [0, RT/2) are gate rows of channels c0 + 16*rt + l16, tiles
-      // [RT/2, RT) the up rows of the same channels
-      const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT);
-      const int ch = c0 + (rt % (RT / 2)) * 16 + l16;
-      ok = ch < a.ffn;
-      r = (rt < RT / 2) ? ch : a.ffn + ch;
+      // tiles [0, RT/2) are gate rows of channels c0 + 16*rt + [0, 16),
+      // tiles [RT/2, RT) the up rows of the same channels
+      const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT) + (rt % (RT / 2)) * 16;
+      ok = c0 < a.ffn;
+      r0 = (rt < RT / 2) ? c0 : a.ffn + c0;
     } else {
-      r = n_base + (wave * RT + rt) * 16 + l16;
-      ok = r < a.N;
+      r0 = n_base + (wave * RT + rt) * 16;
+      ok = r0 < a.N;
     }
-    wsrc[rt] = wgroup + (long long)(ok ? r : 0) * a.K * ESZ + 16 * lg;
+    wsrc[rt] = wgroup + pack_block_offset(ok ? r0 >> 4 : 0, 0, a.K, ESZ) + 16 * lane;
   }
   const int nk = a.K / KC;
 

@@ -92,6 +92,8 @@ _SIGS = {
     "dg_kv_len": (_I, [_P, _I]),
     "dg_op_rmsnorm": (_I, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
     "dg_op_linear": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
+    "dg_packed_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "dg_pack_weights": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "dg_op_canvas_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                                     ctypes.POINTER(_I), ctypes.POINTER(_I), _I,
                                     _I, _P, _P, ctypes.c_size_t, _P]),
@@ -157,6 +159,55 @@ def layer_weights(lw):
                                     "gate_up_scale", "down_scale")])
 
 
+_PACKED_KEYS = ("w_qkv", "w_o", "w_router", "w_gate_up", "w_down")
+
+
+class Packed:
+    """A weight matrix in libdg's packed (MFMA-tiled) layout: groups x
+    [rows, cols] row-major made into 1 KB blocks by dg_pack_weights."""
+
+    def __init__(self, buf, groups, rows, cols, dtype):
+        self.buf, self.groups, self.rows, self.cols = buf, groups, rows, cols
+        self.dtype = dtype
+
+    def data_ptr(self):
+        return self.buf.data_ptr()
+
+
+def pack(t):
+    """Packed copy of a row-major device matrix [R, K] or [G, R, K] (bf16,
+    or uint8 holding e4m3 bytes)."""
+    if isinstance(t, Packed):
+        return t
+    L = lib()
+    g, r, c = (t.shape if t.dim() == 3 else (1, *t.shape))
+    dt = BF16 if t.dtype == torch.bfloat16 else FP8_E4M3
+    nb = L.dg_packed_bytes(g, r, c, dt)
+    if nb == 0:
+        raise DgError(2, f"cannot pack a {tuple(t.shape)} {t.dtype} matrix")
+    buf = torch.empty(nb, dtype=torch.uint8, device=t.device)
+    src = t.contiguous()
+    _check(L.dg_pack_weights(_ptr(src), g, r, c, dt, _ptr(buf), _stream()))
+    return Packed(buf, g, r, c, dt)
+
+
+def pack_weights(weights):
+    """Copy of a weight dict (as ``synth.make_weights`` makes it) with the
+    embedding and every layer matrix packed; other entries are shared."""
+    out = dict(weights)
+    out["embed"] = pack(weights["embed"])
+    out["layers"] = []
+    for lw in weights["layers"]:
+        if lw is None:
+            out["layers"].append(None)
+            continue
+        d = dict(lw)
+        for k in _PACKED_KEYS:
+            d[k] = pack(lw[k])
+        out["layers"].append(d)
+    return out
+
+
 def _i32_array(values):
     arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
     return arr
@@ -173,6 +224,7 @@ class Engine:
                  max_canvases=1, device="cuda"):
         L = lib()
         self.shape = shape
+        weights = pack_weights(weights)  # (already-packed matrices pass through)
         self.weights = weights  # keep alive
         self.desc = model_desc(shape)
         self._layers = (LayerWeights * shape.n_layers)(
@@ -290,8 +342,10 @@ def op_rmsnorm(x, g, eps, out):
 
 
 def op_linear(x, w, out, mode):
+    """w: row-major [N, K] (packed here) or a Packed matrix."""
+    w = pack(w)
     _check(lib().dg_op_linear(_ptr(x), x.shape[0], x.shape[1], _ptr(w),
-                              w.shape[0], mode, _ptr(out), _stream()))
+                              w.rows, mode, _ptr(out), _stream()))
 
 
 def op_canvas_attention(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,
@@ -318,6 +372,9 @@ def op_router_topk(logits, top_k, idx, w):
 def op_moe(shape, lw, xhat, y, route_idx=None, route_w=None, counts=None):
     L = lib()
     desc = model_desc(shape)
+    lw = dict(lw)
+    for k in ("w_router", "w_gate_up", "w_down"):
+        lw[k] = pack(lw[k])
     w = layer_weights(lw)
     nb = L.dg_op_moe_workspace_bytes(ctypes.byref(desc), xhat.shape[0])
     ws = _ws(nb, xhat.device)
@@ -328,11 +385,13 @@ def op_moe(shape, lw, xhat, y, route_idx=None, route_w=None, counts=None):
 
 
 def op_lmhead_entropy(xhat, embed, entropy, lse, argmax, logits=None):
+    """embed: row-major [V, H] (packed here) or a Packed matrix."""
     L = lib()
-    nb = L.dg_op_lmhead_workspace_bytes(xhat.shape[0], embed.shape[0])
+    embed = pack(embed)
+    nb = L.dg_op_lmhead_workspace_bytes(xhat.shape[0], embed.rows)
     ws = _ws(nb, xhat.device)
     _check(L.dg_op_lmhead_entropy(_ptr(xhat), xhat.shape[0], xhat.shape[1],
-                                  _ptr(embed), embed.shape[0], _ptr(entropy),
+                                  _ptr(embed), embed.rows, _ptr(entropy),
                                   _ptr(lse), _ptr(argmax), _ptr(logits),
                                   _ptr(ws), ws.numel(), _stream()))
     return ws

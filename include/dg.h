@@ -82,22 +82,42 @@ typedef struct {
   int32_t expert_dtype;   /* dg_dtype of w_gate_up / w_down */
 } dg_model_desc;
 
+/* Packed weight layout.  Every weight matrix the kernels read (w_qkv, w_o,
+ * w_router, w_gate_up, w_down and the embedding) is passed in a tiled form
+ * made by dg_pack_weights from the row-major matrix [R, K] (per group for
+ * the expert matrices): blocks of 1024 bytes, each 16 rows x 64/b values (b
+ * = element bytes), block (rb, kb) at byte (rb * K * b / 64 + kb) * 1024,
+ * and in a block the 16 bytes at 16 * (r + 16 q) hold row 16 rb + r, values
+ * kb * 64/b + q * 16/b .. + 16/b - 1.  This is the operand order of the
+ * 16x16x32 MFMA, so the kernels stream weights with one contiguous
+ * kilobyte per wave load.  Rows are zero-padded to a multiple of 16 (with
+ * groups > 1 the rows per group must be a multiple of 16); K must be a
+ * multiple of 64/b. */
+size_t dg_packed_bytes(int32_t groups, int32_t rows, int32_t cols, int32_t dtype);
+
+/* Pack groups x [rows, cols] row-major (bf16 or e4m3 bytes, device memory)
+ * into dst (dg_packed_bytes bytes, device, must not overlap src), enqueued
+ * on stream.  DG_ERR_SHAPE for shapes the layout cannot hold,
+ * DG_ERR_INVALID_ARG for NULL pointers or another dtype. */
+dg_status dg_pack_weights(const void* src, int32_t groups, int32_t rows,
+                          int32_t cols, int32_t dtype, void* dst, void* stream);
+
 /* Weights of one layer (all device pointers, read-only, must outlive the
- * context). */
+ * context).  Matrices are in the packed layout above. */
 typedef struct {
   const float* attn_norm;     /* [H] fp32 RMSNorm gain before attention */
   const void* w_qkv;          /* [(Hq + 2 Hkv) D, H] bf16: Q rows, K rows, V rows */
   const void* w_o;            /* [H, Hq D] bf16 */
   const float* ffn_norm;      /* [H] fp32 RMSNorm gain before the MoE */
   const void* w_router;       /* [E, H] bf16 */
-  const void* w_gate_up;      /* [E, 2F, H] bf16 or e4m3: F gate rows, then F up rows */
-  const void* w_down;         /* [E, H, F] bf16 or e4m3 */
+  const void* w_gate_up;      /* E groups of [2F, H] bf16 or e4m3: F gate rows, then F up rows */
+  const void* w_down;         /* E groups of [H, F] bf16 or e4m3 */
   const float* gate_up_scale; /* [E, 2F] fp32 per-row scale (e4m3 only, else NULL) */
   const float* down_scale;    /* [E, H] fp32 per-row scale (e4m3 only, else NULL) */
 } dg_layer_weights;
 
 typedef struct {
-  const void* embed;               /* [V, H] bf16; also the tied LM head */
+  const void* embed;               /* [V, H] bf16, packed; also the tied LM head */
   const float* final_norm;         /* [H] fp32 */
   const dg_layer_weights* layers;  /* (host) array of n_layers entries, copied */
 } dg_weights;

@@ -24,7 +24,8 @@ dg_status dg_op_rmsnorm(const float* x, int32_t rows, int32_t hidden,
 
 /* Dense projection y = x W^T with bf16 operands and fp32 accumulation
  * (Q/K/V, output projection and router logits of every layer).
- * x [M, K] bf16, w [N, K] bf16, K a multiple of 64.
+ * x [M, K] bf16, w [N, K] bf16 in the packed layout (dg.h), K a multiple
+ * of 64.
  * mode 0: out [M, N] bf16 = y;  1: out [M, N] fp32 = y;
  * mode 2: out [M, N] fp32 += y (residual add). */
 dg_status dg_op_linear(const void* x, int32_t m, int32_t k, const void* w,
@@ -68,7 +69,7 @@ dg_status dg_op_router_topk(const float* logits, int32_t tokens,
  * SwiGLU, grouped down GEMM scaled by the gate weight, un-permute.
  *   y_t = sum_j w_tj W_d,e (silu(W_g,e x_t) * W_u,e x_t),  e = idx_tj.
  * desc: hidden, n_experts, top_k, expert_ffn, expert_dtype are used;
- * weights: w_router, w_gate_up, w_down and the e4m3 scales are used.
+ * weights: w_router, w_gate_up, w_down (packed) and the e4m3 scales are used.
  * xhat [T, H] bf16 -> y [T, H] fp32.  route_idx [T, k] / route_w [T, k] /
  * counts [E] (tokens per expert) are optional outputs (NULL to skip). */
 dg_status dg_op_moe(const dg_model_desc* desc, const dg_layer_weights* weights,
@@ -81,7 +82,7 @@ size_t dg_op_moe_workspace_bytes(const dg_model_desc* desc, int32_t tokens);
  * vocabulary): z = xhat E^T per row; lse = log sum exp z; entropy =
  * lse - sum softmax(z) z (nats, clamped at 0); argmax = lowest id of max z.
  * Logits are not materialised unless `logits` is non-NULL.
- * xhat [M, H] bf16, embed [V, H] bf16 -> entropy, lse [M] fp32,
+ * xhat [M, H] bf16, embed [V, H] bf16 packed -> entropy, lse [M] fp32,
  * argmax [M] int32, logits NULL or [M, V] fp32. */
 dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                                const void* embed, int32_t vocab,

@@ -148,3 +148,19 @@ def test_sampler_and_ops_validation():
     assert L.dg_op_kv_append(f, 1, 256, 16, 8, 128, f, f, 1, 4096, req, row0,
                              None) == 3
     assert L.dg_status_string(5) == b"DG_ERR_HIP"
+
+
+def test_packed_layout_sizes_and_validation():
+    L = dg.lib()
+    # rows padded to whole 16-row tiles; K a multiple of 32 (bf16) / 64 (e4m3)
+    assert L.dg_packed_bytes(1, 200, 256, dg.BF16) == 208 * 256 * 2
+    assert L.dg_packed_bytes(1, 262144, 2048, dg.BF16) == 262144 * 2048 * 2
+    assert L.dg_packed_bytes(128, 1536, 2048, dg.FP8_E4M3) == 128 * 1536 * 2048
+    assert L.dg_packed_bytes(2, 200, 256, dg.BF16) == 0     # groups need whole tiles
+    assert L.dg_packed_bytes(1, 64, 48, dg.BF16) == 0       # K not a multiple of 32
+    assert L.dg_packed_bytes(1, 64, 32, dg.FP8_E4M3) == 0   # K not a multiple of 64
+    assert L.dg_packed_bytes(1, 64, 64, 7) == 0
+    f = ctypes.c_void_p(0x1000)
+    assert L.dg_pack_weights(None, 1, 16, 64, dg.BF16, f, None) == 1
+    assert L.dg_pack_weights(f, 1, 16, 64, 7, f, None) == 1
+    assert L.dg_pack_weights(f, 2, 20, 64, dg.BF16, f, None) == 2

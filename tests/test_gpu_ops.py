@@ -54,6 +54,42 @@ def test_linear_three_modes(m, k, n):
     assert e_bf < 8e-3 and e32 < 1e-5 and e_add < 1e-5
 
 
+# ------------------------------------------------------------------ packing
+
+def _pack_reference(a, esz):
+    """The packed layout by its definition (include/dg.h): groups x [R, K]
+    byte matrices -> 1 KB blocks of 16 rows x 64/esz values, block (rb, kb)
+    at (rb * K*esz/64 + kb) * 1024, piece r + 16 q = row 16 rb + r, values
+    kb * 64/esz + q * 16/esz .. +16/esz - 1; rows zero-padded to 16."""
+    g, r, kbytes = a.shape
+    rp = (r + 15) // 16 * 16
+    pad = np.zeros((g, rp, kbytes), np.uint8)
+    pad[:, :r] = a
+    out = np.zeros((g, rp // 16, kbytes // 64, 64, 16), np.uint8)
+    for rb in range(rp // 16):
+        for kb in range(kbytes // 64):
+            for q in range(4):
+                for rr in range(16):
+                    out[:, rb, kb, rr + 16 * q] = pad[:, 16 * rb + rr,
+                                                     64 * kb + 16 * q:64 * kb + 16 * q + 16]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("groups,rows,cols,e4m3", [(1, 40, 96, False), (3, 32, 128, True)])
+def test_pack_weights_matches_layout_definition(groups, rows, cols, e4m3):
+    gen = torch.Generator().manual_seed(11)
+    if e4m3:
+        t = torch.randint(0, 256, (groups, rows, cols), dtype=torch.uint8, generator=gen)
+        a = t.numpy()
+    else:
+        t = torch.randn(groups, rows, cols, generator=gen).to(torch.bfloat16)
+        a = t.view(torch.uint8).numpy().reshape(groups, rows, cols * 2)
+    p = dg.pack(t.to(DEV) if groups > 1 else t[0].to(DEV))
+    torch.cuda.synchronize()
+    got = p.buf.cpu().numpy()
+    assert np.array_equal(got, _pack_reference(a, 1 if e4m3 else 2))
+
+
 # ------------------------------------------------------------------ rmsnorm
 
 @pytest.mark.parametrize("rows,h", [(37, 256), (256, 2048)])
