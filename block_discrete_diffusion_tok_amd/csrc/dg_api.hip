@@ -105,6 +105,7 @@ struct dg_ctx {
   uint16_t* act;
   float* y;
   int32_t* row_map;
+  int32_t* pos_map;
   int32_t* m_dev;
   float4* lm_part;
 };
@@ -215,6 +216,7 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
   const size_t o_op = cv.take(split_rows * d.head_dim * 4);
   const size_t o_lp = cv.take(split_rows * 4);
   const size_t o_rm = cv.take(T * 4);
+  const size_t o_pm = cv.take(T * 4);
   const size_t o_md = cv.take(4);
   const size_t o_lm = cv.take(T * lm_tiles(d.vocab) * 16);
   const size_t o_moe = cv.take(moe_layout(d, (int)T, nullptr, nullptr));
@@ -227,6 +229,7 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->opart = (float*)(w + o_op);
     c->lpart = (float*)(w + o_lp);
     c->row_map = (int32_t*)(w + o_rm);
+    c->pos_map = (int32_t*)(w + o_pm);
     c->m_dev = (int32_t*)(w + o_md);
     c->lm_part = (float4*)(w + o_lm);
     MoeBufs mb;
@@ -344,10 +347,14 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
 
 // MoE FFN on xh [T, H] bf16: y mixture added into x (if x) and/or stored
 // into moe_out (if moe_out).
+// With next_g, the un-permute also applies the next RMSNorm (gain next_g)
+// into next_xh (rows mapped by next_row, see launch_unpermute_norm).
 hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
                    const uint16_t* xh, int T, const MoeBufs& b, float* x,
                    float* moe_out, int32_t* counts, hipStream_t s,
-                   Profiler* prof = nullptr) {
+                   Profiler* prof = nullptr, const float* next_g = nullptr,
+                   uint16_t* next_xh = nullptr, float* next_copy = nullptr,
+                   const int32_t* next_row = nullptr) {
   const int H = d.hidden, E = d.n_experts, k = d.top_k, F = d.expert_ffn;
   const bool w8 = d.expert_dtype == DG_FP8_E4M3;
   const int pairs = T * k;
@@ -409,6 +416,9 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
       if ((e = launch_stream(EPI_DOWN, w8, dn, E, s)) != hipSuccess) return e;
     }
     ProfScope ps10(prof, 10);
+    if (next_g)
+      return launch_unpermute_norm(b.y, T, k, H, x, moe_out, next_g, d.rms_eps,
+                                   next_xh, next_copy, next_row, s);
     return launch_unpermute(b.y, T, k, H, x, moe_out, s);
   }
   const int grid_m = (pairs + kGroupBM - 1) / kGroupBM + std::min(E, pairs);
@@ -440,6 +450,9 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     if ((e = launch_gemm(EPI_DOWN, w8, dn, grid_m, s)) != hipSuccess) return e;
   }
   ProfScope ps10(prof, 10);
+  if (next_g)
+    return launch_unpermute_norm(b.y, T, k, H, x, moe_out, next_g, d.rms_eps,
+                                 next_xh, next_copy, next_row, s);
   return launch_unpermute(b.y, T, k, H, x, moe_out, s);
 }
 
@@ -477,9 +490,13 @@ dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt, bool distinct) {
   return DG_OK;
 }
 
-// One decoder layer over the canvas rows in c->x.  commit: write the layer's
-// canvas K/V into the cache first, causal attention, and stop after the K/V
-// of the last layer.
+// One decoder layer over the canvas rows in c->x, whose attention RMSNorm
+// is already in c->xh (made by the embedding or the previous layer's
+// un-permute).  The layer's un-permute makes the next layer's normed input,
+// or after the last layer of a denoise step the final-norm rows of the
+// uncommitted positions in compacted order (c->pos_map).  commit: write the
+// layer's canvas K/V into the cache first, causal attention, and stop after
+// the K/V of the last layer.
 dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
                     bool commit, const dg_capture* cap) {
   const dg_model_desc& d = c->d;
@@ -491,8 +508,6 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   const long long req_stride = (long long)Hkv * head_stride;
   const long long layer_stride = (long long)c->max_requests * req_stride;
   hipStream_t s = c->stream;
-  KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.attn_norm, d.rms_eps, c->xh, nullptr,
-                           nullptr, nullptr, s));
   GemmArgs g = gemm_dense(c->xh, T, H, w.w_qkv, qkvN, c->qkv, qkvN);
   KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
   uint16_t* kc = c->k_cache + l * layer_stride;
@@ -537,8 +552,11 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
                            nullptr, nullptr, s));
   float* moe_out = (cap && cap->moe_out) ? cap->moe_out + (size_t)l * T * H : nullptr;
+  const bool last = l == d.n_layers - 1;
+  const float* next_g = last ? c->final_norm : c->layers[l + 1].attn_norm;
+  float* next_copy = (last && cap && cap->final_xhat) ? cap->final_xhat : nullptr;
   HIPCHK(c, run_moe(d, w, c->xh, T, ctx_moe_bufs(c), c->x, moe_out, nullptr, s,
-                    &c->prof));
+                    &c->prof, next_g, c->xh, next_copy, last ? c->pos_map : nullptr));
   if (cap) {
     const size_t tk = (size_t)T * d.top_k;
     if (cap->route_idx)
@@ -758,15 +776,13 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     plen[b] = c->kv_len[req[b]];
   }
   hipStream_t s = c->stream;
-  KRUN(c, 0, launch_embed(bt->tokens, T, c->embed, d.vocab, H, c->x, s));
+  KRUN(c, 11, launch_compact(bt->committed, T, c->row_map, c->m_dev, c->pos_map, s));
+  KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, d.vocab, H, c->x,
+                               c->layers[0].attn_norm, d.rms_eps, c->xh, s));
   for (int l = 0; l < d.n_layers; ++l) {
     st = run_layer(c, l, n, req, plen, false, out->capture);
     if (st != DG_OK) return st;
   }
-  KRUN(c, 11, launch_compact(bt->committed, T, c->row_map, c->m_dev, s));
-  float* fx = (out->capture && out->capture->final_xhat) ? out->capture->final_xhat : nullptr;
-  KRUN(c, 1, launch_rmsnorm(c->x, T, H, c->final_norm, d.rms_eps, c->xh,
-                           c->row_map, c->m_dev, fx, s));
   int n_tiles = 0;
   KRUN(c, 12, run_lm_head(c->xh, T, c->m_dev, H, c->embed, d.vocab, c->lm_part,
                           out->logits, c->row_map, &n_tiles, s));
@@ -804,7 +820,8 @@ dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
     if (plen[b] + DG_CANVAS > c->max_kv_len)
       return fail(c, DG_ERR_CAPACITY, "KV cache full: kv_len + 256 > max_kv_len");
   }
-  KRUN(c, 0, launch_embed(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x, c->stream));
+  KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x,
+                               c->layers[0].attn_norm, c->d.rms_eps, c->xh, c->stream));
   for (int l = 0; l < c->d.n_layers; ++l) {
     st = run_layer(c, l, n, req, plen, true, nullptr);
     if (st != DG_OK) return st;

@@ -213,10 +213,19 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* tile_offsets, int32_t* counts,
                           int32_t* perm, hipStream_t s);
 int permute_chunks(int n_pairs);
+// x = E[tok] fused with the first RMSNorm (packed table).
+hipError_t launch_embed_norm(const int32_t* tokens, int T, const uint16_t* embed,
+                             int V, int H, float* x, const float* g, float eps,
+                             uint16_t* xh, hipStream_t s);
+// x += un-permuted expert rows, fused with the next RMSNorm into xh.
+hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
+                                 float* moe_out, const float* g, float eps,
+                                 uint16_t* xh, float* copy_f32,
+                                 const int32_t* out_row, hipStream_t s);
 hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
                             float* moe_out, hipStream_t s);
 hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
-                          int32_t* m_dev, hipStream_t s);
+                          int32_t* m_dev, int32_t* pos_map, hipStream_t s);
 hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* m_dev, int m_max,
                            const int32_t* row_map, float* entropy, float* lse,

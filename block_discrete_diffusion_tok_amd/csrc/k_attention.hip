@@ -268,30 +268,53 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the KV-split partials: one wave per (canvas, head, position) row.
+// Merge of the KV-split partials: one wave per (canvas, head, position) row;
+// the partials of up to 8 splits are loaded together, then added in split
+// order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  constexpr int PER = D / 64;
+  constexpr int U = 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_rows = a.n * a.Hq * a.C;
   const int row_id = blockIdx.x * 4 + wave;
   if (row_id >= n_rows) return;
+  float ls[32];
   float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s)
-    mx = fmaxf(mx, a.lpart[(long long)s * n_rows + row_id]);
-  constexpr int PER = D / 64;
+#pragma unroll
+  for (int s = 0; s < 32; ++s)
+    if (s < a.splits) {
+      ls[s] = a.lpart[(long long)s * n_rows + row_id];
+      mx = fmaxf(mx, ls[s]);
+    }
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = a.lpart[(long long)s * n_rows + row_id];
-      if (ls == -INFINITY) continue;
-      const float w = exp2f(ls - mx);
-      wsum += w;
-      const float* op = a.opart + ((long long)s * n_rows + row_id) * D;
+    for (int s0 = 0; s0 < a.splits; s0 += U) {
+      float o[U][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * op[lane + 64 * e];
+      for (int u = 0; u < U; ++u)
+        if (s0 + u < a.splits) {
+          const float* op = a.opart + ((long long)(s0 + u) * n_rows + row_id) * D;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[u][e] = op[lane + 64 * e];
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sp = s0 + u;
+        if (sp >= a.splits) break;
+        float lsp = ls[0];
+#pragma unroll
+        for (int q = 0; q < 32; ++q)
+          if (q == sp) lsp = ls[q];
+        if (lsp == -INFINITY) continue;
+        const float w = exp2f(lsp - mx);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * o[u][e];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -65,24 +65,25 @@ __global__ __launch_bounds__(256) void pack_kernel(const char* src, int rows,
 // ---------------------------------------------------------------- RMSNorm
 // out[r, :] = bf16(x[src, :] / sqrt(mean(x^2) + eps) * g), one wave per row;
 // src = row_map[r] when given, rows beyond *m_dev skipped.
-// One wave per row.  Each pass keeps 8 float4 loads in flight per lane
-// (2048 floats per round), so a row costs a couple of memory latencies.
+// One workgroup per row; a thread holds up to 4 float4 of the row (H up to
+// 4096 in registers, longer rows are read twice).
 __global__ __launch_bounds__(256) void rmsnorm_kernel(
     const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
     const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
-  constexpr int U = 8;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + wave;
+  constexpr int U = 4;
+  __shared__ float red[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = blockIdx.x;
   const int n = m_dev ? *m_dev : rows;
   if (r >= n) return;
   const int src = row_map ? row_map[r] : r;
   const float* xr = x + (long long)src * H;
+  float4 v[U];
   float ss = 0.f;
-  for (int base = 0; base < H; base += 256 * U) {
-    float4 v[U];
+  for (int base = 0; base < H; base += 1024 * U) {
 #pragma unroll
     for (int c = 0; c < U; ++c) {
-      const int i = base + 256 * c + lane * 4;
+      const int i = base + 1024 * c + tid * 4;
       v[c] = i < H ? *(const float4*)(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
@@ -91,24 +92,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
   const float inv = rsqrtf(ss / (float)H + eps);
   uint16_t* o = out + (long long)r * H;
-  for (int base = 0; base < H; base += 256 * U) {
-    float4 v[U], gg[U];
+  for (int base = 0; base < H; base += 1024 * U) {
+    if (H > 1024 * U) {  // rows longer than the registers hold: read again
 #pragma unroll
-    for (int c = 0; c < U; ++c) {
-      const int i = base + 256 * c + lane * 4;
-      if (i < H) {
-        v[c] = *(const float4*)(xr + i);
-        gg[c] = *(const float4*)(g + i);
+      for (int c = 0; c < U; ++c) {
+        const int i = base + 1024 * c + tid * 4;
+        if (i < H) v[c] = *(const float4*)(xr + i);
       }
     }
 #pragma unroll
     for (int c = 0; c < U; ++c) {
-      const int i = base + 256 * c + lane * 4;
+      const int i = base + 1024 * c + tid * 4;
       if (i >= H) continue;
-      const uint16_t b0 = f2bf(v[c].x * inv * gg[c].x), b1 = f2bf(v[c].y * inv * gg[c].y);
-      const uint16_t b2 = f2bf(v[c].z * inv * gg[c].z), b3 = f2bf(v[c].w * inv * gg[c].w);
+      const float4 gg = *(const float4*)(g + i);
+      const uint16_t b0 = f2bf(v[c].x * inv * gg.x), b1 = f2bf(v[c].y * inv * gg.y);
+      const uint16_t b2 = f2bf(v[c].z * inv * gg.z), b3 = f2bf(v[c].w * inv * gg.w);
       *(uint2*)(o + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
                                     (uint32_t)b2 | ((uint32_t)b3 << 16));
       if (copy_f32)
@@ -118,69 +121,50 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
   }
 }
 
+// ---------------------------------------------------------------- router top-k
+// One workgroup per token, thread e holding logit e.  A logit's rank is the
+// number of logits above it (equal logits: lower expert ids first), counted
+// over LDS broadcasts; the k lowest ranks are the selection, in rank order.
+// Gate weights: softmax over the selected logits, summed in rank order.
 __global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T,
                                                    int E, int k, int32_t* idx,
                                                    float* w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  float v[4];
-  bool taken[4];
+  __shared__ __attribute__((aligned(16))) float lv[256];
+  __shared__ float sel[16];
+  const int t = blockIdx.x, e = threadIdx.x;
+  const float v = e < E ? logits[(long long)t * E + e] : -INFINITY;
+  lv[e] = v;
+  __syncthreads();
+  // entries past E hold -inf with higher ids: they never rank above a real
+  // logit
+  int rk = 0;
+  const int E16 = (E + 15) & ~15;
+  for (int q0 = 0; q0 < E16; q0 += 16) {
+    float4 o4[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? logits[(long long)t * E + e] : -INFINITY;
-    taken[j] = e >= E;
+    for (int u = 0; u < 4; ++u) o4[u] = *(const float4*)&lv[q0 + 4 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float o[4] = {o4[u].x, o4[u].y, o4[u].z, o4[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        rk += (o[c] > v || (o[c] == v && q0 + 4 * u + c < e)) ? 1 : 0;
+    }
   }
-  float sel_v[16];
-  int sel_i[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r >= k) break;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = shfl_xor(bv, off);
-      const int oi = shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (bi == lane + 64 * j) taken[j] = true;
-    sel_v[r] = bv;
-    sel_i[r] = bi;
+  if (e < E && rk < k) {
+    idx[(long long)t * k + rk] = e;
+    sel[rk] = v;
   }
-  const float mx = sel_v[0];
-  float sum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (r < k) sum += __expf(sel_v[r] - mx);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < k && lane == r) {
-      idx[(long long)t * k + r] = sel_i[r];
-      w[(long long)t * k + r] = __expf(sel_v[r] - mx) / sum;
-    }
+  __syncthreads();
+  if (e < k) {
+    const float mx = sel[0];
+    float sum = 0.f;
+    for (int r = 0; r < k; ++r) sum += __expf(sel[r] - mx);
+    w[(long long)t * k + e] = __expf(sel[e] - mx) / sum;
   }
 }
 
 // ---------------------------------------------------------------- permute
-// Stable counting sort of the T*k (token, rank) pairs by expert, in three
-// passes over chunks of 256 pairs: per-chunk histogram and in-chunk rank,
-// scan over (expert, chunk), scatter.  Pair p = t*k + j lands at
-// perm[offsets[e] + #{pairs p' < p with expert e}].
 constexpr int kChunk = 256;
 
 __global__ __launch_bounds__(kChunk) void moe_count_kernel(
@@ -252,19 +236,121 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(
   perm[chunk_base[(long long)blockIdx.x * E + e] + local_rank[p]] = p;
 }
 
+// Stable counting sort of up to kSmallPairs pairs in one workgroup of 16
+// waves.  Wave w takes pairs [w*per, (w+1)*per) in rounds of 64; a pair's
+// rank among the earlier pairs of its expert in the wave's range comes from
+// one ballot per distinct expert of the round (a running per-wave count in
+// LDS carries it across rounds).  A wave scan gives the expert offsets, a
+// running sum over the waves each wave's base per expert, and every pair
+// lands at base + rank: order (expert, pair index), as the chunked path.
+constexpr int kSmallPairs = 4096;
+constexpr int kPermWaves = 16;
+__global__ __launch_bounds__(1024) void moe_permute_small_kernel(
+    const int32_t* idx, int n_pairs, int E, int bm, int32_t* offsets,
+    int32_t* tile_offsets, int32_t* counts, int32_t* perm) {
+  __shared__ int hist[kPermWaves][256];  // per-wave counts, then bases
+  __shared__ int tot[256], tiles[256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < kPermWaves * 256; i += 1024) hist[i >> 8][i & 255] = 0;
+  __syncthreads();
+  const int per = ((n_pairs + kPermWaves - 1) / kPermWaves + 63) & ~63;  // <= 256
+  int me[4], mr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = wave * per + 64 * r + lane;
+    const bool valid = 64 * r < per && p < n_pairs;
+    const int e = valid ? idx[p] : -1;
+    unsigned long long active = __ballot(valid);
+    int rank = 0;
+    while (active) {
+      const int leader = __ffsll((long long)active) - 1;
+      const int v = __builtin_amdgcn_readlane(e, leader);
+      const unsigned long long m = __ballot(e == v);
+      const int base = hist[wave][v];  // every lane reads before the leader writes
+      if (e == v) rank = base + __popcll(m & ((1ull << lane) - 1));
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) hist[wave][v] = base + __popcll(m);
+      active &= ~m;
+    }
+    me[r] = e;
+    mr[r] = rank;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int t = 0;
+    if (tid < E)
+#pragma unroll
+      for (int w = 0; w < kPermWaves; ++w) t += hist[w][tid];
+    tot[tid] = t;
+    tiles[tid] = (t + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scans of counts and tiles, 4 experts a lane
+    int c4[4], t4[4], cs = 0, ts = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      c4[c] = tot[4 * lane + c];
+      t4[c] = tiles[4 * lane + c];
+      cs += c4[c];
+      ts += t4[c];
+    }
+    int ci = cs, ti = ts;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int co = __shfl_up(ci, off), to = __shfl_up(ti, off);
+      if (lane >= off) { ci += co; ti += to; }
+    }
+    int cr = ci - cs, tr = ti - ts;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * lane + c;
+      if (e < E) {
+        offsets[e] = cr;
+        tile_offsets[e] = tr;
+        if (counts) counts[e] = c4[c];
+        tot[e] = cr;  // becomes the exclusive offset
+      }
+      cr += c4[c];
+      tr += t4[c];
+    }
+    if (lane == 63) {
+      offsets[E] = ci;
+      tile_offsets[E] = ti;
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    int base = tot[tid];
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = hist[w][tid];
+      hist[w][tid] = base;
+      base += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (me[r] >= 0) perm[hist[wave][me[r]] + mr[r]] = wave * per + 64 * r + lane;
+}
+
 // ---------------------------------------------------------------- un-permute
 // x[t, :] += sum_j y[t*k + j, :] in rank order (no atomics); optionally the
 // sum alone is written to moe_out.  x may be null (store only).
 __global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
                                                         int H, float* x,
                                                         float* moe_out) {
+  constexpr int KMAX = 16;
   const int t = blockIdx.x;
   for (int i = threadIdx.x * 4; i < H; i += 1024) {
+    float4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) v[j] = *(const float4*)(y + ((long long)t * k + j) * H + i);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float4 v = *(const float4*)(y + ((long long)t * k + j) * H + i);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) { s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w; }
     if (x) {
       float4* xp = (float4*)(x + (long long)t * H + i);
       float4 o = *xp;
@@ -275,12 +361,129 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
   }
 }
 
+// ---------------------------------------------------------------- fused row norms
+// Block-wide RMSNorm of a row whose values this thread holds as v[c] at
+// columns base + 1024 c + 4 tid (c < U); rows longer than 1024 U are read
+// back from xr (written earlier by this same thread).  out = bf16(x * inv
+// * g); copy_f32 optionally receives the bf16 values widened.
+template <int U>
+__device__ __forceinline__ void norm_row(float4 (&v)[U], float ss, const float* xr,
+                                         int H, const float* g, float eps,
+                                         uint16_t* out, float* copy_f32,
+                                         float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float inv = rsqrtf(ss / (float)H + eps);
+  for (int base = 0; base < H; base += 1024 * U) {
+    if (H > 1024 * U) {
+#pragma unroll
+      for (int c = 0; c < U; ++c) {
+        const int i = base + 1024 * c + tid * 4;
+        if (i < H) v[c] = *(const float4*)(xr + i);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = base + 1024 * c + tid * 4;
+      if (i >= H) continue;
+      const float4 gg = *(const float4*)(g + i);
+      const uint16_t b0 = f2bf(v[c].x * inv * gg.x), b1 = f2bf(v[c].y * inv * gg.y);
+      const uint16_t b2 = f2bf(v[c].z * inv * gg.z), b3 = f2bf(v[c].w * inv * gg.w);
+      *(uint2*)(out + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
+                                      (uint32_t)b2 | ((uint32_t)b3 << 16));
+      if (copy_f32)
+        *(float4*)(copy_f32 + i) = make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
+    }
+  }
+}
+
+// Embedding gather (packed table, ids clamped) fused with the first layer's
+// attention RMSNorm: x[t] = E[tok[t]] (fp32), xh[t] = RMSNorm(x[t]; g).
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok,
+                                                         const uint16_t* E, int V,
+                                                         int H, float* x,
+                                                         const float* g, float eps,
+                                                         uint16_t* xh) {
+  constexpr int U = 4;
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int id = min(max(tok[t], 0), V - 1);
+  const char* base = (const char*)E;
+  float* xr = x + (long long)t * H;
+  float4 v[U];
+  float ss = 0.f;
+  for (int b0 = 0; b0 < H; b0 += 1024 * U) {
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      // columns i..i+3: half of one 16-byte packed piece
+      const int i = b0 + 1024 * c + tid * 4;
+      if (i < H) {
+        const long long off = pack_block_offset(id >> 4, i >> 5, H, 2) +
+                              16 * ((id & 15) + 16 * ((i & 31) >> 3)) + 2 * (i & 7);
+        const uint2 w = *(const uint2*)(base + off);
+        v[c] = make_float4(bf2f((uint16_t)(w.x & 0xffff)), bf2f((uint16_t)(w.x >> 16)),
+                           bf2f((uint16_t)(w.y & 0xffff)), bf2f((uint16_t)(w.y >> 16)));
+        *(float4*)(xr + i) = v[c];
+        ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+      }
+    }
+  }
+  norm_row<U>(v, ss, xr, H, g, eps, xh + (long long)t * H, nullptr, red);
+}
+
+// Un-permute fused with the next RMSNorm: x[t] += sum_j y[t*k + j] in rank
+// order (moe_out[t] = the sum, if given), then xh[r] = RMSNorm(x[t]; g) with
+// r = out_row[t] (no output when -1) or t (copy_f32[r] = widened xh[r], if
+// given).
+__global__ __launch_bounds__(256) void unpermute_norm_kernel(
+    const float* y, int k, int H, float* x, float* moe_out, const float* g,
+    float eps, uint16_t* xh, float* copy_f32, const int32_t* out_row) {
+  constexpr int U = 4, KMAX = 16;
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  float* xr = x + (long long)t * H;
+  float4 v[U];
+  float ss = 0.f;
+  for (int b0 = 0; b0 < H; b0 += 1024 * U) {
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const int i = b0 + 1024 * c + tid * 4;
+      if (i >= H) continue;
+      float4 yy[KMAX];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) yy[j] = *(const float4*)(y + ((long long)t * k + j) * H + i);
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) { sum.x += yy[j].x; sum.y += yy[j].y; sum.z += yy[j].z; sum.w += yy[j].w; }
+      float4 o = *(const float4*)(xr + i);
+      o.x += sum.x; o.y += sum.y; o.z += sum.z; o.w += sum.w;
+      *(float4*)(xr + i) = o;
+      if (moe_out) *(float4*)(moe_out + (long long)t * H + i) = sum;
+      v[c] = o;
+      ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+    }
+  }
+  // the norm goes to row out_row[t] (skipped when -1), or to row t
+  const int orow = out_row ? out_row[t] : t;
+  if (orow < 0) return;
+  norm_row<U>(v, ss, xr, H, g, eps, xh + (long long)orow * H,
+              copy_f32 ? copy_f32 + (long long)orow * H : nullptr, red);
+}
+
 // ---------------------------------------------------------------- compaction
 // row_map[0..M) = indices t with committed[t] == 0 in increasing order;
-// *m_dev = M.  One workgroup of 1024 threads.
+// *m_dev = M; pos_map[t] (if given) = t's index in row_map, or -1.  One
+// workgroup of 1024 threads.
 __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
                                                        int T, int32_t* row_map,
-                                                       int32_t* m_dev) {
+                                                       int32_t* m_dev,
+                                                       int32_t* pos_map) {
   __shared__ int s[1024];
   __shared__ int run;
   const int tid = threadIdx.x;
@@ -298,6 +501,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
       __syncthreads();
     }
     if (f) row_map[run + s[tid] - 1] = t;
+    if (pos_map && t < T) pos_map[t] = f ? run + s[tid] - 1 : -1;
     const int total = s[1023];
     __syncthreads();
     if (tid == 0) run += total;
@@ -500,14 +704,15 @@ hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
                           const int32_t* m_dev, float* copy_f32,
                           hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x,
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x,
                      rows, H, g, eps, out, row_map, m_dev, copy_f32);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx,
                        float* w, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(256), 0, s, logits,
                      T, E, k, idx, w);
   return hipGetLastError();
 }
@@ -519,6 +724,11 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* chunk_base, int32_t* offsets,
                           int32_t* tile_offsets, int32_t* counts,
                           int32_t* perm, hipStream_t s) {
+  if (n_pairs <= kSmallPairs && E <= 256) {
+    hipLaunchKernelGGL(moe_permute_small_kernel, dim3(1), dim3(1024), 0, s, idx,
+                       n_pairs, E, bm, offsets, tile_offsets, counts, perm);
+    return hipGetLastError();
+  }
   const int nc = permute_chunks(n_pairs);
   hipLaunchKernelGGL(moe_count_kernel, dim3(nc), dim3(kChunk), 0, s, idx,
                      n_pairs, E, chunk_counts, local_rank);
@@ -533,6 +743,25 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
   return hipGetLastError();
 }
 
+hipError_t launch_embed_norm(const int32_t* tokens, int T, const uint16_t* embed,
+                             int V, int H, float* x, const float* g, float eps,
+                             uint16_t* xh, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_norm_kernel, dim3(T), dim3(256), 0, s, tokens, embed,
+                     V, H, x, g, eps, xh);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
+                                 float* moe_out, const float* g, float eps,
+                                 uint16_t* xh, float* copy_f32,
+                                 const int32_t* out_row, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(unpermute_norm_kernel, dim3(T), dim3(256), 0, s, y, k, H, x,
+                     moe_out, g, eps, xh, copy_f32, out_row);
+  return hipGetLastError();
+}
+
 hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
                             float* moe_out, hipStream_t s) {
   hipLaunchKernelGGL(unpermute_kernel, dim3(T), dim3(256), 0, s, y, k, H, x,
@@ -541,9 +770,9 @@ hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
 }
 
 hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
-                          int32_t* m_dev, hipStream_t s) {
+                          int32_t* m_dev, int32_t* pos_map, hipStream_t s) {
   hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, committed, T,
-                     row_map, m_dev);
+                     row_map, m_dev, pos_map);
   return hipGetLastError();
 }
 
