@@ -172,12 +172,22 @@ struct MoeBufs {
   float* y;
 };
 
+// Router logits are computed in up to kRouterSlabs K splits, each writing
+// its own fp32 slab [T, E]; the top-k kernel adds them in order.
+constexpr int kRouterSlabs = 8;
+int router_splits(int K) {
+  const int steps = K / 64;
+  int s = 1;
+  while (s * 2 <= kRouterSlabs && steps % (s * 2) == 0 && steps / (s * 2) >= 2) s *= 2;
+  return s;
+}
+
 // Workspace of the MoE pipeline for T tokens.
 size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   Carve cv;
   const long long pairs = (long long)T * d.top_k;
   const int nc = permute_chunks((int)pairs);
-  const size_t o_rl = cv.take((size_t)T * d.n_experts * 4);
+  const size_t o_rl = cv.take((size_t)kRouterSlabs * T * d.n_experts * 4);
   const size_t o_ri = cv.take((size_t)pairs * 4);
   const size_t o_rw = cv.take((size_t)pairs * 4);
   const size_t o_cc = cv.take((size_t)nc * d.n_experts * 4);
@@ -360,13 +370,15 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   const int pairs = T * k;
   hipError_t e;
   GemmArgs r = gemm_dense(xh, T, H, w.w_router, E, b.rlogits, E);
+  r.splits = router_splits(H);
+  r.split_stride = (long long)T * E;
   {
     ProfScope ps(prof, 5);
     if ((e = launch_gemm(EPI_STORE_F32, false, r, grid_m_dense(T, EPI_STORE_F32), s)) != hipSuccess) return e;
   }
   {
     ProfScope ps(prof, 6);
-    if ((e = launch_topk(b.rlogits, T, E, k, b.ridx, b.rw, s)) != hipSuccess) return e;
+    if ((e = launch_topk(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, s)) != hipSuccess) return e;
   }
   {
     ProfScope ps(prof, 7);
@@ -939,8 +951,8 @@ dg_status dg_op_router_topk(const float* logits, int32_t tokens,
       top_k > 16 || top_k > n_experts)
     return fail(nullptr, DG_ERR_SHAPE, "need 1 <= top_k <= min(16, n_experts), n_experts <= 256");
   if (tokens == 0) return DG_OK;
-  HIPCHK(nullptr, launch_topk(logits, tokens, n_experts, top_k, idx, w,
-                              (hipStream_t)stream));
+  HIPCHK(nullptr, launch_topk(const_cast<float*>(logits), tokens, n_experts, top_k, 1,
+                              idx, w, (hipStream_t)stream));
   return DG_OK;
 }
 

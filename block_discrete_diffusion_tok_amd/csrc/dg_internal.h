@@ -135,6 +135,8 @@ struct GemmArgs {
   int n_tiles;
   float* logits;           // EPI_LMSTATS: optional [rows, N] (row_map placed)
   const int32_t* row_map;  // EPI_LMSTATS: logits row of each A row
+  int splits;              // EPI_STORE_F32: K splits (gridDim.z), 0/1 = none;
+  long long split_stride;  //   split z writes its own slab C + z * split_stride
 };
 
 // Tile sizes of the grouped GEMMs (rows of one expert are tiled by this).
@@ -205,7 +207,9 @@ hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
                           float eps, uint16_t* out, const int32_t* row_map,
                           const int32_t* m_dev, float* copy_f32,
                           hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx,
+// logits: `splits` fp32 slabs [T, E] (partial sums over K) added in slab
+// order; with splits > 1 the sum is also written back to slab 0.
+hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
                        float* w, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* chunk_counts, int32_t* local_rank,

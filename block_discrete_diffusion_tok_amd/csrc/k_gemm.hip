@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   constexpr int XA = BM / 32;                 // token 16-byte loads per thread
   constexpr int XB = W8 ? BN / 64 : BN / 32;  // weight 16-byte loads per thread
   constexpr int ESZ = W8 ? 1 : 2;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  static_assert(BM % 32 == 0 && BN % 64 == 0, "tile");
   __shared__ __attribute__((aligned(16))) uint16_t Ts[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDK];
 
@@ -141,15 +141,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     row_end = m_rows;
   }
 
-  // ---- per-thread source addresses
-  const int nk = a.K / BK;
+  // ---- K range of this split (router logits: each split writes its own
+  // slab; the consumer adds them) and the per-thread source addresses
+  const int nk = a.K / BK / (int)gridDim.z;
+  const long long k0 = (long long)blockIdx.z * nk * BK;
+  if (EPI == EPI_STORE_F32) a.C = (float*)a.C + blockIdx.z * a.split_stride;
   const uint16_t* tsrc[XA];
   const int32_t* const amap = a.a_map;
   static_for<XA>([&](auto j) {
     const int c = tid + 256 * j;
     const int row = min(row_begin + (c >> 3), row_end - 1);
     const int src = amap ? amap[row] / a.a_map_div : row;
-    tsrc[j] = a.A + (long long)src * a.lda + (c & 7) * 8;
+    tsrc[j] = a.A + (long long)src * a.lda + k0 + (c & 7) * 8;
   });
   const char* wsrc[XB];
   const char* const wgroup = (const char*)a.B + (long long)group * a.b_group_stride * ESZ;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     } else {
       rb = min(nt * (BN / 16) + tile, (a.N + 15) / 16 - 1);  // zero-padded last tile
     }
-    wsrc[j] = wgroup + pack_block_offset(rb, kb, a.K, ESZ) + 16 * ln;
+    wsrc[j] = wgroup + pack_block_offset(rb, kb, a.K, ESZ) + (k0 / BK) * ESZ * kPackBlock + 16 * ln;
   });
 
   f32x4_t acc[TM][TN];
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // P register sets keep the global loads of P K steps in flight (one
   // step's loads alone would leave the loop waiting a full memory latency
   // per step).  Invariant at step k: set (k+1) % P holds step k+1.
-  constexpr int P = BM == 64 ? 4 : 2;
+  constexpr int P = BM <= 64 ? 4 : 2;
   static_assert(P % 2 == 0, "LDS buffer parity follows the step parity");
   u32x4_t tr[P][XA], wr[P][XB];
   const uint16_t* const tfrag = &Ts[0][(wm * (BM / 2) + l16) * LDK + lg * 8];
@@ -374,7 +377,8 @@ hipError_t launch_one(const GemmArgs& a, int grid_m, hipStream_t s) {
   if (EPI == EPI_SWIGLU) grid_n = (a.ffn + BN / 2 - 1) / (BN / 2);
   else grid_n = (a.N + BN - 1) / BN;
   if (grid_m <= 0 || grid_n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, W8>), dim3(grid_n, grid_m),
+  const int splits = (EPI == EPI_STORE_F32 && a.splits > 1) ? a.splits : 1;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, W8>), dim3(grid_n, grid_m, splits),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -384,12 +388,26 @@ hipError_t launch_one(const GemmArgs& a, int grid_m, hipStream_t s) {
 int gemm_bm(int epi) { return epi == EPI_LMSTATS ? 128 : 64; }
 int gemm_bn(int epi) { return epi == EPI_LMSTATS ? 128 : 64; }
 
+// Dense products whose 64 x 64 tiles would leave most CUs without a
+// workgroup (a few hundred token rows) run 32 x 64 tiles instead.
+static bool small_dense(const GemmArgs& a, int grid_m) {
+  const long long tiles = (long long)grid_m * ((a.N + 63) / 64) * (a.splits > 1 ? a.splits : 1);
+  return a.group_offsets == nullptr && !a.M_dev && tiles < 192;
+}
+
 hipError_t launch_gemm(int epi, bool w8, const GemmArgs& a, int grid_m,
                        hipStream_t s) {
+  const int grid_m32 = (a.M + 31) / 32;
   switch (epi) {
-    case EPI_STORE_BF16: return launch_one<64, 64, EPI_STORE_BF16, false>(a, grid_m, s);
-    case EPI_STORE_F32: return launch_one<64, 64, EPI_STORE_F32, false>(a, grid_m, s);
-    case EPI_ADD_F32: return launch_one<64, 64, EPI_ADD_F32, false>(a, grid_m, s);
+    case EPI_STORE_BF16:
+      return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_BF16, false>(a, grid_m32, s)
+                                    : launch_one<64, 64, EPI_STORE_BF16, false>(a, grid_m, s);
+    case EPI_STORE_F32:
+      return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_F32, false>(a, grid_m32, s)
+                                    : launch_one<64, 64, EPI_STORE_F32, false>(a, grid_m, s);
+    case EPI_ADD_F32:
+      return small_dense(a, grid_m) ? launch_one<32, 64, EPI_ADD_F32, false>(a, grid_m32, s)
+                                    : launch_one<64, 64, EPI_ADD_F32, false>(a, grid_m, s);
     case EPI_SWIGLU:
       return w8 ? launch_one<64, 64, EPI_SWIGLU, true>(a, grid_m, s)
                 : launch_one<64, 64, EPI_SWIGLU, false>(a, grid_m, s);

@@ -126,13 +126,27 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
 // number of logits above it (equal logits: lower expert ids first), counted
 // over LDS broadcasts; the k lowest ranks are the selection, in rank order.
 // Gate weights: softmax over the selected logits, summed in rank order.
-__global__ __launch_bounds__(256) void topk_kernel(const float* logits, int T,
-                                                   int E, int k, int32_t* idx,
+__global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
+                                                   int k, int splits, int32_t* idx,
                                                    float* w) {
   __shared__ __attribute__((aligned(16))) float lv[256];
   __shared__ float sel[16];
   const int t = blockIdx.x, e = threadIdx.x;
-  const float v = e < E ? logits[(long long)t * E + e] : -INFINITY;
+  // the router's K splits left `splits` partial slabs: add them in order
+  float v = -INFINITY;
+  if (e < E) {
+    const long long slab = (long long)T * E, o = (long long)t * E + e;
+    float part[8];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      if (sp < splits) part[sp] = logits[sp * slab + o];
+    v = part[0];
+#pragma unroll
+    for (int sp = 1; sp < 8; ++sp)
+      if (sp < splits) v += part[sp];
+    for (int sp = 8; sp < splits; ++sp) v += logits[sp * slab + o];
+    if (splits > 1) logits[o] = v;
+  }
   lv[e] = v;
   __syncthreads();
   // entries past E hold -inf with higher ids: they never rank above a real
@@ -236,60 +250,35 @@ __global__ __launch_bounds__(kChunk) void moe_scatter_kernel(
   perm[chunk_base[(long long)blockIdx.x * E + e] + local_rank[p]] = p;
 }
 
-// Stable counting sort of up to kSmallPairs pairs in one workgroup of 16
-// waves.  Wave w takes pairs [w*per, (w+1)*per) in rounds of 64; a pair's
-// rank among the earlier pairs of its expert in the wave's range comes from
-// one ballot per distinct expert of the round (a running per-wave count in
-// LDS carries it across rounds).  A wave scan gives the expert offsets, a
-// running sum over the waves each wave's base per expert, and every pair
-// lands at base + rank: order (expert, pair index), as the chunked path.
+// Counting sort of up to kSmallPairs pairs in one workgroup: LDS histogram,
+// one scan for the expert offsets and tile offsets, then each pair takes the
+// next free slot of its expert from an LDS cursor.  The order of the pairs
+// inside an expert's range is arbitrary and does not matter: every pair's
+// expert output is its own dot products, and the un-permute adds a token's
+// pairs in rank order, so results are the same for any order.
 constexpr int kSmallPairs = 4096;
-constexpr int kPermWaves = 16;
 __global__ __launch_bounds__(1024) void moe_permute_small_kernel(
     const int32_t* idx, int n_pairs, int E, int bm, int32_t* offsets,
     int32_t* tile_offsets, int32_t* counts, int32_t* perm) {
-  __shared__ int hist[kPermWaves][256];  // per-wave counts, then bases
-  __shared__ int tot[256], tiles[256];
+  __shared__ int hist[256], cursor[256], tiles[256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < kPermWaves * 256; i += 1024) hist[i >> 8][i & 255] = 0;
+  if (tid < 256) hist[tid] = 0;
   __syncthreads();
-  const int per = ((n_pairs + kPermWaves - 1) / kPermWaves + 63) & ~63;  // <= 256
-  int me[4], mr[4];
+  int e4[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int p = wave * per + 64 * r + lane;
-    const bool valid = 64 * r < per && p < n_pairs;
-    const int e = valid ? idx[p] : -1;
-    unsigned long long active = __ballot(valid);
-    int rank = 0;
-    while (active) {
-      const int leader = __ffsll((long long)active) - 1;
-      const int v = __builtin_amdgcn_readlane(e, leader);
-      const unsigned long long m = __ballot(e == v);
-      const int base = hist[wave][v];  // every lane reads before the leader writes
-      if (e == v) rank = base + __popcll(m & ((1ull << lane) - 1));
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) hist[wave][v] = base + __popcll(m);
-      active &= ~m;
-    }
-    me[r] = e;
-    mr[r] = rank;
+    const int p = tid + 1024 * r;
+    e4[r] = p < n_pairs ? idx[p] : -1;
+    if (e4[r] >= 0) atomicAdd(&hist[e4[r]], 1);
   }
   __syncthreads();
-  if (tid < 256) {
-    int t = 0;
-    if (tid < E)
-#pragma unroll
-      for (int w = 0; w < kPermWaves; ++w) t += hist[w][tid];
-    tot[tid] = t;
-    tiles[tid] = (t + bm - 1) / bm;
-  }
+  if (tid < 256) tiles[tid] = tid < E ? (hist[tid] + bm - 1) / bm : 0;
   __syncthreads();
   if (wave == 0) {  // exclusive scans of counts and tiles, 4 experts a lane
     int c4[4], t4[4], cs = 0, ts = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      c4[c] = tot[4 * lane + c];
+      c4[c] = 4 * lane + c < E ? hist[4 * lane + c] : 0;
       t4[c] = tiles[4 * lane + c];
       cs += c4[c];
       ts += t4[c];
@@ -308,7 +297,7 @@ __global__ __launch_bounds__(1024) void moe_permute_small_kernel(
         offsets[e] = cr;
         tile_offsets[e] = tr;
         if (counts) counts[e] = c4[c];
-        tot[e] = cr;  // becomes the exclusive offset
+        cursor[e] = cr;
       }
       cr += c4[c];
       tr += t4[c];
@@ -319,19 +308,9 @@ __global__ __launch_bounds__(1024) void moe_permute_small_kernel(
     }
   }
   __syncthreads();
-  if (tid < E) {
-    int base = tot[tid];
-#pragma unroll
-    for (int w = 0; w < kPermWaves; ++w) {
-      const int c = hist[w][tid];
-      hist[w][tid] = base;
-      base += c;
-    }
-  }
-  __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    if (me[r] >= 0) perm[hist[wave][me[r]] + mr[r]] = wave * per + 64 * r + lane;
+    if (e4[r] >= 0) perm[atomicAdd(&cursor[e4[r]], 1)] = tid + 1024 * r;
 }
 
 // ---------------------------------------------------------------- un-permute
@@ -579,43 +558,25 @@ __global__ __launch_bounds__(256) void eb_kernel(
     const float* entropy, const int32_t* argmax, uint8_t* committed,
     int32_t* tokens, int32_t* step, const float* gamma, int cap, int refine,
     int32_t* n_new, uint8_t* done) {
-  __shared__ unsigned long long keys[DG_CANVAS];
+  static_assert(DG_CANVAS == 256, "one thread per canvas position");
+  __shared__ __align__(16) unsigned long long keys[DG_CANVAS];
   __shared__ float sorted_h[DG_CANVAS];
-  __shared__ int s_nstar;
-  const int b = blockIdx.x, j = threadIdx.x;
+  __shared__ double wave_sum[4];
+  __shared__ int s_first;
+  const int b = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
   const long long base = (long long)b * DG_CANVAS;
   const bool unc = committed[base + j] == 0;
+  const int steps_done = step[b];  // read by all before thread 0 updates it
   float h = unc ? entropy[base + j] : 0.f;
   if (h == 0.f) h = 0.f;  // -0 -> +0
   uint32_t u = __float_as_uint(h);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving
+  // (entropy, position) as one key: ties go to the lower position
   const unsigned long long key =
       unc ? (((unsigned long long)u << 32) | (unsigned)j) : ~0ull;
   keys[j] = key;
+  if (j == 0) s_first = DG_CANVAS;
   const int n_unc = __syncthreads_count(unc);
-  int rank = 0;
-  if (unc) {
-    for (int i = 0; i < DG_CANVAS; ++i) rank += keys[i] < key;
-    sorted_h[rank] = h;
-  }
-  __syncthreads();
-  if (j == 0) {
-    int n = 0;
-    if (n_unc > 0) {
-      const double lim = (double)gamma[b];
-      double tot = 0.0;
-      for (int r = 0; r < n_unc; ++r) {
-        tot += (double)sorted_h[r];
-        if (tot <= lim) ++n;
-        else break;
-      }
-      if (n < 1) n = 1;
-      if (step[b] + 1 >= cap) n = n_unc;
-    }
-    s_nstar = n;
-  }
-  __syncthreads();
-  const int n = s_nstar;
   if (n_unc == 0) {
     if (j == 0) {
       n_new[b] = 0;
@@ -623,6 +584,32 @@ __global__ __launch_bounds__(256) void eb_kernel(
     }
     return;
   }
+  // rank = number of smaller keys; committed positions hold the largest key
+  int rank = 0;
+  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(keys);
+#pragma unroll 8
+  for (int i = 0; i < DG_CANVAS / 2; ++i) {
+    const ulonglong2 kk = k2[i];
+    rank += (kk.x < key) + (kk.y < key);
+  }
+  if (unc) sorted_h[rank] = h;
+  __syncthreads();
+  // inclusive prefix sums of the sorted entropies in fp64
+  double c = j < n_unc ? (double)sorted_h[j] : 0.0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(c, o, 64);
+    if (lane >= o) c += t;
+  }
+  if (lane == 63) wave_sum[w] = c;
+  __syncthreads();
+  for (int q = 0; q < w; ++q) c += wave_sum[q];
+  // n* = length of the longest sorted prefix whose sum stays within gamma
+  if (j < n_unc && c > (double)gamma[b]) atomicMin(&s_first, j);
+  __syncthreads();
+  int n = min(s_first, n_unc);
+  if (n < 1) n = 1;
+  if (steps_done + 1 >= cap) n = n_unc;
   if (unc) {
     if (rank < n) {
       committed[base + j] = 1;
@@ -632,7 +619,7 @@ __global__ __launch_bounds__(256) void eb_kernel(
     }
   }
   if (j == 0) {
-    step[b] += 1;
+    step[b] = steps_done + 1;
     n_new[b] = n;
     done[b] = (n == n_unc) ? 1 : 0;
   }
@@ -709,11 +696,11 @@ hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx,
+hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
                        float* w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(256), 0, s, logits,
-                     T, E, k, idx, w);
+                     T, E, k, splits, idx, w);
   return hipGetLastError();
 }
 

@@ -27,12 +27,13 @@ def _randn(shape, std, name, dtype=torch.bfloat16, seed=7):
 # ------------------------------------------------------------------ linear
 
 # Projection shapes of one 2048-hidden layer (Q/K/V, output, router) at 256
-# rows, plus ragged rows/columns (90 columns: scalar stores) and K not a
-# multiple of the 4-step pipeline (K = 448, 320).
+# rows (32 x 64 tiles), plus ragged rows/columns (90 columns: scalar
+# stores), K not a multiple of the 4-step pipeline (K = 448, 320) and a
+# many-row product on 64 x 64 tiles (4096 x 512).
 @pytest.mark.parametrize("m,k,n", [(300, 256, 200), (1, 128, 64),
                                    (256, 2048, 4096), (256, 2048, 2048),
                                    (256, 2048, 128), (200, 448, 96),
-                                   (200, 320, 90)])
+                                   (200, 320, 90), (4096, 256, 512)])
 def test_linear_three_modes(m, k, n):
     log(f"linear m={m} k={k} n={n}")
     x = _randn((m, k), 1.0, f"lin.x{m}")
