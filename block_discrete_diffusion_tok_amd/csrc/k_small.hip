@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256) void eb_kernel(
     int32_t* tokens, int32_t* step, const float* gamma, int cap, int refine,
     int32_t* n_new, uint8_t* done) {
   static_assert(DG_CANVAS == 256, "one thread per canvas position");
-  __shared__ __align__(16) unsigned long long keys[DG_CANVAS];
+  __shared__ __attribute__((aligned(16))) unsigned long long keys[DG_CANVAS];
   __shared__ float sorted_h[DG_CANVAS];
   __shared__ double wave_sum[4];
   __shared__ int s_first;

@@ -28,9 +28,9 @@ def round_bf16(x):
     return np.ldexp(np.rint(f * 256.0) / 256.0, e)
 
 
-def decode_e4m3(codes):
-    """Decode OCP FP8 E4M3 byte codes (uint8 array) to fp64 values."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c):
+    """Value of each E4M3 byte code in the int64 array c, by the format's
+    definition (sign, biased exponent, mantissa; subnormals; NaN)."""
     sign = np.where(c & 0x80, -1.0, 1.0)
     exp = (c >> 3) & 0xF
     man = c & 0x7
@@ -38,3 +38,12 @@ def decode_e4m3(codes):
     subnormal = np.ldexp(man / 8.0, -6)
     val = sign * np.where(exp == 0, subnormal, normal)
     return np.where((exp == 0xF) & (man == 0x7), np.nan, val)
+
+
+# the 256 possible codes decoded once; decoding an array is a lookup
+_E4M3_VALUES = _e4m3_value(np.arange(256, dtype=np.int64))
+
+
+def decode_e4m3(codes):
+    """Decode OCP FP8 E4M3 byte codes (uint8 array) to fp64 values."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]

@@ -9,7 +9,12 @@ from block_discrete_diffusion_tok_amd import dg, synth
 
 DEV = "cuda"
 TOL = 2e-2        # max relative error on continuous outputs (per tensor)
-MARGIN = 1e-3     # decisions closer than this (oracle values) are not compared
+# Decisions (top-k routing, argmax) whose oracle margin, relative to the
+# largest magnitude among the values decided on, is below MARGIN are not
+# required to agree: the bf16 activations the path stores round differently
+# from the oracle's fp64 values whenever the two straddle a rounding boundary,
+# which moves router and vocabulary logits by ~1e-3 of their scale.
+MARGIN = 1e-3
 
 
 def log(msg):
@@ -44,21 +49,28 @@ def rel_err(g, o):
     return float(np.max(np.abs(g - o)) / (scale if scale > 0 else 1.0))
 
 
+def _relative(gap, vals):
+    scale = np.max(np.abs(vals), axis=1)
+    return gap / np.where(scale > 0, scale, 1.0)
+
+
 def top2_margin(z):
-    """Gap between the largest and second-largest value of each row."""
+    """Gap between the largest and second-largest value of each row, relative
+    to the row's largest magnitude (the decision margin of an argmax)."""
     part = np.partition(z, -2, axis=1)
-    return part[:, -1] - part[:, -2]
+    return _relative(part[:, -1] - part[:, -2], z)
 
 
 def routing_margin(r, k):
     """Smallest gap between consecutive sorted router logits among the first
     k + 1 ranks of each token (the rank order of the selected experts and the
-    cut between selected and not selected)."""
+    cut between selected and not selected), relative to the row's largest
+    magnitude."""
     s = -np.sort(-r, axis=1)
     last = min(k, r.shape[1] - 1)
     if last == 0:
         return np.full(r.shape[0], np.inf)
-    return np.min(s[:, :last] - s[:, 1:last + 1], axis=1)
+    return _relative(np.min(s[:, :last] - s[:, 1:last + 1], axis=1), r)
 
 
 def new_canvas_tensors(cv, dev=DEV):

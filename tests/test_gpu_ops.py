@@ -268,6 +268,14 @@ def test_moe_full_size_layer_shape():
     _moe_case(GEMMA, 256, "gemma")
 
 
+def test_moe_tiled_path_full_size_layer_shape():
+    # 1024 tokens x top-8 over 128 experts: 64 rows per expert on average,
+    # beyond the weight-streaming range (the grouped tiled GEMM runs)
+    _moe_case(GEMMA, 1024, "gemma_tiled")
+    g8 = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": "fp8_e4m3"})
+    _moe_case(g8, 1024, "gemma_fp8_tiled")
+
+
 def test_moe_e4m3_experts():
     s8 = synth.ModelShape(**{**TINY.__dict__, "expert_dtype": "fp8_e4m3"})
     _moe_case(s8, 256, "tiny_fp8")
@@ -311,6 +319,11 @@ def test_lmhead_tiny_and_ragged_vocab():
 
 def test_lmhead_full_vocab():
     _lm_case(128, 2048, 262144, "gemma")
+
+
+def test_lmhead_full_vocab_tiled_path():
+    # more than 256 rows: the tiled kernel, with a ragged last row tile
+    _lm_case(300, 2048, 262144, "gemma_tiled")
 
 
 def test_lmhead_uniform_and_tied_logits():
