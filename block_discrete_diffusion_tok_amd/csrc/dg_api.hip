@@ -624,8 +624,8 @@ size_t dg_packed_bytes(int32_t groups, int32_t rows, int32_t cols, int32_t dtype
   if (dtype != DG_BF16 && dtype != DG_FP8_E4M3) return 0;
   const int esz = dtype == DG_BF16 ? 2 : 1;
   if (groups < 1 || rows < 1 || cols < 1 || cols % pack_k(esz)) return 0;
-  if (groups > 1 && rows % 16) return 0;
-  return (size_t)groups * ((rows + 15) / 16 * 16) * cols * esz;
+  if (groups > 1 && rows % kPackRows) return 0;
+  return (size_t)groups * ((rows + kPackRows - 1) / kPackRows * kPackRows) * cols * esz;
 }
 
 dg_status dg_pack_weights(const void* src, int32_t groups, int32_t rows,
@@ -636,7 +636,7 @@ dg_status dg_pack_weights(const void* src, int32_t groups, int32_t rows,
   if (dg_packed_bytes(groups, rows, cols, dtype) == 0)
     return fail(nullptr, DG_ERR_SHAPE,
                 "cols must be a multiple of 32 (bf16) or 64 (e4m3), rows per group a "
-                "multiple of 16 when groups > 1");
+                "multiple of 64 when groups > 1");
   HIPCHK(nullptr, launch_pack(src, groups, rows, cols, dtype == DG_BF16 ? 2 : 1, dst,
                               (hipStream_t)stream));
   return DG_OK;

@@ -279,42 +279,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int n_rows = a.n * a.Hq * a.C;
   const int row_id = blockIdx.x * 4 + wave;
   if (row_id >= n_rows) return;
-  float ls[32];
-  float mx = -INFINITY;
+  // lane s holds split s's log-sum (splits <= 32): one load for all of
+  // them, the maximum by a wave reduction, split s's value by a broadcast
+  const float l_my = a.lpart[(long long)(lane < a.splits ? lane : 0) * n_rows + row_id];
+  float mx = lane < a.splits ? l_my : -INFINITY;
 #pragma unroll
-  for (int s = 0; s < 32; ++s)
-    if (s < a.splits) {
-      ls[s] = a.lpart[(long long)s * n_rows + row_id];
-      mx = fmaxf(mx, ls[s]);
-    }
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int s0 = 0; s0 < a.splits; s0 += U) {
-      float o[U][PER];
+  // (a row with no visible key has every split at -inf: all are skipped)
+  for (int s0 = 0; s0 < a.splits; s0 += U) {
+    float o[U][PER];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (s0 + u < a.splits) {
-          const float* op = a.opart + ((long long)(s0 + u) * n_rows + row_id) * D;
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u < a.splits ? s0 + u : 0;
+      const float* op = a.opart + ((long long)sp * n_rows + row_id) * D;
 #pragma unroll
-          for (int e = 0; e < PER; ++e) o[u][e] = op[lane + 64 * e];
-        }
+      for (int e = 0; e < PER; ++e) o[u][e] = op[lane + 64 * e];
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int sp = s0 + u;
-        if (sp >= a.splits) break;
-        float lsp = ls[0];
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + u;
+      if (sp >= a.splits) break;
+      const float lsp = __shfl(l_my, sp, 64);
+      if (lsp == -INFINITY) continue;
+      const float w = exp2f(lsp - mx);
+      wsum += w;
 #pragma unroll
-        for (int q = 0; q < 32; ++q)
-          if (q == sp) lsp = ls[q];
-        if (lsp == -INFINITY) continue;
-        const float w = exp2f(lsp - mx);
-        wsum += w;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * o[u][e];
-      }
+      for (int e = 0; e < PER; ++e) acc[e] += w * o[u][e];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -84,7 +84,7 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
     tr[p][j] = *(const u32x4_t*)(tsrc[j] + (long long)(kt) * BK);             \
   });                                                                         \
   static_for<XB>([&](auto j) {                                                \
-    wr[p][j] = *(const u32x4_t*)(wsrc[j] + (long long)(kt) * ESZ * kPackBlock); \
+    wr[p][j] = *(const u32x4_t*)(wsrc[j] + (long long)(kt) * ESZ * kPackKStride); \
   });
 #define DG_LSTORE(b, p)                                                       \
   static_for<XA>([&](auto j) {                                                \
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     } else {
       rb = min(nt * (BN / 16) + tile, (a.N + 15) / 16 - 1);  // zero-padded last tile
     }
-    wsrc[j] = wgroup + pack_block_offset(rb, kb, a.K, ESZ) + (k0 / BK) * ESZ * kPackBlock + 16 * ln;
+    wsrc[j] = wgroup + pack_block_offset(rb, kb, a.K, ESZ) + (k0 / BK) * ESZ * kPackKStride + 16 * ln;
   });
 
   f32x4_t acc[TM][TN];

@@ -52,8 +52,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const char* src, int rows,
     const long long g = p / pieces_per_group, pin = p % pieces_per_group;
     const long long block = pin >> 6;
     const int lane = (int)(pin & 63);
-    const long long rb = block / kb_n;
-    const int kb = (int)(block % kb_n);
+    // block -> (tile group, kb, tile in group), see pack_block_offset
+    const long long tg = block / ((long long)kb_n * kPackTiles);
+    const int rem = (int)(block % ((long long)kb_n * kPackTiles));
+    const int kb = rem / kPackTiles;
+    const long long rb = tg * kPackTiles + rem % kPackTiles;
     const long long row = rb * 16 + (lane & 15);
     const long long col = (long long)kb * pack_k(esz) + (lane >> 4) * per_piece;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -67,114 +70,181 @@ __global__ __launch_bounds__(256) void pack_kernel(const char* src, int rows,
 // src = row_map[r] when given, rows beyond *m_dev skipped.
 // One workgroup per row; a thread holds up to 4 float4 of the row (H up to
 // 4096 in registers, longer rows are read twice).
-__global__ __launch_bounds__(256) void rmsnorm_kernel(
-    const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
-    const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
-  constexpr int U = 4;
-  __shared__ float red[4];
+// Loads sit outside branches, at clamped (valid) addresses with the unused
+// values dropped by selects: a load inside a branch makes the compiler wait
+// for every load before it, one memory latency per load.
+__device__ __forceinline__ int clamp_col(int i, int H) { return i < H ? i : H - 4; }
+
+template <int U>
+__device__ __forceinline__ void load_gains(float4 (&gg)[U], const float* g, int H) {
+#pragma unroll
+  for (int c = 0; c < U; ++c)
+    gg[c] = *(const float4*)(g + clamp_col(1024 * c + (int)threadIdx.x * 4, H));
+}
+
+template <int U>
+__device__ __forceinline__ void norm_row(float4 (&v)[U], const float4 (&g0)[U],
+                                         float ss, const float* xr, int H,
+                                         const float* g, float eps,
+                                         uint16_t* out, float* copy_f32,
+                                         float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = blockIdx.x;
-  const int n = m_dev ? *m_dev : rows;
-  if (r >= n) return;
-  const int src = row_map ? row_map[r] : r;
-  const float* xr = x + (long long)src * H;
-  float4 v[U];
-  float ss = 0.f;
-  for (int base = 0; base < H; base += 1024 * U) {
-#pragma unroll
-    for (int c = 0; c < U; ++c) {
-      const int i = base + 1024 * c + tid * 4;
-      v[c] = i < H ? *(const float4*)(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int c = 0; c < U; ++c)
-      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
-  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
   ss = red[0] + red[1] + red[2] + red[3];
   const float inv = rsqrtf(ss / (float)H + eps);
-  uint16_t* o = out + (long long)r * H;
   for (int base = 0; base < H; base += 1024 * U) {
+    float4 gg[U];
+#pragma unroll
+    for (int c = 0; c < U; ++c) gg[c] = g0[c];
     if (H > 1024 * U) {  // rows longer than the registers hold: read again
 #pragma unroll
       for (int c = 0; c < U; ++c) {
-        const int i = base + 1024 * c + tid * 4;
-        if (i < H) v[c] = *(const float4*)(xr + i);
+        const int i = clamp_col(base + 1024 * c + tid * 4, H);
+        v[c] = *(const float4*)(xr + i);
+        gg[c] = *(const float4*)(g + i);
       }
     }
 #pragma unroll
     for (int c = 0; c < U; ++c) {
       const int i = base + 1024 * c + tid * 4;
       if (i >= H) continue;
-      const float4 gg = *(const float4*)(g + i);
-      const uint16_t b0 = f2bf(v[c].x * inv * gg.x), b1 = f2bf(v[c].y * inv * gg.y);
-      const uint16_t b2 = f2bf(v[c].z * inv * gg.z), b3 = f2bf(v[c].w * inv * gg.w);
-      *(uint2*)(o + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
-                                    (uint32_t)b2 | ((uint32_t)b3 << 16));
+      const uint16_t b0 = f2bf(v[c].x * inv * gg[c].x), b1 = f2bf(v[c].y * inv * gg[c].y);
+      const uint16_t b2 = f2bf(v[c].z * inv * gg[c].z), b3 = f2bf(v[c].w * inv * gg[c].w);
+      *(uint2*)(out + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
+                                      (uint32_t)b2 | ((uint32_t)b3 << 16));
       if (copy_f32)
-        *(float4*)(copy_f32 + (long long)r * H + i) =
-            make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
+        *(float4*)(copy_f32 + i) = make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
     }
   }
 }
 
+__global__ __launch_bounds__(256) void rmsnorm_kernel(
+    const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
+    const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
+  constexpr int U = 4;
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const int n = m_dev ? *m_dev : rows;
+  const int src = row_map ? row_map[r] : r;
+  float4 gg[U];
+  load_gains<U>(gg, g, H);
+  if (r >= n) return;
+  const float* xr = x + (long long)src * H;
+  float4 v[U];
+  float ss = 0.f;
+  // the first 1024*U columns straight-line (a loop header would wait for
+  // the gain loads), the rest of a longer row in a loop
+#pragma unroll
+  for (int c = 0; c < U; ++c)
+    v[c] = *(const float4*)(xr + clamp_col(1024 * c + tid * 4, H));
+  for (int base = 0;;) {
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      if (base + 1024 * c + tid * 4 >= H) v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+    base += 1024 * U;
+    if (base >= H) break;
+#pragma unroll
+    for (int c = 0; c < U; ++c)
+      v[c] = *(const float4*)(xr + clamp_col(base + 1024 * c + tid * 4, H));
+  }
+  norm_row<U>(v, gg, ss, xr, H, g, eps, out + (long long)r * H,
+              copy_f32 ? copy_f32 + (long long)r * H : nullptr, red);
+}
+
 // ---------------------------------------------------------------- router top-k
-// One workgroup per token, thread e holding logit e.  A logit's rank is the
-// number of logits above it (equal logits: lower expert ids first), counted
-// over LDS broadcasts; the k lowest ranks are the selection, in rank order.
-// Gate weights: softmax over the selected logits, summed in rank order.
+// One wave per token; lane l holds the logits of experts l, l+64, l+128 and
+// l+192.  Each logit becomes a unique 64-bit key (order-preserving bits of
+// the logit above, 255 - expert id below), so "larger logit first, lower id
+// first among equal logits" is plain key order; k rounds of a wave-wide
+// maximum pick the selection in rank order, the owner of each winner
+// dropping it.  Gate weights: softmax over the selected logits, summed in
+// rank order.
+constexpr int kTopkMaxE = 256, kTopkMaxK = 16;
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  if (v == 0.f) v = 0.f;  // -0 and +0 are equal logits
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
                                                    int k, int splits, int32_t* idx,
                                                    float* w) {
-  __shared__ __attribute__((aligned(16))) float lv[256];
-  __shared__ float sel[16];
-  const int t = blockIdx.x, e = threadIdx.x;
+  constexpr int PER = kTopkMaxE / kWave;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const long long slab = (long long)T * E, row = (long long)t * E;
   // the router's K splits left `splits` partial slabs: add them in order
-  float v = -INFINITY;
-  if (e < E) {
-    const long long slab = (long long)T * E, o = (long long)t * E + e;
-    float part[8];
+  float part[PER][8];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = min(lane + kWave * i, E - 1);
 #pragma unroll
     for (int sp = 0; sp < 8; ++sp)
-      if (sp < splits) part[sp] = logits[sp * slab + o];
-    v = part[0];
-#pragma unroll
-    for (int sp = 1; sp < 8; ++sp)
-      if (sp < splits) v += part[sp];
-    for (int sp = 8; sp < splits; ++sp) v += logits[sp * slab + o];
-    if (splits > 1) logits[o] = v;
+      part[i][sp] = logits[(sp < splits ? sp : 0) * slab + row + e];
   }
-  lv[e] = v;
-  __syncthreads();
-  // entries past E hold -inf with higher ids: they never rank above a real
-  // logit
-  int rk = 0;
-  const int E16 = (E + 15) & ~15;
-  for (int q0 = 0; q0 < E16; q0 += 16) {
-    float4 o4[4];
+  unsigned long long key[PER];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o4[u] = *(const float4*)&lv[q0 + 4 * u];
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = 0;  // below every real key
+    if (e < E) {
+      float v = part[i][0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float o[4] = {o4[u].x, o4[u].y, o4[u].z, o4[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        rk += (o[c] > v || (o[c] == v && q0 + 4 * u + c < e)) ? 1 : 0;
+      for (int sp = 1; sp < 8; ++sp)
+        if (sp < splits) v += part[i][sp];
+      for (int sp = 8; sp < splits; ++sp) v += logits[sp * slab + row + e];
+      if (splits > 1) logits[row + e] = v;
+      key[i] = ((unsigned long long)ordered_bits(v) << 32) | (uint32_t)(255 - e);
     }
   }
-  if (e < E && rk < k) {
-    idx[(long long)t * k + rk] = e;
-    sel[rk] = v;
+  float sel[kTopkMaxK];
+  int sid[kTopkMaxK];
+#pragma unroll
+  for (int r = 0; r < kTopkMaxK; ++r) {
+    sel[r] = 0.f;
+    sid[r] = 0;
+    if (r < k) {
+      unsigned long long m = key[0];
+#pragma unroll
+      for (int i = 1; i < PER; ++i) m = key[i] > m ? key[i] : m;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = shfl_xor(m, off);
+        m = o > m ? o : m;
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (key[i] == m) key[i] = 0;
+      sel[r] = from_ordered_bits((uint32_t)(m >> 32));
+      sid[r] = 255 - (int)(uint32_t)m;
+    }
   }
-  __syncthreads();
-  if (e < k) {
-    const float mx = sel[0];
-    float sum = 0.f;
-    for (int r = 0; r < k; ++r) sum += __expf(sel[r] - mx);
-    w[(long long)t * k + e] = __expf(sel[e] - mx) / sum;
+  const float mx = sel[0];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kTopkMaxK; ++r)
+    if (r < k) sum += __expf(sel[r] - mx);
+  float my_sel = 0.f;
+  int my_id = 0;
+#pragma unroll
+  for (int r = 0; r < kTopkMaxK; ++r)
+    if (r == lane) {
+      my_sel = sel[r];
+      my_id = sid[r];
+    }
+  if (lane < k) {
+    idx[(long long)t * k + lane] = my_id;
+    w[(long long)t * k + lane] = __expf(my_sel - mx) / sum;
   }
 }
 
@@ -268,7 +338,11 @@ __global__ __launch_bounds__(1024) void moe_permute_small_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int p = tid + 1024 * r;
-    e4[r] = p < n_pairs ? idx[p] : -1;
+    const int e = idx[p < n_pairs ? p : n_pairs - 1];
+    e4[r] = p < n_pairs ? e : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
     if (e4[r] >= 0) atomicAdd(&hist[e4[r]], 1);
   }
   __syncthreads();
@@ -325,12 +399,12 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
     float4 v[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
-      if (j < k) v[j] = *(const float4*)(y + ((long long)t * k + j) * H + i);
+      v[j] = *(const float4*)(y + ((long long)t * k + (j < k ? j : 0)) * H + i);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (j < k) { s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w; }
-    if (x) {
+    if (x) {  // (the x load is issued before the sums wait for y)
       float4* xp = (float4*)(x + (long long)t * H + i);
       float4 o = *xp;
       o.x += s.x; o.y += s.y; o.z += s.z; o.w += s.w;
@@ -345,40 +419,6 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
 // columns base + 1024 c + 4 tid (c < U); rows longer than 1024 U are read
 // back from xr (written earlier by this same thread).  out = bf16(x * inv
 // * g); copy_f32 optionally receives the bf16 values widened.
-template <int U>
-__device__ __forceinline__ void norm_row(float4 (&v)[U], float ss, const float* xr,
-                                         int H, const float* g, float eps,
-                                         uint16_t* out, float* copy_f32,
-                                         float* red) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += shfl_xor(ss, off);
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  ss = red[0] + red[1] + red[2] + red[3];
-  const float inv = rsqrtf(ss / (float)H + eps);
-  for (int base = 0; base < H; base += 1024 * U) {
-    if (H > 1024 * U) {
-#pragma unroll
-      for (int c = 0; c < U; ++c) {
-        const int i = base + 1024 * c + tid * 4;
-        if (i < H) v[c] = *(const float4*)(xr + i);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < U; ++c) {
-      const int i = base + 1024 * c + tid * 4;
-      if (i >= H) continue;
-      const float4 gg = *(const float4*)(g + i);
-      const uint16_t b0 = f2bf(v[c].x * inv * gg.x), b1 = f2bf(v[c].y * inv * gg.y);
-      const uint16_t b2 = f2bf(v[c].z * inv * gg.z), b3 = f2bf(v[c].w * inv * gg.w);
-      *(uint2*)(out + i) = make_uint2((uint32_t)b0 | ((uint32_t)b1 << 16),
-                                      (uint32_t)b2 | ((uint32_t)b3 << 16));
-      if (copy_f32)
-        *(float4*)(copy_f32 + i) = make_float4(bf2f(b0), bf2f(b1), bf2f(b2), bf2f(b3));
-    }
-  }
-}
 
 // Embedding gather (packed table, ids clamped) fused with the first layer's
 // attention RMSNorm: x[t] = E[tok[t]] (fp32), xh[t] = RMSNorm(x[t]; g).
@@ -391,39 +431,53 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok,
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int id = min(max(tok[t], 0), V - 1);
+  float4 gg[U];
+  load_gains<U>(gg, g, H);
   const char* base = (const char*)E;
   float* xr = x + (long long)t * H;
   float4 v[U];
   float ss = 0.f;
   for (int b0 = 0; b0 < H; b0 += 1024 * U) {
+    uint2 w[U];
 #pragma unroll
     for (int c = 0; c < U; ++c) {
       // columns i..i+3: half of one 16-byte packed piece
+      const int i = clamp_col(b0 + 1024 * c + tid * 4, H);
+      const long long off = pack_block_offset(id >> 4, i >> 5, H, 2) +
+                            16 * ((id & 15) + 16 * ((i & 31) >> 3)) + 2 * (i & 7);
+      w[c] = *(const uint2*)(base + off);
+    }
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
       const int i = b0 + 1024 * c + tid * 4;
+      v[c] = make_float4(bf2f((uint16_t)(w[c].x & 0xffff)), bf2f((uint16_t)(w[c].x >> 16)),
+                         bf2f((uint16_t)(w[c].y & 0xffff)), bf2f((uint16_t)(w[c].y >> 16)));
       if (i < H) {
-        const long long off = pack_block_offset(id >> 4, i >> 5, H, 2) +
-                              16 * ((id & 15) + 16 * ((i & 31) >> 3)) + 2 * (i & 7);
-        const uint2 w = *(const uint2*)(base + off);
-        v[c] = make_float4(bf2f((uint16_t)(w.x & 0xffff)), bf2f((uint16_t)(w.x >> 16)),
-                           bf2f((uint16_t)(w.y & 0xffff)), bf2f((uint16_t)(w.y >> 16)));
         *(float4*)(xr + i) = v[c];
         ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
       }
     }
   }
-  norm_row<U>(v, ss, xr, H, g, eps, xh + (long long)t * H, nullptr, red);
+  norm_row<U>(v, gg, ss, xr, H, g, eps, xh + (long long)t * H, nullptr, red);
 }
 
 // Un-permute fused with the next RMSNorm: x[t] += sum_j y[t*k + j] in rank
 // order (moe_out[t] = the sum, if given), then xh[r] = RMSNorm(x[t]; g) with
 // r = out_row[t] (no output when -1) or t (copy_f32[r] = widened xh[r], if
 // given).
+// KMAX: compile-time bound on k (8 or 16), so the y loads of every slot
+// can be issued at once without loading beyond the k slots present.
+template <int KMAX>
 __global__ __launch_bounds__(256) void unpermute_norm_kernel(
     const float* y, int k, int H, float* x, float* moe_out, const float* g,
     float eps, uint16_t* xh, float* copy_f32, const int32_t* out_row) {
-  constexpr int U = 4, KMAX = 16;
+  constexpr int U = 4;
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
+  // the norm goes to row out_row[t] (skipped when -1), or to row t
+  const int orow = out_row ? out_row[t] : t;
+  float4 gg[U];
+  load_gains<U>(gg, g, H);
   float* xr = x + (long long)t * H;
   float4 v[U];
   float ss = 0.f;
@@ -431,27 +485,29 @@ __global__ __launch_bounds__(256) void unpermute_norm_kernel(
 #pragma unroll
     for (int c = 0; c < U; ++c) {
       const int i = b0 + 1024 * c + tid * 4;
-      if (i >= H) continue;
+      const int ic = clamp_col(i, H);
       float4 yy[KMAX];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (j < k) yy[j] = *(const float4*)(y + ((long long)t * k + j) * H + i);
+        yy[j] = *(const float4*)(y + ((long long)t * k + (j < k ? j : 0)) * H + ic);
+      float4 o = *(const float4*)(xr + ic);
       float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (j < k) { sum.x += yy[j].x; sum.y += yy[j].y; sum.z += yy[j].z; sum.w += yy[j].w; }
-      float4 o = *(const float4*)(xr + i);
       o.x += sum.x; o.y += sum.y; o.z += sum.z; o.w += sum.w;
-      *(float4*)(xr + i) = o;
-      if (moe_out) *(float4*)(moe_out + (long long)t * H + i) = sum;
+      if (i < H) {
+        *(float4*)(xr + i) = o;
+        if (moe_out) *(float4*)(moe_out + (long long)t * H + i) = sum;
+        ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+      } else {
+        o = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
       v[c] = o;
-      ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
     }
   }
-  // the norm goes to row out_row[t] (skipped when -1), or to row t
-  const int orow = out_row ? out_row[t] : t;
   if (orow < 0) return;
-  norm_row<U>(v, ss, xr, H, g, eps, xh + (long long)orow * H,
+  norm_row<U>(v, gg, ss, xr, H, g, eps, xh + (long long)orow * H,
               copy_f32 ? copy_f32 + (long long)orow * H : nullptr, red);
 }
 
@@ -463,28 +519,45 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
                                                        int T, int32_t* row_map,
                                                        int32_t* m_dev,
                                                        int32_t* pos_map) {
-  __shared__ int s[1024];
-  __shared__ int run;
-  const int tid = threadIdx.x;
-  if (tid == 0) run = 0;
-  __syncthreads();
-  for (int base = 0; base < T; base += 1024) {
-    const int t = base + tid;
-    const int f = (t < T && committed[t] == 0) ? 1 : 0;
-    s[tid] = f;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? s[tid - off] : 0;
-      __syncthreads();
-      s[tid] += v;
-      __syncthreads();
+  // chunks of 1024 positions, 8 chunks' flags read at once; in-wave ranks
+  // from ballots, wave offsets from the 16 wave counts
+  constexpr int G = 8;
+  __shared__ int wcount[G][16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1;
+  int run = 0;
+  for (int base = 0; base < T; base += 1024 * G) {
+    bool f[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int t = base + 1024 * i + tid;
+      const uint8_t c = committed[t < T ? t : T - 1];
+      f[i] = t < T && c == 0;
     }
-    if (f) row_map[run + s[tid] - 1] = t;
-    if (pos_map && t < T) pos_map[t] = f ? run + s[tid] - 1 : -1;
-    const int total = s[1023];
+    int before[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const unsigned long long bal = __ballot(f[i]);
+      before[i] = __popcll(bal & below);
+      if (lane == 0) wcount[i][wv] = __popcll(bal);
+    }
     __syncthreads();
-    if (tid == 0) run += total;
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      int off = run, total = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int c = wcount[i][q];
+        off += q < wv ? c : 0;
+        total += c;
+      }
+      const int t = base + 1024 * i + tid;
+      const int r = off + before[i];
+      if (f[i]) row_map[r] = t;
+      if (pos_map && t < T) pos_map[t] = f[i] ? r : -1;
+      run += total;
+    }
+    __syncthreads();  // wcount is reused
   }
   if (tid == 0) *m_dev = run;
 }
@@ -565,9 +638,15 @@ __global__ __launch_bounds__(256) void eb_kernel(
   __shared__ int s_first;
   const int b = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
   const long long base = (long long)b * DG_CANVAS;
-  const bool unc = committed[base + j] == 0;
+  // every global read issued at once (values at committed positions are
+  // read but not used): one memory latency instead of a chain of them
+  const uint8_t cm = committed[base + j];
+  const float h_in = entropy[base + j];
+  const int32_t am_in = argmax[base + j];
+  const float lim = gamma[b];
   const int steps_done = step[b];  // read by all before thread 0 updates it
-  float h = unc ? entropy[base + j] : 0.f;
+  const bool unc = cm == 0;
+  float h = unc ? h_in : 0.f;
   if (h == 0.f) h = 0.f;  // -0 -> +0
   uint32_t u = __float_as_uint(h);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving
@@ -605,7 +684,7 @@ __global__ __launch_bounds__(256) void eb_kernel(
   __syncthreads();
   for (int q = 0; q < w; ++q) c += wave_sum[q];
   // n* = length of the longest sorted prefix whose sum stays within gamma
-  if (j < n_unc && c > (double)gamma[b]) atomicMin(&s_first, j);
+  if (j < n_unc && c > (double)lim) atomicMin(&s_first, j);
   __syncthreads();
   int n = min(s_first, n_unc);
   if (n < 1) n = 1;
@@ -613,9 +692,9 @@ __global__ __launch_bounds__(256) void eb_kernel(
   if (unc) {
     if (rank < n) {
       committed[base + j] = 1;
-      tokens[base + j] = argmax[base + j];
+      tokens[base + j] = am_in;
     } else if (refine) {
-      tokens[base + j] = argmax[base + j];
+      tokens[base + j] = am_in;
     }
   }
   if (j == 0) {
@@ -671,7 +750,8 @@ __global__ __launch_bounds__(256) void kv_install_kernel(const uint16_t* src,
 
 hipError_t launch_pack(const void* src, int groups, int rows, int cols, int esz,
                        void* dst, hipStream_t s) {
-  const long long ppg = (long long)((rows + 15) / 16 * 16) * cols * esz / 16;
+  const long long ppg =
+      (long long)((rows + kPackRows - 1) / kPackRows * kPackRows) * cols * esz / 16;
   if (ppg * groups <= 0) return hipSuccess;
   const long long blocks = std::min<long long>((ppg * groups + 255) / 256, 65536);
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
@@ -699,7 +779,8 @@ hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
 hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
                        float* w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(256), 0, s, logits,
+  if (E > kTopkMaxE || k > kTopkMaxK || k > E) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
                      T, E, k, splits, idx, w);
   return hipGetLastError();
 }
@@ -744,8 +825,13 @@ hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
                                  uint16_t* xh, float* copy_f32,
                                  const int32_t* out_row, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(unpermute_norm_kernel, dim3(T), dim3(256), 0, s, y, k, H, x,
-                     moe_out, g, eps, xh, copy_f32, out_row);
+  if (k > 16) return hipErrorInvalidValue;
+  if (k <= 8)
+    hipLaunchKernelGGL(unpermute_norm_kernel<8>, dim3(T), dim3(256), 0, s, y, k, H, x,
+                       moe_out, g, eps, xh, copy_f32, out_row);
+  else
+    hipLaunchKernelGGL(unpermute_norm_kernel<16>, dim3(T), dim3(256), 0, s, y, k, H, x,
+                       moe_out, g, eps, xh, copy_f32, out_row);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 // in the LM head), so the kernel is organised around HBM streaming:
 //
 //   * each wave owns RT x 16 weight rows and reads them straight from HBM
-//     into registers, D chunks ahead of the MFMAs (weights are used once, so
-//     they never pass through LDS).  The weights are in the packed
+//     into D+1 register sets, D chunks ahead of the MFMAs (weights are used
+//     once, so they never pass through LDS); a chunk's successor D chunks
+//     ahead is issued before its MFMAs start.  The weights are in the packed
 //     (MFMA-tiled) layout, so every wave load instruction reads one
 //     contiguous kilobyte of full cache lines: with a row-major layout each
 //     instruction would touch 16 lines and use half of each, and the L1's
@@ -33,6 +34,8 @@
 // order).  This is the order of the packed layout's blocks: a lane's q-th
 // 16-byte weight load of chunk kc is block kc * KC/(32 or 64) + q.
 #include <math.h>
+
+#include <type_traits>
 
 #include "dg_internal.h"
 
@@ -63,7 +66,8 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 // select between a global and a private "zero" would turn them into flat
 // loads, which the waitcnt pass can only wait for all at once).
 // In the packed layout the q-th load of chunk kc is block kc * WREGS + q of
-// the row tile: one contiguous kilobyte per wave load.
+// the row tile: one contiguous kilobyte per wave load, and the 4 tiles of a
+// tile group (2 waves) read one contiguous run per block column.
 template <int RT, int WREGS, int ESZ, int KC>
 __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
                                        const char* const (&src)[RT], int kc) {
@@ -71,7 +75,7 @@ __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int q = 0; q < WREGS; ++q)
-      w[rt][q] = *(const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackBlock);
+      w[rt][q] = *(const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackKStride);
 }
 
 // LDS-DMA of 16 bytes per lane: lane l's bytes land at lds_wave_base +
@@ -141,9 +145,12 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
   }
 }
 
-template <int RT, int NT, int KC, int D, int EPI, bool W8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void stream_kernel(StreamArgs a) {
+  // the gate/up products read their token rows through the expert
+  // permutation (row = x_map[r] / x_map_div), the others directly
+  constexpr bool MAPPED = EPI == EPI_SWIGLU;
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
   static_assert(KC == 64 || KC == 128, "K chunk");
   constexpr int WROWS = 4 * RT * 16;  // weight rows per workgroup
@@ -215,11 +222,12 @@ void stream_kernel(StreamArgs a) {
       const int row = u / (KC / 8);
       const int c = (u % (KC / 8)) ^ (row & 7);
       const int trow = t0 + (row < nt_rows ? row : 0);
-      const int src = xmap ? xmap[trow] / xdiv : trow;
+      const int src = MAPPED ? xmap[trow] / xdiv : trow;
       xsrc[i] = xbase + (long long)src * ldx + c * 8;
     });
-    // D weight register sets; chunk k uses set k % D and stage k % S.
-    u32x4_t w[D][RT][WREGS];
+    // chunk k uses weight register set k % NSET and token stage k % S
+    constexpr int NSET = D + 1;  // register sets: chunk k+D loads while chunk k computes
+    u32x4_t w[NSET][RT][WREGS];
 
     f32x4_t acc[RT][NT];
 #pragma unroll
@@ -227,29 +235,32 @@ void stream_kernel(StreamArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int last = nk - 1;
-    // Loads of chunk k (clamped to the last chunk: a redundant, valid load
-    // into a stage and a register set whose chunk is already consumed).
+    // Loads of chunk k < nk: its token DMA into stage k % S, its weights
+    // into register set p = k % NSET.
     auto issue = [&](auto p, int k) {
-      const int kk = min(k, last);
       uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
-      static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)kk * KC, st + i * 64 * 8); });
-      load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, kk);
+      static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
+      load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, k);
     };
-    // Chunk k: wait for its loads (all but the (D-1) younger chunks'),
-    // barrier (every wave's token DMA has landed; every wave is past chunk
-    // k-1, whose stage the chunk k+D DMA reuses), MFMAs, then issue chunk
-    // k+D.  The barrier is the bare instruction: a workgroup fence here
-    // would wait for every DMA in flight.
-    auto step = [&](auto p, int k) {
-      __builtin_amdgcn_s_waitcnt(vm_wait((D - 1) * LOADS));
+    // Chunk k, with `younger` chunks issued after it: wait for its loads
+    // (the vector-memory counter completes in issue order), barrier (every
+    // wave's token DMA has landed; every wave is past chunk k-1, whose
+    // stage the chunk k+D DMA reuses), issue chunk k+D if it exists (into
+    // the register set no chunk in flight uses), then the MFMAs of chunk
+    // k, so D chunks stay in flight while they run.  The barrier is the
+    // bare instruction: a workgroup fence here would wait for every DMA in
+    // flight.
+    auto step = [&](auto p, int k, int younger, bool more) {
+      static_for<D>([&](auto y) {
+        if (younger == y) __builtin_amdgcn_s_waitcnt(vm_wait(decltype(y)::value * LOADS));
+      });
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      mfma_chunk<RT, NT, KC, WREGS, W8>(acc, w[p], &Xs[(k % S) * STAGE], l16, lg);
+      if (more) issue(std::integral_constant<int, (decltype(p)::value + D) % NSET>(), k + D);
       __builtin_amdgcn_sched_barrier(0);
-      issue(p, k + D);
+      mfma_chunk<RT, NT, KC, WREGS, W8>(acc, w[p], &Xs[(k % S) * STAGE], l16, lg);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -258,19 +269,24 @@ void stream_kernel(StreamArgs a) {
       issue(p, (int)p);
       __builtin_amdgcn_sched_barrier(0);
     });
-    // Whole groups of D chunks as straight-line code in a loop entered
-    // unconditionally (nk >= D is a launch precondition), so the issue
-    // order is the same on entry and on the back edge and every wait stays
-    // exact; then the remaining nk % D chunks.
+    // Groups of NSET chunks as straight-line code (register set k % NSET
+    // is static) while every chunk of the group issues chunk k+D < nk; the
+    // state at each group boundary is the same (chunks kc..kc+D-1 in
+    // flight), so the fixed waits stay exact.  Then the last chunks: those
+    // with k+D < nk still issue, the last D drain with waits for exactly
+    // the chunks still in flight (nk >= D is a launch precondition).
     int kc = 0;
-    do {
-      static_for<D>([&](auto p) { step(p, kc + p); });
-      kc += D;
-    } while (kc + D <= nk);
-    static_for<D - 1>([&](auto p) {
-      if (kc + p < nk) step(p, kc + p);
+    while (kc + NSET + D <= nk) {
+      static_for<NSET>([&](auto p) { step(p, kc + p, D - 1, true); });
+      kc += NSET;
+    }
+    static_for<NSET + D>([&](auto j) {
+      const int k = kc + j;
+      if (k < nk)
+        step(std::integral_constant<int, j % NSET>(), k, min(D - 1, nk - 1 - k),
+             k + D < nk);
     });
-    __syncthreads();  // drains the redundant DMAs before LDS is reused
+    __syncthreads();  // every wave is done with the stages before LDS is reused
 
     // ---- epilogues: lane holds token column t0 + 16*nt + l16 and weight
     // rows 4*lg + e of each row tile
@@ -400,14 +416,15 @@ void stream_kernel(StreamArgs a) {
   }
 }
 
-template <int RT, int NT, int KC, int D, int EPI, bool W8>
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC>
 hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
   constexpr int WROWS = 4 * RT * 16;
+  if ((a.x_map != nullptr) != (EPI == EPI_SWIGLU)) return hipErrorInvalidValue;
   int grid_x;
   if (EPI == EPI_SWIGLU) grid_x = (a.ffn + WROWS / 2 - 1) / (WROWS / 2);
   else grid_x = (a.N + WROWS - 1) / WROWS;
   if (grid_x <= 0 || groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, D, EPI, W8>), dim3(grid_x, groups),
+  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, D, EPI, W8, OCC>), dim3(grid_x, groups),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -415,11 +432,12 @@ hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
 }  // namespace
 
 // LM head: 2 row tiles per wave (128 vocabulary rows per workgroup), 128
-// token columns per pass, K chunks of 64, 4 chunks in flight (5 stages of
-// 16 KB).  Experts: 2 row tiles, 32 token columns, K chunks of 128, 3 in
-// flight (4 stages of 8 KB).
-constexpr int kLmRT = 2, kLmKC = 64, kLmD = 4;
-constexpr int kMoeRT = 2, kMoeKC = 128, kMoeD = 3;
+// token columns per pass, K chunks of 64, 3 chunks in flight (4 stages of
+// 16 KB, 4 weight register sets).  Experts: 2 row tiles, 32 token
+// columns, K chunks of 128, 3 in flight (4 stages of 8 KB, 4 weight
+// register sets).
+constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2;
+constexpr int kMoeRT = 2, kMoeKC = 128, kMoeD = 3, kMoeOcc = 2;
 
 int stream_rows_per_wg() { return 4 * kLmRT * 16; }
 bool stream_lm_ok(int hidden) {
@@ -435,15 +453,15 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
   switch (epi) {
     case EPI_LMSTATS:
       if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
-      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false>(a, groups, s);
+      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc>(a, groups, s);
     case EPI_SWIGLU:
       if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false>(a, groups, s);
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true, kMoeOcc>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false, kMoeOcc>(a, groups, s);
     case EPI_DOWN:
       if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false>(a, groups, s);
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true, kMoeOcc>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false, kMoeOcc>(a, groups, s);
   }
   return hipErrorInvalidValue;
 }

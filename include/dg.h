@@ -86,13 +86,15 @@ typedef struct {
  * w_router, w_gate_up, w_down and the embedding) is passed in a tiled form
  * made by dg_pack_weights from the row-major matrix [R, K] (per group for
  * the expert matrices): blocks of 1024 bytes, each 16 rows x 64/b values (b
- * = element bytes), block (rb, kb) at byte (rb * K * b / 64 + kb) * 1024,
- * and in a block the 16 bytes at 16 * (r + 16 q) hold row 16 rb + r, values
- * kb * 64/b + q * 16/b .. + 16/b - 1.  This is the operand order of the
- * 16x16x32 MFMA, so the kernels stream weights with one contiguous
- * kilobyte per wave load.  Rows are zero-padded to a multiple of 16 (with
- * groups > 1 the rows per group must be a multiple of 16); K must be a
- * multiple of 64/b. */
+ * = element bytes); in a block the 16 bytes at 16 * (r + 16 q) hold row
+ * 16 rb + r, values kb * 64/b + q * 16/b .. + 16/b - 1, which is the operand
+ * order of the 16x16x32 MFMA (one contiguous kilobyte per wave load).  Row
+ * tiles come in groups of 4 (64 rows) and inside a group the blocks are
+ * ordered by kb, then tile: block (rb, kb) is at byte
+ * ((rb / 4) * 4 * KB + kb * 4 + rb % 4) * 1024, KB = K * b / 64, so the
+ * tiles of a group streamed together in K order form one contiguous run.
+ * Rows are zero-padded to a multiple of 64 (with groups > 1 the rows per
+ * group must be a multiple of 64); K must be a multiple of 64/b. */
 size_t dg_packed_bytes(int32_t groups, int32_t rows, int32_t cols, int32_t dtype);
 
 /* Pack groups x [rows, cols] row-major (bf16 or e4m3 bytes, device memory)

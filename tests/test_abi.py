@@ -152,11 +152,15 @@ def test_sampler_and_ops_validation():
 
 def test_packed_layout_sizes_and_validation():
     L = dg.lib()
-    # rows padded to whole 16-row tiles; K a multiple of 32 (bf16) / 64 (e4m3)
-    assert L.dg_packed_bytes(1, 200, 256, dg.BF16) == 208 * 256 * 2
+    # rows padded to whole 64-row tile groups; K a multiple of 32 (bf16) /
+    # 64 (e4m3)
+    assert L.dg_packed_bytes(1, 200, 256, dg.BF16) == 256 * 256 * 2
+    assert L.dg_packed_bytes(1, 64, 256, dg.BF16) == 64 * 256 * 2
     assert L.dg_packed_bytes(1, 262144, 2048, dg.BF16) == 262144 * 2048 * 2
     assert L.dg_packed_bytes(128, 1536, 2048, dg.FP8_E4M3) == 128 * 1536 * 2048
     assert L.dg_packed_bytes(2, 200, 256, dg.BF16) == 0     # groups need whole tiles
+    assert L.dg_packed_bytes(2, 32, 256, dg.BF16) == 0      # ... of 64 rows
+    assert L.dg_packed_bytes(2, 128, 256, dg.BF16) == 2 * 128 * 256 * 2
     assert L.dg_packed_bytes(1, 64, 48, dg.BF16) == 0       # K not a multiple of 32
     assert L.dg_packed_bytes(1, 64, 32, dg.FP8_E4M3) == 0   # K not a multiple of 64
     assert L.dg_packed_bytes(1, 64, 64, 7) == 0

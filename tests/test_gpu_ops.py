@@ -59,24 +59,28 @@ def test_linear_three_modes(m, k, n):
 
 def _pack_reference(a, esz):
     """The packed layout by its definition (include/dg.h): groups x [R, K]
-    byte matrices -> 1 KB blocks of 16 rows x 64/esz values, block (rb, kb)
-    at (rb * K*esz/64 + kb) * 1024, piece r + 16 q = row 16 rb + r, values
-    kb * 64/esz + q * 16/esz .. +16/esz - 1; rows zero-padded to 16."""
+    byte matrices -> 1 KB blocks of 16 rows x 64/esz values, piece r + 16 q
+    of block (rb, kb) = row 16 rb + r, values kb * 64/esz + q * 16/esz ..
+    +16/esz - 1; block (rb, kb) at ((rb // 4) * 4 * KB + kb * 4 + rb % 4) KB,
+    KB = K*esz/64; rows zero-padded to 64."""
     g, r, kbytes = a.shape
-    rp = (r + 15) // 16 * 16
+    rp = (r + 63) // 64 * 64
+    kbn = kbytes // 64
     pad = np.zeros((g, rp, kbytes), np.uint8)
     pad[:, :r] = a
-    out = np.zeros((g, rp // 16, kbytes // 64, 64, 16), np.uint8)
+    out = np.zeros((g, rp // 16 * kbn, 64, 16), np.uint8)
     for rb in range(rp // 16):
-        for kb in range(kbytes // 64):
+        for kb in range(kbn):
+            at = (rb // 4) * 4 * kbn + kb * 4 + rb % 4
             for q in range(4):
                 for rr in range(16):
-                    out[:, rb, kb, rr + 16 * q] = pad[:, 16 * rb + rr,
-                                                     64 * kb + 16 * q:64 * kb + 16 * q + 16]
+                    out[:, at, rr + 16 * q] = pad[:, 16 * rb + rr,
+                                                  64 * kb + 16 * q:64 * kb + 16 * q + 16]
     return out.reshape(-1)
 
 
-@pytest.mark.parametrize("groups,rows,cols,e4m3", [(1, 40, 96, False), (3, 32, 128, True)])
+@pytest.mark.parametrize("groups,rows,cols,e4m3", [(1, 40, 96, False), (1, 200, 64, False),
+                                                    (3, 64, 128, True)])
 def test_pack_weights_matches_layout_definition(groups, rows, cols, e4m3):
     gen = torch.Generator().manual_seed(11)
     if e4m3:
