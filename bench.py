@@ -70,6 +70,46 @@ def algorithmic(kind, s, wl, mean_rows):
     return None
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "traffic_moe_layer_h2048_v262k_p2048.md")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers the kernels are built from;
+    traffic figures measured on other sources are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    dirs = [os.path.join(ROOT, "block_discrete_diffusion_tok_amd", "csrc"),
+            os.path.join(ROOT, "include")]
+    for d in dirs:
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h")):
+                h.update(f.encode())
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch of a kernel kind from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none or it was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    vals = {}
+    for ln in lines:
+        if ln.startswith("    ") and ":" in ln:
+            k, v = ln.strip().split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    v = vals.get(f"traffic_bytes_per_launch[{kind}]")
+    return int(v) if v else None
+
+
 def copy_calibration():
     import torch
     n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
@@ -263,7 +303,7 @@ def main():
             roofline = {"kernel": name, "bound": "hbm",
                         "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                        "traffic": None,
+                        "traffic": measured_traffic(name),
                         "algorithmic_bytes_per_launch": int(nbytes),
                         "avg_launch_us": round(t_avg * 1e6, 2)}
         else:
@@ -271,7 +311,7 @@ def main():
             roofline = {"kernel": name, "bound": "mfma",
                         "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                        "traffic": None,
+                        "traffic": measured_traffic(name),
                         "algorithmic_flops_per_launch": int(flops),
                         "avg_launch_us": round(t_avg * 1e6, 2)}
         break

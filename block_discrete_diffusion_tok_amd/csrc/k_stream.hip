@@ -169,7 +169,7 @@ void stream_kernel(StreamArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int group = blockIdx.y;
+  const int group = blockIdx.y, bx = blockIdx.x;
 
   // ---- token rows of this group
   int t_begin, t_end;
@@ -186,7 +186,7 @@ void stream_kernel(StreamArgs a) {
   // ---- this wave's weight row tiles (16 rows each) and the packed address
   // of this lane's piece of their first block; tiles past the matrix read
   // tile 0 (valid addresses, results never stored)
-  const int n_base = blockIdx.x * WROWS;
+  const int n_base = bx * WROWS;
   const char* wgroup = (const char*)a.W + (long long)group * a.w_group_stride * ESZ;
   const char* wsrc[RT];
 #pragma unroll
@@ -196,7 +196,7 @@ void stream_kernel(StreamArgs a) {
     if (EPI == EPI_SWIGLU) {
       // tiles [0, RT/2) are gate rows of channels c0 + 16*rt + [0, 16),
       // tiles [RT/2, RT) the up rows of the same channels
-      const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT) + (rt % (RT / 2)) * 16;
+      const int c0 = bx * (WROWS / 2) + wave * (8 * RT) + (rt % (RT / 2)) * 16;
       ok = c0 < a.ffn;
       r0 = (rt < RT / 2) ? c0 : a.ffn + c0;
     } else {
@@ -351,7 +351,7 @@ void stream_kernel(StreamArgs a) {
           const float4 q = red[w * NT * 16 + tid];
           smerge(m, s, t, am, q.x, q.y, q.z, __float_as_int(q.w));
         }
-        a.part[(long long)(t0 + tid) * a.n_tiles + blockIdx.x] =
+        a.part[(long long)(t0 + tid) * a.n_tiles + bx] =
             make_float4(m, s, t, __int_as_float(am));
       }
     } else {
@@ -360,7 +360,7 @@ void stream_kernel(StreamArgs a) {
         const int tok = t0 + nt * 16 + l16;
         if (nt >= nt_act || tok >= t_end) continue;
         if (EPI == EPI_SWIGLU) {
-          const int c0 = blockIdx.x * (WROWS / 2) + wave * (8 * RT);
+          const int c0 = bx * (WROWS / 2) + wave * (8 * RT);
 #pragma unroll
           for (int h = 0; h < RT / 2; ++h) {
             const int ch = c0 + h * 16 + 4 * lg;
