@@ -72,6 +72,29 @@ struct ProfScope {
 };
 }  // namespace
 
+// Workspace of the MoE pipeline (carved by moe_layout).
+struct MoeBufs {
+  float* rlogits;
+  int32_t* ridx;
+  float* rw;
+  int32_t* chunk_counts;
+  int32_t* local_rank;
+  int32_t* chunk_base;
+  int32_t* offsets;
+  int32_t* tile_offsets;
+  int32_t* perm;
+  uint16_t* act;
+  float* y;
+  // weight-streaming path: fixed-capacity expert slots filled by top-k
+  int cap;              // slots per expert (0: the path is never taken)
+  int32_t* counts;      // [E] tokens per expert (zeroed before the top-k)
+  int32_t* slot_pair;   // [E*cap] pair index t*k + r of each slot
+  float* slot_w;        // [E*cap] gate weight of each slot
+  int32_t* slot_tok;    // [E*cap + kSlotPad] token of each slot
+};
+// slot_tok is read up to one pass of 32 slots past an expert's last slot
+constexpr int kSlotPad = 64;
+
 struct dg_ctx {
   dg_model_desc d;
   const uint16_t* embed;
@@ -93,17 +116,7 @@ struct dg_ctx {
   uint16_t* attn;
   float* opart;
   float* lpart;
-  float* rlogits;
-  int32_t* ridx;
-  float* rw;
-  int32_t* chunk_counts;
-  int32_t* local_rank;
-  int32_t* chunk_base;
-  int32_t* offsets;
-  int32_t* tile_offsets;
-  int32_t* perm;
-  uint16_t* act;
-  float* y;
+  MoeBufs moe;
   int32_t* row_map;
   int32_t* pos_map;
   int32_t* m_dev;
@@ -158,19 +171,6 @@ long long attn_split_rows(const dg_model_desc& d, int max_canvases) {
   return best;
 }
 
-struct MoeBufs {
-  float* rlogits;
-  int32_t* ridx;
-  float* rw;
-  int32_t* chunk_counts;
-  int32_t* local_rank;
-  int32_t* chunk_base;
-  int32_t* offsets;
-  int32_t* tile_offsets;
-  int32_t* perm;
-  uint16_t* act;
-  float* y;
-};
 
 // Router logits are computed in up to kRouterSlabs K splits, each writing
 // its own fp32 slab [T, E]; the top-k kernel adds them in order.
@@ -182,11 +182,25 @@ int router_splits(int K) {
   return s;
 }
 
+// Weight-streaming kernels when the expert matrices see few rows each (a
+// batch of a few canvases): on average at most 32 (token, expert) pairs per
+// expert, and K dimensions that are multiples of the streaming K chunk.
+bool use_stream_moe(const dg_model_desc& d, int T) {
+  const long long pairs = (long long)T * d.top_k;
+  return pairs <= 32LL * d.n_experts && stream_moe_ok(d.hidden, d.expert_ffn);
+}
+
 // Workspace of the MoE pipeline for T tokens.
 size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   Carve cv;
   const long long pairs = (long long)T * d.top_k;
   const int nc = permute_chunks((int)pairs);
+  // slots per expert for the streaming path: every T it is taken for
+  // (a token picks an expert at most once, so T slots always suffice)
+  const int cap = stream_moe_ok(d.hidden, d.expert_ffn)
+                      ? (int)std::min<long long>(T, 32LL * d.n_experts / d.top_k)
+                      : 0;
+  const long long slots = (long long)d.n_experts * cap;
   const size_t o_rl = cv.take((size_t)kRouterSlabs * T * d.n_experts * 4);
   const size_t o_ri = cv.take((size_t)pairs * 4);
   const size_t o_rw = cv.take((size_t)pairs * 4);
@@ -196,8 +210,12 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   const size_t o_of = cv.take((size_t)(d.n_experts + 1) * 4);
   const size_t o_to = cv.take((size_t)(d.n_experts + 1) * 4);
   const size_t o_pm = cv.take((size_t)pairs * 4);
-  const size_t o_ac = cv.take((size_t)pairs * d.expert_ffn * 2);
+  const size_t o_ac = cv.take((size_t)std::max(pairs, slots) * d.expert_ffn * 2);
   const size_t o_y = cv.take((size_t)pairs * d.hidden * 4);
+  const size_t o_cn = cv.take((size_t)d.n_experts * 4);
+  const size_t o_sp = cv.take((size_t)slots * 4);
+  const size_t o_sw = cv.take((size_t)slots * 4);
+  const size_t o_st = cv.take((size_t)(slots + kSlotPad) * 4);
   if (b) {
     b->rlogits = (float*)(base + o_rl);
     b->ridx = (int32_t*)(base + o_ri);
@@ -210,6 +228,11 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
     b->perm = (int32_t*)(base + o_pm);
     b->act = (uint16_t*)(base + o_ac);
     b->y = (float*)(base + o_y);
+    b->cap = cap;
+    b->counts = (int32_t*)(base + o_cn);
+    b->slot_pair = (int32_t*)(base + o_sp);
+    b->slot_w = (float*)(base + o_sw);
+    b->slot_tok = (int32_t*)(base + o_st);
   }
   return cv.off;
 }
@@ -242,19 +265,7 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->pos_map = (int32_t*)(w + o_pm);
     c->m_dev = (int32_t*)(w + o_md);
     c->lm_part = (float4*)(w + o_lm);
-    MoeBufs mb;
-    moe_layout(d, (int)T, w + o_moe, &mb);
-    c->rlogits = mb.rlogits;
-    c->ridx = mb.ridx;
-    c->rw = mb.rw;
-    c->chunk_counts = mb.chunk_counts;
-    c->local_rank = mb.local_rank;
-    c->chunk_base = mb.chunk_base;
-    c->offsets = mb.offsets;
-    c->tile_offsets = mb.tile_offsets;
-    c->perm = mb.perm;
-    c->act = mb.act;
-    c->y = mb.y;
+    moe_layout(d, (int)T, w + o_moe, &c->moe);
   }
   return cv.off;
 }
@@ -308,13 +319,6 @@ GemmArgs gemm_dense(const uint16_t* A, int M, int K, const void* W, int N,
 
 int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi); }
 
-// Weight-streaming kernels when the expert matrices see few rows each (a
-// batch of a few canvases): on average at most 32 (token, expert) pairs per
-// expert, and K dimensions that are multiples of the streaming K chunk.
-bool use_stream_moe(const dg_model_desc& d, int T) {
-  const long long pairs = (long long)T * d.top_k;
-  return pairs <= 32LL * d.n_experts && stream_moe_ok(d.hidden, d.expert_ffn);
-}
 
 // The LM head streams the tied embedding once per 128 rows; beyond 256 rows
 // the tiled kernel reuses it better.
@@ -359,12 +363,14 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
 // into moe_out (if moe_out).
 // With next_g, the un-permute also applies the next RMSNorm (gain next_g)
 // into next_xh (rows mapped by next_row, see launch_unpermute_norm).
+// counts_zeroed: b.counts was cleared by an earlier kernel on the stream
+// (the FFN RMSNorm of the layer); otherwise it is cleared here.
 hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
                    const uint16_t* xh, int T, const MoeBufs& b, float* x,
                    float* moe_out, int32_t* counts, hipStream_t s,
                    Profiler* prof = nullptr, const float* next_g = nullptr,
                    uint16_t* next_xh = nullptr, float* next_copy = nullptr,
-                   const int32_t* next_row = nullptr) {
+                   const int32_t* next_row = nullptr, bool counts_zeroed = false) {
   const int H = d.hidden, E = d.n_experts, k = d.top_k, F = d.expert_ffn;
   const bool w8 = d.expert_dtype == DG_FP8_E4M3;
   const int pairs = T * k;
@@ -376,31 +382,36 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     ProfScope ps(prof, 5);
     if ((e = launch_gemm(EPI_STORE_F32, false, r, grid_m_dense(T, EPI_STORE_F32), s)) != hipSuccess) return e;
   }
-  {
-    ProfScope ps(prof, 6);
-    if ((e = launch_topk(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, s)) != hipSuccess) return e;
-  }
-  {
-    ProfScope ps(prof, 7);
-    if ((e = launch_permute(b.ridx, pairs, E, kGroupBM, b.chunk_counts,
-                            b.local_rank, b.chunk_base, b.offsets,
-                            b.tile_offsets, counts, b.perm, s)) != hipSuccess)
-      return e;
-  }
   if (use_stream_moe(d, T)) {
+    // Weight-streaming path: top-k hands every (token, rank) pair a slot of
+    // its expert (fixed rows e*cap + i), so a GEMM workgroup finds its
+    // tokens with one lookup and no prefix sum.
+    if (T > b.cap) return hipErrorInvalidValue;
+    if (!counts_zeroed && (e = launch_zero_i32(b.counts, E, s)) != hipSuccess) return e;
+    {
+      ProfScope ps(prof, 6);
+      if ((e = launch_topk_slots(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, b.counts,
+                                 b.cap, b.slot_pair, b.slot_w, b.slot_tok, s)) != hipSuccess)
+        return e;
+    }
+    if (counts &&
+        (e = hipMemcpyAsync(counts, b.counts, (size_t)E * 4, hipMemcpyDeviceToDevice, s)) !=
+            hipSuccess)
+      return e;
     StreamArgs gu;
     memset(&gu, 0, sizeof(gu));
     gu.X = xh;
     gu.ldx = H;
-    gu.x_map = b.perm;
-    gu.x_map_div = k;
+    gu.M = T;
+    gu.row_of = b.slot_tok;
     gu.W = w.w_gate_up;
     gu.w_group_stride = (long long)2 * F * H;
     gu.w_scale = w.gate_up_scale;
     gu.scale_rows = 2 * F;
     gu.N = 2 * F;
     gu.K = H;
-    gu.group_offsets = b.offsets;
+    gu.group_count = b.counts;
+    gu.cap = b.cap;
     gu.C = b.act;
     gu.ldc = F;
     gu.ffn = F;
@@ -418,11 +429,12 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     dn.scale_rows = H;
     dn.N = H;
     dn.K = F;
-    dn.group_offsets = b.offsets;
+    dn.group_count = b.counts;
+    dn.cap = b.cap;
     dn.C = b.y;
     dn.ldc = H;
-    dn.c_map = b.perm;
-    dn.row_scale = b.rw;
+    dn.c_map = b.slot_pair;
+    dn.row_scale = b.slot_w;
     {
       ProfScope ps(prof, 9);
       if ((e = launch_stream(EPI_DOWN, w8, dn, E, s)) != hipSuccess) return e;
@@ -432,6 +444,17 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
       return launch_unpermute_norm(b.y, T, k, H, x, moe_out, next_g, d.rms_eps,
                                    next_xh, next_copy, next_row, s);
     return launch_unpermute(b.y, T, k, H, x, moe_out, s);
+  }
+  {
+    ProfScope ps(prof, 6);
+    if ((e = launch_topk(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, s)) != hipSuccess) return e;
+  }
+  {
+    ProfScope ps(prof, 7);
+    if ((e = launch_permute(b.ridx, pairs, E, kGroupBM, b.chunk_counts,
+                            b.local_rank, b.chunk_base, b.offsets,
+                            b.tile_offsets, counts, b.perm, s)) != hipSuccess)
+      return e;
   }
   const int grid_m = (pairs + kGroupBM - 1) / kGroupBM + std::min(E, pairs);
   GemmArgs gu = gemm_dense(xh, pairs, H, w.w_gate_up, 2 * F, b.act, F);
@@ -468,21 +491,7 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   return launch_unpermute(b.y, T, k, H, x, moe_out, s);
 }
 
-MoeBufs ctx_moe_bufs(dg_ctx* c) {
-  MoeBufs b;
-  b.rlogits = c->rlogits;
-  b.ridx = c->ridx;
-  b.rw = c->rw;
-  b.chunk_counts = c->chunk_counts;
-  b.local_rank = c->local_rank;
-  b.chunk_base = c->chunk_base;
-  b.offsets = c->offsets;
-  b.tile_offsets = c->tile_offsets;
-  b.perm = c->perm;
-  b.act = c->act;
-  b.y = c->y;
-  return b;
-}
+const MoeBufs& ctx_moe_bufs(const dg_ctx* c) { return c->moe; }
 
 dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt, bool distinct) {
   if (!bt) return fail(c, DG_ERR_INVALID_ARG, "batch is NULL");
@@ -561,25 +570,26 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
                              hipMemcpyDeviceToDevice, s));
   GemmArgs o = gemm_dense(c->attn, T, Hq * D, w.w_o, H, c->x, H);
   KRUN(c, 4, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
+  const MoeBufs& mb = ctx_moe_bufs(c);
   KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
-                           nullptr, nullptr, s));
+                           nullptr, nullptr, s, mb.counts, d.n_experts));
   float* moe_out = (cap && cap->moe_out) ? cap->moe_out + (size_t)l * T * H : nullptr;
   const bool last = l == d.n_layers - 1;
   const float* next_g = last ? c->final_norm : c->layers[l + 1].attn_norm;
   float* next_copy = (last && cap && cap->final_xhat) ? cap->final_xhat : nullptr;
-  HIPCHK(c, run_moe(d, w, c->xh, T, ctx_moe_bufs(c), c->x, moe_out, nullptr, s,
-                    &c->prof, next_g, c->xh, next_copy, last ? c->pos_map : nullptr));
+  HIPCHK(c, run_moe(d, w, c->xh, T, mb, c->x, moe_out, nullptr, s, &c->prof, next_g,
+                    c->xh, next_copy, last ? c->pos_map : nullptr, true));
   if (cap) {
     const size_t tk = (size_t)T * d.top_k;
     if (cap->route_idx)
-      HIPCHK(c, hipMemcpyAsync(cap->route_idx + l * tk, c->ridx, tk * 4,
+      HIPCHK(c, hipMemcpyAsync(cap->route_idx + l * tk, mb.ridx, tk * 4,
                                hipMemcpyDeviceToDevice, s));
     if (cap->route_w)
-      HIPCHK(c, hipMemcpyAsync(cap->route_w + l * tk, c->rw, tk * 4,
+      HIPCHK(c, hipMemcpyAsync(cap->route_w + l * tk, mb.rw, tk * 4,
                                hipMemcpyDeviceToDevice, s));
     if (cap->router_logits)
       HIPCHK(c, hipMemcpyAsync(cap->router_logits + (size_t)l * T * d.n_experts,
-                               c->rlogits, (size_t)T * d.n_experts * 4,
+                               mb.rlogits, (size_t)T * d.n_experts * 4,
                                hipMemcpyDeviceToDevice, s));
   }
   return DG_OK;
@@ -788,9 +798,9 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     plen[b] = c->kv_len[req[b]];
   }
   hipStream_t s = c->stream;
-  KRUN(c, 11, launch_compact(bt->committed, T, c->row_map, c->m_dev, c->pos_map, s));
   KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, d.vocab, H, c->x,
-                               c->layers[0].attn_norm, d.rms_eps, c->xh, s));
+                               c->layers[0].attn_norm, d.rms_eps, c->xh, s, bt->committed,
+                               c->row_map, c->m_dev, c->pos_map));
   for (int l = 0; l < d.n_layers; ++l) {
     st = run_layer(c, l, n, req, plen, false, out->capture);
     if (st != DG_OK) return st;

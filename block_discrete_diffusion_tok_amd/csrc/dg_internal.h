@@ -34,19 +34,21 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
-// OCP E4M3 byte -> bf16 bits (exact: 3 mantissa bits and exponents 2^-9..2^8
-// all fit in bfloat16).  Exponent field 0 is subnormal m * 2^-9; the code
-// S.1111.111 is NaN.
-__device__ __forceinline__ uint16_t e4m3_to_bf(uint32_t c) {
-  uint32_t s = (c & 0x80u) << 8;
-  uint32_t e = (c >> 3) & 0xFu;
-  uint32_t m = c & 0x7u;
-  if (e == 0xFu && m == 0x7u) return (uint16_t)(s | 0x7fc0u);
-  if (e != 0) return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
-  if (m == 0) return (uint16_t)s;
-  // subnormal: m * 2^-9 with m in 1..7 -> normalise
-  float v = (float)m * 0.001953125f;  // 2^-9
-  return (uint16_t)(s | (__float_as_uint(v) >> 16));
+// 16 OCP E4M3 bytes -> 16 bf16 (exact: 3 mantissa bits and exponents
+// 2^-9..2^8 all fit in bfloat16), by gfx950's packed conversion with unit
+// scale: each instruction widens the two bytes of one half-word, byte 0 of
+// the pair into the low half of the result.  lo takes bytes 0..7, hi 8..15.
+__device__ __forceinline__ void widen_e4m3x16(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, false));
+    o[2 * i + 1] = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[i], 1.0f, true));
+  }
+  lo = u32x4_t{o[0], o[1], o[2], o[3]};
+  hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
 // One bf16 MFMA: D(16x16) += A(16x32) * B(32x16).  Lane l supplies row
@@ -161,19 +163,24 @@ int gemm_bm(int epi);   // BM of the instance used for an epilogue
 struct StreamArgs {
   const uint16_t* X;       // bf16 token rows [rows, K]
   int ldx;
-  const int32_t* x_map;    // optional: X row = x_map[row] / x_map_div
-  int x_map_div;
-  const void* W;           // weights [N, K] per group (bf16 or e4m3)
+  const void* W;           // weights [N, K] per group (bf16 or e4m3), packed
   long long w_group_stride;  // elements between groups
   const float* w_scale;    // e4m3 per-row scales [groups][scale_rows]
   int scale_rows;
   int M;                   // token rows (dense)
   const int32_t* M_dev;    // optional device token count (dense)
   int N, K;                // K as stream_lm_ok / stream_moe_ok require
-  const int32_t* group_offsets;  // grouped: [G+1] token-row offsets
+  // Grouped (expert) mode when group_count != null: group g owns the
+  // fixed-capacity slots [g*cap, g*cap + group_count[g]).  EPI_SWIGLU reads
+  // slot s's token from X row row_of[s] (clamped to [0, M); row_of readable
+  // up to g*cap + cap + 32) and writes C row s; EPI_DOWN reads X row s and
+  // c_map / row_scale at s.
+  const int32_t* group_count;
+  int cap;
+  const int32_t* row_of;
   void* C;
   int ldc;
-  const int32_t* c_map;    // EPI_DOWN: pair index of each token row
+  const int32_t* c_map;    // EPI_DOWN: pair index of each slot row
   const float* row_scale;  // EPI_DOWN: gate weight per pair
   int ffn;                 // EPI_SWIGLU: F
   float4* part;            // EPI_LMSTATS: [rows][n_tiles]
@@ -214,25 +221,42 @@ int attention_auto_splits(int n, int C, int Hq, int Hkv, int max_keys);
 hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
                         int V, int H, float* x, hipStream_t s);
 // row_map (optional) must hold `rows` readable entries; rows r >= *m_dev
-// (when given) are skipped.
+// (when given) are skipped.  zero (optional): n_zero ints the first
+// workgroup clears (the expert counters of the following top-k).
 hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
                           float eps, uint16_t* out, const int32_t* row_map,
                           const int32_t* m_dev, float* copy_f32,
-                          hipStream_t s);
+                          hipStream_t s, int32_t* zero = nullptr, int n_zero = 0);
 // logits: `splits` fp32 slabs [T, E] (partial sums over K) added in slab
 // order; with splits > 1 the sum is also written back to slab 0.
 hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
                        float* w, hipStream_t s);
+// Top-k that also hands each (token, rank) pair a slot of its expert
+// (slot = atomicAdd(&counts[e], 1), counts zeroed beforehand; order within
+// an expert is arbitrary, cap >= T), records pair = t*k + r in
+// slot_pair[e*cap + slot], its gate weight in slot_w[e*cap + slot] and the
+// token t in slot_tok[e*cap + slot].
+hipError_t launch_topk_slots(float* logits, int T, int E, int k, int splits,
+                             int32_t* idx, float* w, int32_t* counts, int cap,
+                             int32_t* slot_pair, float* slot_w, int32_t* slot_tok,
+                             hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* chunk_counts, int32_t* local_rank,
                           int32_t* chunk_base, int32_t* offsets,
                           int32_t* tile_offsets, int32_t* counts,
                           int32_t* perm, hipStream_t s);
 int permute_chunks(int n_pairs);
-// x = E[tok] fused with the first RMSNorm (packed table).
+// x = E[tok] fused with the first RMSNorm (packed table).  With committed
+// given, one more workgroup meanwhile writes row_map[0..M) = the rows t with
+// committed[t] == 0 in increasing order, *m_dev = M and pos_map[t] (if
+// given) = t's index in row_map or -1.
 hipError_t launch_embed_norm(const int32_t* tokens, int T, const uint16_t* embed,
                              int V, int H, float* x, const float* g, float eps,
-                             uint16_t* xh, hipStream_t s);
+                             uint16_t* xh, hipStream_t s,
+                             const uint8_t* committed = nullptr,
+                             int32_t* row_map = nullptr, int32_t* m_dev = nullptr,
+                             int32_t* pos_map = nullptr);
 // x += un-permuted expert rows, fused with the next RMSNorm into xh.
 hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
                                  float* moe_out, const float* g, float eps,
@@ -240,8 +264,6 @@ hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
                                  const int32_t* out_row, hipStream_t s);
 hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
                             float* moe_out, hipStream_t s);
-hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
-                          int32_t* m_dev, int32_t* pos_map, hipStream_t s);
 hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* m_dev, int m_max,
                            const int32_t* row_map, float* entropy, float* lse,

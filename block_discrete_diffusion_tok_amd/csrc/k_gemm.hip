@@ -54,19 +54,6 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float& t,
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
-// 16 e4m3 bytes -> 16 bf16 (exact).
-__device__ __forceinline__ void widen16(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = q[i];
-    o[2 * i] = (uint32_t)e4m3_to_bf(w & 0xff) | ((uint32_t)e4m3_to_bf((w >> 8) & 0xff) << 16);
-    o[2 * i + 1] = (uint32_t)e4m3_to_bf((w >> 16) & 0xff) | ((uint32_t)e4m3_to_bf(w >> 24) << 16);
-  }
-  lo = u32x4_t{o[0], o[1], o[2], o[3]};
-  hi = u32x4_t{o[4], o[5], o[6], o[7]};
-}
-
 __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -95,7 +82,7 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
     const int c = tid + 256 * j, blk = c >> 6, ln = c & 63;                   \
     if (W8) {                                                                 \
       u32x4_t lo, hi;                                                         \
-      widen16(wr[p][j], lo, hi);                                              \
+      widen_e4m3x16(wr[p][j], lo, hi);                                              \
       const int o = (blk * 16 + (ln & 15)) * LDK + (ln >> 4) * 16;            \
       *(u32x4_t*)&Ws[b][o] = lo;                                              \
       *(u32x4_t*)&Ws[b][o + 8] = hi;                                          \

@@ -123,11 +123,14 @@ __device__ __forceinline__ void norm_row(float4 (&v)[U], const float4 (&g0)[U],
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(
     const float* x, int rows, int H, const float* g, float eps, uint16_t* out,
-    const int32_t* row_map, const int32_t* m_dev, float* copy_f32) {
+    const int32_t* row_map, const int32_t* m_dev, float* copy_f32,
+    int32_t* zero, int n_zero) {
   constexpr int U = 4;
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
+  if (r == 0)
+    for (int i = tid; i < n_zero; i += 256) zero[i] = 0;
   const int n = m_dev ? *m_dev : rows;
   const int src = row_map ? row_map[r] : r;
   float4 gg[U];
@@ -175,9 +178,12 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+template <bool SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
                                                    int k, int splits, int32_t* idx,
-                                                   float* w) {
+                                                   float* w, int32_t* counts, int cap,
+                                                   int32_t* slot_pair, float* slot_w,
+                                                   int32_t* slot_tok) {
   constexpr int PER = kTopkMaxE / kWave;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -242,9 +248,16 @@ __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
       my_sel = sel[r];
       my_id = sid[r];
     }
+  const float my_w = __expf(my_sel - mx) / sum;
   if (lane < k) {
     idx[(long long)t * k + lane] = my_id;
-    w[(long long)t * k + lane] = __expf(my_sel - mx) / sum;
+    w[(long long)t * k + lane] = my_w;
+  }
+  if (SLOTS && lane < k) {  // lane r < k takes a slot of expert sid[r]
+    const long long sl = (long long)my_id * cap + atomicAdd(&counts[my_id], 1);
+    slot_pair[sl] = t * k + lane;
+    slot_w[sl] = my_w;
+    slot_tok[sl] = t;
   }
 }
 
@@ -421,15 +434,23 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const float* y, int k,
 // * g); copy_f32 optionally receives the bf16 values widened.
 
 // Embedding gather (packed table, ids clamped) fused with the first layer's
-// attention RMSNorm: x[t] = E[tok[t]] (fp32), xh[t] = RMSNorm(x[t]; g).
-__global__ __launch_bounds__(256) void embed_norm_kernel(const int32_t* tok,
-                                                         const uint16_t* E, int V,
-                                                         int H, float* x,
-                                                         const float* g, float eps,
-                                                         uint16_t* xh) {
+// attention RMSNorm: x[t] = E[tok[t]] (fp32), xh[t] = RMSNorm(x[t]; g), one
+// workgroup per row t < T.  With committed given, workgroup T compacts the
+// uncommitted rows (compact_rows) meanwhile.
+template <int NTH>
+__device__ void compact_rows(const uint8_t* committed, int T, int32_t* row_map,
+                             int32_t* m_dev, int32_t* pos_map);
+__global__ __launch_bounds__(256) void embed_norm_kernel(
+    const int32_t* tok, int T, const uint16_t* E, int V, int H, float* x, const float* g,
+    float eps, uint16_t* xh, const uint8_t* committed, int32_t* row_map, int32_t* m_dev,
+    int32_t* pos_map) {
   constexpr int U = 4;
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
+  if (t >= T) {
+    compact_rows<256>(committed, T, row_map, m_dev, pos_map);
+    return;
+  }
   const int id = min(max(tok[t], 0), V - 1);
   float4 gg[U];
   load_gains<U>(gg, g, H);
@@ -512,25 +533,29 @@ __global__ __launch_bounds__(256) void unpermute_norm_kernel(
 }
 
 // ---------------------------------------------------------------- compaction
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 // row_map[0..M) = indices t with committed[t] == 0 in increasing order;
-// *m_dev = M; pos_map[t] (if given) = t's index in row_map, or -1.  One
-// workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
-                                                       int T, int32_t* row_map,
-                                                       int32_t* m_dev,
-                                                       int32_t* pos_map) {
-  // chunks of 1024 positions, 8 chunks' flags read at once; in-wave ranks
-  // from ballots, wave offsets from the 16 wave counts
-  constexpr int G = 8;
-  __shared__ int wcount[G][16];
+// *m_dev = M; pos_map[t] (if given) = t's index in row_map, or -1.  Run by
+// one workgroup of NTH threads: chunks of NTH positions, 8 chunks' flags
+// read at once; in-wave ranks from ballots, wave offsets from the wave
+// counts.
+template <int NTH>
+__device__ void compact_rows(const uint8_t* committed, int T, int32_t* row_map,
+                             int32_t* m_dev, int32_t* pos_map) {
+  constexpr int G = 8, NW = NTH / 64;
+  __shared__ int wcount[G][NW];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const unsigned long long below = (1ull << lane) - 1;
   int run = 0;
-  for (int base = 0; base < T; base += 1024 * G) {
+  for (int base = 0; base < T; base += NTH * G) {
     bool f[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const int t = base + 1024 * i + tid;
+      const int t = base + NTH * i + tid;
       const uint8_t c = committed[t < T ? t : T - 1];
       f[i] = t < T && c == 0;
     }
@@ -546,12 +571,12 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* committed,
     for (int i = 0; i < G; ++i) {
       int off = run, total = 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < NW; ++q) {
         const int c = wcount[i][q];
         off += q < wv ? c : 0;
         total += c;
       }
-      const int t = base + 1024 * i + tid;
+      const int t = base + NTH * i + tid;
       const int r = off + before[i];
       if (f[i]) row_map[r] = t;
       if (pos_map && t < T) pos_map[t] = f[i] ? r : -1;
@@ -769,10 +794,17 @@ hipError_t launch_embed(const int32_t* tokens, int T, const uint16_t* embed,
 hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
                           float eps, uint16_t* out, const int32_t* row_map,
                           const int32_t* m_dev, float* copy_f32,
-                          hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
+                          hipStream_t s, int32_t* zero, int n_zero) {
+  if (rows <= 0) return launch_zero_i32(zero, zero ? n_zero : 0, s);
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, x,
-                     rows, H, g, eps, out, row_map, m_dev, copy_f32);
+                     rows, H, g, eps, out, row_map, m_dev, copy_f32, zero,
+                     zero ? n_zero : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 
@@ -780,8 +812,19 @@ hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* 
                        float* w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (E > kTopkMaxE || k > kTopkMaxK || k > E) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
-                     T, E, k, splits, idx, w);
+  hipLaunchKernelGGL(topk_kernel<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits,
+                     T, E, k, splits, idx, w, nullptr, 0, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_slots(float* logits, int T, int E, int k, int splits,
+                             int32_t* idx, float* w, int32_t* counts, int cap,
+                             int32_t* slot_pair, float* slot_w, int32_t* slot_tok,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (E > kTopkMaxE || k > kTopkMaxK || k > E || cap < T) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_kernel<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits,
+                     T, E, k, splits, idx, w, counts, cap, slot_pair, slot_w, slot_tok);
   return hipGetLastError();
 }
 
@@ -813,10 +856,13 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
 
 hipError_t launch_embed_norm(const int32_t* tokens, int T, const uint16_t* embed,
                              int V, int H, float* x, const float* g, float eps,
-                             uint16_t* xh, hipStream_t s) {
+                             uint16_t* xh, hipStream_t s, const uint8_t* committed,
+                             int32_t* row_map, int32_t* m_dev, int32_t* pos_map) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(embed_norm_kernel, dim3(T), dim3(256), 0, s, tokens, embed,
-                     V, H, x, g, eps, xh);
+  if (committed && (!row_map || !m_dev)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_norm_kernel, dim3(T + (committed ? 1 : 0)), dim3(256), 0, s,
+                     tokens, T, embed, V, H, x, g, eps, xh, committed, row_map, m_dev,
+                     pos_map);
   return hipGetLastError();
 }
 
@@ -842,12 +888,6 @@ hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const uint8_t* committed, int T, int32_t* row_map,
-                          int32_t* m_dev, int32_t* pos_map, hipStream_t s) {
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, committed, T,
-                     row_map, m_dev, pos_map);
-  return hipGetLastError();
-}
 
 hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* m_dev, int m_max,

@@ -14,13 +14,14 @@
 //     contiguous kilobyte of full cache lines: with a row-major layout each
 //     instruction would touch 16 lines and use half of each, and the L1's
 //     outstanding-miss capacity, not HBM, would bound the stream;
-//   * the group's token rows (gathered through the expert permutation when
-//     needed) go HBM/L2 -> LDS directly (LDS-DMA loads, no registers) into
-//     a ring of D+1 chunk stages shared by the 4 waves.  Each chunk's token
-//     DMA and weight loads are issued together D chunks ahead, so the wait
-//     for a chunk covers exactly the loads issued D chunks earlier (the
-//     load counter completes in issue order: a token load issued after
-//     younger weight loads would force those to land first);
+//   * the group's token rows (an expert's fixed-capacity slots, whose token
+//     ids the top-k kernel wrote, or the rows of a dense operand) go
+//     HBM/L2 -> LDS directly (LDS-DMA loads, no registers) into a ring of
+//     D+1 chunk stages shared by the 4 waves.  Each chunk's weight loads
+//     and token DMA are issued together D chunks ahead, so the wait for a
+//     chunk covers exactly the loads issued D chunks earlier (the load
+//     counter completes in issue order: a token load issued after younger
+//     weight loads would force those to land first);
 //   * MFMA 16x16x32 bf16 with the weights as the A operand, so a lane's
 //     accumulators hold one token column and 4 consecutive weight rows: the
 //     epilogues (SwiGLU of paired gate/up rows, gate-weight scaling with the
@@ -83,6 +84,12 @@ __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
 #ifndef DG_LDS_PTR
 #define DG_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 #endif
+// A pointer to memory no thread writes during the kernel, in the constant
+// address space: uniform loads through it are scalar loads.
+#ifndef DG_CONST_PTR
+#define DG_CONST_PTR(T, p) ((const __attribute__((address_space(4))) T*)(p))
+#endif
+
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, DG_LDS_PTR(lds_wave_base), 16, 0, 0);
 }
@@ -91,18 +98,6 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 // of this wave are outstanding (other counters untouched).
 constexpr int vm_wait(int n) {
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
-__device__ __forceinline__ void widen_e4m3(const u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = q[i];
-    o[2 * i] = (uint32_t)e4m3_to_bf(w & 0xff) | ((uint32_t)e4m3_to_bf((w >> 8) & 0xff) << 16);
-    o[2 * i + 1] = (uint32_t)e4m3_to_bf((w >> 16) & 0xff) | ((uint32_t)e4m3_to_bf(w >> 24) << 16);
-  }
-  lo = u32x4_t{o[0], o[1], o[2], o[3]};
-  hi = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
 __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -125,7 +120,7 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
     for (int rt = 0; rt < RT; ++rt) {
       if (W8) {
         u32x4_t lo, hi;
-        widen_e4m3(w[rt][j >> 1], lo, hi);
+        widen_e4m3x16(w[rt][j >> 1], lo, hi);
         af[rt] = (j & 1) ? hi : lo;
       } else {
         af[rt] = w[rt][j];
@@ -145,15 +140,19 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
   }
 }
 
-template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void stream_kernel(StreamArgs a) {
-  // the gate/up products read their token rows through the expert
-  // permutation (row = x_map[r] / x_map_div), the others directly
-  constexpr bool MAPPED = EPI == EPI_SWIGLU;
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
+  static_assert(EPI == EPI_LMSTATS || EPI == EPI_SWIGLU || EPI == EPI_DOWN, "epilogue");
+  // the gate/up products read a slot's token row through row_of; the down
+  // products read the slot rows of the SwiGLU output directly
+  constexpr bool MAPPED = EPI == EPI_SWIGLU;
+  // the expert products run over groups (experts) of slots; the LM head
+  // over the rows of one dense operand
+  constexpr bool GROUPED = EPI != EPI_LMSTATS;
   static_assert(KC == 64 || KC == 128, "K chunk");
-  constexpr int WROWS = 4 * RT * 16;  // weight rows per workgroup
+  constexpr int WROWS = WV * RT * 16;  // weight rows per workgroup (WV waves)
   constexpr int ESZ = W8 ? 1 : 2;     // bytes per weight element
   // 16-byte weight loads per row tile per chunk (KC/4 k values per lane)
   constexpr int WREGS = (KC / 4) * ESZ / 16;
@@ -161,8 +160,8 @@ void stream_kernel(StreamArgs a) {
   constexpr int S = D + 1;                     // token stages
   constexpr int STAGE = NT * 16 * KC;          // elements per stage
   constexpr int UNITS = STAGE / 8;             // 16-byte units per stage
-  static_assert(UNITS % 256 == 0, "token units per thread");
-  constexpr int IPW = UNITS / 256;             // token DMAs per wave per chunk
+  static_assert(UNITS % (64 * WV) == 0, "token units per thread");
+  constexpr int IPW = UNITS / (64 * WV);       // token DMAs per wave per chunk
   constexpr int LOADS = IPW + RT * WREGS;      // loads per wave per chunk
   static_assert((D - 1) * LOADS <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint16_t Xs[S * STAGE];
@@ -170,18 +169,6 @@ void stream_kernel(StreamArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int group = blockIdx.y, bx = blockIdx.x;
-
-  // ---- token rows of this group
-  int t_begin, t_end;
-  if (a.group_offsets) {
-    t_begin = a.group_offsets[group];
-    t_end = a.group_offsets[group + 1];
-  } else {
-    t_begin = 0;
-    t_end = a.M;
-    if (a.M_dev) t_end = min(t_end, a.M_dev[0]);
-  }
-  if (t_end <= t_begin) return;
 
   // ---- this wave's weight row tiles (16 rows each) and the packed address
   // of this lane's piece of their first block; tiles past the matrix read
@@ -206,42 +193,108 @@ void stream_kernel(StreamArgs a) {
     wsrc[rt] = wgroup + pack_block_offset(ok ? r0 >> 4 : 0, 0, a.K, ESZ) + 16 * lane;
   }
   const int nk = a.K / KC;
+  // chunk k uses weight register set k % NSET and token stage k % S
+  constexpr int NSET = D + 1;  // register sets: chunk k+D loads while chunk k computes
 
-  for (int t0 = t_begin; t0 < t_end; t0 += NT * 16) {
-    const int nt_rows = min(NT * 16, t_end - t0);
-    const int nt_act = (nt_rows + 15) >> 4;
+  // ---- token rows: slots [group*cap, group*cap + count) of a group (the
+  // X row of a slot is row_of[slot] when given, else the slot itself), or
+  // rows [0, M) (M_dev when given) in dense mode.  A group's count is a
+  // uniform scalar load, counted apart from the vector loads, read after the
+  // first D chunks are issued: a group's passes read slots below cap (slots
+  // past the count hold stale but valid rows and ids whose results are
+  // dropped), so the down products issue their first chunks at once and the
+  // gate/up products wait only for the slots' token ids.  The dense operand
+  // repeats its last live row (one line per pass for few rows).
+  constexpr int TROWS = NT * 16;
+  const long long row0 = GROUPED ? (long long)group * a.cap : 0;
+  int t_end = 0;  // loaded once the first weight loads are out
 
-    // token unit u = 64*(wave*IPW + i) + lane of a stage holds row
-    // u / (KC/8), logical unit (u % (KC/8)) ^ (row & 7)
-    const uint16_t* xsrc[IPW];
-    const uint16_t* const xbase = a.X;
-    const int32_t* const xmap = a.x_map;
-    const int xdiv = a.x_map_div, ldx = a.ldx;
+  // EPI_DOWN: the pair index and gate weight of this lane's token columns,
+  // loaded before the pass's first chunk (older than every chunk load, so no
+  // chunk wait changes) and used by the epilogue
+  int pair_of[NT];
+  float wgt_of[NT];
+  auto load_ids = [&](int t0) {
+    if (EPI == EPI_DOWN) {
+      static_for<NT>([&](auto nt) {
+        const long long slot = row0 + min(t0 + nt * 16 + l16, a.cap - 1);
+        pair_of[nt] = a.c_map[slot];
+        wgt_of[nt] = a.row_scale[slot];
+      });
+    }
+  };
+  // token unit u = 64*(wave*IPW + i) + lane of a stage holds row
+  // u / (KC/8), logical unit (u % (KC/8)) ^ (row & 7)
+  auto unit_row = [&](int i) { return (64 * (wave * IPW + i) + lane) / (KC / 8); };
+  int tok_id[IPW];
+  auto load_tok_ids = [&](int t0) {
+    if (MAPPED)
+      static_for<IPW>([&](auto i) {
+        tok_id[i] = a.row_of[row0 + min(t0 + unit_row(i), a.cap - 1)];
+      });
+  };
+  const uint16_t* xsrc[IPW];
+  auto set_rows = [&](int t0) {
+    const int lim = GROUPED ? a.cap : max(t_end, 1);
     static_for<IPW>([&](auto i) {
       const int u = 64 * (wave * IPW + i) + lane;
       const int row = u / (KC / 8);
       const int c = (u % (KC / 8)) ^ (row & 7);
-      const int trow = t0 + (row < nt_rows ? row : 0);
-      const int src = MAPPED ? xmap[trow] / xdiv : trow;
-      xsrc[i] = xbase + (long long)src * ldx + c * 8;
+      const long long trow = MAPPED ? (long long)min((unsigned)tok_id[i], (unsigned)(a.M - 1))
+                                    : row0 + min(t0 + row, lim - 1);
+      xsrc[i] = a.X + trow * a.ldx + c * 8;
     });
-    // chunk k uses weight register set k % NSET and token stage k % S
-    constexpr int NSET = D + 1;  // register sets: chunk k+D loads while chunk k computes
-    u32x4_t w[NSET][RT][WREGS];
+  };
 
+  u32x4_t w[NSET][RT][WREGS];
+  // Loads of chunk k < nk: its token DMA into stage k % S, its weights into
+  // register set p = k % NSET (the chunk waits rely only on each chunk's
+  // loads being contiguous in issue order, chunks in order).
+  auto issue = [&](auto p, int k) {
+    uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
+    static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
+    load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, k);
+  };
+  auto prologue = [&]() {
+    static_for<D>([&](auto p) {
+      issue(p, (int)p);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  load_ids(0);
+  load_tok_ids(0);
+  if (!GROUPED) {
+    t_end = a.M;
+    if (a.M_dev) t_end = min(t_end, a.M_dev[0]);
+  }
+  set_rows(0);
+  prologue();
+  // the count is read-only here (an earlier kernel wrote it): a scalar load
+  // through the constant address space, so its wait is not a vector-memory
+  // wait for every chunk in flight
+  if (GROUPED) t_end = *DG_CONST_PTR(int32_t, a.group_count + group);
+  if (t_end <= 0) {  // an empty group: let the loads land before leaving
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    return;
+  }
+
+  for (int t0 = 0; t0 < t_end; t0 += TROWS) {
+    const int nt_rows = min(TROWS, t_end - t0);
+    const int nt_act = (nt_rows + 15) >> 4;
+    if (t0 > 0) {
+      load_ids(t0);
+      load_tok_ids(t0);
+      set_rows(t0);
+      __syncthreads();  // the previous pass is done with Xs
+      prologue();
+    }
     f32x4_t acc[RT][NT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // Loads of chunk k < nk: its token DMA into stage k % S, its weights
-    // into register set p = k % NSET.
-    auto issue = [&](auto p, int k) {
-      uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
-      static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
-      load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, k);
-    };
     // Chunk k, with `younger` chunks issued after it: wait for its loads
     // (the vector-memory counter completes in issue order), barrier (every
     // wave's token DMA has landed; every wave is past chunk k-1, whose
@@ -264,15 +317,10 @@ void stream_kernel(StreamArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    __syncthreads();  // the previous pass is done with Xs
-    static_for<D>([&](auto p) {
-      issue(p, (int)p);
-      __builtin_amdgcn_sched_barrier(0);
-    });
     // Groups of NSET chunks as straight-line code (register set k % NSET
     // is static) while every chunk of the group issues chunk k+D < nk; the
-    // state at each group boundary is the same (chunks kc..kc+D-1 in
-    // flight), so the fixed waits stay exact.  Then the last chunks: those
+    // state at each group boundary is the same (at most chunks kc..kc+D-1
+    // in flight), so the fixed waits stay exact.  Then the last chunks: those
     // with k+D < nk still issue, the last D drain with waits for exactly
     // the chunks still in flight (nk >= D is a launch precondition).
     int kc = 0;
@@ -291,8 +339,8 @@ void stream_kernel(StreamArgs a) {
     // ---- epilogues: lane holds token column t0 + 16*nt + l16 and weight
     // rows 4*lg + e of each row tile
     if (EPI == EPI_LMSTATS) {
-      float4* red = (float4*)&Xs[0];  // [4 waves][NT*16]
-      static_assert(4 * NT * 16 * 16 <= S * STAGE * 2, "LDS reuse");
+      float4* red = (float4*)&Xs[0];  // [WV waves][NT*16]
+      static_assert(WV * NT * 16 * 16 <= S * STAGE * 2, "LDS reuse");
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float m = -INFINITY, s = 0.f, t = 0.f;
@@ -347,7 +395,7 @@ void stream_kernel(StreamArgs a) {
         float m = p.x, s = p.y, t = p.z;
         int am = __float_as_int(p.w);
 #pragma unroll
-        for (int w = 1; w < 4; ++w) {
+        for (int w = 1; w < WV; ++w) {
           const float4 q = red[w * NT * 16 + tid];
           smerge(m, s, t, am, q.x, q.y, q.z, __float_as_int(q.w));
         }
@@ -376,7 +424,7 @@ void stream_kernel(StreamArgs a) {
                 u[e] *= sc[a.ffn + ch + e];
               }
             }
-            *(uint2*)((uint16_t*)a.C + (long long)tok * a.ldc + ch) =
+            *(uint2*)((uint16_t*)a.C + (row0 + tok) * a.ldc + ch) =
                 make_uint2(pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
                            pack_bf2(silu(g[2]) * u[2], silu(g[3]) * u[3]));
           }
@@ -387,8 +435,14 @@ void stream_kernel(StreamArgs a) {
             if (n >= a.N) continue;
             f32x4_t v = acc[rt][nt];
             if (EPI == EPI_DOWN) {
-              const int pair = a.c_map[tok];
-              const float wgt = a.row_scale[pair];
+              int pair = 0;
+              float wgt = 0.f;
+              static_for<NT>([&](auto q) {
+                if (q == nt) {
+                  pair = pair_of[q];
+                  wgt = wgt_of[q];
+                }
+              });
               float sc4[4] = {1.f, 1.f, 1.f, 1.f};
               if (W8) {
                 const float* sc = a.w_scale + (long long)group * a.scale_rows + n;
@@ -397,17 +451,6 @@ void stream_kernel(StreamArgs a) {
               *(float4*)((float*)a.C + (long long)pair * a.ldc + n) =
                   make_float4(v[0] * wgt * sc4[0], v[1] * wgt * sc4[1],
                               v[2] * wgt * sc4[2], v[3] * wgt * sc4[3]);
-            } else if (EPI == EPI_STORE_BF16) {
-              *(uint2*)((uint16_t*)a.C + (long long)tok * a.ldc + n) =
-                  make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-            } else if (EPI == EPI_STORE_F32) {
-              *(float4*)((float*)a.C + (long long)tok * a.ldc + n) =
-                  make_float4(v[0], v[1], v[2], v[3]);
-            } else if (EPI == EPI_ADD_F32) {
-              float4* cp = (float4*)((float*)a.C + (long long)tok * a.ldc + n);
-              float4 o = *cp;
-              o.x += v[0]; o.y += v[1]; o.z += v[2]; o.w += v[3];
-              *cp = o;
             }
           }
         }
@@ -416,16 +459,23 @@ void stream_kernel(StreamArgs a) {
   }
 }
 
-template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC>
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
 hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
-  constexpr int WROWS = 4 * RT * 16;
-  if ((a.x_map != nullptr) != (EPI == EPI_SWIGLU)) return hipErrorInvalidValue;
+  constexpr int WROWS = WV * RT * 16;
+  if ((EPI == EPI_SWIGLU || EPI == EPI_DOWN) != (a.group_count != nullptr) ||
+      (EPI == EPI_SWIGLU) != (a.row_of != nullptr))
+    return hipErrorInvalidValue;
+  // every load reads rows below a bound known here (cap slots of a group,
+  // M rows of a dense or mapped operand), so those bounds must hold rows
+  if (a.group_count && a.cap <= 0) return hipErrorInvalidValue;
+  if ((!a.group_count || EPI == EPI_SWIGLU) && a.M <= 0)
+    return a.group_count ? hipErrorInvalidValue : hipSuccess;
   int grid_x;
   if (EPI == EPI_SWIGLU) grid_x = (a.ffn + WROWS / 2 - 1) / (WROWS / 2);
   else grid_x = (a.N + WROWS - 1) / WROWS;
   if (grid_x <= 0 || groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, D, EPI, W8, OCC>), dim3(grid_x, groups),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((stream_kernel<RT, NT, KC, D, EPI, W8, OCC, WV>), dim3(grid_x, groups),
+                     dim3(64 * WV), 0, s, a);
   return hipGetLastError();
 }
 
@@ -436,10 +486,10 @@ hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
 // 16 KB, 4 weight register sets).  Experts: 2 row tiles, 32 token
 // columns, K chunks of 128, 3 in flight (4 stages of 8 KB, 4 weight
 // register sets).
-constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2;
-constexpr int kMoeRT = 2, kMoeKC = 128, kMoeD = 3, kMoeOcc = 2;
+constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2, kLmWaves = 4;
+constexpr int kMoeRT = 2, kMoeKC = 128, kMoeD = 3, kMoeOcc = 2, kMoeWaves = 4;
 
-int stream_rows_per_wg() { return 4 * kLmRT * 16; }
+int stream_rows_per_wg() { return kLmWaves * kLmRT * 16; }
 bool stream_lm_ok(int hidden) {
   return hidden % kLmKC == 0 && hidden / kLmKC >= kLmD;
 }
@@ -453,15 +503,15 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
   switch (epi) {
     case EPI_LMSTATS:
       if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
-      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc>(a, groups, s);
+      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_SWIGLU:
       if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true, kMoeOcc>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false, kMoeOcc>(a, groups, s);
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true, kMoeOcc, kMoeWaves>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false, kMoeOcc, kMoeWaves>(a, groups, s);
     case EPI_DOWN:
       if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true, kMoeOcc>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false, kMoeOcc>(a, groups, s);
+      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true, kMoeOcc, kMoeWaves>(a, groups, s)
+                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false, kMoeOcc, kMoeWaves>(a, groups, s);
   }
   return hipErrorInvalidValue;
 }

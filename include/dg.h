@@ -223,7 +223,9 @@ int32_t dg_kv_len(const dg_ctx* ctx, int32_t req); /* -1 on a bad slot */
  * kernel kind into ms[DG_PROF_KINDS] and launches[DG_PROF_KINDS] (host
  * arrays), clears the record and returns 0, 1 if events were dropped
  * because more than 2^20 were recorded between reads, or -1 on error.
- * Kind k is named by dg_profile_kind_name(k). */
+ * Kind k is named by dg_profile_kind_name(k).  The denoise step's row
+ * compaction runs inside its embedding launch (kind "embed"); kind
+ * "compact" counts no launches. */
 #define DG_PROF_KINDS 17
 dg_status dg_profile_enable(dg_ctx* ctx, int32_t on);
 int32_t dg_profile_read(dg_ctx* ctx, float* ms, int32_t* launches);
