@@ -140,9 +140,11 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
   }
 }
 
-template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
-__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void stream_kernel(StreamArgs a) {
+// The kernel body for NT token tiles per pass.  Xs: the LDS token stages
+// (at least (D+1) * NT*16 * KC elements).  dense_rows: the row count of a
+// dense operand (already read), unused for groups.
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int WV>
+__device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, int dense_rows) {
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
   static_assert(EPI == EPI_LMSTATS || EPI == EPI_SWIGLU || EPI == EPI_DOWN, "epilogue");
   // the gate/up products read a slot's token row through row_of; the down
@@ -164,7 +166,6 @@ void stream_kernel(StreamArgs a) {
   constexpr int IPW = UNITS / (64 * WV);       // token DMAs per wave per chunk
   constexpr int LOADS = IPW + RT * WREGS;      // loads per wave per chunk
   static_assert((D - 1) * LOADS <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[S * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -264,10 +265,7 @@ void stream_kernel(StreamArgs a) {
 
   load_ids(0);
   load_tok_ids(0);
-  if (!GROUPED) {
-    t_end = a.M;
-    if (a.M_dev) t_end = min(t_end, a.M_dev[0]);
-  }
+  if (!GROUPED) t_end = dense_rows;
   set_rows(0);
   prologue();
   // the count is read-only here (an earlier kernel wrote it): a scalar load
@@ -456,6 +454,31 @@ void stream_kernel(StreamArgs a) {
         }
       }
     }
+  }
+}
+
+// The LM head runs its rows in passes of 2, 4 or 8 token tiles, whichever
+// is the fewest that cover the live rows in one pass (the token DMA and the
+// MFMAs scale with the tiles, the weight stream does not).
+template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void stream_kernel(StreamArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[(D + 1) * NT * 16 * KC];
+  if constexpr (EPI == EPI_LMSTATS && NT == 8) {
+    int rows = a.M;
+    if (a.M_dev) rows = min(rows, a.M_dev[0]);
+    if (rows <= 32)
+      stream_run<RT, 2, KC, D, EPI, W8, WV>(a, Xs, rows);
+    else if (rows <= 64)
+      stream_run<RT, 4, KC, D, EPI, W8, WV>(a, Xs, rows);
+    else
+      stream_run<RT, 8, KC, D, EPI, W8, WV>(a, Xs, rows);
+  } else if constexpr (EPI == EPI_LMSTATS) {
+    int rows = a.M;
+    if (a.M_dev) rows = min(rows, a.M_dev[0]);
+    stream_run<RT, NT, KC, D, EPI, W8, WV>(a, Xs, rows);
+  } else {
+    stream_run<RT, NT, KC, D, EPI, W8, WV>(a, Xs, 0);
   }
 }
 

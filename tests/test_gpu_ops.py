@@ -325,6 +325,17 @@ def test_lmhead_full_vocab():
     _lm_case(128, 2048, 262144, "gemma")
 
 
+def test_lmhead_tile_counts():
+    # the streaming LM head runs 2, 4 or 8 token tiles per pass by row
+    # count: both sides of each boundary, and two passes of 8 tiles
+    for m in (32, 33, 64, 65, 200):
+        _lm_case(m, 256, 3000, f"tiles{m}")
+
+
+def test_lmhead_full_vocab_four_tiles():
+    _lm_case(48, 2048, 262144, "gemma48")
+
+
 def test_lmhead_full_vocab_tiled_path():
     # more than 256 rows: the tiled kernel, with a ragged last row tile
     _lm_case(300, 2048, 262144, "gemma_tiled")
