@@ -69,14 +69,20 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 // In the packed layout the q-th load of chunk kc is block kc * WREGS + q of
 // the row tile: one contiguous kilobyte per wave load, and the 4 tiles of a
 // tile group (2 waves) read one contiguous run per block column.
-template <int RT, int WREGS, int ESZ, int KC>
+// NTL: non-temporal loads (the weights are read once).  Measured per kernel:
+// the LM head streams faster with them; the expert kernels, whose token
+// rows are re-read through L2, do not (the down products slow down), so
+// they keep plain loads.
+template <int RT, int WREGS, int ESZ, int KC, bool NTL>
 __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
                                        const char* const (&src)[RT], int kc) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int q = 0; q < WREGS; ++q)
-      w[rt][q] = *(const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackKStride);
+    for (int q = 0; q < WREGS; ++q) {
+      const u32x4_t* p = (const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackKStride);
+      w[rt][q] = NTL ? __builtin_nontemporal_load(p) : *p;
+    }
 }
 
 // LDS-DMA of 16 bytes per lane: lane l's bytes land at lds_wave_base +
@@ -254,7 +260,7 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   auto issue = [&](auto p, int k) {
     uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
     static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
-    load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, k);
+    load_w<RT, WREGS, ESZ, KC, (EPI == EPI_LMSTATS)>(w[p], wsrc, k);
   };
   auto prologue = [&]() {
     static_for<D>([&](auto p) {
