@@ -172,8 +172,8 @@ struct StreamArgs {
   int N, K;                // K as stream_lm_ok / stream_moe_ok require
   // Grouped (expert) mode when group_count != null: group g owns the
   // fixed-capacity slots [g*cap, g*cap + group_count[g]).  EPI_SWIGLU reads
-  // slot s's token from X row row_of[s] (clamped to [0, M); row_of readable
-  // up to g*cap + cap + 32) and writes C row s; EPI_DOWN reads X row s and
+  // slot s's token from X row row_of[s] (clamped to [0, M); every slot read
+  // is below g*cap + cap) and writes C row s; EPI_DOWN reads X row s and
   // c_map / row_scale at s.
   const int32_t* group_count;
   int cap;
@@ -188,8 +188,8 @@ struct StreamArgs {
   float* logits;           // EPI_LMSTATS: optional [rows, N]
   const int32_t* row_map;  // EPI_LMSTATS: logits row of each token row
 };
-// Epilogues EPI_LMSTATS (128 token columns per pass) and EPI_SWIGLU /
-// EPI_DOWN (32 per pass).  K must satisfy stream_lm_ok / stream_moe_ok.
+// Epilogues EPI_LMSTATS (up to 128 token columns per pass), EPI_SWIGLU (128)
+// and EPI_DOWN (64).  K must satisfy stream_lm_ok / stream_moe_ok.
 hipError_t launch_stream(int epi, bool w_e4m3, const StreamArgs& a, int groups,
                          hipStream_t s);
 bool stream_lm_ok(int hidden);

@@ -512,20 +512,25 @@ hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
 
 // LM head: 2 row tiles per wave (128 vocabulary rows per workgroup), up to
 // 128 token columns per pass, K chunks of 64, 3 chunks in flight (4 stages
-// of 16 KB, 4 weight register sets).  Experts: 2 row tiles, 32 token
-// columns, K chunks of 64, 4 in flight (5 stages of 4 KB, 5 weight register
-// sets; measured side by side in the step against chunks of 128 with 3 in
-// flight: ~2 us faster in each of the two expert kernels).
+// of 16 KB, 4 weight register sets), 2 workgroups per CU.  Experts: one
+// 8-wave workgroup per CU, 2 row tiles per wave, K chunks of 64, 2 chunks
+// in flight; gate/up passes of 128 token columns, down passes of 64.
+// Measured side by side in the step against 4 waves, 32 token columns,
+// 4 chunks in flight: gate/up 168 -> 144 us, down 91.5 -> 88.7 us (an
+// expert has ~16 tokens: the wider passes cost MFMAs on clamped columns,
+// and the 8 waves share one token stage over twice the weight rows).
 constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2, kLmWaves = 4;
-constexpr int kMoeRT = 2, kMoeKC = 64, kMoeD = 4, kMoeOcc = 2, kMoeWaves = 4;
+constexpr int kMoeRT = 2, kMoeKC = 64, kMoeOcc = 2, kMoeWaves = 8;
+constexpr int kGuNT = 8, kGuD = 2;  // gate/up
+constexpr int kDnNT = 4, kDnD = 2;  // down
 
 int stream_rows_per_wg() { return kLmWaves * kLmRT * 16; }
 bool stream_lm_ok(int hidden) {
   return hidden % kLmKC == 0 && hidden / kLmKC >= kLmD;
 }
 bool stream_moe_ok(int hidden, int ffn) {
-  return hidden % kMoeKC == 0 && ffn % kMoeKC == 0 && hidden / kMoeKC >= kMoeD &&
-         ffn / kMoeKC >= kMoeD;
+  return hidden % kMoeKC == 0 && ffn % kMoeKC == 0 && hidden / kMoeKC >= kGuD &&
+         ffn / kMoeKC >= kDnD;
 }
 
 hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
@@ -535,13 +540,13 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
       if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
       return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_SWIGLU:
-      if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, true, kMoeOcc, kMoeWaves>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_SWIGLU, false, kMoeOcc, kMoeWaves>(a, groups, s);
+      if (a.K % kMoeKC || a.K / kMoeKC < kGuD) return hipErrorInvalidValue;
+      return w8 ? launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, true, kMoeOcc, kMoeWaves>(a, groups, s)
+                : launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, false, kMoeOcc, kMoeWaves>(a, groups, s);
     case EPI_DOWN:
-      if (a.K % kMoeKC || a.K / kMoeKC < kMoeD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, true, kMoeOcc, kMoeWaves>(a, groups, s)
-                : launch_s<kMoeRT, 2, kMoeKC, kMoeD, EPI_DOWN, false, kMoeOcc, kMoeWaves>(a, groups, s);
+      if (a.K % kMoeKC || a.K / kMoeKC < kDnD) return hipErrorInvalidValue;
+      return w8 ? launch_s<kMoeRT, kDnNT, kMoeKC, kDnD, EPI_DOWN, true, kMoeOcc, kMoeWaves>(a, groups, s)
+                : launch_s<kMoeRT, kDnNT, kMoeKC, kDnD, EPI_DOWN, false, kMoeOcc, kMoeWaves>(a, groups, s);
   }
   return hipErrorInvalidValue;
 }
