@@ -463,9 +463,10 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   }
 }
 
-// The LM head runs its rows in passes of 2, 4 or 8 token tiles, whichever
+// The LM head runs its rows in passes of 2, 4, 6 or 8 token tiles, whichever
 // is the fewest that cover the live rows in one pass (the token DMA and the
-// MFMAs scale with the tiles, the weight stream does not).
+// MFMAs scale with the tiles, the weight stream does not; 3, 5 and 7 tiles
+// would not split into whole DMA instructions over 4 waves).
 template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void stream_kernel(StreamArgs a) {
@@ -477,6 +478,8 @@ void stream_kernel(StreamArgs a) {
       stream_run<RT, 2, KC, D, EPI, W8, WV>(a, Xs, rows);
     else if (rows <= 64)
       stream_run<RT, 4, KC, D, EPI, W8, WV>(a, Xs, rows);
+    else if (rows <= 96)
+      stream_run<RT, 6, KC, D, EPI, W8, WV>(a, Xs, rows);
     else
       stream_run<RT, 8, KC, D, EPI, W8, WV>(a, Xs, rows);
   } else if constexpr (EPI == EPI_LMSTATS) {

@@ -326,9 +326,9 @@ def test_lmhead_full_vocab():
 
 
 def test_lmhead_tile_counts():
-    # the streaming LM head runs 2, 4 or 8 token tiles per pass by row
+    # the streaming LM head runs 2, 4, 6 or 8 token tiles per pass by row
     # count: both sides of each boundary, and two passes of 8 tiles
-    for m in (32, 33, 64, 65, 200):
+    for m in (32, 33, 64, 65, 96, 97, 200):
         _lm_case(m, 256, 3000, f"tiles{m}")
 
 
