@@ -146,7 +146,10 @@ class Bench:
         self.am = torch.zeros((1, 256), dtype=torch.int32, device=dev)
         self.gamma = torch.full((1,), wl.gamma, dtype=torch.float32, device=dev)
         self.n_new = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.done = torch.zeros(1, dtype=torch.uint8, device=dev)
+        # the stopping flag lives in pinned host memory: the EB kernel writes
+        # it there directly, so the loop reads it after a stream sync with no
+        # device-to-host copy launched per step
+        self.done = torch.zeros(1, dtype=torch.uint8, pin_memory=True)
         torch.cuda.synchronize()
         log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
 
@@ -168,7 +171,8 @@ class Bench:
                                self.ent, self.am, self.gamma,
                                self.wl.step_cap, True, self.n_new, self.done)
             n += 1
-            if int(self.done.item()):   # adaptive stopping: one sync per step
+            self.torch.cuda.current_stream().synchronize()   # adaptive stopping: one sync per step
+            if int(self.done[0]):
                 break
         self.eng.commit_block([0], st["tokens"], st["committed"], st["step"])
         return n

@@ -199,7 +199,9 @@ dg_status dg_denoise_step(dg_ctx* ctx, const dg_canvas_batch* batch,
  * n_new[b] = n*, done[b] = (U now empty).  A canvas whose U is already empty
  * is left unchanged with n_new = 0, done = 1.
  * entropy / argmax: [n, 256] as written by dg_denoise_step; gamma: [n] fp32
- * (device); step_cap in 1..65535; n_new, done: [n] device outputs. */
+ * (device); step_cap in 1..65535; n_new, done: [n] device outputs (any
+ * device-accessible memory: done in pinned host memory lets a host loop
+ * test it after a stream sync without a copy). */
 dg_status dg_eb_select(dg_ctx* ctx, const dg_canvas_batch* batch,
                        const float* entropy, const int32_t* argmax,
                        const float* gamma, int32_t step_cap, int32_t refine,
