@@ -227,7 +227,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU "
+        print("bench.py runs on exactly one GPU: libdg has no multi-GPU "
               "path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
