@@ -103,7 +103,7 @@ def _capture(shape, n, L):
     }
 
 
-@pytest.mark.parametrize("uncommitted", [256, 128])
+@pytest.mark.parametrize("uncommitted", [256, 128, 1])
 def test_denoise_step_tiny_elementwise(uncommitted):
     shape = TINY_WL.shape
     log(f"tiny step, {uncommitted} uncommitted")
@@ -119,6 +119,31 @@ def test_denoise_step_tiny_elementwise(uncommitted):
     # committed positions are left untouched
     committed = cv["committed"].numpy()[0] == 1
     assert np.all(np.isnan(ent.cpu().numpy()[0, committed]))
+
+
+def test_denoise_step_fully_committed_canvas():
+    """No uncommitted position: the step still runs every layer (whose
+    outputs do not depend on which positions are committed: the captures
+    equal those of the same tokens with 128 positions uncommitted, bit for
+    bit) and writes no row output."""
+    shape = TINY_WL.shape
+    eng, _, _ = _setup(shape, [512], 1024)
+    caps = []
+    for unc in (0, 128):
+        log(f"tiny step, {unc} uncommitted (captures)")
+        cv = synth.make_canvas(shape, 1, unc, seed=5)
+        tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                              cv["step"]))
+        ent, lse, am, _ = step_outputs(1)
+        cap = _capture(shape, 1, 1)
+        eng.denoise_step([0], tok, com, step, ent, lse, am, None, cap)
+        torch.cuda.synchronize()
+        caps.append(cap)
+        if unc == 0:
+            assert torch.isnan(ent).all() and torch.isnan(lse).all()
+            assert (am == -1).all()
+    for k in caps[0]:
+        assert torch.equal(caps[0][k], caps[1][k]), k
 
 
 def test_denoise_step_two_layers_three_canvases():
