@@ -65,8 +65,10 @@ dg_status dg_op_router_topk(const float* logits, int32_t tokens,
                             float* w, void* stream);
 
 /* Mixture-of-experts FFN of one layer on normalised rows: router logits,
- * top-k, stable counting-sort permute by expert, grouped gate/up GEMM with
- * SwiGLU, grouped down GEMM scaled by the gate weight, un-permute.
+ * top-k, grouping of the (token, rank) pairs by expert (per-expert slots
+ * when the experts average at most 32 pairs, else a stable counting-sort
+ * permutation), grouped gate/up GEMM with SwiGLU, grouped down GEMM scaled
+ * by the gate weight, un-permute summing each token's pairs in rank order.
  *   y_t = sum_j w_tj W_d,e (silu(W_g,e x_t) * W_u,e x_t),  e = idx_tj.
  * desc: hidden, n_experts, top_k, expert_ffn, expert_dtype are used;
  * weights: w_router, w_gate_up, w_down (packed) and the e4m3 scales are used.
