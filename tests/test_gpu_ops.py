@@ -215,7 +215,9 @@ def test_router_topk_bit_exact_on_identical_logits(t, e, k):
 
 # ------------------------------------------------------------------ MoE
 
-def _moe_case(shape, T, tag, top_k=None):
+def _moe_case(shape, T, tag, top_k=None, same_rows=False):
+    """same_rows: one random row repeated T times, so every token picks the
+    same k experts (T tokens in each: several token passes per expert)."""
     if top_k is not None:
         shape = synth.ModelShape(**{**shape.__dict__, "top_k": top_k})
     log(f"moe {tag}: T={T} H={shape.hidden} E={shape.n_experts} "
@@ -225,6 +227,8 @@ def _moe_case(shape, T, tag, top_k=None):
                            seed=11)
     lw = w["layers"][0]
     xh = _randn((T, shape.hidden), 1.0, f"moe.x{tag}")
+    if same_rows:
+        xh = xh[:1].repeat(T, 1)
     lwd = {k: (v.to(DEV).contiguous() if v is not None else None)
            for k, v in lw.items()}
     y = torch.zeros((T, shape.hidden), dtype=torch.float32, device=DEV)
@@ -262,6 +266,15 @@ def test_moe_tiny_shape():
     _moe_case(TINY, 256, "tiny")
     _moe_case(TINY, 37, "tiny_ragged")
     _moe_case(TINY, 1, "tiny_one")
+
+
+def test_moe_full_shape_every_token_in_the_same_experts():
+    # 160 identical rows at the full layer shape: 8 experts hold 160 tokens
+    # each (two gate/up and three down token passes per expert), bf16 and
+    # e4m3 experts
+    _moe_case(GEMMA, 160, "gemma_same", same_rows=True)
+    g8 = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": "fp8_e4m3"})
+    _moe_case(g8, 160, "gemma_fp8_same", same_rows=True)
 
 
 def test_moe_all_experts_selected():
