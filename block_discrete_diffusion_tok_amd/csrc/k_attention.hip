@@ -42,7 +42,7 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
-  constexpr int KP = D + 8;      // padded K row (elements)
+  constexpr int KP = D + 16;     // padded K row (elements; +16 measured ~0.5 us faster than +8)
   constexpr int VQ = D * 4 + 8;  // padded key-quad stride (elements; 16-byte rows)
   constexpr int DC = D / 32;     // 32-wide d chunks (MFMA k for S)
   constexpr int DT = D / 16;     // 16-wide d tiles (MFMA rows for O^T)
