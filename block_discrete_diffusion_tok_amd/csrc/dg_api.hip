@@ -2,6 +2,7 @@
 // orchestration of the kernels and the extern "C" entry points of dg.h and
 // dg_ops.h.  No device memory is allocated here: every buffer comes from the
 // caller.
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -129,9 +130,23 @@ static dg_status fail(dg_ctx* c, dg_status s, const std::string& msg) {
   return s;
 }
 
+// DG_DEBUG_SYNC=1 in the environment (read once per process): every HIP
+// call the library checks is followed by a device synchronisation, so an
+// asynchronous device fault is reported (DG_ERR_HIP, naming the call) by
+// the entry point that launched the faulting kernel rather than at a later
+// synchronisation of the caller's.
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = getenv("DG_DEBUG_SYNC");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
 #define HIPCHK(ctx, expr)                                                    \
   do {                                                                       \
     hipError_t e_ = (expr);                                                  \
+    if (e_ == hipSuccess && debug_sync()) e_ = hipDeviceSynchronize();       \
     if (e_ != hipSuccess)                                                    \
       return fail(ctx, DG_ERR_HIP, std::string(#expr ": ") +                 \
                                        hipGetErrorString(e_));               \

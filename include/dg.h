@@ -26,8 +26,11 @@
  *   - Arguments, shapes and capacities are validated on the host before any
  *     launch; a failed validation returns an error status and enqueues
  *     nothing.  A failed launch returns DG_ERR_HIP.  Faults inside kernels
- *     surface at the caller's next synchronisation.  Nothing aborts, exits or
- *     throws across the ABI.
+ *     surface at the caller's next synchronisation, or, with DG_DEBUG_SYNC=1
+ *     in the environment (read once per process), as DG_ERR_HIP from the
+ *     call that launched the faulting kernel: every launch is then followed
+ *     by a device synchronisation.  Nothing aborts, exits or throws across
+ *     the ABI.
  *   - bf16 means IEEE bfloat16 stored as 16-bit words; e4m3 means OCP FP8
  *     E4M3 ("fn": no infinities, max 448) bytes.
  *   - Matrices are row-major [rows, cols] with cols contiguous; a weight

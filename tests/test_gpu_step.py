@@ -146,6 +146,48 @@ def test_denoise_step_fully_committed_canvas():
         assert torch.equal(caps[0][k], caps[1][k]), k
 
 
+def test_debug_sync_mode_gives_the_same_step():
+    """DG_DEBUG_SYNC=1 (a device synchronisation after every launch) changes
+    nothing but the timing: a tiny step in a child process with it set
+    returns the same outputs as this process's step, bit for bit."""
+    import subprocess
+    import sys
+    code = r'''
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from block_discrete_diffusion_tok_amd import dg, synth
+shape = synth.WORKLOADS["tiny_l1_h256_p512"].shape
+w = synth.make_weights(shape, seed=0, device="cuda")
+k, v = synth.make_prefix_kv(shape, 512, 0, seed=0, device="cuda")
+eng = dg.Engine(shape, w, max_requests=1, max_kv_len=1024, max_canvases=1)
+eng.prefill_kv(0, k.contiguous(), v.contiguous())
+cv = synth.make_canvas(shape, 1, 128, seed=5)
+t = {kk: x.to("cuda") for kk, x in cv.items()}
+ent = torch.full((1, 256), float("nan"), device="cuda")
+lse = torch.full_like(ent, float("nan"))
+am = torch.full((1, 256), -1, dtype=torch.int32, device="cuda")
+eng.denoise_step([0], t["tokens"], t["committed"], t["step"], ent, lse, am)
+torch.cuda.synchronize()
+torch.save({"ent": ent.cpu(), "lse": lse.cpu(), "am": am.cpu()}, sys.argv[2])
+'''
+    import os
+    import tempfile
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = []
+    for flag in ("1", "0"):
+        with tempfile.TemporaryDirectory() as d:
+            path = os.path.join(d, "out.pt")
+            env = {**os.environ, "DG_DEBUG_SYNC": flag}
+            r = subprocess.run([sys.executable, "-c", code, root, path], env=env,
+                               capture_output=True, text=True, timeout=240)
+            assert r.returncode == 0, r.stderr[-2000:]
+            outs.append(torch.load(path, weights_only=True))
+    for kk in outs[0]:
+        # committed rows stay NaN: equal positions count as equal
+        torch.testing.assert_close(outs[0][kk], outs[1][kk], rtol=0, atol=0,
+                                   equal_nan=True, msg=kk)
+
+
 def test_denoise_step_two_layers_three_canvases():
     shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096)
     log("two layers, three canvases with prefixes 512 / 0 / 77")
