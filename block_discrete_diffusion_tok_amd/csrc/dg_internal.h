@@ -20,18 +20,21 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even, by gfx950's packed conversion
+// instruction: one instruction rounds two values, bit for bit the same as
+// adding 0x7fff plus the kept lsb and truncating, for every input that is not
+// a NaN (a NaN stays a NaN; its payload is the hardware's).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
-}
-__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
 // 16 OCP E4M3 bytes -> 16 bf16 (exact: 3 mantissa bits and exponents

@@ -213,9 +213,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       for (int h2 = 0; h2 < 4; ++h2) {
         const float a0 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1)];
         const float a1 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1) + 1];
-        const uint16_t b0 = f2bf(a0), b1 = f2bf(a1);
-        hi[h2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
-        lo[h2] = pack_bf2(a0 - bf2f(b0), a1 - bf2f(b1));
+        const uint32_t h = pack_bf2(a0, a1);
+        hi[h2] = h;
+        lo[h2] = pack_bf2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
       }
       pf[kc] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
       pl[kc] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
