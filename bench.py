@@ -146,10 +146,12 @@ class Bench:
         self.am = torch.zeros((1, 256), dtype=torch.int32, device=dev)
         self.gamma = torch.full((1,), wl.gamma, dtype=torch.float32, device=dev)
         self.n_new = torch.zeros(1, dtype=torch.int32, device=dev)
-        # the stopping flag lives in pinned host memory: the EB kernel writes
-        # it there directly, so the loop reads it after a stream sync with no
-        # device-to-host copy launched per step
-        self.done = torch.zeros(1, dtype=torch.uint8, pin_memory=True)
+        # the stopping flags live in pinned host memory: the EB kernel writes
+        # them there directly, so the loop reads them after an event sync with
+        # no device-to-host copy launched per step.  Two flags and two events:
+        # step n + 1 is queued before step n's flag is read.
+        self.done = torch.zeros(2, dtype=torch.uint8, pin_memory=True)
+        self.ev = [torch.cuda.Event(), torch.cuda.Event()]
         torch.cuda.synchronize()
         log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
 
@@ -158,22 +160,38 @@ class Bench:
         self.eng.denoise_step([0], st["tokens"], st["committed"], st["step"],
                               self.ent, self.lse, self.am)
 
-    def block(self):
-        """Decode one block from the initial canvas; returns denoise steps."""
+    def _launch_step(self, i):
+        st = self.st
+        self.denoise()
+        self.eng.eb_select([0], st["tokens"], st["committed"], st["step"],
+                           self.ent, self.am, self.gamma, self.wl.step_cap, True,
+                           self.n_new, self.done[i % 2:i % 2 + 1])
+        self.ev[i % 2].record()
+
+    def block(self, lookahead=True):
+        """Decode one block from the initial canvas; returns denoise steps.
+
+        Adaptive stopping reads each step's done flag on the host.  With
+        lookahead the next step is queued first, so the GPU does not idle
+        while the host reads the flag; the one step queued after the last is
+        a denoise step and EB selection of a canvas with nothing left to
+        unmask, which changes neither tokens, mask nor step counter."""
         st, init = self.st, self.init
         for kk in st:
             st[kk].copy_(init[kk])
         self.eng.set_kv_len(0, self.wl.prefix_len)
         n = 0
+        self._launch_step(0)
         while True:
-            self.denoise()
-            self.eng.eb_select([0], st["tokens"], st["committed"], st["step"],
-                               self.ent, self.am, self.gamma,
-                               self.wl.step_cap, True, self.n_new, self.done)
+            if lookahead:
+                self._launch_step(n + 1)
+            self.ev[n % 2].synchronize()
+            done = int(self.done[n % 2])
             n += 1
-            self.torch.cuda.current_stream().synchronize()   # adaptive stopping: one sync per step
-            if int(self.done[0]):
+            if done:
                 break
+            if not lookahead:
+                self._launch_step(n)
         self.eng.commit_block([0], st["tokens"], st["committed"], st["step"])
         return n
 
@@ -267,9 +285,10 @@ def main():
     value = 256.0 * total_denoise / (ms / 1000.0)
     committed = wl.uncommitted * args.steps / (ms / 1000.0)
 
-    # per-kernel times of one block, hipEvents around every launch
+    # per-kernel times of one block, hipEvents around every launch (no
+    # lookahead: every profiled launch belongs to a step that unmasks)
     b.eng.profile_enable(True)
-    n_prof = b.block()
+    n_prof = b.block(lookahead=False)
     prof = b.eng.profile_read()
     b.eng.profile_enable(False)
     # plain denoise-step time (no per-step host sync) on the initial canvas:

@@ -356,3 +356,29 @@ def test_full_size_layer_step_elementwise():
         np.testing.assert_array_equal(com.cpu().numpy(), o[0])
     else:
         log(f"  EB choice is low-margin ({hs[1] - hs[0]:.2e}); not compared")
+
+
+def test_bench_block_loop_with_lookahead_is_the_same_decode():
+    """The timed decode loop queues step n + 1 before it reads step n's done
+    flag.  The step queued after the last one sees a canvas with nothing
+    left to unmask, so the block must end in the same tokens, mask, step
+    counter and appended K/V, after the same number of steps, as the loop
+    that reads every flag before it launches the next step."""
+    import bench
+    b = bench.Bench(TINY_WL, seed=3)
+    res = {}
+    for la in (False, True, False):
+        n = b.block(lookahead=la)
+        torch.cuda.synchronize()
+        res.setdefault(la, []).append(
+            (n, {k: t.clone() for k, t in b.st.items()}, b.eng.kv_len(0),
+             b.eng.cache_view("k").clone(), b.eng.cache_view("v").clone()))
+    (n0, s0, kv0, k0, v0), (n2, s2, kv2, k2, v2) = res[False]
+    (n1, s1, kv1, k1, v1), = res[True]
+    log(f"  steps {n0} / {n1}, kv_len {kv0} / {kv1}")
+    assert n0 == n1 == n2 > 0
+    assert kv0 == kv1 == kv2 == TINY_WL.prefix_len + 256
+    for k in s0:
+        assert torch.equal(s0[k], s1[k]) and torch.equal(s0[k], s2[k]), k
+    assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    assert torch.equal(k0, k2) and torch.equal(v0, v2)
