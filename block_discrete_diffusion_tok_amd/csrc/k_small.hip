@@ -169,6 +169,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
 // dropping it.  Gate weights: softmax over the selected logits, summed in
 // rank order.
 constexpr int kTopkMaxE = 256, kTopkMaxK = 16;
+// Maximum of x over the wave, returned to every lane as a uniform value:
+// within each row of 16 lanes by DPP row shifts (lane 15 of a row ends with
+// the row's maximum; lanes shifted in from outside the row bring 0, the
+// identity), then the four row maxima by lane reads.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
 __device__ __forceinline__ uint32_t ordered_bits(float v) {
   if (v == 0.f) v = 0.f;  // -0 and +0 are equal logits
   const uint32_t u = __float_as_uint(v);
@@ -220,19 +233,23 @@ __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
     sel[r] = 0.f;
     sid[r] = 0;
     if (r < k) {
-      unsigned long long m = key[0];
+      // the largest key: the largest value, then among the keys holding it
+      // the largest low word (the lowest expert)
+      uint32_t hl = 0;
 #pragma unroll
-      for (int i = 1; i < PER; ++i) m = key[i] > m ? key[i] : m;
+      for (int i = 0; i < PER; ++i) hl = max(hl, (uint32_t)(key[i] >> 32));
+      const uint32_t vmax = wave_max_u32(hl);
+      uint32_t ll = 0;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const unsigned long long o = shfl_xor(m, off);
-        m = o > m ? o : m;
-      }
+      for (int i = 0; i < PER; ++i)
+        if ((uint32_t)(key[i] >> 32) == vmax) ll = max(ll, (uint32_t)key[i]);
+      const uint32_t lmax = wave_max_u32(ll);
+      const unsigned long long m = ((unsigned long long)vmax << 32) | lmax;
 #pragma unroll
       for (int i = 0; i < PER; ++i)
         if (key[i] == m) key[i] = 0;
-      sel[r] = from_ordered_bits((uint32_t)(m >> 32));
-      sid[r] = 255 - (int)(uint32_t)m;
+      sel[r] = from_ordered_bits(vmax);
+      sid[r] = 255 - (int)lmax;
     }
   }
   const float mx = sel[0];
