@@ -554,3 +554,78 @@ def test_attention_scale_is_one_over_sqrt_head_dim():
     empty = np.zeros((1, 0, 4))
     o = oracle.canvas_attention(q, empty, empty, kc, vc)
     np.testing.assert_allclose(o[0, 0], [1.0] * 4, rtol=1e-14)
+
+
+# ----------------------------------------------------------------- hand-worked layers
+
+def _fixture_model(ex):
+    s = ex["shape"]
+    osh = oracle.Shapes(s["n_layers"], s["hidden"], s["n_q_heads"],
+                        s["n_kv_heads"], s["head_dim"], s["n_experts"],
+                        s["top_k"], s["expert_ffn"], s["vocab"], s["rms_eps"])
+    w = {"embed": np.array(ex["embed"], float),
+         "final_norm": np.array(ex["final_norm"], float),
+         "layers": [{k: np.array(v, float) for k, v in lw.items()}
+                    for lw in ex["layers"]]}
+    pre = [(np.array(ex["prefix_k"], float), np.array(ex["prefix_v"], float))]
+    return osh, w, pre, np.array([ex["tokens"]])
+
+
+def test_layer_wiring_hand_example(golden_dir):
+    """Norm gains, Q/K/V slices per head, residual order, routing, SwiGLU,
+    final norm and LM head of a 2-layer model against a hand derivation: a
+    swap of the two norms, the wrong V rows, another residual order or a
+    missing head changes the checked values."""
+    ex = _load(golden_dir, "layer_hand_example.json")
+    osh, w, pre, tok = _fixture_model(ex)
+    e = ex["expected"]
+    cap = []
+    out = oracle.denoise_step(osh, w, tok, np.zeros_like(tok, np.uint8), pre,
+                              mirror=False, capture=cap)
+    np.testing.assert_allclose(cap[0]["attn"], e["layer0_attn"], rtol=1e-13)
+    np.testing.assert_allclose(cap[0]["router_logits"],
+                               e["layer0_router_logits"], rtol=1e-13)
+    np.testing.assert_array_equal(cap[0]["idx"], e["layer0_idx"])
+    np.testing.assert_allclose(cap[0]["moe"], e["layer0_moe"], rtol=1e-13)
+    np.testing.assert_allclose(cap[0]["x"], e["layer0_x"], rtol=1e-13)
+    np.testing.assert_allclose(cap[1]["x"], e["layer0_x"], rtol=1e-13)
+    np.testing.assert_allclose(out["entropy"][0], e["entropy"], rtol=1e-9)
+    np.testing.assert_allclose(out["lse"][0], e["lse"], rtol=1e-13)
+    np.testing.assert_array_equal(out["argmax"][0], e["argmax"])
+
+
+def test_commit_kv_hand_example(golden_dir):
+    """The appended K and V of both layers of the causal encode (the V rows
+    of w_qkv, the causal mask of position 0 and layer 0's full residual
+    reaching layer 1) against the hand derivation."""
+    ex = _load(golden_dir, "layer_hand_example.json")
+    osh, w, pre, tok = _fixture_model(ex)
+    e = ex["expected"]
+    (k, v), = oracle.commit_block(osh, w, tok, pre, mirror=False)
+    # k, v: [L, Hkv=1, C=2, D=1]
+    np.testing.assert_allclose(k[:, 0, :, 0], e["commit_k"], rtol=1e-13)
+    np.testing.assert_allclose(v[:, 0, :, 0], e["commit_v"], rtol=1e-13)
+
+
+def test_mirror_mode_rounds_attention_and_swiglu_outputs(golden_dir):
+    """Mirror mode rounds the attention output and the SwiGLU output to
+    bfloat16 (hand-computed amounts) and leaves the residual stream exact;
+    dropping either rounding point, or rounding the residual, changes the
+    checked values."""
+    ex = _load(golden_dir, "mirror_rounding_example.json")
+    osh, w, pre, tok = _fixture_model(ex)
+    e = ex["expected"]
+    for mirror, tag in ((False, "exact"), (True, "mirror")):
+        cap = []
+        oracle.denoise_step(osh, w, tok, np.zeros_like(tok, np.uint8), pre,
+                            mirror=mirror, capture=cap)
+        np.testing.assert_allclose(cap[0]["attn"],
+                                   np.full((2, 2), e[f"{tag}_attn"]),
+                                   rtol=1e-15)
+        np.testing.assert_allclose(cap[0]["moe"],
+                                   np.full((2, 2), e[f"{tag}_moe"]),
+                                   rtol=1e-15)
+        np.testing.assert_allclose(cap[0]["x"][:, 0], e[f"{tag}_x"],
+                                   rtol=1e-15)
+        np.testing.assert_allclose(cap[0]["x"][:, 1], e[f"{tag}_x"],
+                                   rtol=1e-15)
