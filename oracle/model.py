@@ -40,9 +40,12 @@ R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     decisions are taken on the same operand values.  ``mirror=False`` keeps
     every activation in fp64.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 from .numerics import round_bf16, decode_e4m3
 
@@ -69,6 +72,24 @@ def _f64(a):
 
 def _bf(x, mirror):
     return round_bf16(x) if mirror else x
+
+
+def _map_independent(fn, items):
+    """[fn(i) for i in items] with the items spread over a pool of threads.
+
+    Only used for items whose computations do not depend on each other
+    (attention heads, experts); each item's arithmetic is exactly that of a
+    serial loop, and the callers combine the results in item order, so the
+    results are the same bits as a serial loop's.  BLAS threads are shared
+    out among the workers."""
+    items = list(items)
+    cores = os.cpu_count() or 1
+    workers = max(1, min(len(items), cores))
+    if workers == 1:
+        return [fn(i) for i in items]
+    with threadpool_limits(max(1, cores // workers)):
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))
 
 
 def expert_matrix(w, scale, e):
@@ -113,8 +134,7 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, causal=False,
     if q_pos is None:
         q_pos = np.arange(n)
     q_pos = np.asarray(q_pos)
-    out = np.zeros((hq, n, d))
-    for h in range(hq):
+    def head(h):
         g = h // group
         keys = np.concatenate([_f64(k_prefix[g]), _f64(k_canvas[g])], axis=0)
         vals = np.concatenate([_f64(v_prefix[g]), _f64(v_canvas[g])], axis=0)
@@ -126,7 +146,9 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, causal=False,
         s_max = np.max(s, axis=1, keepdims=True)
         e = np.exp(s - s_max)
         p = e / np.sum(e, axis=1, keepdims=True)
-        out[h] = p @ vals
+        return p @ vals
+
+    out = np.stack(_map_independent(head, range(hq)))
     return out
 
 
@@ -168,7 +190,8 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
     xhat = _f64(xhat)
     t_count, hidden = xhat.shape
     out = np.zeros((t_count, hidden))
-    for e in np.unique(idx):
+
+    def expert(e):
         tt, jj = np.nonzero(idx == e)
         if experts is not None:
             wgu, wd = experts[int(e)]
@@ -180,7 +203,11 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
         up = xhat[tt] @ wgu[f:].T
         act = _bf(silu(gate) * up, mirror)
         y = act @ wd.T
-        out[tt] += w[tt, jj][:, None] * y
+        return tt, w[tt, jj][:, None] * y
+
+    # every expert's products are independent; they are added in expert order
+    for tt, contrib in _map_independent(expert, np.unique(idx)):
+        out[tt] += contrib
     return out
 
 
@@ -275,12 +302,15 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
     embed = weights["embed"]
     x = _f64(embed[np.asarray(tokens).reshape(-1)])  # x_t = E[tok_t]
     for li, lw in enumerate(weights["layers"]):
+        x_in = x
         xh = _bf(rmsnorm(x, lw["attn_norm"], sh.rms_eps), mirror)
         qkv = _bf(xh @ _f64(lw["w_qkv"]).T, mirror)
         q, k, v = _split_qkv(qkv, sh)
         if kv_out is not None:
             kv_out.append((k, v))
             if li == len(weights["layers"]) - 1:
+                if capture is not None:   # what the last layer computed
+                    capture.append({"x_in": x_in, "xh_attn": xh, "qkv": qkv})
                 break
         o = np.zeros((b_count * c_len, sh.n_q_heads * sh.head_dim))
         for b in range(b_count):
@@ -291,6 +321,8 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
             o[rows] = ob.transpose(1, 0, 2).reshape(c_len, -1)
         o = _bf(o, mirror)
         x = x + o @ _f64(lw["w_o"]).T
+        x_mid = x
+        xh_attn = xh
         xh = _bf(rmsnorm(x, lw["ffn_norm"], sh.rms_eps), mirror)
         r = xh @ _f64(lw["w_router"]).T
         idx, w = router_topk(r, sh.top_k)
@@ -299,8 +331,14 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
                         mirror=mirror)
         x = x + y
         if capture is not None:
-            capture.append({"attn": o, "router_logits": r, "idx": idx,
-                            "w": w, "moe": y, "x": x.copy()})
+            # every value the layer computed, in order: its input residual,
+            # attention norm, Q/K/V, attention output, residual after the
+            # attention, FFN norm, router logits, routing, MoE output and
+            # the residual it leaves
+            capture.append({"x_in": x_in, "xh_attn": xh_attn, "qkv": qkv,
+                            "attn": o, "x_mid": x_mid, "xh_ffn": xh,
+                            "router_logits": r, "idx": idx, "w": w,
+                            "moe": y, "x": x.copy()})
     return x
 
 

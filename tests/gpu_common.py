@@ -9,11 +9,9 @@ from block_discrete_diffusion_tok_amd import dg, synth
 
 DEV = "cuda"
 TOL = 2e-2        # max relative error on continuous outputs (per tensor)
-# Decisions (top-k routing, argmax) whose oracle margin, relative to the
-# largest magnitude among the values decided on, is below MARGIN are not
-# required to agree: the bf16 activations the path stores round differently
-# from the oracle's fp64 values whenever the two straddle a rounding boundary,
-# which moves router and vocabulary logits by ~1e-3 of their scale.
+# Decisions (top-k routing, argmax, EB cut) whose oracle margin -- the
+# absolute gap between the competing values -- is below MARGIN are not
+# required to agree.
 MARGIN = 1e-3
 
 
@@ -43,34 +41,56 @@ def np32(t):
 
 
 def rel_err(g, o):
+    """max |g - o| / max |o| over the whole tensor."""
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
-    scale = np.max(np.abs(o))
+    scale = np.max(np.abs(o)) if o.size else 0.0
+    if g.size == 0:
+        return 0.0
     return float(np.max(np.abs(g - o)) / (scale if scale > 0 else 1.0))
 
 
-def _relative(gap, vals):
+def row_err(g, o):
+    """Largest per-row relative error: max over rows of max |g - o| / max |o|
+    within the row, with rows of small magnitude measured against 1e-3 of the
+    tensor's largest |value| (so a row of near-zeros cannot hide a large
+    error behind the tensor-wide scale, nor blow up on rounding noise)."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if g.size == 0:
+        return 0.0
+    g = g.reshape(g.shape[0], -1) if g.ndim > 1 else g.reshape(-1, 1)
+    o = o.reshape(o.shape[0], -1) if o.ndim > 1 else o.reshape(-1, 1)
+    floor = 1e-3 * max(np.max(np.abs(o)), 1e-30)
+    scale = np.maximum(np.max(np.abs(o), axis=1), floor)
+    return float(np.max(np.max(np.abs(g - o), axis=1) / scale))
+
+
+def _scaled(gap, vals, relative):
+    if not relative:
+        return gap
     scale = np.max(np.abs(vals), axis=1)
     return gap / np.where(scale > 0, scale, 1.0)
 
 
-def top2_margin(z):
-    """Gap between the largest and second-largest value of each row, relative
-    to the row's largest magnitude (the decision margin of an argmax)."""
+def top2_margin(z, relative=False):
+    """Gap between the largest and second-largest value of each row (the
+    decision margin of an argmax); relative=True divides by the row's
+    largest magnitude (a diagnostic reading only)."""
     part = np.partition(z, -2, axis=1)
-    return _relative(part[:, -1] - part[:, -2], z)
+    return _scaled(part[:, -1] - part[:, -2], z, relative)
 
 
-def routing_margin(r, k):
+def routing_margin(r, k, relative=False):
     """Smallest gap between consecutive sorted router logits among the first
     k + 1 ranks of each token (the rank order of the selected experts and the
-    cut between selected and not selected), relative to the row's largest
-    magnitude."""
+    cut between selected and not selected); relative=True divides by the
+    row's largest magnitude (a diagnostic reading only)."""
     s = -np.sort(-r, axis=1)
     last = min(k, r.shape[1] - 1)
     if last == 0:
         return np.full(r.shape[0], np.inf)
-    return _relative(np.min(s[:, :last] - s[:, 1:last + 1], axis=1), r)
+    return _scaled(np.min(s[:, :last] - s[:, 1:last + 1], axis=1), r, relative)
 
 
 def new_canvas_tensors(cv, dev=DEV):

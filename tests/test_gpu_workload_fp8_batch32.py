@@ -3,12 +3,15 @@ expert weights (per-output-channel scales), 32 requests with their own
 2048-token prefixes, 32 canvases denoised together (8192 rows per MoE grouped
 GEMM and per LM head).
 
-* One denoise step of the 32 all-masked canvases: two of them (the first and
-  the last, so both ends of every row and key mapping) against the oracle on
-  the first layers, up to the first low-margin routing difference (canvases
-  are independent, so these are outputs the oracle can compute one by one);
-  all 32 canvases through all 30 layers against the single-op entry points
-  (composition).
+* One denoise step of the 32 all-masked canvases.  Lockstep (see
+  tests/lockstep.py): the oracle runs canvases 0 and 31 (the first and the
+  last, so both ends of every row and key mapping; canvases are
+  independent) through its own 30-layer chain, and every layer's ops, the
+  LM head and the EB selection are fed the oracle's values for those
+  canvases at their rows of the full 32-canvas batch, so the ops take the
+  paths the step takes (tiled MoE and LM head at 8192 rows).  Composition:
+  all 32 canvases through all 30 layers of the step against the single-op
+  entry points.
 * The EB sampler (gamma 1) per request until every canvas is finished, then
   the 32 commits, checked by invariants.
 
@@ -23,7 +26,8 @@ import torch
 import oracle
 from block_discrete_diffusion_tok_amd import dg, synth
 from gpu_common import (DEV, log, new_canvas_tensors, oshape, step_outputs)
-from workload_common import (ChainChecker, HostPerLayer, capture_buffers,
+from lockstep import Lockstep, lockstep_eb, lockstep_head
+from workload_common import (HostPerLayer, capture_buffers,
                              check_composition, host_model)
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +35,6 @@ pytestmark = pytest.mark.gpu
 WL = synth.WORKLOADS["stack30_fp8_b32_p2048"]
 SHAPE = WL.shape
 ORACLE_CANVASES = (0, 31)
-ORACLE_LAYERS = 4   # at most this many layers go through the oracle
 
 
 @pytest.fixture(scope="module")
@@ -55,38 +58,45 @@ def batch32():
     eng.close()
 
 
-def test_fp8_batch32_step_sampled_canvases_against_oracle(batch32):
+@pytest.mark.timeout(900)
+def test_fp8_batch32_step_lockstep_and_composition(batch32):
     eng, w = batch32["eng"], batch32["w"]
     n = WL.batch
-    for r in range(n):
+    req = list(range(n))
+    plen = [WL.prefix_len] * n
+    for r in req:
         eng.set_kv_len(r, WL.prefix_len)
     cv = synth.make_canvas(SHAPE, n, 256, seed=1)
     tok, com, step = new_canvas_tensors(cv)
     ent, lse, am, _ = step_outputs(n)
     cap = capture_buffers(SHAPE, n * 256, SHAPE.n_layers, final=False)
-    eng.denoise_step(list(range(n)), tok, com, step, ent, lse, am, None, cap)
+    eng.denoise_step(req, tok, com, step, ent, lse, am, None, cap)
     torch.cuda.synchronize()
-    log(f"  device step done; oracle on canvases {ORACLE_CANVASES}, "
-        f"first {ORACLE_LAYERS} layers")
-    sel = list(ORACLE_CANVASES)
-    pre = [(HostPerLayer(batch32["prefixes"][b][0]),
-            HostPerLayer(batch32["prefixes"][b][1])) for b in sel]
-    cap_o = []
-    grow = np.concatenate([np.arange(b * 256, (b + 1) * 256) for b in sel])
-    chk = ChainChecker(SHAPE, cap, cap_o, grow, "fp8 b32")
-    oracle.model._layers_forward(oshape(SHAPE),
-                                 host_model(w, ORACLE_LAYERS, stop=chk),
-                                 cv["tokens"].numpy()[sel], pre, True, False,
-                                 cap_o)
-    chk.finish()
-    check_composition(eng, SHAPE, w, tok, list(range(n)),
-                      [WL.prefix_len] * n, cap, "fp8 b32")
-    # every canvas: entropy and argmax well formed
     e = ent.cpu().numpy()
     a = am.cpu().numpy()
     assert np.all(np.isfinite(e)) and np.all(e >= 0)
     assert np.all(e <= math.log(SHAPE.vocab) * (1 + 1e-5))
     assert np.all((a >= 0) & (a < SHAPE.vocab))
+    log("  composition: all 32 canvases, all layers")
+    check_composition(eng, SHAPE, w, tok, req, plen, cap, "fp8 b32")
+    del cap
+    sel = list(ORACLE_CANVASES)
+    log(f"  lockstep: oracle canvases {sel}, all {SHAPE.n_layers} layers")
+    pre = [(HostPerLayer(batch32["prefixes"][b][0]),
+            HostPerLayer(batch32["prefixes"][b][1])) for b in sel]
+    cap_o = []
+    ls = Lockstep(SHAPE, eng, w, n, req, plen, sel, cap_o, "fp8 b32", seed=1)
+    ref = oracle.denoise_step(oshape(SHAPE), host_model(w, stop=ls),
+                              cv["tokens"].numpy()[sel],
+                              cv["committed"].numpy()[sel], pre, mirror=True,
+                              want_logits=True, capture=cap_o)
+    assert ls.finish() == SHAPE.n_layers
+    ls.report()
+    lockstep_head(SHAPE, eng, w, ref, ls.x_last, cv["committed"].numpy(), n,
+                  sel, "fp8 b32", seed=1)
+    lockstep_eb(ref["entropy"], ref["argmax"], cv["committed"].numpy()[sel],
+                cv["tokens"].numpy()[sel], cv["step"].numpy()[sel], WL.gamma,
+                WL.step_cap, "fp8 b32")
 
 
 def test_fp8_batch32_decode_until_every_block_is_committed(batch32):
