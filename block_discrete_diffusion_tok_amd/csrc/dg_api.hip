@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1038,6 +1039,76 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                               &n_tiles, s));
   HIPCHK(nullptr, launch_lm_merge((const float4*)workspace, n_tiles, nullptr, m,
                                   nullptr, entropy, lse, argmax, s));
+  return DG_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ static scratch
+// Device memory of the allocation-free LM-head entry point: one array per
+// GPU, part of the library's code object, alive until the process ends.
+// Host code never uses the array's name as an address: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[DG_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array; nullptr (and *err set) on
+// failure.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
+                                      int32_t hidden, const void* embed,
+                                      int32_t vocab, float* entropy,
+                                      float* lse, int32_t* argmax,
+                                      void* stream) {
+  if (!xhat || !embed || !entropy || !lse || !argmax)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (m < 1 || vocab < 1 || hidden < 64 || hidden % 64)
+    return fail(nullptr, DG_ERR_SHAPE, "need m >= 1, vocab >= 1, hidden a multiple of 64");
+  if (dg_op_lmhead_workspace_bytes(m, vocab) > (size_t)DG_STATIC_SCRATCH_BYTES)
+    return fail(nullptr, DG_ERR_CAPACITY,
+                "m * ceil(vocab / 128) * 16 bytes of partials exceed the static "
+                "scratch (DG_STATIC_SCRATCH_BYTES)");
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws)
+    return fail(nullptr, DG_ERR_HIP,
+                std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  hipStream_t s = (hipStream_t)stream;
+  int n_tiles = 0;
+  // every partial a row's merge reads is written first by the LM head of
+  // this call (rows < m, all tiles), so nothing needs clearing
+  HIPCHK(nullptr, run_lm_head((const uint16_t*)xhat, m, nullptr, hidden, embed,
+                              vocab, (float4*)ws, nullptr, nullptr, &n_tiles, s));
+  HIPCHK(nullptr, launch_lm_merge((const float4*)ws, n_tiles, nullptr, m, nullptr,
+                                  entropy, lse, argmax, s));
   return DG_OK;
 }
 

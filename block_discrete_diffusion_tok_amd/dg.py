@@ -106,6 +106,7 @@ _SIGS = {
     "dg_op_lmhead_entropy": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     "dg_op_lmhead_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "dg_op_lmhead_entropy_static": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dg_op_eb_select": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                              ctypes.POINTER(_I), ctypes.POINTER(_I), _P]),
@@ -395,6 +396,16 @@ def op_lmhead_entropy(xhat, embed, entropy, lse, argmax, logits=None):
                                   _ptr(lse), _ptr(argmax), _ptr(logits),
                                   _ptr(ws), ws.numel(), _stream()))
     return ws
+
+
+def op_lmhead_entropy_static(xhat, embed, entropy, lse, argmax):
+    """dg_op_lmhead_entropy_static: no workspace, no allocation.
+    embed: a Packed matrix (packing allocates, so it is done beforehand)."""
+    if not isinstance(embed, Packed):
+        raise TypeError("embed must be a Packed matrix (pack it beforehand)")
+    _check(lib().dg_op_lmhead_entropy_static(
+        _ptr(xhat), xhat.shape[0], xhat.shape[1], _ptr(embed), embed.rows,
+        _ptr(entropy), _ptr(lse), _ptr(argmax), _stream()))
 
 
 def op_eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,

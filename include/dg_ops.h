@@ -93,6 +93,27 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                                size_t workspace_bytes, void* stream);
 size_t dg_op_lmhead_workspace_bytes(int32_t m, int32_t vocab);
 
+/* Allocation-free variant of dg_op_lmhead_entropy, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * results as dg_op_lmhead_entropy without logits or workspace: the per-tile
+ * partials go to a static device array of DG_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call with that device
+ * current).  Calls nothing that allocates.  Limit: m * ceil(vocab / 128) *
+ * 16 bytes must fit the array (256 rows at a 262144-token vocabulary hold
+ * 8 MiB), else DG_ERR_CAPACITY before any launch.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's partials: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  DG_ERR_HIP if the array's address cannot be
+ * obtained. */
+#define DG_STATIC_SCRATCH_BYTES (16u << 20)
+dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
+                                      int32_t hidden, const void* embed,
+                                      int32_t vocab, float* entropy,
+                                      float* lse, int32_t* argmax,
+                                      void* stream);
+
 /* Entropy-bounded selection on explicit state (same rule as dg_eb_select):
  * entropy [n, 256] fp32, argmax [n, 256] int32, committed [n, 256] uint8
  * in/out, tokens [n, 256] int32 in/out, step [n] int32 in/out, gamma [n]
