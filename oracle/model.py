@@ -33,6 +33,13 @@ R6  Entropy-bounded selection over the uncommitted positions U: sort by
 R7  Uncommitted positions that are not selected take the step's argmax token
     as well ("refine"), committed ones are frozen; with refine off they keep
     their current token.  The canvas is finished once U is empty.
+R9  Several canvases of one request (multi-canvas sampling, model card
+    feature list "block-autoregressive multi-canvas sampling"; write-up
+    Table 7 "number of canvases"): they sit next to each other in the batch,
+    in block order, and canvas j attends to the request's cached prefix,
+    then to every position of the request's canvases before it (earlier
+    blocks are fully visible, later ones not: block-causal), then to its own
+    canvas (bidirectional, or causal in the commit pass).
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -290,15 +297,35 @@ def _split_qkv(qkv, sh):
     return q, k, v
 
 
+def _earlier_canvases(request, b_count):
+    """For each canvas, the batch indices of the earlier canvases of its
+    request (reading R9; canvases of a request are contiguous)."""
+    if request is None:
+        return [[] for _ in range(b_count)]
+    request = list(request)
+    out = []
+    for b in range(b_count):
+        first = b
+        while first > 0 and request[first - 1] == request[b]:
+            first -= 1
+        assert request[b] not in request[:first], \
+            "canvases of one request must be contiguous"
+        out.append(list(range(first, b)))
+    return out
+
+
 def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
-                    kv_out=None):
+                    kv_out=None, request=None):
     """Embedding plus the L residual layers over B canvases.
 
     tokens [B, C]; prefix: list over canvases of (K, V), each [L, Hkv, P_b, D].
+    request: optional [B] request ids; canvases sharing one see the earlier
+    ones (reading R9).
     With ``kv_out`` (a list) the per-layer canvas K/V [Hkv, B*C, D] are
     appended to it and the last layer stops after its K/V projection.
     """
     b_count, c_len = tokens.shape
+    earlier = _earlier_canvases(request, b_count)
     embed = weights["embed"]
     x = _f64(embed[np.asarray(tokens).reshape(-1)])  # x_t = E[tok_t]
     for li, lw in enumerate(weights["layers"]):
@@ -316,7 +343,12 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
         for b in range(b_count):
             rows = slice(b * c_len, (b + 1) * c_len)
             kp, vp = prefix[b]
-            ob = canvas_attention(q[:, rows], kp[li], vp[li], k[:, rows],
+            kp, vp = _f64(kp[li]), _f64(vp[li])
+            if earlier[b]:   # the request's earlier canvases follow its prefix
+                sl = [slice(e * c_len, (e + 1) * c_len) for e in earlier[b]]
+                kp = np.concatenate([kp] + [k[:, r] for r in sl], axis=1)
+                vp = np.concatenate([vp] + [v[:, r] for r in sl], axis=1)
+            ob = canvas_attention(q[:, rows], kp, vp, k[:, rows],
                                   v[:, rows], causal=causal)
             o[rows] = ob.transpose(1, 0, 2).reshape(c_len, -1)
         o = _bf(o, mirror)
@@ -343,7 +375,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
 
 
 def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
-                 want_logits=False, capture=None):
+                 want_logits=False, capture=None, request=None):
     """One denoising forward over B canvases (write-up Figure 4, stage 2).
 
     weights: {"embed" [V,H], "final_norm" [H], "layers": [per-layer dict with
@@ -359,7 +391,8 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
     tokens = np.asarray(tokens)
     committed = np.asarray(committed)
     b_count, c_len = tokens.shape
-    x = _layers_forward(sh, weights, tokens, prefix, mirror, False, capture)
+    x = _layers_forward(sh, weights, tokens, prefix, mirror, False, capture,
+                        request=request)
     rows = np.nonzero(committed.reshape(-1) == 0)[0]
     xf = _bf(rmsnorm(x[rows], weights["final_norm"], sh.rms_eps), mirror)
     st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
@@ -378,19 +411,20 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
     return out
 
 
-def commit_block(sh, weights, tokens, prefix, mirror=True):
+def commit_block(sh, weights, tokens, prefix, mirror=True, request=None):
     """Encode-and-append of finished canvases (write-up Figure 4, stage 3).
 
     The canvas tokens are run causally through the layers (reading R3) and the
     K/V each layer produces for them are what gets appended to the request's
-    cache at rows [P_b, P_b + C).  Returns a list over canvases of (K, V),
-    each [L, Hkv, C, D].
+    cache at rows [P_b, P_b + C) (after the request's earlier canvases of the
+    batch, reading R9, when ``request`` groups canvases).  Returns a list
+    over canvases of (K, V), each [L, Hkv, C, D].
     """
     tokens = np.asarray(tokens)
     b_count, c_len = tokens.shape
     kv = []
     _layers_forward(sh, weights, tokens, prefix, mirror, True, None,
-                    kv_out=kv)
+                    kv_out=kv, request=request)
     out = []
     for b in range(b_count):
         rows = slice(b * c_len, (b + 1) * c_len)

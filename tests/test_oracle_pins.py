@@ -629,3 +629,80 @@ def test_mirror_mode_rounds_attention_and_swiglu_outputs(golden_dir):
                                    rtol=1e-15)
         np.testing.assert_allclose(cap[0]["x"][:, 1], e[f"{tag}_x"],
                                    rtol=1e-15)
+
+
+# ----------------------------------------------------------------- multi-canvas
+
+def test_multi_canvas_first_block_ignores_later_blocks():
+    """Block-causal visibility: the first canvas of a two-canvas request
+    gives exactly what it gives alone."""
+    sh, osh, w = _tiny_model()
+    tokens = RNG.integers(0, sh.vocab, (2, 12))
+    committed = (RNG.random((2, 12)) < 0.3).astype(np.uint8)
+    pre = _prefix(sh, 5)
+    both = oracle.denoise_step(osh, w, tokens, committed, pre * 2,
+                               mirror=False, request=[4, 4])
+    alone = oracle.denoise_step(osh, w, tokens[:1], committed[:1], pre,
+                                mirror=False)
+    np.testing.assert_allclose(both["entropy"][0], alone["entropy"][0],
+                               rtol=1e-12, equal_nan=True)
+    np.testing.assert_array_equal(both["argmax"][0], alone["argmax"][0])
+
+
+def test_multi_canvas_later_block_sees_earlier_block_after_the_prefix():
+    """The second canvas of a request equals that canvas run alone with the
+    first canvas's per-layer K/V (from the first canvas's own forward)
+    appended to its prefix; and it differs from the second canvas alone."""
+    sh, osh, w = _tiny_model()
+    tokens = RNG.integers(0, sh.vocab, (2, 10))
+    committed = np.zeros((2, 10), np.uint8)
+    pre = _prefix(sh, 4)
+    both = oracle.denoise_step(osh, w, tokens, committed, pre * 2,
+                               mirror=False, request=[0, 0])
+    cap0 = []
+    oracle.denoise_step(osh, w, tokens[:1], committed[:1], pre, mirror=False,
+                        capture=cap0)
+    hq, hkv, d = sh.n_q_heads, sh.n_kv_heads, sh.head_dim
+    k_ext, v_ext = [], []
+    for li, c in enumerate(cap0):
+        qkv = c["qkv"]
+        k0 = qkv[:, hq * d:(hq + hkv) * d].reshape(10, hkv, d).transpose(1, 0, 2)
+        v0 = qkv[:, (hq + hkv) * d:].reshape(10, hkv, d).transpose(1, 0, 2)
+        k_ext.append(np.concatenate([pre[0][0][li], k0], axis=1))
+        v_ext.append(np.concatenate([pre[0][1][li], v0], axis=1))
+    ext = [(np.stack(k_ext), np.stack(v_ext))]
+    second = oracle.denoise_step(osh, w, tokens[1:], committed[1:], ext,
+                                 mirror=False)
+    np.testing.assert_allclose(both["entropy"][1], second["entropy"][0],
+                               rtol=1e-10)
+    np.testing.assert_array_equal(both["argmax"][1], second["argmax"][0])
+    plain = oracle.denoise_step(osh, w, tokens[1:], committed[1:], pre,
+                                mirror=False)
+    assert np.max(np.abs(plain["entropy"][0] - both["entropy"][1])) > 1e-6
+
+
+@pytest.mark.parametrize("expert_dtype", ["bf16", "fp8_e4m3"])
+def test_multi_canvas_commit_equals_block_by_block_commits(expert_dtype):
+    """Committing two canvases of one request in one causal pass gives the
+    K/V of committing the first, appending it, then committing the second."""
+    sh, osh, w = _tiny_model(l_count=3, expert_dtype=expert_dtype)
+    tokens = RNG.integers(0, sh.vocab, (2, 9))
+    pre = _prefix(sh, 4)
+    both = oracle.commit_block(osh, w, tokens, pre * 2, mirror=False,
+                               request=[1, 1])
+    (k0, v0), = oracle.commit_block(osh, w, tokens[:1], pre, mirror=False)
+    ext = [(np.concatenate([pre[0][0], k0], axis=2),
+            np.concatenate([pre[0][1], v0], axis=2))]
+    (k1, v1), = oracle.commit_block(osh, w, tokens[1:], ext, mirror=False)
+    np.testing.assert_allclose(both[0][0], k0, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(both[1][0], k1, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(both[1][1], v1, rtol=1e-10, atol=1e-12)
+
+
+def test_multi_canvas_requests_must_be_contiguous():
+    sh, osh, w = _tiny_model(l_count=1)
+    tokens = RNG.integers(0, sh.vocab, (3, 4))
+    pre = _prefix(sh, 2) * 3
+    with pytest.raises(AssertionError):
+        oracle.denoise_step(osh, w, tokens, np.zeros((3, 4), np.uint8), pre,
+                            request=[0, 1, 0])
