@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -99,6 +100,7 @@ constexpr int kSlotPad = 64;
 
 struct dg_ctx {
   dg_model_desc d;
+  int C;                  // canvas positions (desc canvas_len, 0 -> 256)
   const uint16_t* embed;
   const float* final_norm;
   std::vector<dg_layer_weights> layers;
@@ -123,6 +125,10 @@ struct dg_ctx {
   int32_t* pos_map;
   int32_t* m_dev;
   float4* lm_part;
+  float2* lm_spart;       // [T][V/128] sampled (score, id) per tile
+  float* smp_tau;         // [T] temperature of each LM-head row
+  int32_t* smp_ctr;       // [T][3] Philox counter words of each LM-head row
+  long long split_rows_cap;  // attention partial rows the workspace holds
 };
 
 static dg_status fail(dg_ctx* c, dg_status s, const std::string& msg) {
@@ -175,7 +181,7 @@ struct Carve {
   }
 };
 
-int lm_tiles(int vocab) { return (vocab + gemm_bn(EPI_LMSTATS) - 1) / gemm_bn(EPI_LMSTATS); }
+int lm_tiles(int vocab) { return (vocab + 127) / 128; }
 
 // Largest splits(n) * n over batches 1..max_canvases (attention partials).
 long long attn_split_rows(const dg_model_desc& d, int max_canvases) {
@@ -201,6 +207,12 @@ int router_splits(int K) {
 // Weight-streaming kernels when the expert matrices see few rows each (a
 // batch of a few canvases): on average at most 32 (token, expert) pairs per
 // expert, and K dimensions that are multiples of the streaming K chunk.
+// (token, expert) pairs per token: the top_k routed experts and the shared
+// experts (write-up Table 1: "+ 1 shared"), which every token uses with
+// weight 1; the shared expert is group n_experts of the expert matrices.
+int pairs_per_token(const dg_model_desc& d) { return d.top_k + d.n_shared_experts; }
+int expert_groups(const dg_model_desc& d) { return d.n_experts + d.n_shared_experts; }
+
 bool use_stream_moe(const dg_model_desc& d, int T) {
   const long long pairs = (long long)T * d.top_k;
   return pairs <= 32LL * d.n_experts && stream_moe_ok(d.hidden, d.expert_ffn);
@@ -209,26 +221,27 @@ bool use_stream_moe(const dg_model_desc& d, int T) {
 // Workspace of the MoE pipeline for T tokens.
 size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   Carve cv;
-  const long long pairs = (long long)T * d.top_k;
+  const long long pairs = (long long)T * pairs_per_token(d);
+  const int EG = expert_groups(d);
   const int nc = permute_chunks((int)pairs);
   // slots per expert for the streaming path: every T it is taken for
   // (a token picks an expert at most once, so T slots always suffice)
   const int cap = stream_moe_ok(d.hidden, d.expert_ffn)
                       ? (int)std::min<long long>(T, 32LL * d.n_experts / d.top_k)
                       : 0;
-  const long long slots = (long long)d.n_experts * cap;
+  const long long slots = (long long)EG * cap;
   const size_t o_rl = cv.take((size_t)kRouterSlabs * T * d.n_experts * 4);
   const size_t o_ri = cv.take((size_t)pairs * 4);
   const size_t o_rw = cv.take((size_t)pairs * 4);
-  const size_t o_cc = cv.take((size_t)nc * d.n_experts * 4);
+  const size_t o_cc = cv.take((size_t)nc * EG * 4);
   const size_t o_lr = cv.take((size_t)pairs * 4);
-  const size_t o_cb = cv.take((size_t)nc * d.n_experts * 4);
-  const size_t o_of = cv.take((size_t)(d.n_experts + 1) * 4);
-  const size_t o_to = cv.take((size_t)(d.n_experts + 1) * 4);
+  const size_t o_cb = cv.take((size_t)nc * EG * 4);
+  const size_t o_of = cv.take((size_t)(EG + 1) * 4);
+  const size_t o_to = cv.take((size_t)(EG + 1) * 4);
   const size_t o_pm = cv.take((size_t)pairs * 4);
   const size_t o_ac = cv.take((size_t)std::max(pairs, slots) * d.expert_ffn * 2);
   const size_t o_y = cv.take((size_t)pairs * d.hidden * 4);
-  const size_t o_cn = cv.take((size_t)d.n_experts * 4);
+  const size_t o_cn = cv.take((size_t)EG * 4);
   const size_t o_sp = cv.take((size_t)slots * 4);
   const size_t o_sw = cv.take((size_t)slots * 4);
   const size_t o_st = cv.take((size_t)(slots + kSlotPad) * 4);
@@ -268,6 +281,9 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
   const size_t o_pm = cv.take(T * 4);
   const size_t o_md = cv.take(4);
   const size_t o_lm = cv.take(T * lm_tiles(d.vocab) * 16);
+  const size_t o_sp = cv.take(T * lm_tiles(d.vocab) * 8);
+  const size_t o_tau = cv.take(T * 4);
+  const size_t o_ctr = cv.take(T * 12);
   const size_t o_moe = cv.take(moe_layout(d, (int)T, nullptr, nullptr));
   if (c) {
     char* w = c->ws;
@@ -281,6 +297,10 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->pos_map = (int32_t*)(w + o_pm);
     c->m_dev = (int32_t*)(w + o_md);
     c->lm_part = (float4*)(w + o_lm);
+    c->lm_spart = (float2*)(w + o_sp);
+    c->smp_tau = (float*)(w + o_tau);
+    c->smp_ctr = (int32_t*)(w + o_ctr);
+    c->split_rows_cap = split_rows;
     moe_layout(d, (int)T, w + o_moe, &c->moe);
   }
   return cv.off;
@@ -303,6 +323,11 @@ std::string check_desc(const dg_model_desc* d) {
   if (!(d->rms_eps >= 0.f)) return "rms_eps must be >= 0";
   if (d->expert_dtype != DG_BF16 && d->expert_dtype != DG_FP8_E4M3)
     return "expert_dtype must be DG_BF16 or DG_FP8_E4M3";
+  if (d->canvas_len < 0 || d->canvas_len > DG_CANVAS)
+    return "canvas_len must be in 0..256 (0: 256)";
+  if (d->n_shared_experts < 0 || d->n_shared_experts > 1 ||
+      d->n_experts + d->n_shared_experts > 256)
+    return "n_shared_experts must be 0 or 1 (and n_experts + shared <= 256)";
   return "";
 }
 
@@ -336,19 +361,25 @@ GemmArgs gemm_dense(const uint16_t* A, int M, int K, const void* W, int N,
 int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi); }
 
 
-// The LM head streams the tied embedding once per 128 rows; beyond 256 rows
-// the tiled kernel reuses it better.
-bool use_stream_lm(int rows, int hidden) {
-  return rows <= 256 && stream_lm_ok(hidden);
-}
+// The LM head streams the tied embedding once per pass of up to 128 rows
+// (k_stream.hip); above 128 rows the large-tile kernel (k_mm.hip) reads it
+// once per 256 rows at a higher MFMA rate.  Both write one partial per row
+// and 128 vocabulary rows.  When the row count is on the device (the
+// uncommitted rows of a step) both are launched and each runs only for the
+// row counts it takes.
+constexpr int kLmStreamRows = 128;
 
-// Run the LM head with the vocabulary statistics epilogue; returns the
-// number of partials per row written to part.
+// smp: temperature sampling (EPI_LMSAMPLE, see LmSample) or nullptr.
 hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
                        int hidden, const void* embed, int vocab, float4* part,
                        float* logits, const int32_t* row_map, int* n_tiles,
-                       hipStream_t s) {
-  if (use_stream_lm(rows_max, hidden)) {
+                       hipStream_t s, const LmSample* smp = nullptr) {
+  *n_tiles = (vocab + 127) / 128;
+  const int epi = smp ? EPI_LMSAMPLE : EPI_LMSTATS;
+  const bool stream_ok = stream_lm_ok(hidden) && stream_rows_per_wg() == 128;
+  const bool use_stream = stream_ok && (m_dev || rows_max <= kLmStreamRows);
+  const bool use_mm = !stream_ok || rows_max > kLmStreamRows;
+  if (use_stream) {
     StreamArgs a;
     memset(&a, 0, sizeof(a));
     a.X = xh;
@@ -359,20 +390,24 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
     a.N = vocab;
     a.K = hidden;
     a.part = part;
-    a.n_tiles = (vocab + stream_rows_per_wg() - 1) / stream_rows_per_wg();
+    a.n_tiles = *n_tiles;
     a.logits = logits;
     a.row_map = row_map;
-    *n_tiles = a.n_tiles;
-    return launch_stream(EPI_LMSTATS, false, a, 1, s);
+    a.rows_le = use_mm ? kLmStreamRows : 0;
+    if (smp) a.smp = *smp;
+    hipError_t e = launch_stream(epi, false, a, 1, s);
+    if (e != hipSuccess) return e;
   }
+  if (!use_mm) return hipSuccess;
   GemmArgs g = gemm_dense(xh, rows_max, hidden, embed, vocab, nullptr, 0);
   g.M_dev = m_dev;
+  g.rows_gt = use_stream ? kLmStreamRows : 0;
   g.part = part;
-  g.n_tiles = (vocab + gemm_bn(EPI_LMSTATS) - 1) / gemm_bn(EPI_LMSTATS);
+  g.n_tiles = *n_tiles;
   g.logits = logits;
   g.row_map = row_map;
-  *n_tiles = g.n_tiles;
-  return launch_gemm(EPI_LMSTATS, false, g, grid_m_dense(rows_max, EPI_LMSTATS), s);
+  if (smp) g.smp = *smp;
+  return launch_mm(epi, false, g, (rows_max + mm_bm() - 1) / mm_bm(), s);
 }
 
 // MoE FFN on xh [T, H] bf16: y mixture added into x (if x) and/or stored
@@ -388,8 +423,9 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
                    uint16_t* next_xh = nullptr, float* next_copy = nullptr,
                    const int32_t* next_row = nullptr, bool counts_zeroed = false) {
   const int H = d.hidden, E = d.n_experts, k = d.top_k, F = d.expert_ffn;
+  const int S = d.n_shared_experts, K = k + S, EG = E + S;
   const bool w8 = d.expert_dtype == DG_FP8_E4M3;
-  const int pairs = T * k;
+  const int pairs = T * K;
   hipError_t e;
   GemmArgs r = gemm_dense(xh, T, H, w.w_router, E, b.rlogits, E);
   r.splits = router_splits(H);
@@ -403,11 +439,12 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     // its expert (fixed rows e*cap + i), so a GEMM workgroup finds its
     // tokens with one lookup and no prefix sum.
     if (T > b.cap) return hipErrorInvalidValue;
-    if (!counts_zeroed && (e = launch_zero_i32(b.counts, E, s)) != hipSuccess) return e;
+    if (!counts_zeroed && (e = launch_zero_i32(b.counts, EG, s)) != hipSuccess) return e;
     {
       ProfScope ps(prof, 6);
       if ((e = launch_topk_slots(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, b.counts,
-                                 b.cap, b.slot_pair, b.slot_w, b.slot_tok, s)) != hipSuccess)
+                                 b.cap, b.slot_pair, b.slot_w, b.slot_tok, s, S)) !=
+          hipSuccess)
         return e;
     }
     if (counts &&
@@ -433,7 +470,7 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     gu.ffn = F;
     {
       ProfScope ps(prof, 8);
-      if ((e = launch_stream(EPI_SWIGLU, w8, gu, E, s)) != hipSuccess) return e;
+      if ((e = launch_stream(EPI_SWIGLU, w8, gu, EG, s)) != hipSuccess) return e;
     }
     StreamArgs dn;
     memset(&dn, 0, sizeof(dn));
@@ -453,63 +490,94 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     dn.row_scale = b.slot_w;
     {
       ProfScope ps(prof, 9);
-      if ((e = launch_stream(EPI_DOWN, w8, dn, E, s)) != hipSuccess) return e;
+      if ((e = launch_stream(EPI_DOWN, w8, dn, EG, s)) != hipSuccess) return e;
     }
     ProfScope ps10(prof, 10);
     if (next_g)
-      return launch_unpermute_norm(b.y, T, k, H, x, moe_out, next_g, d.rms_eps,
+      return launch_unpermute_norm(b.y, T, K, H, x, moe_out, next_g, d.rms_eps,
                                    next_xh, next_copy, next_row, s);
-    return launch_unpermute(b.y, T, k, H, x, moe_out, s);
+    return launch_unpermute(b.y, T, K, H, x, moe_out, s);
   }
   {
     ProfScope ps(prof, 6);
-    if ((e = launch_topk(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, s)) != hipSuccess) return e;
-  }
-  {
-    ProfScope ps(prof, 7);
-    if ((e = launch_permute(b.ridx, pairs, E, kGroupBM, b.chunk_counts,
-                            b.local_rank, b.chunk_base, b.offsets,
-                            b.tile_offsets, counts, b.perm, s)) != hipSuccess)
+    if ((e = launch_topk(b.rlogits, T, E, k, r.splits, b.ridx, b.rw, s, S)) != hipSuccess)
       return e;
   }
-  const int grid_m = (pairs + kGroupBM - 1) / kGroupBM + std::min(E, pairs);
+  // experts holding a few hundred rows each take the large-tile kernel
+  // (256-row tiles), fewer the 64-row tiles
+  const bool big = (long long)T * k >= 192LL * E;
+  const int bm = big ? mm_bm() : kGroupBM;
+  {
+    ProfScope ps(prof, 7);
+    if ((e = launch_permute(b.ridx, pairs, EG, bm, b.chunk_counts,
+                            b.local_rank, b.chunk_base, b.offsets,
+                            b.tile_offsets, nullptr, b.perm, s)) != hipSuccess)
+      return e;
+    if (counts &&
+        (e = launch_counts_from_offsets(b.offsets, E, counts, s)) != hipSuccess)
+      return e;
+  }
+  const int grid_m = (pairs + bm - 1) / bm + std::min(EG, pairs);
   GemmArgs gu = gemm_dense(xh, pairs, H, w.w_gate_up, 2 * F, b.act, F);
   gu.a_map = b.perm;
-  gu.a_map_div = k;
+  gu.a_map_div = K;
   gu.b_group_stride = (long long)2 * F * H;
   gu.b_scale = w.gate_up_scale;
   gu.scale_rows = 2 * F;
-  gu.n_groups = E;
+  gu.n_groups = EG;
   gu.group_offsets = b.offsets;
   gu.tile_offsets = b.tile_offsets;
   gu.ffn = F;
   {
     ProfScope ps(prof, 8);
-    if ((e = launch_gemm(EPI_SWIGLU, w8, gu, grid_m, s)) != hipSuccess) return e;
+    if ((e = big ? launch_mm(EPI_SWIGLU, w8, gu, grid_m, s)
+                 : launch_gemm(EPI_SWIGLU, w8, gu, grid_m, s)) != hipSuccess)
+      return e;
   }
   GemmArgs dn = gemm_dense(b.act, pairs, F, w.w_down, H, b.y, H);
   dn.b_group_stride = (long long)H * F;
   dn.b_scale = w.down_scale;
   dn.scale_rows = H;
-  dn.n_groups = E;
+  dn.n_groups = EG;
   dn.group_offsets = b.offsets;
   dn.tile_offsets = b.tile_offsets;
   dn.c_map = b.perm;
   dn.row_scale = b.rw;
   {
     ProfScope ps(prof, 9);
-    if ((e = launch_gemm(EPI_DOWN, w8, dn, grid_m, s)) != hipSuccess) return e;
+    if ((e = big ? launch_mm(EPI_DOWN, w8, dn, grid_m, s)
+                 : launch_gemm(EPI_DOWN, w8, dn, grid_m, s)) != hipSuccess)
+      return e;
   }
   ProfScope ps10(prof, 10);
   if (next_g)
-    return launch_unpermute_norm(b.y, T, k, H, x, moe_out, next_g, d.rms_eps,
+    return launch_unpermute_norm(b.y, T, K, H, x, moe_out, next_g, d.rms_eps,
                                  next_xh, next_copy, next_row, s);
-  return launch_unpermute(b.y, T, k, H, x, moe_out, s);
+  return launch_unpermute(b.y, T, K, H, x, moe_out, s);
+}
+
+// Copy of the routed experts' (idx, w) [T, k] out of the [T, k + S] pairs.
+hipError_t copy_routing(void* dst, const void* src, int T, int k, int K, hipStream_t s) {
+  if (k == K) return hipMemcpyAsync(dst, src, (size_t)T * k * 4, hipMemcpyDeviceToDevice, s);
+  return hipMemcpy2DAsync(dst, (size_t)k * 4, src, (size_t)K * 4, (size_t)k * 4, T,
+                          hipMemcpyDeviceToDevice, s);
 }
 
 const MoeBufs& ctx_moe_bufs(const dg_ctx* c) { return c->moe; }
 
-dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt, bool distinct) {
+// The canvases of one request (multi-canvas sampling) must be contiguous in
+// the batch, in block order; returns false otherwise.  vis0[b] = the first
+// canvas of b's request in the batch.
+bool canvas_groups(int n, const int* req, int* vis0) {
+  for (int b = 0; b < n; ++b) {
+    vis0[b] = (b > 0 && req[b - 1] == req[b]) ? vis0[b - 1] : b;
+    for (int q = 0; q < vis0[b]; ++q)
+      if (req[q] == req[b]) return false;
+  }
+  return true;
+}
+
+dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt) {
   if (!bt) return fail(c, DG_ERR_INVALID_ARG, "batch is NULL");
   if (bt->n < 1 || bt->n > c->max_canvases)
     return fail(c, DG_ERR_CAPACITY, "batch size outside 1..max_canvases");
@@ -519,11 +587,11 @@ dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt, bool distinct) {
     const int r = bt->req[b];
     if (r < 0 || r >= c->max_requests)
       return fail(c, DG_ERR_INVALID_ARG, "request slot out of range");
-    if (distinct)
-      for (int q = 0; q < b; ++q)
-        if (bt->req[q] == r)
-          return fail(c, DG_ERR_INVALID_ARG, "request slots must be distinct");
   }
+  int vis0[DG_MAX_BATCH];
+  if (!canvas_groups(bt->n, bt->req, vis0))
+    return fail(c, DG_ERR_INVALID_ARG,
+                "the canvases of one request must be contiguous in the batch");
   return DG_OK;
 }
 
@@ -535,10 +603,10 @@ dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt, bool distinct) {
 // layer's canvas K/V into the cache first, causal attention, and stop after
 // the K/V of the last layer.
 dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
-                    bool commit, const dg_capture* cap) {
+                    bool commit, const dg_capture* cap, int C = DG_CANVAS) {
   const dg_model_desc& d = c->d;
   const dg_layer_weights& w = c->layers[l];
-  const int T = n * DG_CANVAS, H = d.hidden, D = d.head_dim;
+  const int T = n * C, H = d.hidden, D = d.head_dim;
   const int Hq = d.n_q_heads, Hkv = d.n_kv_heads;
   const int qkvN = (Hq + 2 * Hkv) * D;
   const long long head_stride = (long long)c->max_kv_len * D;
@@ -549,17 +617,22 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
   uint16_t* kc = c->k_cache + l * layer_stride;
   uint16_t* vc = c->v_cache + l * layer_stride;
+  int vis0[DG_MAX_BATCH];
+  canvas_groups(n, req, vis0);   // (checked by the caller)
   if (commit) {
+    // canvas b is appended after its request's earlier canvases of the batch
+    int row0[DG_MAX_BATCH];
+    for (int b = 0; b < n; ++b) row0[b] = plen[b] + (b - vis0[b]) * C;
     KRUN(c, 15, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
-                               DG_CANVAS, Hkv, D, kc, vc, req_stride,
-                               head_stride, req, plen, s));
+                               C, Hkv, D, kc, vc, req_stride,
+                               head_stride, req, row0, s));
     if (l == d.n_layers - 1) return DG_OK;
   }
   AttnArgs aa;
   memset(&aa, 0, sizeof(aa));
   aa.qkv = c->qkv;
   aa.ldqkv = qkvN;
-  aa.C = DG_CANVAS;
+  aa.C = C;
   aa.Hq = Hq;
   aa.Hkv = Hkv;
   aa.D = D;
@@ -570,11 +643,17 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   for (int b = 0; b < n; ++b) {
     aa.req[b] = req[b];
     aa.plen[b] = plen[b];
+    aa.vis0[b] = vis0[b];
   }
   aa.n = n;
   int max_keys = 0;
-  for (int b = 0; b < n; ++b) max_keys = std::max(max_keys, plen[b] + DG_CANVAS);
-  aa.splits = attention_auto_splits(n, DG_CANVAS, Hq, Hkv, max_keys);
+  for (int b = 0; b < n; ++b)
+    max_keys = std::max(max_keys, plen[b] + (b - vis0[b] + 1) * C);
+  aa.splits = attention_auto_splits(n, C, Hq, Hkv, max_keys);
+  // (shorter canvases than the workspace was sized for may ask for more
+  // splits than its partials hold)
+  aa.splits = (int)std::max<long long>(
+      1, std::min<long long>(aa.splits, c->split_rows_cap / ((long long)n * Hq * C)));
   aa.causal = commit ? 1 : 0;
   aa.out = c->attn;
   aa.opart = c->opart;
@@ -597,12 +676,11 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
                     c->xh, next_copy, last ? c->pos_map : nullptr, true));
   if (cap) {
     const size_t tk = (size_t)T * d.top_k;
+    const int K = pairs_per_token(d);
     if (cap->route_idx)
-      HIPCHK(c, hipMemcpyAsync(cap->route_idx + l * tk, mb.ridx, tk * 4,
-                               hipMemcpyDeviceToDevice, s));
+      HIPCHK(c, copy_routing(cap->route_idx + l * tk, mb.ridx, T, d.top_k, K, s));
     if (cap->route_w)
-      HIPCHK(c, hipMemcpyAsync(cap->route_w + l * tk, mb.rw, tk * 4,
-                               hipMemcpyDeviceToDevice, s));
+      HIPCHK(c, copy_routing(cap->route_w + l * tk, mb.rw, T, d.top_k, K, s));
     if (cap->router_logits)
       HIPCHK(c, hipMemcpyAsync(cap->router_logits + (size_t)l * T * d.n_experts,
                                mb.rlogits, (size_t)T * d.n_experts * 4,
@@ -686,9 +764,10 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   if (max_requests < 1 || max_kv_len < DG_CANVAS)
     return fail(nullptr, DG_ERR_INVALID_ARG,
                 "max_requests must be >= 1 and max_kv_len >= 256");
-  if (max_canvases < 1 || max_canvases > DG_MAX_BATCH || max_canvases > max_requests)
-    return fail(nullptr, DG_ERR_INVALID_ARG,
-                "max_canvases must be in 1..min(64, max_requests)");
+  // (several canvases may belong to one request, so max_canvases may
+  // exceed max_requests)
+  if (max_canvases < 1 || max_canvases > DG_MAX_BATCH)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "max_canvases must be in 1..64");
   if (!k_cache || !v_cache || !workspace)
     return fail(nullptr, DG_ERR_INVALID_ARG, "cache and workspace must not be NULL");
   if (((uintptr_t)workspace % kAlign) != 0)
@@ -699,6 +778,7 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   dg_ctx* c = new (std::nothrow) dg_ctx();
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "out of host memory");
   c->d = *desc;
+  c->C = desc->canvas_len ? desc->canvas_len : DG_CANVAS;
   c->embed = (const uint16_t*)weights->embed;
   c->final_norm = weights->final_norm;
   c->layers.assign(weights->layers, weights->layers + desc->n_layers);
@@ -772,16 +852,32 @@ int32_t dg_kv_len(const dg_ctx* c, int32_t req) {
 dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
                         const int32_t* tokens, const void* k, const void* v) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
-  if (tokens) {
-    if (k || v) return fail(c, DG_ERR_INVALID_ARG, "give either tokens or k/v");
-    return fail(c, DG_ERR_UNSUPPORTED, "token-mode prefill is not provided");
-  }
-  if (!k || !v) return fail(c, DG_ERR_INVALID_ARG, "k and v must not be NULL");
+  if (tokens && (k || v)) return fail(c, DG_ERR_INVALID_ARG, "give either tokens or k/v");
+  if (!tokens && (!k || !v)) return fail(c, DG_ERR_INVALID_ARG, "k and v must not be NULL");
   if (req < 0 || req >= c->max_requests)
     return fail(c, DG_ERR_INVALID_ARG, "request slot out of range");
   if (n < 0 || n > c->max_kv_len)
     return fail(c, DG_ERR_CAPACITY, "prefix longer than max_kv_len");
   const dg_model_desc& d = c->d;
+  if (tokens) {
+    // token mode: the causal encode of the commit, over chunks of up to 256
+    // prompt tokens; chunk i attends to the cache rows the chunks before it
+    // wrote and causally within itself, so the result is the causal encode
+    // of the whole prompt
+    int plen = 0;
+    for (int off = 0; off < n; off += DG_CANVAS) {
+      const int C = std::min(DG_CANVAS, n - off);
+      KRUN(c, 0, launch_embed_norm(tokens + off, C, c->embed, d.vocab, d.hidden, c->x,
+                                   c->layers[0].attn_norm, d.rms_eps, c->xh, c->stream));
+      for (int l = 0; l < d.n_layers; ++l) {
+        const dg_status st = run_layer(c, l, 1, &req, &plen, true, nullptr, C);
+        if (st != DG_OK) return st;
+      }
+      plen += C;
+    }
+    c->kv_len[req] = n;
+    return DG_OK;
+  }
   const long long head_stride = (long long)c->max_kv_len * d.head_dim;
   const long long req_stride = (long long)d.n_kv_heads * head_stride;
   const long long layer_stride = (long long)c->max_requests * req_stride;
@@ -802,12 +898,18 @@ dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
 dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
                           const dg_step_out* out) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
-  dg_status st = check_batch(c, bt, false);
+  dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
   if (!out || !out->entropy || !out->lse || !out->argmax)
     return fail(c, DG_ERR_INVALID_ARG, "step outputs must not be NULL");
+  const dg_sampling* smp = out->sampling;
+  if (smp) {
+    if (!smp->sample) return fail(c, DG_ERR_INVALID_ARG, "sampling->sample is NULL");
+    if (!(smp->tau0 >= 0.f) || !std::isfinite(smp->tau0) || smp->budget < 0)
+      return fail(c, DG_ERR_INVALID_ARG, "need finite tau0 >= 0 and budget >= 0");
+  }
   const dg_model_desc& d = c->d;
-  const int n = bt->n, T = n * DG_CANVAS, H = d.hidden;
+  const int n = bt->n, C = c->C, T = n * C, H = d.hidden;
   int req[DG_MAX_BATCH], plen[DG_MAX_BATCH];
   for (int b = 0; b < n; ++b) {
     req[b] = bt->req[b];
@@ -818,14 +920,26 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
                                c->layers[0].attn_norm, d.rms_eps, c->xh, s, bt->committed,
                                c->row_map, c->m_dev, c->pos_map));
   for (int l = 0; l < d.n_layers; ++l) {
-    st = run_layer(c, l, n, req, plen, false, out->capture);
+    st = run_layer(c, l, n, req, plen, false, out->capture, C);
     if (st != DG_OK) return st;
   }
   int n_tiles = 0;
+  LmSample ls = {};
+  if (smp) {
+    KRUN(c, 13, launch_sample_rows(c->row_map, c->m_dev, T, bt->step, C, smp->tau0,
+                                   smp->budget, c->smp_tau, c->smp_ctr, s));
+    ls.tau = c->smp_tau;
+    ls.ctr = c->smp_ctr;
+    ls.key0 = (uint32_t)smp->seed;
+    ls.key1 = (uint32_t)(smp->seed >> 32);
+    ls.spart = c->lm_spart;
+  }
   KRUN(c, 12, run_lm_head(c->xh, T, c->m_dev, H, c->embed, d.vocab, c->lm_part,
-                          out->logits, c->row_map, &n_tiles, s));
+                          out->logits, c->row_map, &n_tiles, s, smp ? &ls : nullptr));
   KRUN(c, 13, launch_lm_merge(c->lm_part, n_tiles, c->m_dev, T, c->row_map,
-                            out->entropy, out->lse, out->argmax, s));
+                              out->entropy, out->lse, out->argmax, s,
+                              smp ? c->smp_tau : nullptr, smp ? c->lm_spart : nullptr,
+                              smp ? smp->sample : nullptr));
   return DG_OK;
 }
 
@@ -834,7 +948,7 @@ dg_status dg_eb_select(dg_ctx* c, const dg_canvas_batch* bt,
                        const float* gamma, int32_t step_cap, int32_t refine,
                        int32_t* n_new, uint8_t* done) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
-  dg_status st = check_batch(c, bt, false);
+  dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
   if (!entropy || !argmax || !gamma || !n_new || !done)
     return fail(c, DG_ERR_INVALID_ARG, "sampler pointers must not be NULL");
@@ -842,29 +956,31 @@ dg_status dg_eb_select(dg_ctx* c, const dg_canvas_batch* bt,
     return fail(c, DG_ERR_INVALID_ARG, "step_cap must be in 1..65535");
   KRUN(c, 14, launch_eb_select(bt->n, entropy, argmax, bt->committed, bt->tokens,
                              bt->step, gamma, step_cap, refine, n_new, done,
-                             c->stream));
+                             c->stream, c->C));
   return DG_OK;
 }
 
 dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
-  dg_status st = check_batch(c, bt, true);
+  dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
-  const int n = bt->n, T = n * DG_CANVAS;
-  int req[DG_MAX_BATCH], plen[DG_MAX_BATCH];
+  const int n = bt->n, C = c->C, T = n * C;
+  int req[DG_MAX_BATCH], plen[DG_MAX_BATCH], vis0[DG_MAX_BATCH];
+  canvas_groups(n, bt->req, vis0);
   for (int b = 0; b < n; ++b) {
     req[b] = bt->req[b];
     plen[b] = c->kv_len[req[b]];
-    if (plen[b] + DG_CANVAS > c->max_kv_len)
-      return fail(c, DG_ERR_CAPACITY, "KV cache full: kv_len + 256 > max_kv_len");
+    if (plen[b] + (b - vis0[b] + 1) * C > c->max_kv_len)
+      return fail(c, DG_ERR_CAPACITY,
+                  "KV cache full: kv_len + canvas_len x canvases > max_kv_len");
   }
   KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x,
                                c->layers[0].attn_norm, c->d.rms_eps, c->xh, c->stream));
   for (int l = 0; l < c->d.n_layers; ++l) {
-    st = run_layer(c, l, n, req, plen, true, nullptr);
+    st = run_layer(c, l, n, req, plen, true, nullptr, C);
     if (st != DG_OK) return st;
   }
-  for (int b = 0; b < n; ++b) c->kv_len[req[b]] += DG_CANVAS;
+  for (int b = 0; b < n; ++b) c->kv_len[req[b]] += C;  // per canvas
   return DG_OK;
 }
 
@@ -932,6 +1048,10 @@ dg_status dg_op_canvas_attention(const void* qkv, int32_t n, int32_t canvas_len,
     if (prefix_len[b] < 0 || prefix_len[b] > max_kv_len)
       return fail(nullptr, DG_ERR_CAPACITY, "prefix_len outside 0..max_kv_len");
   }
+  int vis0[DG_MAX_BATCH];
+  if (!canvas_groups(n, req, vis0))
+    return fail(nullptr, DG_ERR_INVALID_ARG,
+                "the canvases of one request must be contiguous in the batch");
   const size_t need = dg_op_attention_workspace_bytes(n, canvas_len, n_q_heads,
                                                       n_kv_heads, head_dim, kv_splits);
   if (workspace_bytes < need || (need > kAlign && !workspace))
@@ -951,10 +1071,12 @@ dg_status dg_op_canvas_attention(const void* qkv, int32_t n, int32_t canvas_len,
   for (int b = 0; b < n; ++b) {
     aa.req[b] = req[b];
     aa.plen[b] = prefix_len[b];
+    aa.vis0[b] = vis0[b];
   }
   aa.n = n;
   int max_keys = 0;
-  for (int b = 0; b < n; ++b) max_keys = std::max(max_keys, prefix_len[b] + canvas_len);
+  for (int b = 0; b < n; ++b)
+    max_keys = std::max(max_keys, prefix_len[b] + (b - vis0[b] + 1) * canvas_len);
   aa.splits = kv_splits > 0 ? kv_splits
                             : attention_auto_splits(n, canvas_len, n_q_heads, n_kv_heads,
                                                     max_keys);
@@ -997,8 +1119,8 @@ dg_status dg_op_moe(const dg_model_desc* desc, const dg_layer_weights* w,
     return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
   const std::string le = check_layer(*desc, *w, true);
   if (!le.empty()) return fail(nullptr, DG_ERR_INVALID_ARG, le);
-  if (tokens < 1 || (long long)tokens * desc->top_k > (1LL << 24))
-    return fail(nullptr, DG_ERR_SHAPE, "tokens outside 1..2^24/top_k");
+  if (tokens < 1 || (long long)tokens * pairs_per_token(*desc) > (1LL << 24))
+    return fail(nullptr, DG_ERR_SHAPE, "tokens outside 1..2^24/(top_k + shared)");
   if (((uintptr_t)workspace % kAlign) != 0)
     return fail(nullptr, DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < moe_layout(*desc, tokens, nullptr, nullptr))
@@ -1008,11 +1130,11 @@ dg_status dg_op_moe(const dg_model_desc* desc, const dg_layer_weights* w,
   hipStream_t s = (hipStream_t)stream;
   HIPCHK(nullptr, run_moe(*desc, *w, (const uint16_t*)xhat, tokens, b, nullptr,
                           y, counts, s));
-  const size_t tk = (size_t)tokens * desc->top_k;
+  const int K = pairs_per_token(*desc);
   if (route_idx)
-    HIPCHK(nullptr, hipMemcpyAsync(route_idx, b.ridx, tk * 4, hipMemcpyDeviceToDevice, s));
+    HIPCHK(nullptr, copy_routing(route_idx, b.ridx, tokens, desc->top_k, K, s));
   if (route_w)
-    HIPCHK(nullptr, hipMemcpyAsync(route_w, b.rw, tk * 4, hipMemcpyDeviceToDevice, s));
+    HIPCHK(nullptr, copy_routing(route_w, b.rw, tokens, desc->top_k, K, s));
   return DG_OK;
 }
 
@@ -1039,6 +1161,41 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                               &n_tiles, s));
   HIPCHK(nullptr, launch_lm_merge((const float4*)workspace, n_tiles, nullptr, m,
                                   nullptr, entropy, lse, argmax, s));
+  return DG_OK;
+}
+
+size_t dg_op_lmhead_sample_workspace_bytes(int32_t m, int32_t vocab) {
+  if (m < 1 || vocab < 1) return 0;
+  return align_up((size_t)m * lm_tiles(vocab) * 16) +
+         align_up((size_t)m * lm_tiles(vocab) * 8);
+}
+
+dg_status dg_op_lmhead_sample(const void* xhat, int32_t m, int32_t hidden,
+                              const void* embed, int32_t vocab, const float* tau,
+                              const int32_t* ctr, uint64_t seed, float* entropy,
+                              float* lse, int32_t* argmax, int32_t* sample,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!xhat || !embed || !tau || !ctr || !entropy || !lse || !argmax || !sample ||
+      !workspace)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (m < 1 || vocab < 1 || hidden < 64 || hidden % 64)
+    return fail(nullptr, DG_ERR_SHAPE, "need m >= 1, vocab >= 1, hidden a multiple of 64");
+  if (workspace_bytes < dg_op_lmhead_sample_workspace_bytes(m, vocab))
+    return fail(nullptr, DG_ERR_CAPACITY, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  float4* part = (float4*)workspace;
+  LmSample ls = {};
+  ls.tau = tau;
+  ls.ctr = ctr;
+  ls.key0 = (uint32_t)seed;
+  ls.key1 = (uint32_t)(seed >> 32);
+  ls.spart = (float2*)((char*)workspace + align_up((size_t)m * lm_tiles(vocab) * 16));
+  int n_tiles = 0;
+  HIPCHK(nullptr, run_lm_head((const uint16_t*)xhat, m, nullptr, hidden, embed,
+                              vocab, part, nullptr, nullptr, &n_tiles, s, &ls));
+  HIPCHK(nullptr, launch_lm_merge(part, n_tiles, nullptr, m, nullptr, entropy, lse,
+                                  argmax, s, tau, ls.spart, sample));
   return DG_OK;
 }
 
@@ -1112,7 +1269,7 @@ dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
   return DG_OK;
 }
 
-dg_status dg_op_eb_select(int32_t n, const float* entropy,
+dg_status dg_op_eb_select(int32_t n, int32_t canvas_len, const float* entropy,
                           const int32_t* argmax, uint8_t* committed,
                           int32_t* tokens, int32_t* step, const float* gamma,
                           int32_t step_cap, int32_t refine, int32_t* n_new,
@@ -1123,9 +1280,12 @@ dg_status dg_op_eb_select(int32_t n, const float* entropy,
   if (n < 1 || n > 65535) return fail(nullptr, DG_ERR_CAPACITY, "n outside 1..65535");
   if (step_cap < 1 || step_cap > 65535)
     return fail(nullptr, DG_ERR_INVALID_ARG, "step_cap must be in 1..65535");
+  if (canvas_len < 0 || canvas_len > DG_CANVAS)
+    return fail(nullptr, DG_ERR_SHAPE, "canvas_len outside 0..256");
   HIPCHK(nullptr, launch_eb_select(n, entropy, argmax, committed, tokens, step,
                                    gamma, step_cap, refine, n_new, done,
-                                   (hipStream_t)stream));
+                                   (hipStream_t)stream,
+                                   canvas_len ? canvas_len : DG_CANVAS));
   return DG_OK;
 }
 

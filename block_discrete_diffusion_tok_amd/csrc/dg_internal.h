@@ -113,6 +113,51 @@ __host__ __device__ inline long long pack_block_offset(int rb, int kb, int K, in
 hipError_t launch_pack(const void* src, int groups, int rows, int cols, int esz,
                        void* dst, hipStream_t s);
 
+// ------------------------------------------------------------------ sampling
+// Temperature sampling in the LM head's epilogue (rows are the LM head's
+// token rows): the statistics are taken of z / tau (tau > 0) and the
+// sampled token is argmax_v (z_v / tau + g_v), g_v = -ln(-ln u_v) with u_v
+// from Philox4x32-10 (counter (v / 4, ctr[row]), key (key0, key1), output
+// v % 4, top 24 bits + 1/2 times 2^-24).  tau <= 0: statistics of the raw
+// logits and the argmax as the sample (the merge reports entropy 0).
+struct LmSample {
+  const float* tau;      // [rows] temperature of each row; nullptr: no sampling
+  const int32_t* ctr;    // [rows][3] counter words 1..3 (position, step, canvas)
+  uint32_t key0, key1;
+  float2* spart;         // [rows][n_tiles] (best score, its vocabulary id as bits)
+};
+
+// Philox4x32-10 (Salmon et al., SC 2011): 10 rounds of two 32x32->64-bit
+// products, the key advanced by the Weyl increments between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = c[0] * 0xD2511F53u, hi0 = __umulhi(c[0], 0xD2511F53u);
+    const uint32_t lo1 = c[2] * 0xCD9E8D57u, hi1 = __umulhi(c[2], 0xCD9E8D57u);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+// -ln(-ln u) of a Philox output word (u in (0, 1), exact in fp32)
+__device__ __forceinline__ float gumbel_of(uint32_t x) {
+  const float u = ((float)(x >> 8) + 0.5f) * 5.9604644775390625e-8f;
+  return -logf(-logf(u));
+}
+// Keep the better (score, id): larger score, lower id on ties.
+__device__ __forceinline__ void best_merge(float& g, int& gi, float g2, int gi2) {
+  if (g2 > g || (g2 == g && gi2 < gi)) {
+    g = g2;
+    gi = gi2;
+  }
+}
+
 // ------------------------------------------------------------------ launches
 // Every launcher returns hipSuccess or the launch error; shapes were checked
 // by the caller.
@@ -123,8 +168,10 @@ enum GemmEpi : int {
   EPI_ADD_F32 = 2,     // C fp32 [M, N] += acc
   EPI_SWIGLU = 3,      // act bf16 [rows, F] = silu(gate) * up
   EPI_DOWN = 4,        // y fp32 [pair, N] = w_pair * acc (scattered rows)
-  EPI_LMSTATS = 5      // per-row (max, sum exp, sum exp*(z-max), argmax)
+  EPI_LMSTATS = 5,     // per-row (max, sum exp, sum exp*(z-max), argmax)
+  EPI_LMSAMPLE = 6     // EPI_LMSTATS at the rows' temperatures + sampled tokens
 };
+constexpr bool epi_is_lm(int epi) { return epi == EPI_LMSTATS || epi == EPI_LMSAMPLE; }
 
 struct GemmArgs {
   const uint16_t* A;       // bf16 [rows, K]
@@ -152,6 +199,9 @@ struct GemmArgs {
   const int32_t* row_map;  // EPI_LMSTATS: logits row of each A row
   int splits;              // EPI_STORE_F32: K splits (gridDim.z), 0/1 = none;
   long long split_stride;  //   split z writes its own slab C + z * split_stride
+  int rows_gt;             // with M_dev: the launch does nothing unless
+                           //   *M_dev > rows_gt (another kernel takes fewer rows)
+  LmSample smp;            // EPI_LMSTATS: temperature sampling (smp.tau null: off)
 };
 
 // Tile sizes of the grouped GEMMs (rows of one expert are tiled by this).
@@ -161,6 +211,17 @@ hipError_t launch_gemm(int epi, bool w_e4m3, const GemmArgs& a, int grid_m,
                        hipStream_t s);
 int gemm_bn(int epi);   // BN of the instance used for an epilogue
 int gemm_bm(int epi);   // BM of the instance used for an epilogue
+
+// Large-tile GEMM (k_mm.hip): 256 weight rows x 256 token rows per
+// workgroup, for thousands of token rows (dense) or hundreds per group.
+// Same arguments and epilogues as launch_gemm, no K splits; grid_m counts
+// 256-row tiles (group tile offsets in units of mm_bm()).  EPI_LMSTATS
+// writes two partials per workgroup, one per 128 vocabulary rows, so a
+// row's partials are indexed like the streaming LM head's (n_tiles =
+// ceil(N / 128)).
+hipError_t launch_mm(int epi, bool w_e4m3, const GemmArgs& a, int grid_m, hipStream_t s);
+int mm_bm();
+int mm_bn();
 
 // Weight-streaming GEMM (few token rows per weight matrix); see k_stream.hip.
 struct StreamArgs {
@@ -190,6 +251,9 @@ struct StreamArgs {
   int n_tiles;
   float* logits;           // EPI_LMSTATS: optional [rows, N]
   const int32_t* row_map;  // EPI_LMSTATS: logits row of each token row
+  int rows_le;             // EPI_LMSTATS with M_dev: the launch does nothing
+                           //   unless *M_dev <= rows_le (0: no limit)
+  LmSample smp;            // EPI_LMSTATS: temperature sampling (smp.tau null: off)
 };
 // Epilogues EPI_LMSTATS (up to 128 token columns per pass), EPI_SWIGLU (128)
 // and EPI_DOWN (64).  K must satisfy stream_lm_ok / stream_moe_ok.
@@ -209,6 +273,9 @@ struct AttnArgs {
   long long head_stride;  // elements between KV heads (= max_kv_len * D)
   int req[DG_MAX_BATCH];
   int plen[DG_MAX_BATCH];
+  int vis0[DG_MAX_BATCH];  // first canvas of the batch canvas b also sees
+                           //   (b itself: none; canvases vis0..b-1 are the
+                           //   earlier blocks of b's request)
   int n;
   int splits;
   int causal;
@@ -232,8 +299,10 @@ hipError_t launch_rmsnorm(const float* x, int rows, int H, const float* g,
                           hipStream_t s, int32_t* zero = nullptr, int n_zero = 0);
 // logits: `splits` fp32 slabs [T, E] (partial sums over K) added in slab
 // order; with splits > 1 the sum is also written back to slab 0.
+// S = 0 or 1 shared experts: idx / w are [T, k + S] with rank k the shared
+// expert (id E, weight 1).
 hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
-                       float* w, hipStream_t s);
+                       float* w, hipStream_t s, int S = 0);
 // Top-k that also hands each (token, rank) pair a slot of its expert
 // (slot = atomicAdd(&counts[e], 1), counts zeroed beforehand; order within
 // an expert is arbitrary, cap >= T), records pair = t*k + r in
@@ -242,7 +311,7 @@ hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* 
 hipError_t launch_topk_slots(float* logits, int T, int E, int k, int splits,
                              int32_t* idx, float* w, int32_t* counts, int cap,
                              int32_t* slot_pair, float* slot_w, int32_t* slot_tok,
-                             hipStream_t s);
+                             hipStream_t s, int S = 0);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* chunk_counts, int32_t* local_rank,
@@ -250,6 +319,9 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* tile_offsets, int32_t* counts,
                           int32_t* perm, hipStream_t s);
 int permute_chunks(int n_pairs);
+// counts[e] = offsets[e + 1] - offsets[e], e < E
+hipError_t launch_counts_from_offsets(const int32_t* offsets, int E, int32_t* counts,
+                                      hipStream_t s);
 // x = E[tok] fused with the first RMSNorm (packed table).  With committed
 // given, one more workgroup meanwhile writes row_map[0..M) = the rows t with
 // committed[t] == 0 in increasing order, *m_dev = M and pos_map[t] (if
@@ -267,14 +339,27 @@ hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
                                  const int32_t* out_row, hipStream_t s);
 hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
                             float* moe_out, hipStream_t s);
+// With tau / spart / sample given: the rows' sampled tokens into sample,
+// entropy 0 where tau <= 0.
 hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* m_dev, int m_max,
                            const int32_t* row_map, float* entropy, float* lse,
-                           int32_t* argmax, hipStream_t s);
+                           int32_t* argmax, hipStream_t s,
+                           const float* tau = nullptr, const float2* spart = nullptr,
+                           int32_t* sample = nullptr);
+// Per LM-head row r < *m_dev (m_max without m_dev): the canvas position
+// t = row_map[r] (r without row_map), its canvas b = t / C and step
+// st = step[b]; tau[r] = tau0 (1 - st / budget) for budget > 0, tau0
+// otherwise, clamped at 0; ctr[r] = (t % C, st, b).
+hipError_t launch_sample_rows(const int32_t* row_map, const int32_t* m_dev, int m_max,
+                              const int32_t* step, int C, float tau0, int budget,
+                              float* tau, int32_t* ctr, hipStream_t s);
+// EB selection over n canvases of C <= 256 positions each.
 hipError_t launch_eb_select(int n, const float* entropy, const int32_t* argmax,
                             uint8_t* committed, int32_t* tokens, int32_t* step,
                             const float* gamma, int step_cap, int refine,
-                            int32_t* n_new, uint8_t* done, hipStream_t s);
+                            int32_t* n_new, uint8_t* done, hipStream_t s,
+                            int C = DG_CANVAS);
 hipError_t launch_kv_append(const uint16_t* qkv, int ldqkv, int col0_k,
                             int col0_v, int n, int C, int Hkv, int D,
                             uint16_t* kc, uint16_t* vc, long long req_stride,

@@ -1,26 +1,38 @@
 // Canvas attention: for each canvas, query head h and canvas position i,
 //   o = sum_j softmax_j(q . k_j / sqrt(D)) v_j
-// over the request's cached prefix keys followed by the canvas keys (all of
-// them, or j <= i in the causal encode pass), KV head h / (Hq / Hkv).
+// over the request's cached prefix keys, the keys of the request's earlier
+// canvases in the batch (multi-canvas sampling: earlier blocks are fully
+// visible, later ones not; model card feature list), then the canvas's own
+// keys (all of them, or j <= i in the causal encode pass), KV head
+// h / (Hq / Hkv) (write-up Figure 4 stages 2 and 3; model card "Model
+// Overview").
 //
-// One workgroup (8 waves) takes one KV head of one canvas, 128 query rows
-// (the G = Hq / Hkv query heads sharing that KV head x canvas positions) and
-// one contiguous range of 64-key tiles (KV split).  K and V tiles are staged
-// in double-buffered LDS and shared by all 128 rows; the next tile's global
-// loads are issued before the current tile's MFMAs, one barrier per tile.
-// Each wave computes S^T = K Q^T for its 16 query columns with bf16 MFMA
-// (16 columns per wave keeps registers low enough for two waves per SIMD,
-// which hides the LDS and MFMA latencies), so that every lane owns exactly one query
-// column: the running max / sum of the online softmax are per-lane scalars
-// and the rescale of the output accumulator is a per-lane multiply.  P^T is
-// taken straight from the S^T accumulators as the B operand of O^T = V^T P^T;
-// V is stored in LDS as key quads ([key/4][d][4]) so that the matching A
-// operand is two 8-byte reads.  P enters the MFMA as two bf16 terms,
-// P = hi + lo with hi = bf16(P) and lo = bf16(P - hi), so the probabilities
-// keep ~16 significant bits instead of 8: rounding P to a single bf16 adds a
-// relative error of ~2^-9 per weight, which survives the averaging over keys
-// at full size and moves router logits downstream by more than 1e-3.
-// Splits write (O / l, log2 l + max) partials that a second kernel merges
+// Work decomposition.  The G = Hq / Hkv query heads sharing a KV head give
+// G x C query rows per (canvas, KV head).  A workgroup (8 waves) takes
+// 128 * QB of them (each wave 16 * QB rows) and one contiguous range of
+// 64-key tiles (KV split); K and V tiles are staged in double-buffered LDS
+// and shared by all its rows, the next tile's global loads issued before
+// the current tile's MFMAs, one barrier per tile.  QB = 2 (256 rows per
+// workgroup) halves the K/V bytes each query row costs against QB = 1; the
+// workgroups that share one (canvas, KV head, split) are numbered so that
+// they run on the same XCD (workgroups are dealt to the 8 XCDs round-robin
+// by id), so their K/V tiles come from one L2.
+//
+// Per wave: S^T = K Q^T with bf16 MFMA 16x16x32 (K tile rows as the A
+// operand, read from LDS once per tile and used for all QB query blocks),
+// so that every lane owns one query column per block and 4 keys of each
+// 16-key block: the running max / sum of the online softmax are per-lane
+// scalars.  P^T is taken straight from the S^T accumulators (bf16) as the B
+// operand of O^T = V^T P^T; V is stored in LDS as key quads ([key/4][d][4])
+// so that the matching A operand is two 8-byte reads.  Scores are scaled
+// inside the exponent (exp2 of s * log2(e)/sqrt(D) - m).  The running max is
+// raised only when a tile's max exceeds it by more than 2^8 in the
+// exponential (or at the first tile): exact, since every probability and
+// the running sum use the same m, and it skips the rescale of the output
+// accumulators on almost every tile.  Probabilities below 2^8 times the
+// largest so far stay well inside bf16 / fp32 range.
+//
+// Splits write (O / l, log2 l + m) partials that a second kernel merges
 // with log-sum-exp weights.
 #include <math.h>
 
@@ -31,18 +43,40 @@
 namespace dg {
 namespace {
 
-constexpr int KT = 64;        // keys per tile
-constexpr int kThreads = 512;  // 8 waves of 16 query columns each
-constexpr int kRows = 128;     // query rows (head x position) per workgroup
+constexpr int KT = 64;         // keys per tile
+constexpr int kThreads = 512;  // 8 waves
+constexpr float kLazy = 8.f;   // raise the running max only past this (log2)
 
 __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
-  constexpr int KP = D + 16;     // padded K row (elements; +16 measured ~0.5 us faster than +8)
+// Workgroup id -> (row chunk, KV head, canvas, split).  Groups of one
+// (KV head, canvas, split) hold n_chunks workgroups; 8 groups at a time are
+// laid out chunk-major so that the workgroups of one group have ids equal
+// mod 8 (same XCD).  Ids of a partial last set of 8 groups past the end
+// return false.
+struct AttnTile {
+  int chunk, g, b, split;
+};
+__device__ __forceinline__ bool attn_tile(const AttnArgs& a, int n_chunks, AttnTile& t) {
+  const int id = blockIdx.x;
+  const int per8 = 8 * n_chunks;
+  const int group = (id / per8) * 8 + id % 8;
+  t.chunk = (id % per8) / 8;
+  const int n_groups = a.Hkv * a.n * a.splits;
+  if (group >= n_groups) return false;
+  t.g = group % a.Hkv;
+  const int bs = group / a.Hkv;
+  t.b = bs / a.splits;
+  t.split = bs % a.splits;
+  return true;
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks) {
+  constexpr int KP = D + 16;     // padded K row (elements)
   constexpr int VQ = D * 4 + 8;  // padded key-quad stride (elements; 16-byte rows)
   constexpr int DC = D / 32;     // 32-wide d chunks (MFMA k for S)
   constexpr int DT = D / 16;     // 16-wide d tiles (MFMA rows for O^T)
@@ -50,34 +84,45 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   constexpr int KCH = (KITEMS + kThreads - 1) / kThreads;
   constexpr int VITEMS = (KT / 4) * (D / 8);     // V items: 4 keys x 8 d
   constexpr int VIT = (VITEMS + kThreads - 1) / kThreads;
+  constexpr int ROWS = 128 * QB;                 // query rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vq[2][(KT / 4) * VQ];
 
+  AttnTile tl;
+  if (!attn_tile(a, n_chunks, tl)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int qt = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / a.splits, split = blockIdx.z % a.splits;
+  const int g = tl.g, b = tl.b, split = tl.split;
   const int C = a.C, G = a.Hq / a.Hkv;
   const int P = a.plen[b];
-  const int N = P + C;
+  const int b0 = a.vis0[b];
+  const int PE = P + (b - b0) * C;   // prefix + earlier canvases of the request
+  const int N = PE + C;
   const int n_rows = a.n * a.Hq * C;
 
-  // ---- this wave's 16 query columns: lane's column is row r of the
-  // workgroup's 128 (query head g*G + r / C, canvas position r % C)
-  const int r = qt * kRows + wave * 16 + l16;
-  const bool qvalid = r < G * C;
-  const int rr = qvalid ? r : 0;
-  const int qpos = rr % C;
-  const int qhead = g * G + rr / C;
-  u32x4_t qf[DC];
-  {
-    const uint16_t* qp = a.qkv + (long long)(b * C + qpos) * a.ldqkv + qhead * D + lg * 8;
+  // ---- this wave's query columns: block qb's lane column is row r of the
+  // (canvas, KV head)'s G*C rows (query head g*G + r / C, position r % C)
+  int qpos[QB], qhead[QB], klim[QB];
+  bool qvalid[QB];
+  u32x4_t qf[QB][DC];
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) qf[dc] = *(const u32x4_t*)(qp + dc * 32);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = tl.chunk * ROWS + wave * (16 * QB) + qb * 16 + l16;
+    qvalid[qb] = r < G * C;
+    const int rr = qvalid[qb] ? r : 0;
+    qpos[qb] = rr % C;
+    qhead[qb] = g * G + rr / C;
+    const uint16_t* qp =
+        a.qkv + (long long)(b * C + qpos[qb]) * a.ldqkv + qhead[qb] * D + lg * 8;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) qf[qb][dc] = *(const u32x4_t*)(qp + dc * 32);
+    // keys kk < klim are visible to this lane's query (all keys, or the
+    // prefix and canvas keys up to the query's own position when causal)
+    klim[qb] = a.causal ? min(N, PE + qpos[qb] + 1) : N;
   }
-  // keys kk < klim are visible to this lane's query (all keys, or the
-  // prefix and canvas keys up to the query's own position when causal)
-  const int klim = a.causal ? min(N, P + qpos + 1) : N;
+  // smallest visible-key bound over the workgroup's possible queries:
+  // tiles below it need no mask
+  const int klim_all = a.causal ? PE + 1 : N;
 
   const int n_kt = (N + KT - 1) / KT;
   const int kt_begin = (int)((long long)split * n_kt / a.splits);
@@ -87,9 +132,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                          (long long)g * a.head_stride;
   const uint16_t* vpre = a.vc + (long long)a.req[b] * a.req_stride +
                          (long long)g * a.head_stride;
-  const uint16_t* kcan = a.qkv + (long long)(b * C) * a.ldqkv + (a.Hq + g) * D;
+  // canvas keys: the request's earlier canvases b0..b-1 and canvas b are
+  // consecutive rows of qkv, so key kk >= P is canvas row b0*C + (kk - P)
+  const uint16_t* kcan = a.qkv + (long long)(b0 * C) * a.ldqkv + (a.Hq + g) * D;
   const uint16_t* vcan =
-      a.qkv + (long long)(b * C) * a.ldqkv + (a.Hq + a.Hkv + g) * D;
+      a.qkv + (long long)(b0 * C) * a.ldqkv + (a.Hq + a.Hkv + g) * D;
   // Key kk's row (keys past N read the last key: a valid row whose score
   // is masked to -inf, so its probability is exactly 0).
   auto krow = [&](const uint16_t* pre, const uint16_t* can, int kk) {
@@ -143,10 +190,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   };
 
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[DT];
+  float m_run[QB], l_run[QB];
+  f32x4_t oacc[QB][DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) oacc[qb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (kt_begin < kt_end) {
     gload(kt_begin);
@@ -162,66 +214,76 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const uint16_t* ks = Ks[buf];
     const uint16_t* vq = Vq[buf];
 
-    // ---- S^T = K Q^T: lane holds its query column, keys 16*t4 + 4*lg + e
-    f32x4_t sacc[4];
+    // ---- S^T = K Q^T: lane holds its query column of each block, keys
+    // 16*t4 + 4*lg + e
+    f32x4_t sacc[QB][4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
-      sacc[t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const u32x4_t kf = *(const u32x4_t*)&ks[(t4 * 16 + l16) * KP + dc * 32 + lg * 8];
-        sacc[t4] = mfma_v(kf, qf[dc], sacc[t4]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = mfma_v(kf, qf[qb][dc], sacc[qb][t4]);
       }
     }
 
-    // ---- online softmax of the column (branch-free: a column with no
-    // visible key so far keeps m = -inf, p = 0, and its zero accumulators)
-    float sv[4][4];
-    float mt = -INFINITY;
+    // ---- online softmax of each column (a column with no visible key so
+    // far keeps m = -inf, p = 0 and zero accumulators)
+    const bool full = key0 + KT <= klim_all;  // no key of the tile is masked
+    u32x4_t pf[QB][2];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mt = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = key0 + t4 * 16 + lg * 4 + e;
-        sv[t4][e] = kk < klim ? sacc[t4][e] * sc : -INFINITY;
-        mt = fmaxf(mt, sv[t4][e]);
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (!full) {
+            const int kk = key0 + t4 * 16 + lg * 4 + e;
+            if (kk >= klim[qb]) sacc[qb][t4][e] = -INFINITY;
+          }
+          mt = fmaxf(mt, sacc[qb][t4][e]);
+        }
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      mt *= sc;  // sc > 0: the max of the scaled scores
+      // raise the running max (and rescale) only when some column of the
+      // wave needs it
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kLazy) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha =
+            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
+        m_run[qb] = m_new;
       }
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    // exponents are <= 0; results below 2^-126 flush to 0 (negligible)
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float p[4][4];
-    float ls = 0.f;
+      // exponents are <= kLazy; results below 2^-126 flush to 0 (negligible)
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      float p[4][4];
+      float ls = 0.f;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[t4][e] = __builtin_amdgcn_exp2f(sv[t4][e] - m_use);
-        ls += p[t4][e];
-      }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+        for (int e = 0; e < 4; ++e) {
+          p[t4][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t4][e], sc, -m_use));
+          ls += p[t4][e];
+        }
+      l_run[qb] += ls;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-    u32x4_t pf[2], pl[2];
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) {
-        const float a0 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1)];
-        const float a1 = p[2 * kc + (h2 >> 1)][2 * (h2 & 1) + 1];
-        const uint32_t h = pack_bf2(a0, a1);
-        hi[h2] = h;
-        lo[h2] = pack_bf2(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xffff0000u));
-      }
-      pf[kc] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
-      pl[kc] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+      for (int kc = 0; kc < 2; ++kc)
+        pf[qb][kc] = u32x4_t{pack_bf2(p[2 * kc][0], p[2 * kc][1]),
+                             pack_bf2(p[2 * kc][2], p[2 * kc][3]),
+                             pack_bf2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
+                             pack_bf2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T.  k-slot 4 h + e of lane group lg is key
+    // 32 kc + 16 h + 4 lg + e (h = 0, 1), the order the S^T accumulators
+    // hold the probabilities in; the V operand reads the same keys (quads
+    // 8 kc + lg and 8 kc + 4 + lg at d)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -230,8 +292,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         const uint2 lo = *(const uint2*)&vq[(8 * kc + lg) * VQ + d * 4];
         const uint2 hi = *(const uint2*)&vq[(8 * kc + 4 + lg) * VQ + d * 4];
         const u32x4_t vf = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        oacc[dt] = mfma_v(vf, pf[kc], oacc[dt]);
-        oacc[dt] = mfma_v(vf, pl[kc], oacc[dt]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma_v(vf, pf[qb][kc], oacc[qb][dt]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -242,29 +304,34 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 
   // ---- finalise: lane holds its query column, d = 16*dt + 4*lg + e
-  float l = l_run;
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (!qvalid) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (a.splits == 1) {
-    uint16_t* op = a.out + (long long)(b * C + qpos) * (a.Hq * D) + qhead * D + lg * 4;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4_t o = oacc[dt];
-      *(uint2*)(op + dt * 16) =
-          make_uint2(pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv));
-    }
-  } else {
-    const int row_id = (b * a.Hq + qhead) * C + qpos;
-    float* op = a.opart + ((long long)split * n_rows + row_id) * D + lg * 4;
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = l_run[qb];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (!qvalid[qb]) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.splits == 1) {
+      uint16_t* op =
+          a.out + (long long)(b * C + qpos[qb]) * (a.Hq * D) + qhead[qb] * D + lg * 4;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const f32x4_t o = oacc[dt];
-      *(float4*)(op + dt * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4_t o = oacc[qb][dt];
+        *(uint2*)(op + dt * 16) =
+            make_uint2(pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv));
+      }
+    } else {
+      const int row_id = (b * a.Hq + qhead[qb]) * C + qpos[qb];
+      float* op = a.opart + ((long long)split * n_rows + row_id) * D + lg * 4;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4_t o = oacc[qb][dt];
+        *(float4*)(op + dt * 16) = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      }
+      if (lg == 0)
+        a.lpart[(long long)split * n_rows + row_id] =
+            l > 0.f ? m_run[qb] + log2f(l) : -INFINITY;
     }
-    if (lg == 0)
-      a.lpart[(long long)split * n_rows + row_id] = l > 0.f ? m_run + log2f(l) : -INFINITY;
   }
 }
 
@@ -279,7 +346,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int n_rows = a.n * a.Hq * a.C;
   const int row_id = blockIdx.x * 4 + wave;
   if (row_id >= n_rows) return;
-  // lane s holds split s's log-sum (splits <= 32): one load for all of
+  // lane s holds split s's log-sum (splits <= 64): one load for all of
   // them, the maximum by a wave reduction, split s's value by a broadcast
   const float l_my = a.lpart[(long long)(lane < a.splits ? lane : 0) * n_rows + row_id];
   float mx = lane < a.splits ? l_my : -INFINITY;
@@ -320,30 +387,62 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int e = 0; e < PER; ++e) out[lane + 64 * e] = f2bf(acc[e] * inv);
 }
 
-}  // namespace
-
-int attention_auto_splits(int n, int C, int Hq, int Hkv, int max_keys) {
-  // one round of workgroups (one per CU: the kernel's registers allow one
-  // 4-wave workgroup per CU), each walking at least 4 key tiles
+// Splits for qb query blocks per wave: one round of workgroups over the
+// 256 CUs, each walking at least 4 key tiles (max_keys > 0).
+int splits_for(int qb, int n, int C, int Hq, int Hkv, int max_keys) {
   const int G = Hq / Hkv;
-  const int natural = n * Hkv * ((G * C + 127) / 128);
+  const int rows = 128 * qb;
+  const int natural = n * Hkv * ((G * C + rows - 1) / rows);
   int s = (256 + natural - 1) / natural;
-  if (s > 16) s = 16;
+  if (s > 64) s = 64;
   if (max_keys > 0) {
     const int tiles = (max_keys + KT - 1) / KT;
     s = std::min(s, std::max(1, tiles / 4));
   }
-  if (s < 1) s = 1;
-  return s;
+  return std::max(s, 1);
+}
+
+// Query blocks per wave for a launch: 2 (256 rows per workgroup, half the
+// K/V bytes per query row) when the key range is long enough that every
+// workgroup still walks >= 8 tiles with the whole chip busy, else 1.
+int attn_qb(int n, int C, int Hq, int Hkv, int max_keys) {
+  const int G = Hq / Hkv;
+  if (max_keys <= 0 || G * C <= 128) return 1;
+  const int tiles = (max_keys + KT - 1) / KT;
+  return tiles / splits_for(2, n, C, Hq, Hkv, 0) >= 8 ? 2 : 1;
+}
+
+}  // namespace
+
+// Splits of a launch over canvases whose longest key range is max_keys;
+// max_keys <= 0 asks for the largest count any key range can get (to size
+// the partials' workspace).
+int attention_auto_splits(int n, int C, int Hq, int Hkv, int max_keys) {
+  if (max_keys <= 0)
+    return std::max(splits_for(1, n, C, Hq, Hkv, 0), splits_for(2, n, C, Hq, Hkv, 0));
+  return splits_for(attn_qb(n, C, Hq, Hkv, max_keys), n, C, Hq, Hkv, max_keys);
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  dim3 grid((G * a.C + 127) / 128, a.Hkv, a.n * a.splits);
-  if (a.D == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(kThreads), 0, s, a);
+  int max_keys = 0;
+  for (int b = 0; b < a.n; ++b)
+    max_keys = std::max(max_keys, a.plen[b] + (b - a.vis0[b] + 1) * a.C);
+  const int qb = attn_qb(a.n, a.C, a.Hq, a.Hkv, max_keys);
+  const int n_chunks = (G * a.C + 128 * qb - 1) / (128 * qb);
+  const int n_groups = a.Hkv * a.n * a.splits;
+  const dim3 grid((unsigned)(((n_groups + 7) / 8) * 8 * n_chunks));
+  if (a.D == 128) {
+    if (qb == 2)
+      hipLaunchKernelGGL((attn_kernel<128, 2>), grid, dim3(kThreads), 0, s, a, n_chunks);
+    else
+      hipLaunchKernelGGL((attn_kernel<128, 1>), grid, dim3(kThreads), 0, s, a, n_chunks);
+  } else {
+    if (qb == 2)
+      hipLaunchKernelGGL((attn_kernel<64, 2>), grid, dim3(kThreads), 0, s, a, n_chunks);
+    else
+      hipLaunchKernelGGL((attn_kernel<64, 1>), grid, dim3(kThreads), 0, s, a, n_chunks);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int n_rows = a.n * a.Hq * a.C;

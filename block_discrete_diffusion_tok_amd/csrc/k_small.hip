@@ -75,6 +75,19 @@ __global__ __launch_bounds__(256) void pack_kernel(const char* src, int rows,
 // for every load before it, one memory latency per load.
 __device__ __forceinline__ int clamp_col(int i, int H) { return i < H ? i : H - 4; }
 
+// acc + x^2 + y^2 + z^2 + w^2 as an explicit chain of fused multiply-adds:
+// every kernel that norms a row (the RMSNorm, the embedding and the
+// un-permute it is fused into) sums the squares in this one order, so a
+// row gets the same norm bits whichever kernel norms it (left to the
+// compiler, the contraction of a*a + b*b + ... depends on the surrounding
+// code).
+__device__ __forceinline__ float sumsq4(float4 v, float acc) {
+  acc = fmaf(v.x, v.x, acc);
+  acc = fmaf(v.y, v.y, acc);
+  acc = fmaf(v.z, v.z, acc);
+  return fmaf(v.w, v.w, acc);
+}
+
 template <int U>
 __device__ __forceinline__ void load_gains(float4 (&gg)[U], const float* g, int H) {
 #pragma unroll
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(
 #pragma unroll
     for (int c = 0; c < U; ++c) {
       if (base + 1024 * c + tid * 4 >= H) v[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+      ss = sumsq4(v[c], ss);
     }
     base += 1024 * U;
     if (base >= H) break;
@@ -191,9 +204,12 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// With S shared experts (0 or 1) a token's pairs are K = k + S: ranks
+// 0..k-1 the routed experts, rank k the shared expert (id E, weight 1);
+// idx / w are [T, K].
 template <bool SLOTS>
 __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
-                                                   int k, int splits, int32_t* idx,
+                                                   int k, int S, int splits, int32_t* idx,
                                                    float* w, int32_t* counts, int cap,
                                                    int32_t* slot_pair, float* slot_w,
                                                    int32_t* slot_tok) {
@@ -265,14 +281,19 @@ __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
       my_sel = sel[r];
       my_id = sid[r];
     }
-  const float my_w = __expf(my_sel - mx) / sum;
-  if (lane < k) {
-    idx[(long long)t * k + lane] = my_id;
-    w[(long long)t * k + lane] = my_w;
+  float my_w = __expf(my_sel - mx) / sum;
+  if (S && lane == k) {  // the shared expert: every token, weight 1
+    my_id = E;
+    my_w = 1.f;
   }
-  if (SLOTS && lane < k) {  // lane r < k takes a slot of expert sid[r]
+  const int K = k + S;
+  if (lane < K) {
+    idx[(long long)t * K + lane] = my_id;
+    w[(long long)t * K + lane] = my_w;
+  }
+  if (SLOTS && lane < K) {  // lane r < K takes a slot of its expert
     const long long sl = (long long)my_id * cap + atomicAdd(&counts[my_id], 1);
-    slot_pair[sl] = t * k + lane;
+    slot_pair[sl] = t * K + lane;
     slot_w[sl] = my_w;
     slot_tok[sl] = t;
   }
@@ -417,6 +438,14 @@ __global__ __launch_bounds__(1024) void moe_permute_small_kernel(
     if (e4[r] >= 0) perm[atomicAdd(&cursor[e4[r]], 1)] = tid + 1024 * r;
 }
 
+// counts[e] = offsets[e + 1] - offsets[e] for e < E (the routed experts'
+// token counts out of the permutation's offsets over all expert groups)
+__global__ __launch_bounds__(256) void counts_kernel(const int32_t* offsets, int E,
+                                                     int32_t* counts) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) counts[e] = offsets[e + 1] - offsets[e];
+}
+
 // ---------------------------------------------------------------- un-permute
 // x[t, :] += sum_j y[t*k + j, :] in rank order (no atomics); optionally the
 // sum alone is written to moe_out.  x may be null (store only).
@@ -492,7 +521,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(
                          bf2f((uint16_t)(w[c].y & 0xffff)), bf2f((uint16_t)(w[c].y >> 16)));
       if (i < H) {
         *(float4*)(xr + i) = v[c];
-        ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+        ss = sumsq4(v[c], ss);
       }
     }
   }
@@ -537,7 +566,7 @@ __global__ __launch_bounds__(256) void unpermute_norm_kernel(
       if (i < H) {
         *(float4*)(xr + i) = o;
         if (moe_out) *(float4*)(moe_out + (long long)t * H + i) = sum;
-        ss += o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+        ss = sumsq4(o, ss);
       } else {
         o = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -628,9 +657,11 @@ __device__ __forceinline__ void merge_stats(float& m, float& s, float& t,
 // (loads issued together), then the wave and the 4 waves are merged.
 __global__ __launch_bounds__(256) void lm_merge_kernel(
     const float4* part, int n_tiles, const int32_t* m_dev, int m_max,
-    const int32_t* row_map, float* entropy, float* lse, int32_t* argmax) {
+    const int32_t* row_map, float* entropy, float* lse, int32_t* argmax,
+    const float* tau, const float2* spart, int32_t* sample) {
   constexpr int U = 8;
   __shared__ float4 red[4];
+  __shared__ float2 red2[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x;
   const int n = m_dev ? *m_dev : m_max;
@@ -656,6 +687,20 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(
     merge_stats(m, s, t, am, m2, s2, t2, am2);
   }
   if (lane == 0) red[wave] = make_float4(m, s, t, __int_as_float(am));
+  // sampled token: the best (score, id) over the tiles, lower id on ties
+  float g = -INFINITY;
+  int gi = 0x7fffffff;
+  if (sample) {
+    const float2* sp = spart + (long long)r * n_tiles;
+    for (int i = tid; i < n_tiles; i += 256) {
+      const float2 q = sp[i];
+      best_merge(g, gi, q.x, __float_as_int(q.y));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+      best_merge(g, gi, shfl_xor(g, off), shfl_xor(gi, off));
+    if (lane == 0) red2[wave] = make_float2(g, __int_as_float(gi));
+  }
   __syncthreads();
   if (tid == 0) {
 #pragma unroll
@@ -666,25 +711,58 @@ __global__ __launch_bounds__(256) void lm_merge_kernel(
     lse[pos] = m + ls;
     entropy[pos] = fmaxf(ls - t / s, 0.f);
     argmax[pos] = am;
+    if (sample) {
+#pragma unroll
+      for (int w = 1; w < 4; ++w) best_merge(g, gi, red2[w].x, __float_as_int(red2[w].y));
+      // temperature 0: the point mass on the argmax
+      if (!(tau[r] > 0.f)) {
+        entropy[pos] = 0.f;
+        gi = am;
+      }
+      sample[pos] = gi;
+    }
   }
 }
 
+// Temperature and Philox counter words of each LM-head row (see
+// launch_sample_rows).
+__global__ __launch_bounds__(256) void sample_rows_kernel(
+    const int32_t* row_map, const int32_t* m_dev, int m_max, const int32_t* step, int C,
+    float tau0, int budget, float* tau, int32_t* ctr) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int m = m_dev ? *m_dev : m_max;
+  if (r >= m) return;
+  const int t = row_map ? row_map[r] : r;
+  const int b = t / C;
+  const int st = step[b];
+  float tt = tau0;
+  if (budget > 0) tt = tau0 * (1.f - (float)st / (float)budget);
+  tau[r] = fmaxf(tt, 0.f);
+  ctr[3 * r] = t % C;
+  ctr[3 * r + 1] = st;
+  ctr[3 * r + 2] = b;
+}
+
+// One workgroup of 256 threads per canvas of C <= 256 positions (thread j
+// takes position j; threads j >= C hold no position).
 __global__ __launch_bounds__(256) void eb_kernel(
     const float* entropy, const int32_t* argmax, uint8_t* committed,
     int32_t* tokens, int32_t* step, const float* gamma, int cap, int refine,
-    int32_t* n_new, uint8_t* done) {
+    int32_t* n_new, uint8_t* done, int C) {
   static_assert(DG_CANVAS == 256, "one thread per canvas position");
   __shared__ __attribute__((aligned(16))) unsigned long long keys[DG_CANVAS];
   __shared__ float sorted_h[DG_CANVAS];
   __shared__ double wave_sum[4];
   __shared__ int s_first;
   const int b = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
-  const long long base = (long long)b * DG_CANVAS;
+  const long long base = (long long)b * C;
+  const bool here = j < C;
+  const int jc = here ? j : C - 1;   // (a valid address; the value is unused)
   // every global read issued at once (values at committed positions are
   // read but not used): one memory latency instead of a chain of them
-  const uint8_t cm = committed[base + j];
-  const float h_in = entropy[base + j];
-  const int32_t am_in = argmax[base + j];
+  const uint8_t cm = here ? committed[base + jc] : (uint8_t)1;
+  const float h_in = entropy[base + jc];
+  const int32_t am_in = argmax[base + jc];
   const float lim = gamma[b];
   const int steps_done = step[b];  // read by all before thread 0 updates it
   const bool unc = cm == 0;
@@ -826,26 +904,35 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
 }
 
 hipError_t launch_topk(float* logits, int T, int E, int k, int splits, int32_t* idx,
-                       float* w, hipStream_t s) {
+                       float* w, hipStream_t s, int S) {
   if (T <= 0) return hipSuccess;
-  if (E > kTopkMaxE || k > kTopkMaxK || k > E) return hipErrorInvalidValue;
+  if (E > kTopkMaxE || k > kTopkMaxK || k > E || S < 0 || S > 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(topk_kernel<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits,
-                     T, E, k, splits, idx, w, nullptr, 0, nullptr, nullptr, nullptr);
+                     T, E, k, S, splits, idx, w, nullptr, 0, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_slots(float* logits, int T, int E, int k, int splits,
                              int32_t* idx, float* w, int32_t* counts, int cap,
                              int32_t* slot_pair, float* slot_w, int32_t* slot_tok,
-                             hipStream_t s) {
+                             hipStream_t s, int S) {
   if (T <= 0) return hipSuccess;
-  if (E > kTopkMaxE || k > kTopkMaxK || k > E || cap < T) return hipErrorInvalidValue;
+  if (E > kTopkMaxE || k > kTopkMaxK || k > E || cap < T || S < 0 || S > 1)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(topk_kernel<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits,
-                     T, E, k, splits, idx, w, counts, cap, slot_pair, slot_w, slot_tok);
+                     T, E, k, S, splits, idx, w, counts, cap, slot_pair, slot_w, slot_tok);
   return hipGetLastError();
 }
 
 int permute_chunks(int n_pairs) { return (n_pairs + kChunk - 1) / kChunk; }
+
+hipError_t launch_counts_from_offsets(const int32_t* offsets, int E, int32_t* counts,
+                                      hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(counts_kernel, dim3((E + 255) / 256), dim3(256), 0, s, offsets, E,
+                     counts);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                           int32_t* chunk_counts, int32_t* local_rank,
@@ -909,21 +996,33 @@ hipError_t launch_unpermute(const float* y, int T, int k, int H, float* x,
 hipError_t launch_lm_merge(const float4* part, int n_tiles,
                            const int32_t* m_dev, int m_max,
                            const int32_t* row_map, float* entropy, float* lse,
-                           int32_t* argmax, hipStream_t s) {
+                           int32_t* argmax, hipStream_t s, const float* tau,
+                           const float2* spart, int32_t* sample) {
   if (m_max <= 0) return hipSuccess;
+  if (sample && (!tau || !spart)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(lm_merge_kernel, dim3(m_max), dim3(256), 0, s,
                      part, n_tiles, m_dev, m_max, row_map, entropy, lse,
-                     argmax);
+                     argmax, tau, spart, sample);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_rows(const int32_t* row_map, const int32_t* m_dev, int m_max,
+                              const int32_t* step, int C, float tau0, int budget,
+                              float* tau, int32_t* ctr, hipStream_t s) {
+  if (m_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_rows_kernel, dim3((m_max + 255) / 256), dim3(256), 0, s,
+                     row_map, m_dev, m_max, step, C, tau0, budget, tau, ctr);
   return hipGetLastError();
 }
 
 hipError_t launch_eb_select(int n, const float* entropy, const int32_t* argmax,
                             uint8_t* committed, int32_t* tokens, int32_t* step,
                             const float* gamma, int step_cap, int refine,
-                            int32_t* n_new, uint8_t* done, hipStream_t s) {
+                            int32_t* n_new, uint8_t* done, hipStream_t s, int C) {
+  if (C < 1 || C > DG_CANVAS) return hipErrorInvalidValue;
   hipLaunchKernelGGL(eb_kernel, dim3(n), dim3(DG_CANVAS), 0, s, entropy, argmax,
                      committed, tokens, step, gamma, step_cap, refine, n_new,
-                     done);
+                     done, C);
   return hipGetLastError();
 }
 

@@ -153,13 +153,13 @@ __device__ __forceinline__ void mfma_chunk(f32x4_t (&acc)[RT][NT],
 template <int RT, int NT, int KC, int D, int EPI, bool W8, int WV>
 __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, int dense_rows) {
   static_assert(RT % 2 == 0, "gate/up pairing needs an even number of row tiles");
-  static_assert(EPI == EPI_LMSTATS || EPI == EPI_SWIGLU || EPI == EPI_DOWN, "epilogue");
+  static_assert(epi_is_lm(EPI) || EPI == EPI_SWIGLU || EPI == EPI_DOWN, "epilogue");
   // the gate/up products read a slot's token row through row_of; the down
   // products read the slot rows of the SwiGLU output directly
   constexpr bool MAPPED = EPI == EPI_SWIGLU;
   // the expert products run over groups (experts) of slots; the LM head
   // over the rows of one dense operand
-  constexpr bool GROUPED = EPI != EPI_LMSTATS;
+  constexpr bool GROUPED = !epi_is_lm(EPI);
   static_assert(KC == 64 || KC == 128, "K chunk");
   constexpr int WROWS = WV * RT * 16;  // weight rows per workgroup (WV waves)
   constexpr int ESZ = W8 ? 1 : 2;     // bytes per weight element
@@ -261,7 +261,7 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   auto issue = [&](auto p, int k) {
     uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
     static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
-    load_w<RT, WREGS, ESZ, KC, (EPI == EPI_LMSTATS)>(w[p], wsrc, k);
+    load_w<RT, WREGS, ESZ, KC, epi_is_lm(EPI)>(w[p], wsrc, k);
   };
   auto prologue = [&]() {
     static_for<D>([&](auto p) {
@@ -343,11 +343,24 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
 
     // ---- epilogues: lane holds token column t0 + 16*nt + l16 and weight
     // rows 4*lg + e of each row tile
-    if (EPI == EPI_LMSTATS) {
+    if (epi_is_lm(EPI)) {
       float4* red = (float4*)&Xs[0];  // [WV waves][NT*16]
-      static_assert(WV * NT * 16 * 16 <= S * STAGE * 2, "LDS reuse");
+      float2* red2 = (float2*)&red[WV * NT * 16];  // sampling: [WV waves][NT*16]
+      static_assert(WV * NT * 16 * 24 <= S * STAGE * 2, "LDS reuse");
+      constexpr bool smp = EPI == EPI_LMSAMPLE;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        // temperature sampling: statistics of z / tau, Gumbel-max token
+        const int srow = min(t0 + nt * 16 + l16, t_end - 1);
+        float tau = 1.f;
+        uint32_t c1 = 0, c2 = 0, c3 = 0;
+        if (smp) {
+          tau = a.smp.tau[srow];
+          c1 = a.smp.ctr[3 * srow];
+          c2 = a.smp.ctr[3 * srow + 1];
+          c3 = a.smp.ctr[3 * srow + 2];
+        }
+        const float scale = tau > 0.f ? 1.f / tau : 1.f;
         float m = -INFINITY, s = 0.f, t = 0.f;
         int am = 0x7fffffff;
 #pragma unroll
@@ -355,7 +368,7 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int n = n_base + (wave * RT + rt) * 16 + 4 * lg + e;
-            const float v = acc[rt][nt][e];
+            const float v = smp ? acc[rt][nt][e] * scale : acc[rt][nt][e];
             if (n < a.N && v > m) { m = v; am = n; }
           }
         if (m != -INFINITY) {
@@ -365,7 +378,8 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
             for (int e = 0; e < 4; ++e) {
               const int n = n_base + (wave * RT + rt) * 16 + 4 * lg + e;
               if (n < a.N) {
-                const float d = acc[rt][nt][e] - m;
+                const float v = smp ? acc[rt][nt][e] * scale : acc[rt][nt][e];
+                const float d = v - m;
                 const float ex = __expf(d);
                 s += ex;
                 t += ex * d;
@@ -380,6 +394,26 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
           smerge(m, s, t, am, m2, s2, t2, am2);
         }
         if (lg == 0) red[wave * NT * 16 + nt * 16 + l16] = make_float4(m, s, t, __int_as_float(am));
+        if (smp) {
+          float g = -INFINITY;
+          int gi = 0x7fffffff;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int n0 = n_base + (wave * RT + rt) * 16 + 4 * lg;
+            uint32_t c[4] = {(uint32_t)n0 >> 2, c1, c2, c3};
+            if (tau > 0.f) philox4x32_10(c, a.smp.key0, a.smp.key1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (n0 + e >= a.N) continue;
+              const float v = acc[rt][nt][e] * scale;
+              best_merge(g, gi, tau > 0.f ? v + gumbel_of(c[e]) : v, n0 + e);
+            }
+          }
+#pragma unroll
+          for (int off = 16; off < 64; off <<= 1)
+            best_merge(g, gi, shfl_xor(g, off), shfl_xor(gi, off));
+          if (lg == 0) red2[wave * NT * 16 + nt * 16 + l16] = make_float2(g, __int_as_float(gi));
+        }
         if (a.logits) {
           const int tok = t0 + nt * 16 + l16;
           if (tok < t_end) {
@@ -406,6 +440,17 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
         }
         a.part[(long long)(t0 + tid) * a.n_tiles + bx] =
             make_float4(m, s, t, __int_as_float(am));
+        if (smp) {
+          float2 b = red2[tid];
+          float g = b.x;
+          int gi = __float_as_int(b.y);
+#pragma unroll
+          for (int w = 1; w < WV; ++w) {
+            const float2 q = red2[w * NT * 16 + tid];
+            best_merge(g, gi, q.x, __float_as_int(q.y));
+          }
+          a.smp.spart[(long long)(t0 + tid) * a.n_tiles + bx] = make_float2(g, __int_as_float(gi));
+        }
       }
     } else {
 #pragma unroll
@@ -472,9 +517,10 @@ template <int RT, int NT, int KC, int D, int EPI, bool W8, int OCC, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void stream_kernel(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Xs[(D + 1) * NT * 16 * KC];
-  if constexpr (EPI == EPI_LMSTATS && NT == 8) {
+  if constexpr (epi_is_lm(EPI) && NT == 8) {
     int rows = a.M;
     if (a.M_dev) rows = min(rows, a.M_dev[0]);
+    if (a.M_dev && a.rows_le > 0 && rows > a.rows_le) return;  // another kernel's rows
     if (rows <= 32)
       stream_run<RT, 2, KC, D, EPI, W8, WV>(a, Xs, rows);
     else if (rows <= 64)
@@ -483,7 +529,7 @@ void stream_kernel(StreamArgs a) {
       stream_run<RT, 6, KC, D, EPI, W8, WV>(a, Xs, rows);
     else
       stream_run<RT, 8, KC, D, EPI, W8, WV>(a, Xs, rows);
-  } else if constexpr (EPI == EPI_LMSTATS) {
+  } else if constexpr (epi_is_lm(EPI)) {
     int rows = a.M;
     if (a.M_dev) rows = min(rows, a.M_dev[0]);
     stream_run<RT, NT, KC, D, EPI, W8, WV>(a, Xs, rows);
@@ -546,6 +592,9 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
     case EPI_LMSTATS:
       if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
       return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc, kLmWaves>(a, groups, s);
+    case EPI_LMSAMPLE:
+      if (w8 || !stream_lm_ok(a.K) || !a.smp.tau) return hipErrorInvalidValue;
+      return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSAMPLE, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_SWIGLU:
       if (a.K % kMoeKC || a.K / kMoeKC < kGuD) return hipErrorInvalidValue;
       return w8 ? launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, true, kMoeOcc, kMoeWaves>(a, groups, s)

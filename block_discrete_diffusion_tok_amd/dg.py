@@ -36,7 +36,8 @@ class ModelDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
-                ("expert_dtype", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("canvas_len", ctypes.c_int32),
+                ("n_shared_experts", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -62,10 +63,16 @@ class Capture(ctypes.Structure):
         "final_xhat")]
 
 
+class Sampling(ctypes.Structure):
+    _fields_ = [("tau0", ctypes.c_float), ("budget", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("sample", ctypes.c_void_p)]
+
+
 class StepOut(ctypes.Structure):
     _fields_ = [("entropy", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("argmax", ctypes.c_void_p), ("logits", ctypes.c_void_p),
-                ("capture", ctypes.POINTER(Capture))]
+                ("capture", ctypes.POINTER(Capture)),
+                ("sampling", ctypes.POINTER(Sampling))]
 
 
 _P = ctypes.c_void_p
@@ -107,7 +114,10 @@ _SIGS = {
                                   ctypes.c_size_t, _P]),
     "dg_op_lmhead_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dg_op_lmhead_entropy_static": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
-    "dg_op_eb_select": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "dg_op_lmhead_sample": (_I, [_P, _I, _I, _P, _I, _P, _P, ctypes.c_uint64,
+                                 _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "dg_op_lmhead_sample_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "dg_op_eb_select": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                              ctypes.POINTER(_I), ctypes.POINTER(_I), _P]),
 }
@@ -150,7 +160,9 @@ def model_desc(shape):
                      shape.n_kv_heads, shape.head_dim, shape.n_experts,
                      shape.top_k, shape.expert_ffn, shape.vocab,
                      shape.rms_eps,
-                     FP8_E4M3 if shape.expert_dtype == "fp8_e4m3" else BF16)
+                     FP8_E4M3 if shape.expert_dtype == "fp8_e4m3" else BF16,
+                     getattr(shape, "canvas_len", CANVAS),
+                     getattr(shape, "n_shared_experts", 0))
 
 
 def layer_weights(lw):
@@ -270,10 +282,16 @@ class Engine:
                       self.max_kv_len, s.head_dim)
 
     def prefill_kv(self, req, k, v):
-        """k, v: [L, Hkv, n, D] bf16 device tensors (contiguous)."""
+        """Install mode. k, v: [L, Hkv, n, D] bf16 device tensors
+        (contiguous)."""
         n = k.shape[2]
         _check(lib().dg_prefill_kv(self.ctx, req, n, None, _ptr(k), _ptr(v)),
                self.ctx)
+
+    def prefill_tokens(self, req, tokens):
+        """Token mode. tokens: [n] int32 device tensor (the prompt)."""
+        _check(lib().dg_prefill_kv(self.ctx, req, tokens.numel(),
+                                   _ptr(tokens), None, None), self.ctx)
 
     def profile_enable(self, on=True):
         _check(lib().dg_profile_enable(self.ctx, int(on)), self.ctx)
@@ -303,8 +321,14 @@ class Engine:
         return b
 
     def denoise_step(self, req, tokens, committed, step, entropy, lse, argmax,
-                     logits=None, capture=None):
+                     logits=None, capture=None, sampling=None):
+        """sampling: None (greedy) or (tau0, budget, seed, sample tensor)."""
         b = self._batch(req, tokens, committed, step)
+        smp = None
+        if sampling is not None:
+            tau0, budget, seed, sample = sampling
+            smp = Sampling(float(tau0), int(budget), int(seed) & (2**64 - 1),
+                           sample.data_ptr())
         cap = None
         if capture is not None:
             cap = Capture(*[(capture[k].data_ptr() if capture.get(k)
@@ -313,7 +337,8 @@ class Engine:
                 "router_logits", "final_xhat")])
         out = StepOut(entropy.data_ptr(), lse.data_ptr(), argmax.data_ptr(),
                       None if logits is None else logits.data_ptr(),
-                      ctypes.pointer(cap) if cap is not None else None)
+                      ctypes.pointer(cap) if cap is not None else None,
+                      ctypes.pointer(smp) if smp is not None else None)
         _check(lib().dg_denoise_step(self.ctx, ctypes.byref(b),
                                      ctypes.byref(out)), self.ctx)
 
@@ -398,6 +423,22 @@ def op_lmhead_entropy(xhat, embed, entropy, lse, argmax, logits=None):
     return ws
 
 
+def op_lmhead_sample(xhat, embed, tau, ctr, seed, entropy, lse, argmax,
+                     sample):
+    """tau [M] fp32, ctr [M, 3] int32 (position, step, canvas), seed: 64-bit
+    key.  embed: row-major [V, H] (packed here) or a Packed matrix."""
+    L = lib()
+    embed = pack(embed)
+    nb = L.dg_op_lmhead_sample_workspace_bytes(xhat.shape[0], embed.rows)
+    ws = _ws(nb, xhat.device)
+    _check(L.dg_op_lmhead_sample(_ptr(xhat), xhat.shape[0], xhat.shape[1],
+                                 _ptr(embed), embed.rows, _ptr(tau), _ptr(ctr),
+                                 int(seed) & (2**64 - 1), _ptr(entropy),
+                                 _ptr(lse), _ptr(argmax), _ptr(sample),
+                                 _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
 def op_lmhead_entropy_static(xhat, embed, entropy, lse, argmax):
     """dg_op_lmhead_entropy_static: no workspace, no allocation.
     embed: a Packed matrix (packing allocates, so it is done beforehand)."""
@@ -410,7 +451,8 @@ def op_lmhead_entropy_static(xhat, embed, entropy, lse, argmax):
 
 def op_eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,
                  refine, n_new, done):
-    _check(lib().dg_op_eb_select(entropy.shape[0], _ptr(entropy),
+    _check(lib().dg_op_eb_select(entropy.shape[0], entropy.shape[1],
+                                 _ptr(entropy),
                                  _ptr(argmax), _ptr(committed), _ptr(tokens),
                                  _ptr(step), _ptr(gamma), step_cap,
                                  int(refine), _ptr(n_new), _ptr(done),

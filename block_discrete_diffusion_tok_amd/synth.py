@@ -36,6 +36,8 @@ class ModelShape:
     vocab: int
     rms_eps: float = 1e-6
     expert_dtype: str = "bf16"  # "bf16" or "fp8_e4m3"
+    canvas_len: int = CANVAS    # positions per canvas (128 or 256)
+    n_shared_experts: int = 0   # 0 or 1 shared expert (the last expert group)
 
 
 @dataclass(frozen=True)
@@ -146,23 +148,26 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
             "w_router": normal((s.n_experts, s.hidden), 0.02, seed,
                                p + "w_router", device),
         }
+        # the routed experts, then the shared expert (its own draw)
+        eg = s.n_experts
+        gu_shape = (eg, 2 * s.expert_ffn, s.hidden)
+        dn_shape = (eg, s.hidden, s.expert_ffn)
+        dt = torch.bfloat16 if s.expert_dtype == "bf16" else torch.float32
+        gu = normal(gu_shape, 0.02, seed, p + "w_gate_up", device, dt)
+        dn = normal(dn_shape, 0.02, seed, p + "w_down", device, dt)
+        if s.n_shared_experts:
+            gu = torch.cat([gu, normal((1,) + gu_shape[1:], 0.02, seed,
+                                       p + "w_gate_up_shared", device, dt)])
+            dn = torch.cat([dn, normal((1,) + dn_shape[1:], 0.02, seed,
+                                       p + "w_down_shared", device, dt)])
         if s.expert_dtype == "bf16":
-            lw["w_gate_up"] = normal((s.n_experts, 2 * s.expert_ffn,
-                                      s.hidden), 0.02, seed, p + "w_gate_up",
-                                     device)
-            lw["w_down"] = normal((s.n_experts, s.hidden, s.expert_ffn), 0.02,
-                                  seed, p + "w_down", device)
+            lw["w_gate_up"], lw["w_down"] = gu, dn
             lw["gate_up_scale"] = None
             lw["down_scale"] = None
         else:
-            gu = normal((s.n_experts, 2 * s.expert_ffn, s.hidden), 0.02, seed,
-                        p + "w_gate_up", device, torch.float32)
             lw["w_gate_up"], lw["gate_up_scale"] = quantize_e4m3_rows(gu)
-            del gu
-            dn = normal((s.n_experts, s.hidden, s.expert_ffn), 0.02, seed,
-                        p + "w_down", device, torch.float32)
             lw["w_down"], lw["down_scale"] = quantize_e4m3_rows(dn)
-            del dn
+            del gu, dn
         w["layers"].append(lw)
     return w
 
@@ -183,16 +188,18 @@ def make_prefix_kv(shape: ModelShape, prefix_len, request, seed=0,
 
 
 def make_canvas(shape: ModelShape, batch, uncommitted, seed=0, block=0):
-    """Canvas state on the host: tokens int32 [B, C] uniform over the vocab,
+    """Canvas state on the host (C = shape.canvas_len positions per canvas):
+    tokens int32 [B, C] uniform over the vocab,
     committed uint8 [B, C] with exactly ``uncommitted`` zeros per canvas at
     seeded uniformly random positions, step int32 [B] zeros."""
-    tokens = torch.empty((batch, CANVAS), dtype=torch.int32)
-    committed = torch.ones((batch, CANVAS), dtype=torch.uint8)
+    C = shape.canvas_len
+    tokens = torch.empty((batch, C), dtype=torch.int32)
+    committed = torch.ones((batch, C), dtype=torch.uint8)
     for b in range(batch):
         g = _gen(seed, f"canvas.block{block}.b{b}", "cpu")
-        tokens[b] = torch.randint(0, shape.vocab, (CANVAS,), generator=g,
+        tokens[b] = torch.randint(0, shape.vocab, (C,), generator=g,
                                   dtype=torch.int64).to(torch.int32)
-        pos = torch.randperm(CANVAS, generator=g)[:uncommitted]
+        pos = torch.randperm(C, generator=g)[:uncommitted]
         committed[b, pos] = 0
     return {"tokens": tokens, "committed": committed,
             "step": torch.zeros(batch, dtype=torch.int32)}

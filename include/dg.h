@@ -83,6 +83,15 @@ typedef struct {
   int32_t vocab;
   float rms_eps;          /* e.g. 1e-6 */
   int32_t expert_dtype;   /* dg_dtype of w_gate_up / w_down */
+  int32_t canvas_len;     /* positions per canvas, 1..256 (0: 256); the
+                             write-up's Table 7 varies the canvas size (128
+                             or 256).  Every [n, 256] array of the calls
+                             below is [n, canvas_len]. */
+  int32_t n_shared_experts; /* 0 or 1: a shared SwiGLU expert of width
+                             expert_ffn that every token uses with weight 1
+                             next to its top_k routed experts (write-up
+                             Table 1, "+ 1 shared"); it is the last group of
+                             w_gate_up / w_down (and of their scales) */
 } dg_model_desc;
 
 /* Packed weight layout.  Every weight matrix the kernels read (w_qkv, w_o,
@@ -115,10 +124,11 @@ typedef struct {
   const void* w_o;            /* [H, Hq D] bf16 */
   const float* ffn_norm;      /* [H] fp32 RMSNorm gain before the MoE */
   const void* w_router;       /* [E, H] bf16 */
-  const void* w_gate_up;      /* E groups of [2F, H] bf16 or e4m3: F gate rows, then F up rows */
-  const void* w_down;         /* E groups of [H, F] bf16 or e4m3 */
-  const float* gate_up_scale; /* [E, 2F] fp32 per-row scale (e4m3 only, else NULL) */
-  const float* down_scale;    /* [E, H] fp32 per-row scale (e4m3 only, else NULL) */
+  const void* w_gate_up;      /* E + S groups of [2F, H] bf16 or e4m3: F gate rows, then
+                                 F up rows (S = n_shared_experts; the shared expert last) */
+  const void* w_down;         /* E + S groups of [H, F] bf16 or e4m3 */
+  const float* gate_up_scale; /* [E + S, 2F] fp32 per-row scale (e4m3 only, else NULL) */
+  const float* down_scale;    /* [E + S, H] fp32 per-row scale (e4m3 only, else NULL) */
 } dg_layer_weights;
 
 typedef struct {
@@ -147,18 +157,34 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
                     dg_ctx** out);
 void dg_destroy(dg_ctx* ctx); /* frees host state only; NULL is a no-op */
 
-/* Stage 1 (write-up Figure 4, "context encoding").  Install mode: k and v
- * are [n_layers][n_kv_heads][n][head_dim] bf16 (already encoded prompt K/V)
- * and are copied into cache rows [0, n) of slot req; tokens must be NULL.
- * The slot's kv_len becomes n.  Token mode (tokens non-NULL, k = v = NULL)
- * is not provided: it returns DG_ERR_UNSUPPORTED. */
+/* Stage 1 (write-up Figure 4, "context encoding"; model card "Model
+ * Overview": the causal encoder runs over the prompt and fills the cache).
+ * Exactly one of {tokens} or {k, v} is given.
+ * Install mode: k and v are [n_layers][n_kv_heads][n][head_dim] bf16
+ * (already encoded prompt K/V) and are copied into cache rows [0, n) of
+ * slot req.
+ * Token mode: tokens is [n] int32 (device; ids outside [0, V) are clamped
+ * when embedded); the prompt is encoded causally through every layer (the
+ * same computation as dg_commit_block, position i seeing positions <= i) in
+ * chunks of up to 256 tokens, each layer's K/V written to cache rows
+ * [0, n).  Uses the context workspace (a denoise step's intermediate state
+ * is overwritten).
+ * Either way the slot's kv_len becomes n; DG_ERR_CAPACITY if n >
+ * max_kv_len. */
 dg_status dg_prefill_kv(dg_ctx* ctx, int32_t req, int32_t n,
                         const int32_t* tokens, const void* k, const void* v);
 
-/* Canvas state of a batch of n canvases, one per request slot. */
+/* Canvas state of a batch of n canvases.  Several canvases may belong to
+ * one request (multi-canvas sampling, model card feature list
+ * "block-autoregressive multi-canvas sampling"; write-up Table 7, number of
+ * canvases): they are contiguous in the batch, in block order, and canvas j
+ * of a request attends to the request's cache, then to every position of
+ * the request's canvases before it in the batch (earlier blocks fully
+ * visible, later ones not), then to itself.  DG_ERR_INVALID_ARG if the
+ * canvases of a request are not contiguous. */
 typedef struct {
   int32_t n;               /* 1..max_canvases */
-  const int32_t* req;      /* (host) [n] request slot of each canvas, distinct */
+  const int32_t* req;      /* (host) [n] request slot of each canvas */
   int32_t* tokens;         /* [n, 256] int32 current canvas tokens in [0, V),
                               in/out (ids outside are clamped when embedded) */
   uint8_t* committed;      /* [n, 256] 1 = committed (frozen), in/out */
@@ -176,12 +202,31 @@ typedef struct {
                            compacted in the order of the uncommitted rows */
 } dg_capture;
 
+/* Temperature sampling of a step (write-up Figure 9, annealed temperature,
+ * and Figure 10, temperature 1).  At canvas b with step[b] = t steps taken
+ * in its block the temperature is tau_t = tau0 (1 - t / budget) for
+ * budget > 0 and tau0 for budget = 0, clamped at 0.  With tau_t > 0 the
+ * step's entropy and lse are those of softmax(z / tau_t) and sample holds
+ * the Gumbel-max draw argmax_v (z_v / tau_t + g_v): g_v = -ln(-ln u_v),
+ * u_v = ((w >> 8) + 0.5) 2^-24 with w word (v mod 4) of Philox4x32-10
+ * (Salmon et al., SC'11) of counter (v div 4, position, t, b) and key
+ * (low, high 32 bits of seed).  With tau_t = 0: entropy 0, sample = argmax
+ * and lse of the raw logits.  argmax stays the raw logits' argmax.  Pass
+ * sample as the token candidates of dg_eb_select. */
+typedef struct {
+  float tau0;            /* >= 0, finite */
+  int32_t budget;        /* >= 0 */
+  uint64_t seed;
+  int32_t* sample;       /* [n, 256] drawn token (uncommitted positions only) */
+} dg_sampling;
+
 typedef struct {
   float* entropy;        /* [n, 256] nats, >= 0 (uncommitted positions only) */
   float* lse;            /* [n, 256] log-sum-exp of the logits */
   int32_t* argmax;       /* [n, 256] lowest vocab id of the largest logit */
   float* logits;         /* NULL or [n*256, V] fp32 (uncommitted rows only) */
   dg_capture* capture;   /* (host) NULL or capture pointers */
+  const dg_sampling* sampling; /* (host) NULL: greedy step */
 } dg_step_out;
 
 /* Stage 2 forward (write-up Figure 4, "denoising loop"): embed the n
@@ -211,10 +256,12 @@ dg_status dg_eb_select(dg_ctx* ctx, const dg_canvas_batch* batch,
                        int32_t* n_new, uint8_t* done);
 
 /* Stage 3 (write-up Figure 4, "encode & append"): run the canvas tokens
- * causally (position i sees the cache and canvas positions <= i) through the
- * layers and write each layer's K/V of the 256 positions into cache rows
- * [kv_len, kv_len + 256) of each canvas's slot; kv_len += 256.
- * DG_ERR_CAPACITY if kv_len + 256 > max_kv_len. */
+ * causally (position i sees the cache, the request's earlier canvases of
+ * the batch and its own canvas positions <= i) through the layers and write
+ * each layer's K/V of the 256 positions into cache rows [kv_len + 256 j,
+ * kv_len + 256 (j + 1)) of the canvas's slot, j = the canvas's index among
+ * its request's canvases; kv_len += 256 per canvas.
+ * DG_ERR_CAPACITY if a request's kv_len + 256 x its canvases > max_kv_len. */
 dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
 
 dg_status dg_set_kv_len(dg_ctx* ctx, int32_t req, int32_t len);

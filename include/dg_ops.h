@@ -35,9 +35,12 @@ dg_status dg_op_linear(const void* x, int32_t m, int32_t k, const void* w,
  * over the canvas plus attention to the cached context; model card "Model
  * Overview").  For canvas b, query head h, position i:
  *   o = sum_j softmax_j(q . k_j / sqrt(D)) v_j
- * over the prefix_len[b] cached keys of slot req[b] and the canvas_len
- * canvas keys (with causal != 0 only canvas keys j <= i), KV head
- * h / (Hq / Hkv).
+ * over the prefix_len[b] cached keys of slot req[b], the canvas keys of the
+ * canvases before b in the batch with the same req (several canvases of
+ * one request, contiguous in block order: model card "block-autoregressive
+ * multi-canvas sampling"), and the canvas_len keys of canvas b (with
+ * causal != 0 only its keys j <= i), KV head h / (Hq / Hkv).
+ * DG_ERR_INVALID_ARG if equal req entries are not contiguous.
  * qkv [n*canvas_len, (Hq + 2 Hkv) D] bf16 (Q, K, V of the canvas rows as
  * written by the Q/K/V projection); k_cache / v_cache: one layer,
  * [max_requests][Hkv][max_kv_len][D] bf16; out [n*canvas_len, Hq D] bf16.
@@ -64,12 +67,15 @@ dg_status dg_op_router_topk(const float* logits, int32_t tokens,
                             int32_t n_experts, int32_t top_k, int32_t* idx,
                             float* w, void* stream);
 
-/* Mixture-of-experts FFN of one layer on normalised rows: router logits,
+/* Mixture-of-experts FFN of one layer on normalised rows (write-up Table 1:
+ * 8 of 128 experts active per token, "+ 1 shared"): router logits,
  * top-k, grouping of the (token, rank) pairs by expert (per-expert slots
  * when the experts average at most 32 pairs, else a stable counting-sort
  * permutation), grouped gate/up GEMM with SwiGLU, grouped down GEMM scaled
  * by the gate weight, un-permute summing each token's pairs in rank order.
- *   y_t = sum_j w_tj W_d,e (silu(W_g,e x_t) * W_u,e x_t),  e = idx_tj.
+ *   y_t = sum_j w_tj W_d,e (silu(W_g,e x_t) * W_u,e x_t),  e = idx_tj,
+ * plus, with desc->n_shared_experts = 1, the shared expert (group E) with
+ * weight 1 as the token's last pair.
  * desc: hidden, n_experts, top_k, expert_ffn, expert_dtype are used;
  * weights: w_router, w_gate_up, w_down (packed) and the e4m3 scales are used.
  * xhat [T, H] bf16 -> y [T, H] fp32.  route_idx [T, k] / route_w [T, k] /
@@ -114,11 +120,27 @@ dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
                                       float* lse, int32_t* argmax,
                                       void* stream);
 
-/* Entropy-bounded selection on explicit state (same rule as dg_eb_select):
- * entropy [n, 256] fp32, argmax [n, 256] int32, committed [n, 256] uint8
- * in/out, tokens [n, 256] int32 in/out, step [n] int32 in/out, gamma [n]
+/* Tied LM head with temperature sampling (the rule of dg_sampling, with
+ * each row's temperature and counter given): xhat [M, H] bf16, embed
+ * [V, H] bf16 packed, tau [M] fp32 (>= 0), ctr [M, 3] int32 = (position,
+ * step, canvas) words of the Philox counter, seed the 64-bit key ->
+ * entropy, lse [M] of softmax(z / tau) (tau 0: entropy 0, lse of z),
+ * argmax [M] of z, sample [M] drawn token.  All pointers are device
+ * memory; workspace of dg_op_lmhead_sample_workspace_bytes(m, vocab). */
+dg_status dg_op_lmhead_sample(const void* xhat, int32_t m, int32_t hidden,
+                              const void* embed, int32_t vocab, const float* tau,
+                              const int32_t* ctr, uint64_t seed, float* entropy,
+                              float* lse, int32_t* argmax, int32_t* sample,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+size_t dg_op_lmhead_sample_workspace_bytes(int32_t m, int32_t vocab);
+
+/* Entropy-bounded selection on explicit state (same rule as dg_eb_select)
+ * over n canvases of C = canvas_len positions (0: 256):
+ * entropy [n, C] fp32, argmax [n, C] int32, committed [n, C] uint8
+ * in/out, tokens [n, C] int32 in/out, step [n] int32 in/out, gamma [n]
  * fp32, n_new [n] int32 out, done [n] uint8 out. */
-dg_status dg_op_eb_select(int32_t n, const float* entropy,
+dg_status dg_op_eb_select(int32_t n, int32_t canvas_len, const float* entropy,
                           const int32_t* argmax, uint8_t* committed,
                           int32_t* tokens, int32_t* step, const float* gamma,
                           int32_t step_cap, int32_t refine, int32_t* n_new,

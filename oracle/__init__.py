@@ -37,7 +37,10 @@ from .model import (  # noqa: F401
     canvas_attention,
     router_topk,
     moe_mixture,
+    moe_layer,
     lm_head_stats,
+    lm_head_sample,
+    temperature,
     eb_select,
     denoise_step,
     commit_block,

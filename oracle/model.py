@@ -40,6 +40,23 @@ R9  Several canvases of one request (multi-canvas sampling, model card
     then to every position of the request's canvases before it (earlier
     blocks are fully visible, later ones not: block-causal), then to its own
     canvas (bidirectional, or causal in the commit pass).
+R10 "+ 1 shared" expert (write-up Table 1): a SwiGLU expert of the same
+    width that every token uses next to its routed experts, its output
+    added with weight 1 (not gated by the router, which scores the routed
+    experts only); stored as the last expert group.
+R11 Temperature sampling with annealing (write-up Figure 9: "higher N
+    yields milder temperature annealing"; Figure 10: "temperature tau_t = 1"
+    without annealing): at a canvas's step t (steps already taken in its
+    block) the temperature is tau_t = tau_0 (1 - t / N) for a step budget
+    N > 0, tau_0 for N = 0, clamped at 0.  With tau_t > 0 the position's
+    distribution is softmax(z / tau_t): its entropy is what EB ranks, and
+    its token is a draw from it by the Gumbel-max rule, argmax_v
+    (z_v / tau_t + g_v) with g_v = -ln(-ln u_v), u_v from Philox4x32-10
+    (counter (v div 4, position, t, canvas), key = the 64-bit seed; output
+    v mod 4; 24-bit uniforms).  With tau_t = 0 the distribution is the
+    point mass on the argmax: entropy 0, token = argmax, and lse reports
+    the raw logits' log-sum-exp.  Sampling off (the default) is the greedy
+    step of R5.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -55,6 +72,7 @@ import numpy as np
 from threadpoolctl import threadpool_limits
 
 from .numerics import round_bf16, decode_e4m3
+from .philox import philox4x32_10, uniform24
 
 CANVAS = 256
 
@@ -71,6 +89,7 @@ class Shapes:
     expert_ffn: int
     vocab: int
     rms_eps: float = 1e-6
+    n_shared_experts: int = 0   # reading R10
 
 
 def _f64(a):
@@ -239,6 +258,59 @@ def lm_head_stats(xhat, embed, want_logits=False):
     return out
 
 
+def temperature(tau0, budget, step):
+    """tau_t of reading R11 for the steps already taken in the block."""
+    step = np.asarray(step, dtype=np.float64)
+    if budget > 0:
+        return np.maximum(tau0 * (1.0 - step / budget), 0.0)
+    return np.maximum(np.full_like(step, tau0), 0.0)
+
+
+def gumbel(v, pos, step, canvas, seed):
+    """g_v = -ln(-ln u_v) for vocabulary ids v (array) of one position
+    (reading R11)."""
+    v = np.asarray(v, dtype=np.int64)
+    out = philox4x32_10(v // 4, pos, step, canvas, seed & 0xFFFFFFFF,
+                        (seed >> 32) & 0xFFFFFFFF)
+    x = np.choose(v % 4, out)
+    u = uniform24(x)
+    return -np.log(-np.log(u))
+
+
+def lm_head_sample(xhat, embed, tau, ctr, seed):
+    """Vocabulary statistics at the rows' temperatures and the sampled
+    tokens (reading R11).  xhat [M, H]; tau [M]; ctr [M, 3] = (position,
+    step, canvas) of each row; seed: 64-bit key.  Returns dict with lse,
+    entropy (of softmax(z / tau)), argmax (of z) and sample per row."""
+    z = _f64(xhat) @ _f64(embed).T
+    m_rows, v_count = z.shape
+    lse = np.zeros(m_rows)
+    ent = np.zeros(m_rows)
+    sample = np.zeros(m_rows, dtype=np.int64)
+    argmax = np.argmax(z, axis=1)
+    vids = np.arange(v_count)
+    for r in range(m_rows):
+        t = float(tau[r])
+        if t <= 0.0:
+            st = lm_head_stats(xhat[r:r + 1], embed)
+            lse[r] = st["lse"][0]
+            ent[r] = 0.0
+            sample[r] = argmax[r]
+            continue
+        zs = z[r] / t
+        zm = np.max(zs)
+        lse[r] = zm + np.log(np.sum(np.exp(zs - zm)))
+        p = np.exp(zs - lse[r])
+        with np.errstate(divide="ignore", invalid="ignore"):
+            plogp = np.where(p > 0, p * np.log(p), 0.0)
+        ent[r] = max(-np.sum(plogp), 0.0)
+        score = zs + gumbel(vids, int(ctr[r][0]), int(ctr[r][1]),
+                            int(ctr[r][2]), seed)
+        sample[r] = int(np.argmax(score))
+    return {"lse": lse, "entropy": ent, "argmax": argmax, "sample": sample,
+            "logits": z}
+
+
 def eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,
               refine=True):
     """Entropy-bounded selection for a batch of canvases (readings R6, R7).
@@ -286,6 +358,26 @@ def eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,
         n_new[b] = n
         done[b] = 1 if n == len(unc) else 0
     return committed, tokens, step, n_new, done
+
+
+def moe_layer(sh, lw, xh, mirror=True):
+    """The FFN of one layer on normed rows xh [T, H] (readings R4, R10):
+    router logits r = xh W_r^T over the routed experts, top-k routing, and
+    the mixture of the routed experts plus, with a shared expert, that
+    expert (the last group of the expert matrices) with weight 1.
+    Returns (r, idx [T, k], w [T, k], y [T, H])."""
+    r = _f64(xh) @ _f64(lw["w_router"]).T
+    idx, w = router_topk(r, sh.top_k)
+    idx_all, w_all = idx, w
+    if sh.n_shared_experts:
+        t_count = idx.shape[0]
+        idx_all = np.concatenate(
+            [idx, np.full((t_count, 1), sh.n_experts, dtype=idx.dtype)], axis=1)
+        w_all = np.concatenate([w, np.ones((t_count, 1))], axis=1)
+    y = moe_mixture(xh, idx_all, w_all, lw["w_gate_up"], lw["w_down"],
+                    lw.get("gate_up_scale"), lw.get("down_scale"),
+                    mirror=mirror)
+    return r, idx, w, y
 
 
 def _split_qkv(qkv, sh):
@@ -356,11 +448,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
         x_mid = x
         xh_attn = xh
         xh = _bf(rmsnorm(x, lw["ffn_norm"], sh.rms_eps), mirror)
-        r = xh @ _f64(lw["w_router"]).T
-        idx, w = router_topk(r, sh.top_k)
-        y = moe_mixture(xh, idx, w, lw["w_gate_up"], lw["w_down"],
-                        lw.get("gate_up_scale"), lw.get("down_scale"),
-                        mirror=mirror)
+        r, idx, w, y = moe_layer(sh, lw, xh, mirror)
         x = x + y
         if capture is not None:
             # every value the layer computed, in order: its input residual,
@@ -375,7 +463,8 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
 
 
 def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
-                 want_logits=False, capture=None, request=None):
+                 want_logits=False, capture=None, request=None, sampling=None,
+                 step=None):
     """One denoising forward over B canvases (write-up Figure 4, stage 2).
 
     weights: {"embed" [V,H], "final_norm" [H], "layers": [per-layer dict with
@@ -395,7 +484,15 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
                         request=request)
     rows = np.nonzero(committed.reshape(-1) == 0)[0]
     xf = _bf(rmsnorm(x[rows], weights["final_norm"], sh.rms_eps), mirror)
-    st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
+    if sampling is None:
+        st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
+    else:   # reading R11: (tau_0, budget N, seed); step [B] of each canvas
+        tau0, budget, seed = sampling
+        steps = np.asarray(step, dtype=np.int64)
+        canvas = rows // c_len
+        tau = temperature(tau0, budget, steps[canvas])
+        ctr = np.stack([rows % c_len, steps[canvas], canvas], axis=1)
+        st = lm_head_sample(xf, weights["embed"], tau, ctr, seed)
     ent = np.full(b_count * c_len, np.nan)
     lse = np.full(b_count * c_len, np.nan)
     am = np.full(b_count * c_len, -1, dtype=np.int64)
@@ -406,6 +503,10 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
            "lse": lse.reshape(b_count, c_len),
            "argmax": am.reshape(b_count, c_len), "rows": rows,
            "final_xhat": xf}
+    if sampling is not None:
+        smp = np.full(b_count * c_len, -1, dtype=np.int64)
+        smp[rows] = st["sample"]
+        out["sample"] = smp.reshape(b_count, c_len)
     if want_logits:
         out["logits"] = st["logits"]
     return out

@@ -23,7 +23,8 @@ def log(msg):
 def oshape(s):
     return oracle.Shapes(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads,
                          s.head_dim, s.n_experts, s.top_k, s.expert_ffn,
-                         s.vocab, s.rms_eps)
+                         s.vocab, s.rms_eps,
+                         getattr(s, "n_shared_experts", 0))
 
 
 def to_dev(w, dev=DEV):

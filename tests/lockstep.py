@@ -51,13 +51,14 @@ class Lockstep:
     the batch) of the canvases the oracle runs; causal: commit mode."""
 
     def __init__(self, shape, eng, w, n_full, req, plen, sel, cap_o, tag,
-                 causal=False, kv_o=None, seed=0):
+                 causal=False, kv_o=None, seed=0, C=256):
         self.s, self.eng, self.w, self.tag = shape, eng, w, tag
         self.n_full, self.req, self.plen = n_full, list(req), list(plen)
         self.sel, self.cap_o, self.causal = list(sel), cap_o, causal
         self.kv_o = kv_o
-        self.T = n_full * 256
-        self.rows = np.concatenate([np.arange(b * 256, (b + 1) * 256)
+        self.C = C                    # positions per canvas
+        self.T = n_full * C
+        self.rows = np.concatenate([np.arange(b * C, (b + 1) * C)
                                     for b in self.sel])
         self.gi = torch.as_tensor(self.rows, device=DEV, dtype=torch.long)
         self.checked = 0
@@ -133,7 +134,7 @@ class Lockstep:
         qkv_o = self._full(c["qkv"], qkv_n, torch.bfloat16)
         o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
         kc, vc = self.eng.cache_view("k"), self.eng.cache_view("v")
-        dg.op_canvas_attention(qkv_o, self.n_full, 256, Hq, Hkv, D, kc[li],
+        dg.op_canvas_attention(qkv_o, self.n_full, self.C, Hq, Hkv, D, kc[li],
                                vc[li], self.eng.max_requests,
                                self.eng.max_kv_len, self.req, self.plen,
                                self.causal, 0, o)
@@ -195,7 +196,8 @@ def lockstep_head(shape, eng, w, ref, x_last, committed, n_full, sel, tag,
     rows_o = ref["rows"]                        # uncommitted rows, oracle order
     sel = list(sel)
     # the same rows at their places in the full batch
-    glob = np.array([sel[r // 256] * 256 + r % 256 for r in rows_o])
+    C = committed.shape[1]
+    glob = np.array([sel[r // C] * C + r % C for r in rows_o])
     # final norm of the oracle's residual rows
     xin = torch.as_tensor(x_last[rows_o], dtype=torch.float32, device=DEV)
     xf = torch.empty((len(rows_o), H), dtype=torch.bfloat16, device=DEV)

@@ -80,9 +80,13 @@ def test_create_rejects_bad_arguments_without_touching_memory():
     st = L.dg_create(ctypes.byref(d), ctypes.byref(w), 1, 4096, 1, fake, fake,
                      fake, ws - 1, None, ctypes.byref(out))
     assert st == 3
+    st = L.dg_create(ctypes.byref(d), ctypes.byref(w), 1, 4096, 65, fake, fake,
+                     fake, 1 << 40, None, ctypes.byref(out))
+    assert st == 1  # max_canvases > 64
+    # more canvases than requests (multi-canvas), workspace sized for 2
     st = L.dg_create(ctypes.byref(d), ctypes.byref(w), 1, 4096, 2, fake, fake,
                      fake, ws, None, ctypes.byref(out))
-    assert st == 1  # max_canvases > max_requests
+    assert st == 3
     # e4m3 experts without scales
     d8 = _desc(expert_dtype=dg.FP8_E4M3)
     st = L.dg_create(ctypes.byref(d8), ctypes.byref(w), 1, 4096, 1, fake,
@@ -107,17 +111,34 @@ def test_context_host_state_and_validation():
         assert L.dg_kv_len(ctx, 1) == 800
         assert L.dg_set_kv_len(ctx, 1, 1025) == 3
         assert L.dg_set_kv_len(ctx, 5, 0) == 1
-        # token-mode prefill is not provided
-        assert L.dg_prefill_kv(ctx, 0, 4, fake, None, None) == 6
+        # prefill: exactly one of tokens and k/v; capacity and slot checked
+        # before any launch, in both modes
+        assert L.dg_prefill_kv(ctx, 0, 4, fake, fake, fake) == 1
+        assert L.dg_prefill_kv(ctx, 0, 4, None, fake, None) == 1
         assert L.dg_prefill_kv(ctx, 0, 2000, None, fake, fake) == 3
+        assert L.dg_prefill_kv(ctx, 0, 2000, fake, None, None) == 3
+        assert L.dg_prefill_kv(ctx, 7, 4, fake, None, None) == 1
+        assert L.dg_kv_len(ctx, 0) == 0
         # batch validation
         req = (ctypes.c_int32 * 3)(0, 1, 2)
         b = dg.CanvasBatch(3, req, 0x1000, 0x1000, 0x1000)
         out = dg.StepOut(0x1000, 0x1000, 0x1000, None, None)
         assert L.dg_denoise_step(ctx, ctypes.byref(b), ctypes.byref(out)) == 3
-        req2 = (ctypes.c_int32 * 2)(1, 1)
-        b2 = dg.CanvasBatch(2, req2, 0x1000, 0x1000, 0x1000)
-        assert L.dg_commit_block(ctx, ctypes.byref(b2)) == 1  # not distinct
+        # the canvases of one request must be contiguous
+        req2 = (ctypes.c_int32 * 2)(1, 2)
+        req2n = (ctypes.c_int32 * 3)(1, 2, 1)
+        b2 = dg.CanvasBatch(3, req2n, 0x1000, 0x1000, 0x1000)
+        ctx3 = ctypes.c_void_p()
+        assert L.dg_create(ctypes.byref(d), ctypes.byref(w), 3, 1024, 3, fake,
+                           fake, fake, L.dg_workspace_bytes(ctypes.byref(d), 3),
+                           None, ctypes.byref(ctx3)) == 0
+        assert L.dg_commit_block(ctx3, ctypes.byref(b2)) == 1
+        assert L.dg_denoise_step(ctx3, ctypes.byref(b2), ctypes.byref(
+            dg.StepOut(0x1000, 0x1000, 0x1000, None, None))) == 1
+        L.dg_destroy(ctx3)
+        # two canvases of request 1 after 800 rows: 800 + 2 x 256 > 1024
+        b2c = dg.CanvasBatch(2, (ctypes.c_int32 * 2)(1, 1), 0x1000, 0x1000, 0x1000)
+        assert L.dg_commit_block(ctx, ctypes.byref(b2c)) == 3
         req3 = (ctypes.c_int32 * 1)(1)
         b3 = dg.CanvasBatch(1, req3, 0x1000, 0x1000, 0x1000)
         # 800 + 256 > max_kv_len 1024: refused before any launch
@@ -129,9 +150,10 @@ def test_context_host_state_and_validation():
 def test_sampler_and_ops_validation():
     L = dg.lib()
     f = ctypes.c_void_p(0x1000)
-    assert L.dg_op_eb_select(1, f, f, f, f, f, f, 0, 1, f, f, None) == 1
-    assert L.dg_op_eb_select(0, f, f, f, f, f, f, 4, 1, f, f, None) == 3
-    assert L.dg_op_eb_select(1, None, f, f, f, f, f, 4, 1, f, f, None) == 1
+    assert L.dg_op_eb_select(1, 256, f, f, f, f, f, f, 0, 1, f, f, None) == 1
+    assert L.dg_op_eb_select(0, 256, f, f, f, f, f, f, 4, 1, f, f, None) == 3
+    assert L.dg_op_eb_select(1, 256, None, f, f, f, f, f, 4, 1, f, f, None) == 1
+    assert L.dg_op_eb_select(1, 257, f, f, f, f, f, f, 4, 1, f, f, None) == 2
     assert L.dg_op_router_topk(f, 4, 8, 9, f, f, None) == 2
     assert L.dg_op_linear(f, 4, 100, f, 8, 0, f, None) == 2
     assert L.dg_op_linear(f, 4, 128, f, 8, 7, f, None) == 1

@@ -28,12 +28,14 @@ def _randn(shape, std, name, dtype=torch.bfloat16, seed=7):
 
 # Projection shapes of one 2048-hidden layer (Q/K/V, output, router) at 256
 # rows (32 x 64 tiles), plus ragged rows/columns (90 columns: scalar
-# stores), K not a multiple of the 4-step pipeline (K = 448, 320) and a
-# many-row product on 64 x 64 tiles (4096 x 512).
+# stores), K not a multiple of the 4-step pipeline (K = 448, 320), and
+# products over >= 1024 rows on the 256 x 256 tiles (a ragged last row tile,
+# N not a multiple of 256, K = 448).
 @pytest.mark.parametrize("m,k,n", [(300, 256, 200), (1, 128, 64),
                                    (256, 2048, 4096), (256, 2048, 2048),
                                    (256, 2048, 128), (200, 448, 96),
-                                   (200, 320, 90), (4096, 256, 512)])
+                                   (200, 320, 90), (4096, 256, 512),
+                                   (1100, 2048, 4096), (2048, 448, 320)])
 def test_linear_three_modes(m, k, n):
     log(f"linear m={m} k={k} n={n}")
     x = _randn((m, k), 1.0, f"lin.x{m}")
@@ -174,6 +176,16 @@ def test_attention_batch_of_canvases_with_own_prefixes():
     _attn_case(3, 256, 16, 8, 128, [2048, 0, 700], 2048, True, 0, tag="b3c")
 
 
+def test_attention_two_query_blocks_per_wave():
+    """Key ranges long enough for the 256-row workgroups (two 16-row query
+    blocks per wave, workgroups of one KV head and split on one XCD):
+    causal with two canvases of ragged prefixes, one KV head per query head,
+    a ragged canvas whose last workgroup holds invalid rows, head dim 64."""
+    _attn_case(2, 256, 16, 8, 128, [20000, 9001], 20480, True, 0, tag="qb2c")
+    _attn_case(1, 256, 4, 4, 64, [12000], 12288, False, 0, tag="qb2g1")
+    _attn_case(1, 100, 8, 2, 128, [30000], 30208, False, 0, tag="qb2c100")
+
+
 def test_attention_long_prefix_sampled_rows():
     """131072 cached keys (long-context workload) with the launch the step
     uses; the oracle checks 6 sampled canvas positions of every head."""
@@ -241,16 +253,12 @@ def _moe_case(shape, T, tag, top_k=None, same_rows=False):
                                   "final_norm": w["final_norm"],
                                   "layers": [lw]})["layers"][0]
     x64 = np32(xh).astype(np.float64)
-    r = x64 @ lwn["w_router"].astype(np.float64).T
-    o_idx, o_w = oracle.router_topk(r, shape.top_k)
+    r, o_idx, o_w, ref = oracle.moe_layer(oshape(shape), lwn, x64, mirror=True)
     g_idx = ridx.cpu().numpy()
     same = np.all(g_idx == o_idx, axis=1)
     marg = routing_margin(r, shape.top_k)
     assert np.all(marg[~same] < MARGIN), "routing differs at a clear margin"
     log(f"  routing: {int((~same).sum())} low-margin tokens differ")
-    ref = oracle.moe_mixture(x64, o_idx, o_w, lwn["w_gate_up"], lwn["w_down"],
-                             lwn.get("gate_up_scale"), lwn.get("down_scale"),
-                             mirror=True)
     e = rel_err(np32(y)[same], ref[same])
     log(f"  mixture rel err {e:.2e}")
     assert e < TOL
@@ -291,6 +299,25 @@ def test_moe_tiled_path_full_size_layer_shape():
     _moe_case(GEMMA, 1024, "gemma_tiled")
     g8 = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": "fp8_e4m3"})
     _moe_case(g8, 1024, "gemma_fp8_tiled")
+
+
+def test_moe_large_tile_path_full_size_layer_shape():
+    # 4096 tokens x top-8 over 128 experts: 256 rows per expert on average,
+    # the grouped GEMMs on 256-row tiles (ragged per expert), bf16 and e4m3
+    _moe_case(GEMMA, 4096, "gemma_mm")
+    g8 = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": "fp8_e4m3"})
+    _moe_case(g8, 4096, "gemma_fp8_mm")
+
+
+@pytest.mark.parametrize("t", [256, 1024, 4096])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_moe_with_shared_expert(t, dtype):
+    # write-up Table 1 "+ 1 shared": every token's pairs end with the shared
+    # expert (weight 1) on each MoE path: weight streaming (256 tokens),
+    # 64-row tiles (1024) and 256-row tiles (4096)
+    g = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": dtype,
+                            "n_shared_experts": 1})
+    _moe_case(g, t, f"shared_{dtype}_{t}")
 
 
 def test_moe_e4m3_experts():
@@ -350,8 +377,10 @@ def test_lmhead_full_vocab_four_tiles():
 
 
 def test_lmhead_full_vocab_tiled_path():
-    # more than 256 rows: the tiled kernel, with a ragged last row tile
+    # more than 128 rows: the 256 x 256 tile kernel (two partials per
+    # workgroup), with a ragged last row tile
     _lm_case(300, 2048, 262144, "gemma_tiled")
+    _lm_case(129, 2048, 262144, "gemma_129")
 
 
 def test_lmhead_uniform_and_tied_logits():

@@ -391,3 +391,22 @@ def test_bench_block_loop_with_lookahead_is_the_same_decode():
         assert torch.equal(s0[k], s1[k]) and torch.equal(s0[k], s2[k]), k
     assert torch.equal(k0, k1) and torch.equal(v0, v1)
     assert torch.equal(k0, k2) and torch.equal(v0, v2)
+
+
+def test_denoise_step_with_shared_expert():
+    """A two-layer model with the "+ 1 shared" expert (write-up Table 1):
+    the step against the oracle (lockstep through every layer, the head and
+    EB), 180 uncommitted positions."""
+    shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096,
+                             n_shared_experts=1)
+    log("two layers with a shared expert")
+    eng, wn, prefix = _setup(shape, [300], 1024, seed=12)
+    cv = synth.make_canvas(shape, 1, 180, seed=12)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    ent, lse, am, logits = step_outputs(1, shape.vocab)
+    cap = _capture(shape, 1, 2)
+    eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
+    torch.cuda.synchronize()
+    _compare_step(shape, eng, wn, prefix, cv, ent, lse, am, logits, cap, 1,
+                  [300])

@@ -424,14 +424,14 @@ def test_eb_finished_canvas_is_left_alone():
 
 # ----------------------------------------------------------------- full step
 
-def _tiny_model(l_count=2, expert_dtype="bf16"):
+def _tiny_model(l_count=2, expert_dtype="bf16", shared=0):
     from block_discrete_diffusion_tok_amd import synth
     sh = synth.ModelShape(l_count, 32, 4, 2, 8, 6, 2, 16, 50,
-                          expert_dtype=expert_dtype)
+                          expert_dtype=expert_dtype, n_shared_experts=shared)
     w = synth.to_numpy_weights(synth.make_weights(sh, seed=3, gain_std=0.1))
     osh = oracle.Shapes(sh.n_layers, sh.hidden, sh.n_q_heads, sh.n_kv_heads,
                         sh.head_dim, sh.n_experts, sh.top_k, sh.expert_ffn,
-                        sh.vocab, sh.rms_eps)
+                        sh.vocab, sh.rms_eps, shared)
     return sh, osh, w
 
 
@@ -706,3 +706,147 @@ def test_multi_canvas_requests_must_be_contiguous():
     with pytest.raises(AssertionError):
         oracle.denoise_step(osh, w, tokens, np.zeros((3, 4), np.uint8), pre,
                             request=[0, 1, 0])
+
+
+
+# ----------------------------------------------------------------- shared expert
+
+def _first_layer_moe(osh, w, tokens, pre):
+    cap = []
+    oracle.model._layers_forward(osh, w, tokens, pre, False, False, cap)
+    return cap[0]
+
+
+def test_shared_expert_adds_a_routing_independent_term():
+    """With one shared expert the layer's MoE output is the routed mixture
+    plus a term that does not depend on the router: changing the router
+    matrix changes the routed part only, so the difference between the
+    shared and the unshared model (same routed weights) stays the same; the
+    term is not gated (scaling every router logit, which changes the gate
+    weights, leaves it unchanged) and it is linear in the shared down matrix."""
+    sh, osh, w = _tiny_model(l_count=1, shared=1)
+    E = sh.n_experts
+    tokens = RNG.integers(0, sh.vocab, (1, 9))
+    pre = _prefix(sh, 3)
+    osh0 = oracle.Shapes(*[getattr(osh, f) for f in (
+        "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
+        "n_experts", "top_k", "expert_ffn", "vocab", "rms_eps")], 0)
+    w0 = {**w, "layers": [{**w["layers"][0],
+                           "w_gate_up": w["layers"][0]["w_gate_up"][:E],
+                           "w_down": w["layers"][0]["w_down"][:E]}]}
+
+    def diff(wa, wb):
+        a = _first_layer_moe(osh, wa, tokens, pre)
+        b = _first_layer_moe(osh0, wb, tokens, pre)
+        np.testing.assert_array_equal(a["idx"], b["idx"])  # routing unchanged
+        return a["moe"] - b["moe"]
+
+    d1 = diff(w, w0)
+    assert np.max(np.abs(d1)) > 1e-6
+    lw = w["layers"][0]
+    w_r = {**w, "layers": [{**lw, "w_router": lw["w_router"] * 3.0}]}
+    w0_r = {**w0, "layers": [{**w0["layers"][0], "w_router": lw["w_router"] * 3.0}]}
+    np.testing.assert_allclose(diff(w_r, w0_r), d1, rtol=1e-9, atol=1e-13)
+    wd2 = lw["w_down"].copy()
+    wd2[E] *= 2.0
+    w_2 = {**w, "layers": [{**lw, "w_down": wd2}]}
+    np.testing.assert_allclose(diff(w_2, w0), 2.0 * d1, rtol=1e-9, atol=1e-13)
+
+
+def test_shared_expert_equals_a_routed_copy_chosen_by_every_token():
+    """With top-1 routing (gate weight 1 for the chosen expert) and a shared
+    expert equal to routed expert 0, every token routed to expert 0 gets
+    exactly twice expert 0's output."""
+    sh, osh, w = _tiny_model(l_count=1, shared=1)
+    sh1 = oracle.Shapes(*[getattr(osh, f) for f in (
+        "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
+        "n_experts")], 1, osh.expert_ffn, osh.vocab, osh.rms_eps, 1)
+    lw = w["layers"][0]
+    E = sh.n_experts
+    gu = lw["w_gate_up"].copy()
+    dn = lw["w_down"].copy()
+    gu[E], dn[E] = gu[0], dn[0]
+    router = np.zeros_like(lw["w_router"])
+    router[0] = 1.0     # expert 0 wins wherever sum(xhat) > 0 (others score 0)
+    w1 = {**w, "layers": [{**lw, "w_gate_up": gu, "w_down": dn,
+                           "w_router": router}]}
+    tokens = RNG.integers(0, sh.vocab, (1, 7))
+    pre = _prefix(sh, 2)
+    c = _first_layer_moe(sh1, w1, tokens, pre)
+    # with top-1 the gate weight is 1 whatever expert wins; the tokens whose
+    # router picks expert 0 get exactly 2 x expert 0's output
+    pick0 = c["idx"][:, 0] == 0
+    sh0 = oracle.Shapes(*[getattr(sh1, f) for f in (
+        "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim",
+        "n_experts", "top_k", "expert_ffn", "vocab", "rms_eps")], 0)
+    w_only0 = {**w1, "layers": [{**w1["layers"][0],
+                                 "w_gate_up": gu[:E], "w_down": dn[:E]}]}
+    c0 = _first_layer_moe(sh0, w_only0, tokens, pre)
+    assert pick0.any()
+    np.testing.assert_allclose(c["moe"][pick0], 2.0 * c0["moe"][pick0],
+                               rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------- sampling
+
+def test_philox4x32_10_known_answers(golden_dir):
+    from oracle.philox import philox4x32_10
+    ex = _load(golden_dir, "philox4x32_10_kat.json")
+    for case in ex["cases"]:
+        c = [int(x, 16) for x in case["counter"]]
+        k = [int(x, 16) for x in case["key"]]
+        got = philox4x32_10(*c, *k)
+        assert [int(g) for g in got] == [int(x, 16) for x in case["output"]]
+
+
+def test_temperature_schedule():
+    # tau_t = tau_0 (1 - t / N): half way down at N / 2, milder for larger N,
+    # constant without a budget
+    t = np.arange(48)
+    tau48 = oracle.temperature(1.0, 48, t)
+    assert tau48[0] == 1.0 and tau48[24] == 0.5
+    assert tau48[47] == pytest.approx(1.0 / 48.0)
+    tau192 = oracle.temperature(1.0, 192, t)
+    assert np.all(tau192[1:] > tau48[1:])
+    np.testing.assert_array_equal(oracle.temperature(0.8, 0, t), 0.8)
+    assert oracle.temperature(1.0, 48, 60) == 0.0
+
+
+def test_gumbel_max_draws_follow_the_tempered_softmax():
+    """Over 40000 positions the Gumbel-max tokens of fixed logits at
+    temperature 0.7 have the frequencies softmax(z / 0.7) (each within 5
+    standard deviations of a binomial count)."""
+    from oracle.model import gumbel
+    z = np.array([0.3, -1.2, 1.0, 0.0, 0.9])
+    tau = 0.7
+    p = np.exp(z / tau - np.max(z / tau))
+    p /= p.sum()
+    n = 40000
+    counts = np.zeros(5)
+    vids = np.arange(5)
+    g = np.stack([gumbel(vids, pos, 3, 1, 0x1234567890ABCDEF) for pos in range(n)])
+    picks = np.argmax(z / tau + g, axis=1)
+    counts = np.bincount(picks, minlength=5)
+    sd = np.sqrt(n * p * (1 - p))
+    assert np.all(np.abs(counts - n * p) < 5 * sd), (counts, n * p)
+
+
+def test_lm_head_sample_limits():
+    x = RNG.standard_normal((6, 16))
+    emb = RNG.standard_normal((40, 16)) * 0.5
+    ctr = np.stack([np.arange(6), np.zeros(6, int), np.zeros(6, int)], axis=1)
+    st = oracle.lm_head_stats(x, emb)
+    s1 = oracle.lm_head_sample(x, emb, np.ones(6), ctr, 7)
+    np.testing.assert_allclose(s1["entropy"], st["entropy"], rtol=1e-12)
+    np.testing.assert_allclose(s1["lse"], st["lse"], rtol=1e-12)
+    # a tiny temperature draws the argmax; temperature 0 is greedy
+    s_small = oracle.lm_head_sample(x, emb, np.full(6, 1e-4), ctr, 7)
+    np.testing.assert_array_equal(s_small["sample"], st["argmax"])
+    assert np.all(s_small["entropy"] < 1e-6)
+    s0 = oracle.lm_head_sample(x, emb, np.zeros(6), ctr, 7)
+    np.testing.assert_array_equal(s0["sample"], st["argmax"])
+    np.testing.assert_array_equal(s0["entropy"], 0.0)
+    # uniform logits: entropy ln V at any temperature
+    su = oracle.lm_head_sample(np.zeros((2, 16)), emb, np.array([0.3, 2.0]),
+                               ctr[:2], 7)
+    np.testing.assert_allclose(su["entropy"], math.log(40), rtol=1e-12)

@@ -1,6 +1,7 @@
 """Helpers for the parity tests at the larger workload shapes (not collected
 by pytest): lazy host copies of device weights and prefixes for the oracle,
-and the layer-by-layer comparison of the step captures."""
+and the composition checks (the step's fused kernels against the single-op
+entry points on the step's own state)."""
 import numpy as np
 import torch
 
@@ -67,59 +68,6 @@ def capture_buffers(shape, T, L, final=True):
     return cap
 
 
-class ChainChecker:
-    """Layer-by-layer comparison of the device captures (rows ``grow``) with
-    the oracle's capture ``cap_o`` of the same layers, from the same seeded
-    inputs, done while the oracle runs: pass it as the ``stop`` hook of
-    HostLayers.
-
-    Attention output, router logits and MoE output within TOL (max relative
-    error per tensor); routing bit-exact except where the oracle's margin is
-    below MARGIN.  A token routed differently carries a different residual
-    from then on, and through attention every later row depends on it, so
-    the comparison (and the oracle) ends with the first layer that has such
-    a token, its MoE output compared on the other rows."""
-
-    def __init__(self, shape, cap, cap_o, grow, tag):
-        self.shape, self.cap, self.cap_o, self.tag = shape, cap, cap_o, tag
-        self.gi = torch.as_tensor(np.asarray(grow), device=DEV,
-                                  dtype=torch.long)
-        self.checked = 0
-        self.flipped = False
-
-    def __call__(self, i):
-        self.finish()
-        return self.flipped
-
-    def finish(self):
-        while not self.flipped and self.checked < len(self.cap_o):
-            self._check(self.checked)
-            self.checked += 1
-        return self.checked
-
-    def _check(self, li):
-        c, cap, gi = self.cap_o[li], self.cap, self.gi
-        att = np32(cap["attn_out"][li].index_select(0, gi))
-        moe = np32(cap["moe_out"][li].index_select(0, gi))
-        rl = np32(cap["router_logits"][li].index_select(0, gi))
-        idx = cap["route_idx"][li].index_select(0, gi).cpu().numpy()
-        e_att = rel_err(att, c["attn"])
-        e_rl = rel_err(rl, c["router_logits"])
-        diff = np.any(idx != c["idx"], axis=1)
-        marg = routing_margin(c["router_logits"], self.shape.top_k)
-        e_moe = rel_err(moe[~diff], c["moe"][~diff])
-        log(f"  {self.tag} layer {li}: attn {e_att:.2e} router {e_rl:.2e} "
-            f"moe {e_moe:.2e}; routing differences {int(diff.sum())} at "
-            f"relative margins {np.sort(marg[diff]).tolist()}")
-        assert np.all(marg[diff] < MARGIN), \
-            f"{self.tag} layer {li}: routing differs at a clear margin"
-        assert e_att < TOL and e_rl < TOL and e_moe < TOL
-        if diff.any():
-            self.flipped = True
-            log(f"  {self.tag}: low-margin routing difference in layer {li}; "
-                "the later layers are checked by composition")
-
-
 def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
     """Every layer of a step (its captures) against the same layer computed
     by the single-op entry points (each compared with the oracle by the op
@@ -127,9 +75,10 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
     x_0 = E[tokens], x_(l+1) = x_l + attn_out_l W_o^T + moe_out_l.  This
     checks, at the full depth and size, that each layer reads its own
     weights and cache rows and that the fused kernels of the step compute
-    what the separate ops compute.  Agreement is to rounding (the rebuilt
-    residual is a float32 sum in another order), so the bounds are TOL and
-    MARGIN as for the oracle."""
+    what the separate ops compute.  The residual is rebuilt with the step's
+    own output-projection kernel and the same float32 additions, so agreement
+    is expected to be exact; the bounds are TOL and MARGIN as for the
+    oracle."""
     s = shape
     T = tokens.numel()
     H, D, Hq, Hkv = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads
@@ -141,7 +90,7 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
     worst_att = worst_moe = 0.0
     flips = 0
     for li in range(s.n_layers):
-        lw = w["layers"][li]
+        lw = eng.weights["layers"][li]
         o_cap = cap["attn_out"][li]
         if li in layers:
             xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
@@ -149,11 +98,11 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
             qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
             dg.op_linear(xh, lw["w_qkv"], qkv, 0)
             o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
-            dg.op_canvas_attention(qkv, n, 256, Hq, Hkv, D, kc_all[li],
+            dg.op_canvas_attention(qkv, n, T // n, Hq, Hkv, D, kc_all[li],
                                    vc_all[li], eng.max_requests,
                                    eng.max_kv_len, req, plen, False, 0, o)
             e_att = rel_err(np32(o), np32(o_cap))
-        x = x + o_cap.float() @ lw["w_o"].float().t()
+        dg.op_linear(o_cap, lw["w_o"], x, 2)   # the step's own kernel
         if li in layers:
             xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
             dg.op_rmsnorm(x, lw["ffn_norm"], s.rms_eps, xh)
@@ -177,3 +126,54 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
         f"{worst_att:.2e}, moe {worst_moe:.2e}, low-margin routing "
         f"differences {flips}")
     return x
+
+
+def check_commit_composition(eng, shape, w, tokens, req, plen, tag, C=256):
+    """The K/V rows dg_commit_block appended (cache rows [plen, plen + 256)
+    of every layer) against the same causal encode run through the
+    single-op entry points from the same tokens: embedding, then per layer
+    rmsnorm, Q/K/V projection (whose K/V slices must equal the appended
+    rows), causal attention, output projection, rmsnorm and MoE, the
+    residual carried by the ops themselves (the MoE sum is added once, as
+    the step's un-permute adds it)."""
+    s = shape
+    n = len(req)
+    T = n * C
+    H, D, Hq, Hkv = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads
+    qkv_n = (Hq + 2 * Hkv) * D
+    kc_all, vc_all = eng.cache_view("k"), eng.cache_view("v")
+    x = w["embed"][tokens.reshape(-1).long()].float()
+    worst = 0.0
+    for li in range(s.n_layers):
+        lw = eng.weights["layers"][li]
+        xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        dg.op_rmsnorm(x, lw["attn_norm"], s.rms_eps, xh)
+        qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
+        dg.op_linear(xh, lw["w_qkv"], qkv, 0)
+        for b in range(n):
+            rows = slice(b * C, (b + 1) * C)
+            # after the request's earlier canvases of the batch
+            j = 0
+            while b - j - 1 >= 0 and req[b - j - 1] == req[b]:
+                j += 1
+            p = plen[b] + j * C
+            k_op = qkv[rows, Hq * D:(Hq + Hkv) * D].reshape(C, Hkv, D).transpose(0, 1)
+            v_op = qkv[rows, (Hq + Hkv) * D:].reshape(C, Hkv, D).transpose(0, 1)
+            ek = rel_err(np32(kc_all[li, req[b], :, p:p + C]), np32(k_op))
+            ev = rel_err(np32(vc_all[li, req[b], :, p:p + C]), np32(v_op))
+            worst = max(worst, ek, ev)
+            assert ek < TOL and ev < TOL, \
+                f"{tag} commit layer {li} canvas {b}: K {ek:.2e} V {ev:.2e}"
+        if li == s.n_layers - 1:
+            break
+        o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
+        dg.op_canvas_attention(qkv, n, C, Hq, Hkv, D, kc_all[li], vc_all[li],
+                               eng.max_requests, eng.max_kv_len, req, plen,
+                               True, 0, o)
+        dg.op_linear(o, lw["w_o"], x, 2)
+        dg.op_rmsnorm(x, lw["ffn_norm"], s.rms_eps, xh)
+        y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        dg.op_moe(s, lw, xh, y)
+        x = x + y
+    log(f"  {tag} commit composition over {s.n_layers} layers: worst K/V "
+        f"rel err {worst:.2e}")
