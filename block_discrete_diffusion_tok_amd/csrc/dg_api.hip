@@ -905,8 +905,10 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
   const dg_sampling* smp = out->sampling;
   if (smp) {
     if (!smp->sample) return fail(c, DG_ERR_INVALID_ARG, "sampling->sample is NULL");
-    if (!(smp->tau0 >= 0.f) || !std::isfinite(smp->tau0) || smp->budget < 0)
-      return fail(c, DG_ERR_INVALID_ARG, "need finite tau0 >= 0 and budget >= 0");
+    // tau0 below 1e-6 (other than 0) would overflow z / tau in fp32
+    if (!std::isfinite(smp->tau0) || !(smp->tau0 == 0.f || smp->tau0 >= 1e-6f) ||
+        smp->budget < 0)
+      return fail(c, DG_ERR_INVALID_ARG, "need tau0 = 0 or finite >= 1e-6, budget >= 0");
   }
   const dg_model_desc& d = c->d;
   const int n = bt->n, C = c->C, T = n * C, H = d.hidden;

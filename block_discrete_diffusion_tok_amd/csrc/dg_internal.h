@@ -145,10 +145,16 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
     c[3] = lo0;
   }
 }
-// -ln(-ln u) of a Philox output word (u in (0, 1), exact in fp32)
+// -ln(-ln u) of a Philox output word, u = (k + 1/2) 2^-24 with k = x >> 8.
+// u = (2k + 1) 2^-25 is exact in fp32 only below 1/2; above it 1 - u =
+// (2^25 - 2k - 1) 2^-25 is, and -ln u = -log1p(-(1 - u)) keeps full
+// relative accuracy there, where the largest draws (u near 1) come from.
 __device__ __forceinline__ float gumbel_of(uint32_t x) {
-  const float u = ((float)(x >> 8) + 0.5f) * 5.9604644775390625e-8f;
-  return -logf(-logf(u));
+  const uint32_t k = x >> 8;
+  const float l = k < (1u << 23)
+                      ? -logf((float)(2 * k + 1) * 2.98023223876953125e-8f)
+                      : -log1pf(-(float)((1u << 25) - 2 * k - 1) * 2.98023223876953125e-8f);
+  return -logf(l);
 }
 // Keep the better (score, id): larger score, lower id on ties.
 __device__ __forceinline__ void best_merge(float& g, int& gi, float g2, int gi2) {

@@ -214,7 +214,7 @@ typedef struct {
  * and lse of the raw logits.  argmax stays the raw logits' argmax.  Pass
  * sample as the token candidates of dg_eb_select. */
 typedef struct {
-  float tau0;            /* >= 0, finite */
+  float tau0;            /* 0 or finite >= 1e-6, else DG_ERR_INVALID_ARG */
   int32_t budget;        /* >= 0 */
   uint64_t seed;
   int32_t* sample;       /* [n, 256] drawn token (uncommitted positions only) */

@@ -122,7 +122,8 @@ dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
 
 /* Tied LM head with temperature sampling (the rule of dg_sampling, with
  * each row's temperature and counter given): xhat [M, H] bf16, embed
- * [V, H] bf16 packed, tau [M] fp32 (>= 0), ctr [M, 3] int32 = (position,
+ * [V, H] bf16 packed, tau [M] fp32 (0 or >= 1e-6: smaller positive values
+ * overflow z / tau, not checked), ctr [M, 3] int32 = (position,
  * step, canvas) words of the Philox counter, seed the 64-bit key ->
  * entropy, lse [M] of softmax(z / tau) (tau 0: entropy 0, lse of z),
  * argmax [M] of z, sample [M] drawn token.  All pointers are device

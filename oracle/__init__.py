@@ -40,6 +40,7 @@ from .model import (  # noqa: F401
     moe_layer,
     lm_head_stats,
     lm_head_sample,
+    gumbel,
     temperature,
     eb_select,
     denoise_step,
