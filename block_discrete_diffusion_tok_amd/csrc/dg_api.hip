@@ -602,8 +602,12 @@ dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt) {
 // uncommitted positions in compacted order (c->pos_map).  commit: write the
 // layer's canvas K/V into the cache first, causal attention, and stop after
 // the K/V of the last layer.
+// commit: causal canvas attention, K/V appended to the cache; the last layer
+// stops there unless full (AR mode, whose last layer also feeds the LM head,
+// every row in place).
 dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
-                    bool commit, const dg_capture* cap, int C = DG_CANVAS) {
+                    bool commit, const dg_capture* cap, int C = DG_CANVAS,
+                    bool full = false) {
   const dg_model_desc& d = c->d;
   const dg_layer_weights& w = c->layers[l];
   const int T = n * C, H = d.hidden, D = d.head_dim;
@@ -626,7 +630,7 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
     KRUN(c, 15, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
                                C, Hkv, D, kc, vc, req_stride,
                                head_stride, req, row0, s));
-    if (l == d.n_layers - 1) return DG_OK;
+    if (l == d.n_layers - 1 && !full) return DG_OK;
   }
   AttnArgs aa;
   memset(&aa, 0, sizeof(aa));
@@ -673,7 +677,7 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   const float* next_g = last ? c->final_norm : c->layers[l + 1].attn_norm;
   float* next_copy = (last && cap && cap->final_xhat) ? cap->final_xhat : nullptr;
   HIPCHK(c, run_moe(d, w, c->xh, T, mb, c->x, moe_out, nullptr, s, &c->prof, next_g,
-                    c->xh, next_copy, last ? c->pos_map : nullptr, true));
+                    c->xh, next_copy, last && !full ? c->pos_map : nullptr, true));
   if (cap) {
     const size_t tk = (size_t)T * d.top_k;
     const int K = pairs_per_token(d);
@@ -983,6 +987,45 @@ dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
     if (st != DG_OK) return st;
   }
   for (int b = 0; b < n; ++b) c->kv_len[req[b]] += C;  // per canvas
+  return DG_OK;
+}
+
+dg_status dg_ar_step(dg_ctx* c, int32_t n, const int32_t* req,
+                     const int32_t* tokens, const dg_step_out* out) {
+  if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  if (!req || !tokens || !out || !out->entropy || !out->lse || !out->argmax)
+    return fail(c, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (out->sampling || out->capture)
+    return fail(c, DG_ERR_UNSUPPORTED, "AR steps take no sampling or capture");
+  if (n < 1 || n > c->max_canvases * c->C)
+    return fail(c, DG_ERR_CAPACITY, "n outside 1..max_canvases x canvas_len");
+  if (n > DG_MAX_BATCH) return fail(c, DG_ERR_CAPACITY, "n above 64");
+  for (int b = 0; b < n; ++b)
+    if (req[b] < 0 || req[b] >= c->max_requests)
+      return fail(c, DG_ERR_INVALID_ARG, "req outside 0..max_requests-1");
+  const dg_model_desc& d = c->d;
+  int rq[DG_MAX_BATCH], plen[DG_MAX_BATCH], vis0[DG_MAX_BATCH];
+  if (!canvas_groups(n, req, vis0))
+    return fail(c, DG_ERR_INVALID_ARG, "the positions of one sequence must be contiguous");
+  for (int b = 0; b < n; ++b) {
+    rq[b] = req[b];
+    plen[b] = c->kv_len[req[b]];
+    if (plen[b] + (b - vis0[b]) + 1 > c->max_kv_len)
+      return fail(c, DG_ERR_CAPACITY, "KV cache full");
+  }
+  hipStream_t s = c->stream;
+  KRUN(c, 0, launch_embed_norm(tokens, n, c->embed, d.vocab, d.hidden, c->x,
+                               c->layers[0].attn_norm, d.rms_eps, c->xh, s));
+  for (int l = 0; l < d.n_layers; ++l) {
+    dg_status st = run_layer(c, l, n, rq, plen, true, nullptr, 1, true);
+    if (st != DG_OK) return st;
+  }
+  int n_tiles = 0;
+  KRUN(c, 12, run_lm_head(c->xh, n, nullptr, d.hidden, c->embed, d.vocab, c->lm_part,
+                          out->logits, nullptr, &n_tiles, s));
+  KRUN(c, 13, launch_lm_merge(c->lm_part, n_tiles, nullptr, n, nullptr, out->entropy,
+                              out->lse, out->argmax, s));
+  for (int b = 0; b < n; ++b) c->kv_len[req[b]] += 1;
   return DG_OK;
 }
 

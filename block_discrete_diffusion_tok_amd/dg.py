@@ -92,6 +92,7 @@ _SIGS = {
     "dg_eb_select": (_I, [_P, ctypes.POINTER(CanvasBatch), _P, _P, _P, _I, _I,
                           _P, _P]),
     "dg_commit_block": (_I, [_P, ctypes.POINTER(CanvasBatch)]),
+    "dg_ar_step": (_I, [_P, _I, ctypes.POINTER(_I), _P, ctypes.POINTER(StepOut)]),
     "dg_set_kv_len": (_I, [_P, _I, _I]),
     "dg_profile_enable": (_I, [_P, _I]),
     "dg_profile_read": (_I, [_P, _P, _P]),
@@ -349,6 +350,15 @@ class Engine:
                                   _ptr(argmax), _ptr(gamma), step_cap,
                                   int(refine), _ptr(n_new), _ptr(done)),
                self.ctx)
+
+    def ar_step(self, req, tokens, entropy, lse, argmax, logits=None):
+        """One AR decoding step: tokens [n] int32 on the device."""
+        reqs = _i32_array(req)
+        out = StepOut(entropy.data_ptr(), lse.data_ptr(), argmax.data_ptr(),
+                      None if logits is None else logits.data_ptr(), None,
+                      None)
+        _check(lib().dg_ar_step(self.ctx, len(req), reqs, tokens.data_ptr(),
+                                ctypes.byref(out)), self.ctx)
 
     def commit_block(self, req, tokens, committed, step):
         b = self._batch(req, tokens, committed, step)

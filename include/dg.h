@@ -264,6 +264,23 @@ dg_status dg_eb_select(dg_ctx* ctx, const dg_canvas_batch* batch,
  * DG_ERR_CAPACITY if a request's kv_len + 256 x its canvases > max_kv_len. */
 dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
 
+/* AR mode (write-up "What they did": the same weights still decode left to
+ * right; model card "Model Overview"): one causal decoding step for n
+ * positions.  tokens [n] int32 (device): position b holds the token at the
+ * next position of sequence req[b] (host [n]); positions of one sequence
+ * are contiguous and in order (the j-th of them sits at kv_len + j and
+ * sees the cache and the sequence's positions before it, like canvases of
+ * one position in dg_commit_block).  Each layer's K/V of the n positions
+ * are appended to the cache (kv_len += its positions per sequence) and the
+ * final-normed rows go through the tied LM head: entropy, lse, argmax [n]
+ * of each position's next-token distribution, logits NULL or [n, V].
+ * out->capture and out->sampling must be NULL (DG_ERR_UNSUPPORTED).
+ * n <= min(64, max_canvases x canvas_len), else DG_ERR_CAPACITY; a cache
+ * without room for the positions is DG_ERR_CAPACITY before any launch.
+ * Uses the context workspace like dg_denoise_step. */
+dg_status dg_ar_step(dg_ctx* ctx, int32_t n, const int32_t* req,
+                     const int32_t* tokens, const dg_step_out* out);
+
 dg_status dg_set_kv_len(dg_ctx* ctx, int32_t req, int32_t len);
 int32_t dg_kv_len(const dg_ctx* ctx, int32_t req); /* -1 on a bad slot */
 

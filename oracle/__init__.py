@@ -45,6 +45,7 @@ from .model import (  # noqa: F401
     eb_select,
     denoise_step,
     commit_block,
+    ar_step,
     expert_matrix,
 )
 from .numerics import round_bf16, decode_e4m3  # noqa: F401

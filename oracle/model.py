@@ -57,6 +57,13 @@ R11 Temperature sampling with annealing (write-up Figure 9: "higher N
     point mass on the argmax: entropy 0, token = argmax, and lse reports
     the raw logits' log-sum-exp.  Sampling off (the default) is the greedy
     step of R5.
+R12 AR mode (write-up "What they did": the weights still decode left to
+    right; model card "Model Overview"): a step takes one token per
+    sequence at the next position, runs it through the layers as a canvas of
+    one position in the commit pass (causal: it sees the cached prefix and
+    itself, no positional term, reading S9), appends the K/V it makes and
+    reads the next token's statistics off its final-normed row.  Greedy
+    (argmax) decoding only.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -407,14 +414,15 @@ def _earlier_canvases(request, b_count):
 
 
 def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
-                    kv_out=None, request=None):
+                    kv_out=None, request=None, full=False):
     """Embedding plus the L residual layers over B canvases.
 
     tokens [B, C]; prefix: list over canvases of (K, V), each [L, Hkv, P_b, D].
     request: optional [B] request ids; canvases sharing one see the earlier
     ones (reading R9).
     With ``kv_out`` (a list) the per-layer canvas K/V [Hkv, B*C, D] are
-    appended to it and the last layer stops after its K/V projection.
+    appended to it and, unless ``full``, the last layer stops after its K/V
+    projection.
     """
     b_count, c_len = tokens.shape
     earlier = _earlier_canvases(request, b_count)
@@ -427,7 +435,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
         q, k, v = _split_qkv(qkv, sh)
         if kv_out is not None:
             kv_out.append((k, v))
-            if li == len(weights["layers"]) - 1:
+            if li == len(weights["layers"]) - 1 and not full:
                 if capture is not None:   # what the last layer computed
                     capture.append({"x_in": x_in, "xh_attn": xh, "qkv": qkv})
                 break
@@ -509,6 +517,34 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
         out["sample"] = smp.reshape(b_count, c_len)
     if want_logits:
         out["logits"] = st["logits"]
+    return out
+
+
+def ar_step(sh, weights, tokens, prefix, mirror=True, request=None,
+            want_logits=False, capture=None):
+    """One left-to-right decoding step of the same weights (AR mode, reading
+    R12): tokens [n] is the token at position P_b of each sequence b (its
+    cached prefix holds positions 0..P_b-1); it attends causally to the
+    prefix and itself (a canvas of one position in the commit pass), the K/V
+    each layer makes for it are what the cache appends at row P_b, and the
+    final-normed row's logits give the next-token statistics.
+
+    Returns {"entropy", "lse", "argmax"} [n] (plus "logits" [n, V] with
+    ``want_logits``) and "kv": a list over sequences of (K, V), each
+    [L, Hkv, 1, D]."""
+    tokens = np.asarray(tokens).reshape(-1, 1)
+    kv = []
+    x = _layers_forward(sh, weights, tokens, prefix, mirror, True, capture,
+                        kv_out=kv, request=request, full=True)
+    xf = _bf(rmsnorm(x, weights["final_norm"], sh.rms_eps), mirror)
+    st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
+    out = {"entropy": st["entropy"], "lse": st["lse"], "argmax": st["argmax"],
+           "final_xhat": xf}
+    if want_logits:
+        out["logits"] = st["logits"]
+    out["kv"] = [(np.stack([k[:, b:b + 1] for k, _ in kv]),
+                  np.stack([v[:, b:b + 1] for _, v in kv]))
+                 for b in range(tokens.shape[0])]
     return out
 
 

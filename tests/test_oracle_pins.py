@@ -530,6 +530,54 @@ def test_commit_causal_block_equals_sequential_single_token_encodes(
         v_cache = np.concatenate([v_cache, v_new], axis=2)
 
 
+def test_ar_steps_equal_one_causal_chunk():
+    """AR mode (reading R12): decoding five tokens one step at a time, the
+    cache growing by each step's K/V, gives every step the statistics of the
+    matching row of one causal pass over the five tokens, and the K/V of
+    that pass's commit."""
+    sh, osh, w = _tiny_model(l_count=3)
+    n = 5
+    tokens = RNG.integers(0, sh.vocab, (1, n))
+    pre = _prefix(sh, 4)
+    x = _layers_forward(osh, w, tokens, pre, False, True, None, kv_out=[],
+                        full=True)
+    xf = oracle.rmsnorm(x, w["final_norm"], sh.rms_eps)
+    chunk = oracle.lm_head_stats(xf, w["embed"])
+    kb, vb = oracle.commit_block(osh, w, tokens, pre, mirror=False)[0]
+    k_cache, v_cache = pre[0]
+    for i in range(n):
+        out = oracle.ar_step(osh, w, tokens[0, i:i + 1], [(k_cache, v_cache)],
+                             mirror=False)
+        np.testing.assert_allclose(out["entropy"][0], chunk["entropy"][i],
+                                   rtol=1e-10)
+        np.testing.assert_allclose(out["lse"][0], chunk["lse"][i], rtol=1e-12)
+        assert out["argmax"][0] == chunk["argmax"][i]
+        k1, v1 = out["kv"][0]
+        np.testing.assert_allclose(k1[:, :, 0], kb[:, :, i], rtol=1e-10,
+                                   atol=1e-12)
+        np.testing.assert_allclose(v1[:, :, 0], vb[:, :, i], rtol=1e-10,
+                                   atol=1e-12)
+        k_cache = np.concatenate([k_cache, k1], axis=2)
+        v_cache = np.concatenate([v_cache, v1], axis=2)
+
+
+def test_ar_step_with_no_prefix_attends_to_itself_only():
+    """A first token with an empty cache: softmax over one key, so each query
+    head's attention output is its KV head's V of that token (grouped heads:
+    q head h reads KV head h // (Hq / Hkv))."""
+    sh, osh, w = _tiny_model(l_count=1)
+    cap = []
+    tok = RNG.integers(0, sh.vocab, (2,))
+    empty = [(np.zeros((1, sh.n_kv_heads, 0, sh.head_dim)),) * 2] * 2
+    oracle.ar_step(osh, w, tok, empty, mirror=False, capture=cap)
+    hd, hq, hkv = sh.head_dim, sh.n_q_heads, sh.n_kv_heads
+    v = cap[0]["qkv"][:, (hq + hkv) * hd:].reshape(2, hkv, hd)
+    o = cap[0]["attn"].reshape(2, hq, hd)
+    for h in range(hq):
+        np.testing.assert_allclose(o[:, h], v[:, h // (hq // hkv)],
+                                   rtol=1e-12, atol=1e-14)
+
+
 def test_mirror_mode_changes_results_only_by_bf16_rounding_size():
     sh, osh, w = _tiny_model()
     tokens = RNG.integers(0, sh.vocab, (1, 16))
