@@ -18,7 +18,9 @@ times (hipEvents around each denoise step and each EB selection); the same
 block decoded with the final-norm gain scaled so that EB commits ~19.74
 positions per step (the pages' tokens per forward) as a labelled variant;
 per-kernel times with their roofline fractions and the dominant kernel's
-roofline; the CPU oracle timed on a bounded sample of the same workload.
+roofline; labelled extras: AR decoding (greedy, one position per step) and
+token-mode prompt prefill on request 0; the CPU oracle timed on a bounded
+sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
   python bench.py --denoise-only 3     # a few plain denoise steps, for profilers
@@ -422,6 +424,54 @@ def tpf_matched(b, blocks):
                     f"Table 3 tokens per forward); no step queued ahead"}
 
 
+def ar_and_prefill(b, n_tokens=64):
+    """Labelled extras on request 0: AR decoding (n_tokens greedy steps of
+    one position, each fed the previous step's argmax, from the workload's
+    prefix) and token-mode prefill of a prompt of the prefix length; both
+    timed with hipEvents.  They overwrite request 0's cache."""
+    torch, wl = b.torch, b.wl
+    dev = "cuda"
+    ent = torch.zeros(1, dtype=torch.float32, device=dev)
+    lse = torch.zeros_like(ent)
+    am = torch.zeros(1, dtype=torch.int32, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    b.eng.set_kv_len(0, wl.prefix_len)
+    b.eng.ar_step([0], tok, ent, lse, am)          # warm-up
+    b.eng.set_kv_len(0, wl.prefix_len)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_tokens):
+        b.eng.ar_step([0], tok, ent, lse, am)
+        tok.copy_(am)
+    e1.record()
+    torch.cuda.synchronize()
+    ar_ms = e0.elapsed_time(e1)
+    P = min(wl.prefix_len, 8192)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    prompt = torch.randint(0, wl.shape.vocab, (P,), generator=g,
+                           dtype=torch.int32).to(dev)
+    b.eng.prefill_tokens(0, prompt)               # warm-up
+    torch.cuda.synchronize()
+    e0.record()
+    b.eng.prefill_tokens(0, prompt)
+    e1.record()
+    torch.cuda.synchronize()
+    pf_ms = e0.elapsed_time(e1)
+    b.eng.set_kv_len(0, wl.prefix_len)
+    return {"ar_decode": {"tokens": n_tokens, "prefix": wl.prefix_len,
+                          "ms_per_token": round(ar_ms / n_tokens, 4),
+                          "tok_s": round(n_tokens / (ar_ms / 1000.0), 1),
+                          "note": "labelled extra: batch 1, greedy, one "
+                                  "position per dg_ar_step"},
+            "prefill_tokens": {"tokens": P, "ms": round(pf_ms, 3),
+                               "tok_s": round(P / (pf_ms / 1000.0), 1),
+                               "note": "labelled extra: token-mode "
+                                       "dg_prefill_kv, causal encode in "
+                                       "chunks of 256"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawTextHelpFormatter)
@@ -433,6 +483,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tpf-variant", action="store_true")
+    ap.add_argument("--no-ar", action="store_true",
+                    help="skip the AR-decoding and token-prefill extras")
     ap.add_argument("--denoise-only", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -539,6 +591,11 @@ def main():
         log("[bench] TPF-matched variant")
         tpf = tpf_matched(b, args.steps)
 
+    extras = {}
+    if not args.no_ar:
+        log("[bench] AR decoding and token-mode prefill")
+        extras = ar_and_prefill(b)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -582,6 +639,7 @@ def main():
         "kernels": kernels,
         "lm_head_mean_rows": round(mean_rows, 2),
         "tpf_matched": tpf,
+        **extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

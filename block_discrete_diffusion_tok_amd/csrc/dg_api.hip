@@ -671,7 +671,7 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   KRUN(c, 4, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
   const MoeBufs& mb = ctx_moe_bufs(c);
   KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
-                           nullptr, nullptr, s, mb.counts, d.n_experts));
+                           nullptr, nullptr, s, mb.counts, expert_groups(d)));
   float* moe_out = (cap && cap->moe_out) ? cap->moe_out + (size_t)l * T * H : nullptr;
   const bool last = l == d.n_layers - 1;
   const float* next_g = last ? c->final_norm : c->layers[l + 1].attn_norm;

@@ -39,6 +39,7 @@ constexpr int kMmThreads = 512;
 constexpr int kMmBN = 256;   // weight rows per workgroup
 constexpr int kMmBM = 256;   // token rows per workgroup
 constexpr int kMmBK = 64;    // k per step
+constexpr int kSwzM = 8;     // token tiles per block of the tile order
 
 __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -85,13 +86,44 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int wn = wave & 1, wt = wave >> 1;        // 2 x 4 waves
-  const int nt = blockIdx.x, mt = blockIdx.y;
+  // ---- tile of this workgroup.  Workgroups are dealt to the 8 XCDs
+  // round-robin by linear id, each XCD with its own L2.  Tiles are ordered
+  // in blocks of kSwzM token tiles (for each block, every weight tile, for
+  // each the block's token tiles) and each XCD runs one contiguous run of
+  // that order: the ~32 tiles an XCD has in flight are ~4 weight tiles x 8
+  // token tiles, so each operand tile comes into its L2 once for several
+  // workgroups instead of once per workgroup.
+  // The order covers only the tiles that hold rows (the grid is sized for
+  // the most the device-side row counts allow): an expert GEMM's tile count
+  // and a live-row count are read first, and the workgroups past them leave,
+  // so the work spreads evenly over the XCDs.
+  int nt, mt;
+  {
+    const int gn = gridDim.x;
+    int gm = gridDim.y;
+    if (a.group_offsets) {
+      gm = min(gm, a.tile_offsets[a.n_groups]);
+    } else if (a.M_dev) {
+      const int m_rows = min(*a.M_dev, a.M);
+      if (m_rows <= a.rows_gt) return;   // another kernel's rows
+      gm = min(gm, (m_rows + kMmBM - 1) / kMmBM);
+    }
+    const int total = gn * gm;
+    const int lin = blockIdx.x + gn * blockIdx.y;
+    if (lin >= total) return;
+    const int x = lin & 7, q = total >> 3, r = total & 7;
+    const int o = x * q + min(x, r) + (lin >> 3);
+    const int bm = min(kSwzM, gm);
+    const int tb = o / (gn * bm);
+    const int rem = o - tb * gn * bm;
+    const int rows_in = min(bm, gm - tb * bm);
+    nt = rem / rows_in;
+    mt = tb * bm + rem % rows_in;
+  }
 
   // ---- which token rows this tile covers
   int group = 0, row_begin, row_end;
   if (a.group_offsets) {
-    const int total = a.tile_offsets[a.n_groups];
-    if (mt >= total) return;
     int lo = 0, hi = a.n_groups - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -102,7 +134,6 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
     row_end = a.group_offsets[group + 1];
   } else {
     const int m_rows = a.M_dev ? min(*a.M_dev, a.M) : a.M;
-    if (a.M_dev && m_rows <= a.rows_gt) return;   // another kernel's rows
     row_begin = mt * kMmBM;
     if (row_begin >= m_rows) return;
     row_end = m_rows;

@@ -292,10 +292,15 @@ __global__ __launch_bounds__(256) void topk_kernel(float* logits, int T, int E,
     w[(long long)t * K + lane] = my_w;
   }
   if (SLOTS && lane < K) {  // lane r < K takes a slot of its expert
-    const long long sl = (long long)my_id * cap + atomicAdd(&counts[my_id], 1);
-    slot_pair[sl] = t * K + lane;
-    slot_w[sl] = my_w;
-    slot_tok[sl] = t;
+    // (cap >= T and cleared counters leave every slot below cap; the test
+    // keeps a stale counter from writing past the expert's rows)
+    const int i = atomicAdd(&counts[my_id], 1);
+    if (i < cap) {
+      const long long sl = (long long)my_id * cap + i;
+      slot_pair[sl] = t * K + lane;
+      slot_w[sl] = my_w;
+      slot_tok[sl] = t;
+    }
   }
 }
 
@@ -323,24 +328,49 @@ __global__ __launch_bounds__(kChunk) void moe_count_kernel(
   if (tid < E) chunk_counts[(long long)blockIdx.x * E + tid] = hist[tid];
 }
 
-__global__ __launch_bounds__(256) void moe_scan_kernel(
+// Column scans of the chunk histogram [n_chunks][E]: expert offsets (the
+// exclusive scan of the experts' totals), tile offsets and each chunk's
+// base slot per expert.  1024 threads: thread t takes expert t % 256 (E <=
+// 256) and the contiguous run of chunks of part t / 256 (4 parts), so the
+// loads of a thread are independent and 4 x E of them are in flight.
+constexpr int kScanParts = 4;
+__global__ __launch_bounds__(1024) void moe_scan_kernel(
     int n_chunks, int E, int bm, const int32_t* chunk_counts,
     int32_t* chunk_base, int32_t* offsets, int32_t* tile_offsets,
     int32_t* counts) {
-  __shared__ int s_tot[256];
+  __shared__ int s_part[kScanParts][256];
+  __shared__ int s_off[256];
   __shared__ int s_tiles[256];
-  const int e = threadIdx.x;
-  int tot = 0;
+  const int e = threadIdx.x & 255, part = threadIdx.x >> 8;
+  const int per = (n_chunks + kScanParts - 1) / kScanParts;
+  const int c0 = part * per, c1 = min(n_chunks, c0 + per);
+  constexpr int U = 8;
+  int sum = 0;
   if (e < E)
-    for (int c = 0; c < n_chunks; ++c) tot += chunk_counts[(long long)c * E + e];
-  s_tot[e] = e < E ? tot : 0;
-  s_tiles[e] = e < E ? (tot + bm - 1) / bm : 0;
+    for (int c = c0; c < c1; c += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += v[u];
+    }
+  s_part[part][e] = e < E ? sum : 0;
   __syncthreads();
-  if (e == 0) {
+  if (threadIdx.x < 256) {
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < kScanParts; ++q) tot += s_part[q][e];
+    s_off[e] = tot;
+    s_tiles[e] = (tot + bm - 1) / bm;
+    if (e < E && counts) counts[e] = tot;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive scans over the (<= 256) experts
     int run = 0, runt = 0;
     for (int q = 0; q < E; ++q) {
-      const int o = s_tot[q];
-      s_tot[q] = run;
+      const int o = s_off[q];
+      s_off[q] = run;
       run += o;
       const int ot = s_tiles[q];
       s_tiles[q] = runt;
@@ -350,15 +380,26 @@ __global__ __launch_bounds__(256) void moe_scan_kernel(
     tile_offsets[E] = runt;
   }
   __syncthreads();
-  if (e < E) {
-    offsets[e] = s_tot[e];
+  if (threadIdx.x < E) {
+    offsets[e] = s_off[e];
     tile_offsets[e] = s_tiles[e];
-    if (counts) counts[e] = tot;
-    int base = s_tot[e];
-    for (int c = 0; c < n_chunks; ++c) {
-      chunk_base[(long long)c * E + e] = base;
-      base += chunk_counts[(long long)c * E + e];
-    }
+  }
+  if (e >= E) return;
+  // base of this part's first chunk: the expert's offset plus the earlier
+  // parts' counts
+  int base = s_off[e];
+  for (int q = 0; q < part; ++q) base += s_part[q][e];
+  for (int c = c0; c < c1; c += U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = c + u < c1 ? chunk_counts[(long long)(c + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c + u < c1) {
+        chunk_base[(long long)(c + u) * E + e] = base;
+        base += v[u];
+      }
   }
 }
 
@@ -944,12 +985,13 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
                        n_pairs, E, bm, offsets, tile_offsets, counts, perm);
     return hipGetLastError();
   }
+  if (E > 256) return hipErrorInvalidValue;
   const int nc = permute_chunks(n_pairs);
   hipLaunchKernelGGL(moe_count_kernel, dim3(nc), dim3(kChunk), 0, s, idx,
                      n_pairs, E, chunk_counts, local_rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(256), 0, s, nc, E, bm,
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, s, nc, E, bm,
                      chunk_counts, chunk_base, offsets, tile_offsets, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

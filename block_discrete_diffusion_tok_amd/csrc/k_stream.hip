@@ -176,7 +176,19 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int group = blockIdx.y, bx = blockIdx.x;
+  // Expert products: workgroups are dealt to the 8 XCDs round-robin by
+  // linear id, so the natural order spreads every expert's row tiles over
+  // all of them and each XCD's L2 fetches every expert's token rows.  With
+  // the expert count a multiple of 8, XCD x instead runs experts x, x + 8,
+  // ... (its j-th workgroup takes tile j % tiles of expert x + 8 (j / tiles)),
+  // and an expert's token rows come from HBM once.
+  int group = blockIdx.y, bx = blockIdx.x;
+  if (GROUPED && (gridDim.y & 7) == 0) {
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    const int j = lin >> 3;
+    group = (lin & 7) + 8 * (j / gridDim.x);
+    bx = j % gridDim.x;
+  }
 
   // ---- this wave's weight row tiles (16 rows each) and the packed address
   // of this lane's piece of their first block; tiles past the matrix read
@@ -243,7 +255,9 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   };
   const uint16_t* xsrc[IPW];
   auto set_rows = [&](int t0) {
-    const int lim = GROUPED ? a.cap : max(t_end, 1);
+    // (rows past a group's count repeat its last row once the count is
+    // known: the same lines again, from L2, instead of stale slot rows)
+    const int lim = GROUPED ? (t_end > 0 ? t_end : a.cap) : max(t_end, 1);
     static_for<IPW>([&](auto i) {
       const int u = 64 * (wave * IPW + i) + lane;
       const int row = u / (KC / 8);
@@ -278,11 +292,12 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   // the count is read-only here (an earlier kernel wrote it): a scalar load
   // through the constant address space, so its wait is not a vector-memory
   // wait for every chunk in flight
-  if (GROUPED) t_end = *DG_CONST_PTR(int32_t, a.group_count + group);
+  if (GROUPED) t_end = min(*DG_CONST_PTR(int32_t, a.group_count + group), a.cap);
   if (t_end <= 0) {  // an empty group: let the loads land before leaving
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     return;
   }
+  if (GROUPED && !MAPPED) set_rows(0);  // chunks from D on: count-bounded rows
 
   for (int t0 = 0; t0 < t_end; t0 += TROWS) {
     const int nt_rows = min(TROWS, t_end - t0);

@@ -10,7 +10,8 @@ R1  Layer internals are not given (the write-up only says the architecture is
     that of Gemma 4).  Pre-norm residual block: x += Attn(RMSNorm(x));
     x += MoE(RMSNorm(x)); RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g.
     Attention scale 1/sqrt(D).  No positional encoding, no soft-cap, no
-    QK-norm, no sliding window, no shared expert, no self-conditioning MLP,
+    QK-norm, no sliding window, no shared expert (unless the shape has one,
+    R10), no self-conditioning MLP,
     no embedding scale; the LM head is tied to the embedding.
 R2  Query head h reads KV head floor(h / G), G = Hq / Hkv (grouped-query
     attention, consecutive query heads share a KV head).

@@ -9,7 +9,8 @@ from block_discrete_diffusion_tok_amd import dg, synth
 from gpu_common import (DEV, MARGIN, TOL, log, np32, oshape, rel_err,
                         routing_margin, step_outputs, to_dev, top2_margin)
 from lockstep import Lockstep, lockstep_eb, lockstep_head
-from workload_common import check_commit_composition
+from workload_common import (capture_buffers, check_commit_composition,
+                             check_composition)
 
 pytestmark = pytest.mark.gpu
 
@@ -405,8 +406,14 @@ def test_denoise_step_with_shared_expert():
     tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
                                           cv["step"]))
     ent, lse, am, logits = step_outputs(1, shape.vocab)
-    cap = _capture(shape, 1, 2)
-    eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
-    torch.cuda.synchronize()
+    cap = capture_buffers(shape, 256, 2, final=False)
+    # two steps: the second runs on the counters the first left behind
+    # (every expert group's slot counter, the shared one included, is
+    # cleared by each layer)
+    for _ in range(2):
+        eng.denoise_step([0], tok, com, step, ent, lse, am, logits, cap)
+        torch.cuda.synchronize()
+    wd = to_dev(synth.make_weights(shape, seed=12, gain_std=0.1))
+    check_composition(eng, shape, wd, tok, [0], [300], cap, "shared expert")
     _compare_step(shape, eng, wn, prefix, cv, ent, lse, am, logits, cap, 1,
                   [300])
