@@ -117,12 +117,18 @@ def quantize_e4m3_rows(w):
 
 
 def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
-                 layers=None):
+                 layers=None, masters=False):
     """Random-init weights in the engine's storage formats (see module doc).
 
     ``layers`` optionally restricts generation to a subset of layer indices
-    (the others are None), e.g. for host copies of sampled layers."""
+    (the others are None), e.g. for host copies of sampled layers.
+    ``masters``: the matrices as their float32 draws, before the bfloat16
+    rounding (bf16-expert shapes only); rounding them gives the default
+    weights bit for bit."""
     s = shape
+    if masters and s.expert_dtype != "bf16":
+        raise ValueError("float32 masters exist for bf16-expert shapes only")
+    mdt = torch.float32 if masters else torch.bfloat16
     qkv_rows = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
 
     def gain(name):
@@ -131,7 +137,7 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
         return 1.0 + normal((s.hidden,), gain_std, seed, name, device,
                             torch.float32)
 
-    w = {"embed": normal((s.vocab, s.hidden), 0.02, seed, "embed", device),
+    w = {"embed": normal((s.vocab, s.hidden), 0.02, seed, "embed", device, mdt),
          "final_norm": gain("final_norm"), "layers": []}
     for li in range(s.n_layers):
         if layers is not None and li not in layers:
@@ -141,18 +147,18 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
         lw = {
             "attn_norm": gain(p + "attn_norm"),
             "w_qkv": normal((qkv_rows, s.hidden), 0.02, seed, p + "w_qkv",
-                            device),
+                            device, mdt),
             "w_o": normal((s.hidden, s.n_q_heads * s.head_dim), 0.02, seed,
-                          p + "w_o", device),
+                          p + "w_o", device, mdt),
             "ffn_norm": gain(p + "ffn_norm"),
             "w_router": normal((s.n_experts, s.hidden), 0.02, seed,
-                               p + "w_router", device),
+                               p + "w_router", device, mdt),
         }
         # the routed experts, then the shared expert (its own draw)
         eg = s.n_experts
         gu_shape = (eg, 2 * s.expert_ffn, s.hidden)
         dn_shape = (eg, s.hidden, s.expert_ffn)
-        dt = torch.bfloat16 if s.expert_dtype == "bf16" else torch.float32
+        dt = mdt if s.expert_dtype == "bf16" else torch.float32
         gu = normal(gu_shape, 0.02, seed, p + "w_gate_up", device, dt)
         dn = normal(dn_shape, 0.02, seed, p + "w_down", device, dt)
         if s.n_shared_experts:

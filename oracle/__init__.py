@@ -45,6 +45,7 @@ from .model import (  # noqa: F401
     eb_select,
     denoise_step,
     commit_block,
+    accumulate_in,
     ar_step,
     expert_matrix,
 )

@@ -100,12 +100,38 @@ class Shapes:
     n_shared_experts: int = 0   # reading R10
 
 
-def _f64(a):
-    return np.asarray(a, dtype=np.float64)
+# The oracle's real type: fp64, so that every dot product, softmax sum and
+# residual addition is a tighter reference than the GPU's fp32
+# accumulation.  The ORACLE_ACC32 reading (environment variable, or the
+# accumulate_in context) computes the same definitions with fp32 arrays
+# instead, so that the pure-fp32 result can be reported beside it.  The
+# entropy-bounded sampler's running sum stays fp64 in both (reading R6).
+_ACC = [np.float32 if os.environ.get("ORACLE_ACC32") == "1" else np.float64]
+
+
+class accumulate_in:
+    """Context: compute the oracle's arithmetic in the given numpy float
+    type (np.float64 by default, np.float32 for the ORACLE_ACC32 reading)."""
+
+    def __init__(self, dtype):
+        self.dtype = dtype
+
+    def __enter__(self):
+        self.prev = _ACC[0]
+        _ACC[0] = self.dtype
+        return self
+
+    def __exit__(self, *exc):
+        _ACC[0] = self.prev
+        return False
+
+
+def _real(a):
+    return np.asarray(a, dtype=_ACC[0])
 
 
 def _bf(x, mirror):
-    return round_bf16(x) if mirror else x
+    return _real(round_bf16(x)) if mirror else x
 
 
 def _map_independent(fn, items):
@@ -132,15 +158,15 @@ def expert_matrix(w, scale, e):
     per-output-row fp32 ``scale`` [E, rows] (the stored value times the
     scale is the weight)."""
     if scale is None:
-        return _f64(w[e])
-    return decode_e4m3(w[e]) * _f64(scale[e])[:, None]
+        return _real(w[e])
+    return decode_e4m3(w[e]) * _real(scale[e])[:, None]
 
 
 def rmsnorm(x, g, eps):
     """x / sqrt(mean(x^2) + eps) * g over the last axis (reading R1)."""
-    x = _f64(x)
+    x = _real(x)
     ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * _f64(g)
+    return x / np.sqrt(ms + eps) * _real(g)
 
 
 def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, causal=False,
@@ -159,7 +185,7 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, causal=False,
     o = sum_j softmax_j(q . k_j / sqrt(D)) v_j over the visible keys, with the
     full score row materialised and normalised the textbook way.
     """
-    q = _f64(q)
+    q = _real(q)
     hq, n, d = q.shape
     hkv = k_canvas.shape[0]
     group = hq // hkv
@@ -170,8 +196,8 @@ def canvas_attention(q, k_prefix, v_prefix, k_canvas, v_canvas, causal=False,
     q_pos = np.asarray(q_pos)
     def head(h):
         g = h // group
-        keys = np.concatenate([_f64(k_prefix[g]), _f64(k_canvas[g])], axis=0)
-        vals = np.concatenate([_f64(v_prefix[g]), _f64(v_canvas[g])], axis=0)
+        keys = np.concatenate([_real(k_prefix[g]), _real(k_canvas[g])], axis=0)
+        vals = np.concatenate([_real(v_prefix[g]), _real(v_canvas[g])], axis=0)
         s = (q[h] @ keys.T) / np.sqrt(d)
         if causal:
             canvas_j = np.arange(c_len)[None, :]
@@ -190,10 +216,10 @@ def router_topk(logits, k):
     """Top-k routing (reading R4).  logits [T, E] -> idx [T, k] (int64, in
     rank order: largest logit first, lower id first among equal logits) and
     w [T, k] = softmax over the selected logits."""
-    logits = _f64(logits)
+    logits = _real(logits)
     t_count, _ = logits.shape
     idx = np.zeros((t_count, k), dtype=np.int64)
-    w = np.zeros((t_count, k))
+    w = np.zeros((t_count, k), dtype=_ACC[0])
     for t in range(t_count):
         # stable sort of the negated logits keeps lower ids first on ties
         order = np.argsort(-logits[t], kind="stable")[:k]
@@ -221,9 +247,9 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
     another).  ``experts`` optionally supplies fp64 (W_gu, W_d) per expert id
     to avoid decoding them again.
     """
-    xhat = _f64(xhat)
+    xhat = _real(xhat)
     t_count, hidden = xhat.shape
-    out = np.zeros((t_count, hidden))
+    out = np.zeros((t_count, hidden), dtype=_ACC[0])
 
     def expert(e):
         tt, jj = np.nonzero(idx == e)
@@ -252,7 +278,7 @@ def lm_head_stats(xhat, embed, want_logits=False):
     entropy = -sum_v p_v ln p_v (terms with p_v = 0 contribute 0), clamped
     at 0;  argmax = lowest v with the largest z_v.
     """
-    z = _f64(xhat) @ _f64(embed).T
+    z = _real(xhat) @ _real(embed).T
     z_max = np.max(z, axis=1, keepdims=True)
     lse = z_max[:, 0] + np.log(np.sum(np.exp(z - z_max), axis=1))
     p = np.exp(z - lse[:, None])
@@ -290,7 +316,7 @@ def lm_head_sample(xhat, embed, tau, ctr, seed):
     tokens (reading R11).  xhat [M, H]; tau [M]; ctr [M, 3] = (position,
     step, canvas) of each row; seed: 64-bit key.  Returns dict with lse,
     entropy (of softmax(z / tau)), argmax (of z) and sample per row."""
-    z = _f64(xhat) @ _f64(embed).T
+    z = _real(xhat) @ _real(embed).T
     m_rows, v_count = z.shape
     lse = np.zeros(m_rows)
     ent = np.zeros(m_rows)
@@ -374,7 +400,7 @@ def moe_layer(sh, lw, xh, mirror=True):
     the mixture of the routed experts plus, with a shared expert, that
     expert (the last group of the expert matrices) with weight 1.
     Returns (r, idx [T, k], w [T, k], y [T, H])."""
-    r = _f64(xh) @ _f64(lw["w_router"]).T
+    r = _real(xh) @ _real(lw["w_router"]).T
     idx, w = router_topk(r, sh.top_k)
     idx_all, w_all = idx, w
     if sh.n_shared_experts:
@@ -428,11 +454,11 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
     b_count, c_len = tokens.shape
     earlier = _earlier_canvases(request, b_count)
     embed = weights["embed"]
-    x = _f64(embed[np.asarray(tokens).reshape(-1)])  # x_t = E[tok_t]
+    x = _real(embed[np.asarray(tokens).reshape(-1)])  # x_t = E[tok_t]
     for li, lw in enumerate(weights["layers"]):
         x_in = x
         xh = _bf(rmsnorm(x, lw["attn_norm"], sh.rms_eps), mirror)
-        qkv = _bf(xh @ _f64(lw["w_qkv"]).T, mirror)
+        qkv = _bf(xh @ _real(lw["w_qkv"]).T, mirror)
         q, k, v = _split_qkv(qkv, sh)
         if kv_out is not None:
             kv_out.append((k, v))
@@ -440,11 +466,12 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
                 if capture is not None:   # what the last layer computed
                     capture.append({"x_in": x_in, "xh_attn": xh, "qkv": qkv})
                 break
-        o = np.zeros((b_count * c_len, sh.n_q_heads * sh.head_dim))
+        o = np.zeros((b_count * c_len, sh.n_q_heads * sh.head_dim),
+                     dtype=_ACC[0])
         for b in range(b_count):
             rows = slice(b * c_len, (b + 1) * c_len)
             kp, vp = prefix[b]
-            kp, vp = _f64(kp[li]), _f64(vp[li])
+            kp, vp = _real(kp[li]), _real(vp[li])
             if earlier[b]:   # the request's earlier canvases follow its prefix
                 sl = [slice(e * c_len, (e + 1) * c_len) for e in earlier[b]]
                 kp = np.concatenate([kp] + [k[:, r] for r in sl], axis=1)
@@ -453,7 +480,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
                                   v[:, rows], causal=causal)
             o[rows] = ob.transpose(1, 0, 2).reshape(c_len, -1)
         o = _bf(o, mirror)
-        x = x + o @ _f64(lw["w_o"]).T
+        x = x + o @ _real(lw["w_o"]).T
         x_mid = x
         xh_attn = xh
         xh = _bf(rmsnorm(x, lw["ffn_norm"], sh.rms_eps), mirror)

@@ -417,3 +417,51 @@ def test_denoise_step_with_shared_expert():
     check_composition(eng, shape, wd, tok, [0], [300], cap, "shared expert")
     _compare_step(shape, eng, wn, prefix, cv, ent, lse, am, logits, cap, 1,
                   [300])
+
+
+def test_tiny_step_precision_drift_against_float32_masters():
+    """The tiny 1-layer workload with float32 master weights: the GPU
+    consumes their bfloat16 rounding.  Parity (asserted) is against the
+    oracle on the same bfloat16 values; the drift figure (reported, loosely
+    bounded) is against the oracle on the float32 masters with fp64
+    activations, i.e. what bf16 storage costs against full precision."""
+    shape = TINY_WL.shape
+    w32 = synth.make_weights(shape, seed=0, masters=True)
+    wbf = synth.make_weights(shape, seed=0)
+    eng = dg.Engine(shape, to_dev(wbf), max_requests=1, max_kv_len=1024,
+                    max_canvases=1)
+    k, v = synth.make_prefix_kv(shape, 512, 0, seed=0)
+    eng.prefill_kv(0, k.to(DEV).contiguous(), v.to(DEV).contiguous())
+    prefix = [(np32(k), np32(v))]
+    cv = synth.make_canvas(shape, 1, 256, seed=5)
+    tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
+                                          cv["step"]))
+    ent, lse, am, logits = step_outputs(1, shape.vocab)
+    eng.denoise_step([0], tok, com, step, ent, lse, am, logits)
+    torch.cuda.synchronize()
+    args = (oshape(shape), None, cv["tokens"].numpy(), cv["committed"].numpy(),
+            prefix)
+    g_z = logits.cpu().numpy()
+    g_h, g_l = ent.cpu().numpy().reshape(-1), lse.cpu().numpy().reshape(-1)
+    g_a = am.cpu().numpy().reshape(-1)
+    out = {}
+    for name, w, mirror in (("bf16 values, mirror", wbf, True),
+                            ("float32 masters, exact", w32, False)):
+        ref = oracle.denoise_step(args[0], synth.to_numpy_weights(w), *args[2:],
+                                  mirror=mirror, want_logits=True)
+        rows = ref["rows"]
+        e_z = rel_err(g_z[rows], ref["logits"])
+        e_h = rel_err(g_h[rows], ref["entropy"].reshape(-1)[rows])
+        e_l = rel_err(g_l[rows], ref["lse"].reshape(-1)[rows])
+        marg = top2_margin(ref["logits"])
+        diff = g_a[rows] != ref["argmax"].reshape(-1)[rows]
+        log(f"  GPU vs oracle on {name}: logits {e_z:.2e}, entropy {e_h:.2e}, "
+            f"lse {e_l:.2e}; argmax differs at {int(diff.sum())} of {len(rows)} "
+            f"({int((diff & (marg >= MARGIN)).sum())} above the margin)")
+        out[name] = (e_z, e_h, e_l, diff, marg)
+    e_z, e_h, e_l, diff, marg = out["bf16 values, mirror"]
+    assert e_z < TOL and e_h < TOL and e_l < TOL
+    assert not (diff & (marg >= MARGIN)).any()
+    e_z, e_h, e_l, _, _ = out["float32 masters, exact"]
+    assert e_z < 5e-2 and e_h < 5e-2 and e_l < 5e-2
+    eng.close()

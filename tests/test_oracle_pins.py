@@ -578,6 +578,49 @@ def test_ar_step_with_no_prefix_attends_to_itself_only():
                                    rtol=1e-12, atol=1e-14)
 
 
+def test_fp32_accumulator_reading_beside_fp64():
+    """The ORACLE_ACC32 reading: the same step of the 1-layer tiny workload
+    (hidden 256, vocabulary 4096, prefix 512, all 256 positions uncommitted)
+    computed with fp32 arrays, reported beside the fp64 oracle.  Without the
+    bf16 rounding points the two differ by fp32 rounding only (relative
+    1e-5); with them (mirror mode) an fp32 difference that straddles a bf16
+    rounding boundary moves that activation by one bf16 step, so the logits
+    differ by up to a few 1e-4 of their scale; the argmax decisions above
+    the margin agree either way.  The arithmetic really runs in fp32."""
+    from block_discrete_diffusion_tok_amd import synth
+    wl = synth.WORKLOADS["tiny_l1_h256_p512"]
+    sh = wl.shape
+    w = synth.to_numpy_weights(synth.make_weights(sh, seed=0))
+    osh = oracle.Shapes(sh.n_layers, sh.hidden, sh.n_q_heads, sh.n_kv_heads,
+                        sh.head_dim, sh.n_experts, sh.top_k, sh.expert_ffn,
+                        sh.vocab, sh.rms_eps)
+    cv = synth.make_canvas(sh, 1, 256, seed=5)
+    k, v = synth.make_prefix_kv(sh, wl.prefix_len, 0, seed=0)
+    pre = [(k.float().numpy(), v.float().numpy())]
+    args = (osh, w, cv["tokens"].numpy(), cv["committed"].numpy(), pre)
+    for mirror, bound in ((False, 1e-5), (True, 5e-3)):
+        a = oracle.denoise_step(*args, mirror=mirror, want_logits=True)
+        with oracle.accumulate_in(np.float32):
+            b = oracle.denoise_step(*args, mirror=mirror, want_logits=True)
+        assert b["logits"].dtype == np.float32
+        assert a["logits"].dtype == np.float64
+        e_z = np.max(np.abs(b["logits"] - a["logits"])) / \
+            np.max(np.abs(a["logits"]))
+        e_h = np.nanmax(np.abs(b["entropy"] - a["entropy"])) / \
+            np.nanmax(a["entropy"])
+        e_l = np.nanmax(np.abs(b["lse"] - a["lse"])) / \
+            np.nanmax(np.abs(a["lse"]))
+        srt = np.sort(a["logits"], axis=1)
+        marg = srt[:, -1] - srt[:, -2]
+        rows = a["rows"]
+        diff = b["argmax"].reshape(-1)[rows] != a["argmax"].reshape(-1)[rows]
+        print(f"fp32-accumulator reading vs fp64 (mirror={mirror}): logits "
+              f"{e_z:.2e}, entropy {e_h:.2e}, lse {e_l:.2e}; argmax differs "
+              f"at {int(diff.sum())} of {len(diff)}")
+        assert 0 < e_z < bound and e_h < bound and e_l < bound
+        assert np.all(marg[diff] < 1e-3)
+
+
 def test_mirror_mode_changes_results_only_by_bf16_rounding_size():
     sh, osh, w = _tiny_model()
     tokens = RNG.integers(0, sh.vocab, (1, 16))
