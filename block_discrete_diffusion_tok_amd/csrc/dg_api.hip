@@ -94,6 +94,15 @@ struct MoeBufs {
   int32_t* slot_pair;   // [E*cap] pair index t*k + r of each slot
   float* slot_w;        // [E*cap] gate weight of each slot
   int32_t* slot_tok;    // [E*cap + kSlotPad] token of each slot
+  // E4M3 activations (act_dtype DG_FP8_E4M3): the FFN-norm rows and the
+  // SwiGLU rows quantised per row, as codes (large-tile path) or as their
+  // bf16 values (streaming path), with the row scales
+  uint8_t* xq8;         // [T, H]
+  uint16_t* xq16;       // [T, H]
+  float* xs;            // [T]
+  uint8_t* aq8;         // [max(pairs, slots), F]
+  uint16_t* aq16;       // [max(pairs, slots), F]
+  float* as;            // [max(pairs, slots)]
 };
 // slot_tok is read up to one pass of 32 slots past an expert's last slot
 constexpr int kSlotPad = 64;
@@ -245,6 +254,15 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   const size_t o_sp = cv.take((size_t)slots * 4);
   const size_t o_sw = cv.take((size_t)slots * 4);
   const size_t o_st = cv.take((size_t)(slots + kSlotPad) * 4);
+  // E4M3 activation buffers only when the model asks for them
+  const bool a8 = d.act_dtype == DG_FP8_E4M3;
+  const long long arows = std::max(pairs, slots);
+  const size_t o_x8 = a8 ? cv.take((size_t)T * d.hidden) : 0;
+  const size_t o_x16 = a8 ? cv.take((size_t)T * d.hidden * 2) : 0;
+  const size_t o_xs = a8 ? cv.take((size_t)T * 4) : 0;
+  const size_t o_a8 = a8 ? cv.take((size_t)arows * d.expert_ffn) : 0;
+  const size_t o_a16 = a8 ? cv.take((size_t)arows * d.expert_ffn * 2) : 0;
+  const size_t o_as = a8 ? cv.take((size_t)arows * 4) : 0;
   if (b) {
     b->rlogits = (float*)(base + o_rl);
     b->ridx = (int32_t*)(base + o_ri);
@@ -258,6 +276,12 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
     b->act = (uint16_t*)(base + o_ac);
     b->y = (float*)(base + o_y);
     b->cap = cap;
+    b->xq8 = a8 ? (uint8_t*)(base + o_x8) : nullptr;
+    b->xq16 = a8 ? (uint16_t*)(base + o_x16) : nullptr;
+    b->xs = a8 ? (float*)(base + o_xs) : nullptr;
+    b->aq8 = a8 ? (uint8_t*)(base + o_a8) : nullptr;
+    b->aq16 = a8 ? (uint16_t*)(base + o_a16) : nullptr;
+    b->as = a8 ? (float*)(base + o_as) : nullptr;
     b->counts = (int32_t*)(base + o_cn);
     b->slot_pair = (int32_t*)(base + o_sp);
     b->slot_w = (float*)(base + o_sw);
@@ -325,6 +349,11 @@ std::string check_desc(const dg_model_desc* d) {
     return "expert_dtype must be DG_BF16 or DG_FP8_E4M3";
   if (d->canvas_len < 0 || d->canvas_len > DG_CANVAS)
     return "canvas_len must be in 0..256 (0: 256)";
+  if (d->act_dtype != DG_BF16 && d->act_dtype != DG_FP8_E4M3)
+    return "act_dtype must be DG_BF16 or DG_FP8_E4M3";
+  if (d->act_dtype == DG_FP8_E4M3 &&
+      (d->expert_dtype != DG_FP8_E4M3 || d->hidden % 128 || d->expert_ffn % 128))
+    return "E4M3 activations need E4M3 experts and hidden, expert_ffn multiples of 128";
   if (d->n_shared_experts < 0 || d->n_shared_experts > 1 ||
       d->n_experts + d->n_shared_experts > 256)
     return "n_shared_experts must be 0 or 1 (and n_experts + shared <= 256)";
@@ -451,9 +480,17 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
         (e = hipMemcpyAsync(counts, b.counts, (size_t)E * 4, hipMemcpyDeviceToDevice, s)) !=
             hipSuccess)
       return e;
+    const bool a8 = d.act_dtype == DG_FP8_E4M3;
+    if (a8) {
+      ProfScope ps(prof, 7);
+      if ((e = launch_quant_rows(xh, H, T, H, nullptr, 0, nullptr, b.xq16, b.xs, s)) !=
+          hipSuccess)
+        return e;
+    }
     StreamArgs gu;
     memset(&gu, 0, sizeof(gu));
-    gu.X = xh;
+    gu.X = a8 ? b.xq16 : xh;
+    gu.x_scale = a8 ? b.xs : nullptr;
     gu.ldx = H;
     gu.M = T;
     gu.row_of = b.slot_tok;
@@ -472,9 +509,16 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
       ProfScope ps(prof, 8);
       if ((e = launch_stream(EPI_SWIGLU, w8, gu, EG, s)) != hipSuccess) return e;
     }
+    if (a8) {
+      ProfScope ps(prof, 7);
+      if ((e = launch_quant_rows(b.act, F, EG * b.cap, F, b.counts, b.cap, nullptr, b.aq16,
+                                 b.as, s)) != hipSuccess)
+        return e;
+    }
     StreamArgs dn;
     memset(&dn, 0, sizeof(dn));
-    dn.X = b.act;
+    dn.X = a8 ? b.aq16 : b.act;
+    dn.x_scale = a8 ? b.as : nullptr;
     dn.ldx = F;
     dn.W = w.w_down;
     dn.w_group_stride = (long long)H * F;
@@ -504,8 +548,10 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
       return e;
   }
   // experts holding a few hundred rows each take the large-tile kernel
-  // (256-row tiles), fewer the 64-row tiles
-  const bool big = (long long)T * k >= 192LL * E;
+  // (256-row tiles), fewer the 64-row tiles; E4M3 activations always take
+  // the large-tile kernel (its FP8 MFMA)
+  const bool a8 = d.act_dtype == DG_FP8_E4M3;
+  const bool big = a8 || (long long)T * k >= 192LL * E;
   const int bm = big ? mm_bm() : kGroupBM;
   {
     ProfScope ps(prof, 7);
@@ -528,6 +574,15 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   gu.group_offsets = b.offsets;
   gu.tile_offsets = b.tile_offsets;
   gu.ffn = F;
+  if (a8) {
+    ProfScope ps(prof, 7);
+    if ((e = launch_quant_rows(xh, H, T, H, nullptr, 0, b.xq8, nullptr, b.xs, s)) !=
+        hipSuccess)
+      return e;
+    gu.A8 = b.xq8;
+    gu.a_scale = b.xs;
+    gu.lda = H;
+  }
   {
     ProfScope ps(prof, 8);
     if ((e = big ? launch_mm(EPI_SWIGLU, w8, gu, grid_m, s)
@@ -543,6 +598,15 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
   dn.tile_offsets = b.tile_offsets;
   dn.c_map = b.perm;
   dn.row_scale = b.rw;
+  if (a8) {
+    ProfScope ps(prof, 7);
+    if ((e = launch_quant_rows(b.act, F, pairs, F, nullptr, 0, b.aq8, nullptr, b.as, s)) !=
+        hipSuccess)
+      return e;
+    dn.A8 = b.aq8;
+    dn.a_scale = b.as;
+    dn.lda = F;
+  }
   {
     ProfScope ps(prof, 9);
     if ((e = big ? launch_mm(EPI_DOWN, w8, dn, grid_m, s)
@@ -1311,6 +1375,17 @@ dg_status dg_op_lmhead_entropy_static(const void* xhat, int32_t m,
                               vocab, (float4*)ws, nullptr, nullptr, &n_tiles, s));
   HIPCHK(nullptr, launch_lm_merge((const float4*)ws, n_tiles, nullptr, m, nullptr,
                                   entropy, lse, argmax, s));
+  return DG_OK;
+}
+
+dg_status dg_op_quantize_rows(const void* x, int32_t rows, int32_t k,
+                              uint8_t* codes, void* values, float* scale,
+                              void* stream) {
+  if (!x || !scale || (!codes && !values))
+    return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || k < 8 || k % 8) return fail(nullptr, DG_ERR_SHAPE, "k must be a multiple of 8");
+  HIPCHK(nullptr, launch_quant_rows((const uint16_t*)x, k, rows, k, nullptr, 0, codes,
+                                    (uint16_t*)values, scale, (hipStream_t)stream));
   return DG_OK;
 }
 

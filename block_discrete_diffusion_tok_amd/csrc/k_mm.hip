@@ -46,6 +46,13 @@ __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x
       __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+// FP8 MFMA: D(16x16) += A(16x128) * B(128x16), both E4M3 (format 0), unit
+// block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x4_t mfma_f8(const i32x8_t a, const i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 #ifndef DG_LDS_PTR
 #define DG_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 #endif
@@ -74,10 +81,14 @@ __device__ __forceinline__ void mm_stats_merge(float& m, float& s, float& t, int
 
 __device__ __forceinline__ float mm_silu(float v) { return v / (1.f + __expf(-v)); }
 
-template <int EPI, bool W8>
+// A8: token rows are E4M3 codes (a.A8) with a per-row scale (a.a_scale),
+// e4m3 weights, the FP8 MFMA 16x16x128 (k 128 per step).
+template <int EPI, bool W8, bool A8 = false>
 __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
+  static_assert(!A8 || W8, "e4m3 tokens need e4m3 weights");
+  constexpr int BK = A8 ? 2 * kMmBK : kMmBK;      // k per step
   constexpr int ESZ = W8 ? 1 : 2;
-  constexpr int WBLK = 16 * (kMmBK * ESZ / 64);   // weight blocks per step (32 / 16)
+  constexpr int WBLK = 16 * (BK * ESZ / 64);      // weight blocks per step (32 / 16 / 32)
   constexpr int TBLK = 16 * 2;                    // token blocks per step (16 tiles x 2)
   constexpr int WPW = WBLK / 8, TPW = TBLK / 8;   // DMA instructions per wave
   constexpr int STAGE = (WBLK + TBLK) * 1024;     // bytes per LDS stage
@@ -143,24 +154,30 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   // tt (rows row_begin + 16 tt + l16, clamped), k offset 32 h + 8 lg
   // (bf16 weights) or 16 lg + 8 h (e4m3 weights).  Wave w copies token
   // blocks w*TPW .. +TPW-1 and weight blocks w*WPW .. +WPW-1.
-  const uint16_t* tsrc[TPW];
+  // (e4m3 tokens: k offset 64 h + 16 lg, in bytes)
+  const char* tsrc[TPW];
   static_for<TPW>([&](auto j) {
     const int blk = wave * TPW + j;
     const int tt = blk >> 1, h = blk & 1;
     const int row = min(row_begin + 16 * tt + l16, row_end - 1);
     const int src = a.a_map ? a.a_map[row] / a.a_map_div : row;
-    const int koff = W8 ? 16 * lg + 8 * h : 32 * h + 8 * lg;
-    tsrc[j] = a.A + (long long)src * a.lda + koff;
+    if (A8) {
+      tsrc[j] = (const char*)a.A8 + (long long)src * a.lda + 64 * h + 16 * lg;
+    } else {
+      const int koff = W8 ? 16 * lg + 8 * h : 32 * h + 8 * lg;
+      tsrc[j] = (const char*)(a.A + (long long)src * a.lda + koff);
+    }
   });
   // Weight block (rt, kb) of a step: row tile rt of the workgroup's 16,
-  // k block kb of the step (bf16: 2 per step, e4m3: 1).
+  // k block kb of the step (bf16: 2 per step, e4m3: 1, e4m3 with e4m3
+  // tokens: 2).
   const char* wsrc[WPW];
   const char* const wgroup = (const char*)a.B + (long long)group * a.b_group_stride * ESZ;
   const int KB = a.K * ESZ / 64;   // packed blocks per row tile
   static_for<WPW>([&](auto j) {
     const int blk = wave * WPW + j;
-    const int rt = W8 ? blk : (blk >> 1);
-    const int kb = W8 ? 0 : (blk & 1);
+    const int rt = (W8 && !A8) ? blk : (blk >> 1);
+    const int kb = (W8 && !A8) ? 0 : (blk & 1);
     int rb;
     if (EPI == EPI_SWIGLU) {
       // 16 gate rows then the 16 matching up rows, per 32-row block
@@ -173,15 +190,16 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
                            kPackBlock + 16 * lane;
   });
   // bytes between consecutive steps of one weight block stream
-  constexpr long long kWStep = (long long)(kMmBK * ESZ / 64) * kPackKStride;
+  constexpr long long kWStep = (long long)(BK * ESZ / 64) * kPackKStride;
 
   auto issue = [&](int step, int stage) {
     char* st = lds + stage * STAGE;
     static_for<WPW>([&](auto j) {
       dma16(wsrc[j] + step * kWStep, st + (wave * WPW + j) * 1024);
     });
+    // (128 bytes of every token row per step: 64 bf16 or 128 e4m3 values)
     static_for<TPW>([&](auto j) {
-      dma16(tsrc[j] + (long long)step * kMmBK, st + (WBLK + wave * TPW + j) * 1024);
+      dma16(tsrc[j] + (long long)step * 128, st + (WBLK + wave * TPW + j) * 1024);
     });
   };
 
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.K / kMmBK;
+  const int nk = a.K / BK;
   issue(0, 0);
   for (int ks = 0; ks < nk; ++ks) {
     // this wave's DMA for step ks has landed; the barrier makes every
@@ -204,6 +222,31 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
     if (ks + 1 < nk) issue(ks + 1, (ks + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     const char* st = lds + (ks & 1) * STAGE;
+    if (A8) {
+      // one 128-k FP8 MFMA per tile pair: a lane's 32 bytes are k
+      // 16 lg + [0, 16) (block 0) and 64 + 16 lg + [0, 16) (block 1) of
+      // both operands (any k-slot assignment works when A and B share it)
+      i32x8_t tf8[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = wt * 4 + j;
+        const u32x4_t lo = *(const u32x4_t*)(st + (WBLK + tt * 2) * 1024 + 16 * lane);
+        const u32x4_t hi = *(const u32x4_t*)(st + (WBLK + tt * 2 + 1) * 1024 + 16 * lane);
+        tf8[j] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rt = wn * 8 + i;
+        const u32x4_t lo = *(const u32x4_t*)(st + (rt * 2) * 1024 + 16 * lane);
+        const u32x4_t hi = *(const u32x4_t*)(st + (rt * 2 + 1) * 1024 + 16 * lane);
+        const i32x8_t wf8 = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f8(wf8, tf8[j], acc[i][j]);
+      }
+      continue;
+    }
     // two 32-k MFMA sub-steps
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -331,6 +374,8 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int row = row_begin + wt * 64 + j * 16 + l16;
     if (row >= row_end) continue;
+    // e4m3 tokens: the row's scale (of its source row)
+    const float xs = A8 ? a.a_scale[a.a_map ? a.a_map[row] / a.a_map_div : row] : 1.f;
     if (EPI == EPI_SWIGLU) {
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
@@ -346,6 +391,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
             const float* sc = a.b_scale + (long long)group * a.scale_rows;
             g[e] *= sc[ch + e];
             u[e] *= sc[a.ffn + ch + e];
+          }
+          if (A8) {
+            g[e] *= xs;
+            u[e] *= xs;
           }
         }
         *(uint2*)((uint16_t*)a.C + (long long)row * a.ldc + ch) =
@@ -367,9 +416,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
             const float* sc = a.b_scale + (long long)group * a.scale_rows + n;
             sc4[0] = sc[0]; sc4[1] = sc[1]; sc4[2] = sc[2]; sc4[3] = sc[3];
           }
+          const float ws = A8 ? wgt * xs : wgt;
           *(float4*)((float*)a.C + (long long)pair * a.ldc + n) =
-              make_float4(v[0] * wgt * sc4[0], v[1] * wgt * sc4[1],
-                          v[2] * wgt * sc4[2], v[3] * wgt * sc4[3]);
+              make_float4(v[0] * ws * sc4[0], v[1] * ws * sc4[1],
+                          v[2] * ws * sc4[2], v[3] * ws * sc4[3]);
         } else if (vec) {
           if (EPI == EPI_STORE_BF16) {
             *(uint2*)((uint16_t*)a.C + (long long)row * a.ldc + n) =
@@ -398,14 +448,15 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   }
 }
 
-template <int EPI, bool W8>
+template <int EPI, bool W8, bool A8 = false>
 hipError_t launch_mm_one(const GemmArgs& a, int grid_m, hipStream_t s) {
   int grid_n;
   if (EPI == EPI_SWIGLU) grid_n = (a.ffn + kMmBN / 2 - 1) / (kMmBN / 2);
   else grid_n = (a.N + kMmBN - 1) / kMmBN;
   if (grid_m <= 0 || grid_n <= 0) return hipSuccess;
-  if (a.K % kMmBK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mm_kernel<EPI, W8>), dim3(grid_n, grid_m), dim3(kMmThreads), 0, s, a);
+  if (a.K % (A8 ? 2 * kMmBK : kMmBK)) return hipErrorInvalidValue;
+  if (A8 && (!a.A8 || !a.a_scale || a.lda % 16)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mm_kernel<EPI, W8, A8>), dim3(grid_n, grid_m), dim3(kMmThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -421,9 +472,13 @@ hipError_t launch_mm(int epi, bool w8, const GemmArgs& a, int grid_m, hipStream_
     case EPI_STORE_F32: return launch_mm_one<EPI_STORE_F32, false>(a, grid_m, s);
     case EPI_ADD_F32: return launch_mm_one<EPI_ADD_F32, false>(a, grid_m, s);
     case EPI_SWIGLU:
+      if (a.A8) return w8 ? launch_mm_one<EPI_SWIGLU, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
       return w8 ? launch_mm_one<EPI_SWIGLU, true>(a, grid_m, s)
                 : launch_mm_one<EPI_SWIGLU, false>(a, grid_m, s);
     case EPI_DOWN:
+      if (a.A8) return w8 ? launch_mm_one<EPI_DOWN, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
       return w8 ? launch_mm_one<EPI_DOWN, true>(a, grid_m, s)
                 : launch_mm_one<EPI_DOWN, false>(a, grid_m, s);
     case EPI_LMSTATS: return launch_mm_one<EPI_LMSTATS, false>(a, grid_m, s);

@@ -1000,6 +1000,66 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
   return hipGetLastError();
 }
 
+// One workgroup per row: the row's max |x| by a block reduction, then each
+// 8-value run divided by the scale (fp32 division, correctly rounded) and
+// encoded.
+__global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* x, int ldx, int K, const int32_t* count, int cap, uint8_t* q8,
+    uint16_t* q16, float* scale) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (count && r % cap >= count[r / cap]) return;
+  const uint16_t* xr = x + (long long)r * ldx;
+  float amax = 0.f;
+  for (int c = 8 * tid; c < K; c += 8 * 256) {
+    const uint4 v = *(const uint4*)(xr + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[i] & 0xFFFFu))));
+      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[i] >> 16))));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax > 0.f ? amax / 448.f : 1.f;
+  if (tid == 0) scale[r] = sc;
+  for (int c = 8 * tid; c < K; c += 8 * 256) {
+    const uint4 v = *(const uint4*)(xr + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t code[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      code[2 * i] = e4m3_encode(bf2f((uint16_t)(w[i] & 0xFFFFu)) / sc);
+      code[2 * i + 1] = e4m3_encode(bf2f((uint16_t)(w[i] >> 16)) / sc);
+    }
+    if (q8)
+      *(uint2*)(q8 + (long long)r * K + c) =
+          make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                     code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
+    if (q16) {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h[i] = pack_bf2(e4m3_value(code[2 * i]), e4m3_value(code[2 * i + 1]));
+      *(uint4*)(q16 + (long long)r * K + c) = make_uint4(h[0], h[1], h[2], h[3]);
+    }
+  }
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int ldx, int rows, int K,
+                             const int32_t* count, int cap, uint8_t* q8,
+                             uint16_t* q16, float* scale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K <= 0 || K % 8 || ldx % 8 || (count && cap <= 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(rows), dim3(256), 0, s, x, ldx, K, count,
+                     cap, q8, q16, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed_norm(const int32_t* tokens, int T, const uint16_t* embed,
                              int V, int H, float* x, const float* g, float eps,
                              uint16_t* xh, hipStream_t s, const uint8_t* committed,

@@ -472,6 +472,9 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
       for (int nt = 0; nt < NT; ++nt) {
         const int tok = t0 + nt * 16 + l16;
         if (nt >= nt_act || tok >= t_end) continue;
+        // E4M3 token rows (given as their bf16 values): the row's scale
+        float xs = 1.f;
+        if (a.x_scale) xs = a.x_scale[MAPPED ? a.row_of[row0 + tok] : row0 + tok];
         if (EPI == EPI_SWIGLU) {
           const int c0 = bx * (WROWS / 2) + wave * (8 * RT);
 #pragma unroll
@@ -488,6 +491,8 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
                 g[e] *= sc[ch + e];
                 u[e] *= sc[a.ffn + ch + e];
               }
+              g[e] *= xs;
+              u[e] *= xs;
             }
             *(uint2*)((uint16_t*)a.C + (row0 + tok) * a.ldc + ch) =
                 make_uint2(pack_bf2(silu(g[0]) * u[0], silu(g[1]) * u[1]),
@@ -513,6 +518,7 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
                 const float* sc = a.w_scale + (long long)group * a.scale_rows + n;
                 sc4[0] = sc[0]; sc4[1] = sc[1]; sc4[2] = sc[2]; sc4[3] = sc[3];
               }
+              wgt *= xs;
               *(float4*)((float*)a.C + (long long)pair * a.ldc + n) =
                   make_float4(v[0] * wgt * sc4[0], v[1] * wgt * sc4[1],
                               v[2] * wgt * sc4[2], v[3] * wgt * sc4[3]);

@@ -37,7 +37,7 @@ class ModelDesc(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("expert_dtype", ctypes.c_int32), ("canvas_len", ctypes.c_int32),
-                ("n_shared_experts", ctypes.c_int32)]
+                ("n_shared_experts", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -119,6 +119,7 @@ _SIGS = {
                                  _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dg_op_lmhead_sample_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dg_op_eb_select": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
+    "dg_op_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
                              ctypes.POINTER(_I), ctypes.POINTER(_I), _P]),
 }
@@ -163,7 +164,9 @@ def model_desc(shape):
                      shape.rms_eps,
                      FP8_E4M3 if shape.expert_dtype == "fp8_e4m3" else BF16,
                      getattr(shape, "canvas_len", CANVAS),
-                     getattr(shape, "n_shared_experts", 0))
+                     getattr(shape, "n_shared_experts", 0),
+                     FP8_E4M3 if getattr(shape, "act_dtype", "bf16") == "fp8_e4m3"
+                     else BF16)
 
 
 def layer_weights(lw):
@@ -457,6 +460,14 @@ def op_lmhead_entropy_static(xhat, embed, entropy, lse, argmax):
     _check(lib().dg_op_lmhead_entropy_static(
         _ptr(xhat), xhat.shape[0], xhat.shape[1], _ptr(embed), embed.rows,
         _ptr(entropy), _ptr(lse), _ptr(argmax), _stream()))
+
+
+def op_quantize_rows(x, codes, values, scale):
+    """x [rows, K] bf16; codes [rows, K] uint8 and/or values [rows, K] bf16
+    (either may be None); scale [rows] fp32."""
+    _check(lib().dg_op_quantize_rows(_ptr(x), x.shape[0], x.shape[1],
+                                     _ptr(codes), _ptr(values), _ptr(scale),
+                                     _stream()))
 
 
 def op_eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,

@@ -38,6 +38,7 @@ class ModelShape:
     expert_dtype: str = "bf16"  # "bf16" or "fp8_e4m3"
     canvas_len: int = CANVAS    # positions per canvas (128 or 256)
     n_shared_experts: int = 0   # 0 or 1 shared expert (the last expert group)
+    act_dtype: str = "bf16"     # expert GEMM token rows: "bf16" or "fp8_e4m3"
 
 
 @dataclass(frozen=True)
@@ -84,6 +85,13 @@ WORKLOADS = {
                  prefix_len=2048, batch=32, uncommitted=256, gamma=1.0,
                  step_cap=256,
                  notes="30 layers, E4M3 experts, 32 concurrent canvases"),
+        Workload("stack30_w8a8_b32_p2048",
+                 ModelShape(30, **_GEMMA_LAYER, expert_dtype="fp8_e4m3",
+                            act_dtype="fp8_e4m3"),
+                 prefix_len=2048, batch=32, uncommitted=256, gamma=1.0,
+                 step_cap=256,
+                 notes="the 32-canvas batch with E4M3 expert activations "
+                       "too (W8A8)"),
     ]
 }
 

@@ -136,6 +136,16 @@ dg_status dg_op_lmhead_sample(const void* xhat, int32_t m, int32_t hidden,
                               void* stream);
 size_t dg_op_lmhead_sample_workspace_bytes(int32_t m, int32_t vocab);
 
+/* Per-row E4M3 quantisation of activations (the FP8 rows of the expert
+ * GEMMs when act_dtype is DG_FP8_E4M3; write-up Table 3 caption, FP8):
+ * x [rows, K] bf16 (K a multiple of 8) -> scale [rows] fp32 = max|x_r| /
+ * 448 (1 for a zero row) and codes [rows, K] = E4M3(x / scale): nearest,
+ * ties to even, saturating, fp32 division.  codes or values (their bf16
+ * values [rows, K]) may be NULL, not both. */
+dg_status dg_op_quantize_rows(const void* x, int32_t rows, int32_t k,
+                              uint8_t* codes, void* values, float* scale,
+                              void* stream);
+
 /* Entropy-bounded selection on explicit state (same rule as dg_eb_select)
  * over n canvases of C = canvas_len positions (0: 256):
  * entropy [n, C] fp32, argmax [n, C] int32, committed [n, C] uint8

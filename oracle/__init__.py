@@ -49,4 +49,5 @@ from .model import (  # noqa: F401
     ar_step,
     expert_matrix,
 )
-from .numerics import round_bf16, decode_e4m3  # noqa: F401
+from .numerics import (round_bf16, decode_e4m3, encode_e4m3,  # noqa: F401
+                       quantize_rows_e4m3)

@@ -65,6 +65,15 @@ R12 AR mode (write-up "What they did": the weights still decode left to
     itself, no positional term, reading S9), appends the K/V it makes and
     reads the next token's statistics off its final-normed row.  Greedy
     (argmax) decoding only.
+R13 FP8 activations (write-up Table 3 and Figure 11 captions: served in
+    FP8; the pages fix no scaling): with E4M3 experts and ``act_fp8`` the
+    expert products take every row they multiply (a token's FFN-norm row
+    for gate/up, a pair's SwiGLU row for down) as OCP E4M3 codes with one
+    scale per row: a = max |row|, s = a / 448 (1 for a zero row), codes =
+    E4M3(row / s) to nearest, ties to even, saturating, each step in fp32;
+    the product is s_row s_w[n] sum_k q_row[k] q_w[n][k].  Per-row dynamic
+    scales are the plainest reading for activations that change every
+    step.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -79,7 +88,7 @@ from dataclasses import dataclass
 import numpy as np
 from threadpoolctl import threadpool_limits
 
-from .numerics import round_bf16, decode_e4m3
+from .numerics import round_bf16, decode_e4m3, quantize_rows_e4m3
 from .philox import philox4x32_10, uniform24
 
 CANVAS = 256
@@ -98,6 +107,7 @@ class Shapes:
     vocab: int
     rms_eps: float = 1e-6
     n_shared_experts: int = 0   # reading R10
+    act_fp8: bool = False       # reading R13
 
 
 # The oracle's real type: fp64, so that every dot product, softmax sum and
@@ -235,7 +245,7 @@ def silu(v):
 
 
 def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
-                down_scale=None, mirror=True, experts=None):
+                down_scale=None, mirror=True, experts=None, act_fp8=False):
     """Gate-weighted mixture of SwiGLU experts for each token (reading R4):
 
         y_t = sum_j w[t, j] * W_d,e (silu(W_g,e xhat_t) * W_u,e xhat_t),
@@ -246,10 +256,37 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
     per-row product; no token is computed twice and no row depends on
     another).  ``experts`` optionally supplies fp64 (W_gu, W_d) per expert id
     to avoid decoding them again.
+
+    With ``act_fp8`` (reading R13; E4M3 expert weights) each token's row
+    and each pair's SwiGLU row enter their product as E4M3 codes with one
+    scale per row: W q_x is formed from the codes' values and then scaled
+    by s_x and the weight rows' scales.
     """
     xhat = _real(xhat)
     t_count, hidden = xhat.shape
     out = np.zeros((t_count, hidden), dtype=_ACC[0])
+    if act_fp8:
+        qx, sx = quantize_rows_e4m3(xhat)
+        xq = _real(decode_e4m3(qx))
+        sx = _real(sx)
+
+        def expert8(e):
+            tt, jj = np.nonzero(idx == e)
+            cgu = _real(decode_e4m3(w_gate_up[e]))
+            sgu = _real(gate_up_scale[e])
+            cd = _real(decode_e4m3(w_down[e]))
+            sd = _real(down_scale[e])
+            f = cd.shape[1]
+            gate = (xq[tt] @ cgu[:f].T) * sx[tt][:, None] * sgu[:f][None, :]
+            up = (xq[tt] @ cgu[f:].T) * sx[tt][:, None] * sgu[f:][None, :]
+            act = _bf(silu(gate) * up, mirror)
+            qa, sa = quantize_rows_e4m3(act)
+            y = (_real(decode_e4m3(qa)) @ cd.T) * _real(sa)[:, None] * sd[None, :]
+            return tt, w[tt, jj][:, None] * y
+
+        for tt, contrib in _map_independent(expert8, np.unique(idx)):
+            out[tt] += contrib
+        return out
 
     def expert(e):
         tt, jj = np.nonzero(idx == e)
@@ -410,7 +447,7 @@ def moe_layer(sh, lw, xh, mirror=True):
         w_all = np.concatenate([w, np.ones((t_count, 1))], axis=1)
     y = moe_mixture(xh, idx_all, w_all, lw["w_gate_up"], lw["w_down"],
                     lw.get("gate_up_scale"), lw.get("down_scale"),
-                    mirror=mirror)
+                    mirror=mirror, act_fp8=sh.act_fp8)
     return r, idx, w, y
 
 

@@ -1,4 +1,5 @@
-"""Number formats the oracle needs: bfloat16 rounding and OCP e4m3 decoding.
+"""Number formats the oracle needs: bfloat16 rounding, OCP e4m3 decoding and
+encoding, and per-row e4m3 quantisation.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
@@ -47,3 +48,41 @@ _E4M3_VALUES = _e4m3_value(np.arange(256, dtype=np.int64))
 def decode_e4m3(codes):
     """Decode OCP FP8 E4M3 byte codes (uint8 array) to fp64 values."""
     return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+# the finite non-negative E4M3 values in code order (codes 0x00..0x7E are
+# increasing; 0x7F is NaN)
+_E4M3_POS = _E4M3_VALUES[:0x7F]
+
+
+def encode_e4m3(v):
+    """OCP FP8 E4M3 codes of real values: the nearest finite E4M3 value,
+    ties to the even code (mantissa LSB 0), saturating at +-448 (reading
+    R13); the sign bit is the sign of v (so -0.0 and negatives that round to
+    zero give 0x80)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")      # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(_E4M3_POS[hi] == a, hi, code)        # exact values
+    sign = np.signbit(v)
+    return (code | np.where(sign, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x):
+    """Per-row E4M3 quantisation of activations (reading R13), every step in
+    fp32 as the definition states: a = max |x_row|, s = a / 448 (fp32
+    division; s = 1 for an all-zero row), q = encode_e4m3(x / s) with x / s
+    an fp32 division.  x: [rows, K] values exactly representable in fp32
+    (bf16 activations).  Returns (codes uint8 [rows, K], scales float32
+    [rows])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(x32), axis=1)
+    s = np.where(a > 0, a / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (x32 / s[:, None]).astype(np.float32)
+    return encode_e4m3(v), s

@@ -13,6 +13,18 @@ TOL = 2e-2        # max relative error on continuous outputs (per tensor)
 # absolute gap between the competing values -- is below MARGIN are not
 # required to agree.
 MARGIN = 1e-3
+# Per-row bound on the MoE output with E4M3 activations (reading R13): a row
+# element whose value sits within the two sides' fp32 difference of an E4M3
+# rounding boundary takes the neighbouring code on one side, one E4M3 step
+# (at most 2^-3 of the element) apart; gfx950's FP8 MFMA also sums each
+# block of 128 products to ~8.5e-5 of their absolute sum.  A row's output
+# is then bounded by half an E4M3 step of its scale, 2^-4 (the per-tensor
+# bound stays TOL).
+TOL_ROW_FP8_ACT = 2.0 ** -4
+
+
+def fp8_act(shape):
+    return getattr(shape, "act_dtype", "bf16") == "fp8_e4m3"
 
 
 def log(msg):
@@ -24,7 +36,8 @@ def oshape(s):
     return oracle.Shapes(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads,
                          s.head_dim, s.n_experts, s.top_k, s.expert_ffn,
                          s.vocab, s.rms_eps,
-                         getattr(s, "n_shared_experts", 0))
+                         getattr(s, "n_shared_experts", 0),
+                         getattr(s, "act_dtype", "bf16") == "fp8_e4m3")
 
 
 def to_dev(w, dev=DEV):

@@ -11,8 +11,9 @@ import torch
 
 import oracle
 from block_discrete_diffusion_tok_amd import dg, synth
-from gpu_common import (DEV, MARGIN, TOL, log, np32, oshape, rel_err,
-                        routing_margin, to_dev, top2_margin)
+from gpu_common import (DEV, MARGIN, TOL, TOL_ROW_FP8_ACT, fp8_act, log,
+                        np32, oshape, rel_err, routing_margin, row_err, to_dev,
+                        top2_margin)
 
 pytestmark = pytest.mark.gpu
 
@@ -260,8 +261,9 @@ def _moe_case(shape, T, tag, top_k=None, same_rows=False):
     assert np.all(marg[~same] < MARGIN), "routing differs at a clear margin"
     log(f"  routing: {int((~same).sum())} low-margin tokens differ")
     e = rel_err(np32(y)[same], ref[same])
-    log(f"  mixture rel err {e:.2e}")
-    assert e < TOL
+    er = row_err(np32(y)[same], ref[same])
+    log(f"  mixture rel err {e:.2e} (per row {er:.2e})")
+    assert e < TOL and er < (TOL_ROW_FP8_ACT if fp8_act(shape) else TOL)
     c = counts.cpu().numpy()
     assert c.sum() == T * shape.top_k
     np.testing.assert_array_equal(c, np.bincount(g_idx.reshape(-1),

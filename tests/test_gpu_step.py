@@ -6,8 +6,9 @@ import torch
 
 import oracle
 from block_discrete_diffusion_tok_amd import dg, synth
-from gpu_common import (DEV, MARGIN, TOL, log, np32, oshape, rel_err,
-                        routing_margin, step_outputs, to_dev, top2_margin)
+from gpu_common import (DEV, MARGIN, TOL, fp8_act, log, np32, oshape,
+                        rel_err, routing_margin, step_outputs, to_dev,
+                        top2_margin)
 from lockstep import Lockstep, lockstep_eb, lockstep_head
 from workload_common import (capture_buffers, check_commit_composition,
                              check_composition)
@@ -68,7 +69,10 @@ def _compare_step(shape, eng, wn, prefix, cv, ent, lse, am, logits, cap, n,
         log(f"  free-running layer {li}: attn rel err {e_att:.2e}, moe rel err "
             f"{e_moe:.2e}, routing differences {int(diff.sum())} (absolute "
             f"margins {np.sort(marg[diff]).tolist()})")
-        assert e_att < TOL and e_moe < TOL
+        # (with E4M3 activations the upstream differences of a free-running
+        # chain move activation codes by whole E4M3 steps: the MoE output is
+        # reported, and asserted in lockstep)
+        assert e_att < TOL and (e_moe < TOL or fp8_act(shape))
         if diff.any():
             log(f"  free-running chains part in layer {li}")
             full = False

@@ -1,5 +1,6 @@
 """The concurrency workload at its full size: the 30-layer stack with E4M3
-expert weights (per-output-channel scales), 32 requests with their own
+expert weights (per-output-channel scales) -- and its W8A8 variant, whose
+expert GEMMs also take E4M3 token rows (reading R13) --, 32 requests with their own
 2048-token prefixes, 32 canvases denoised together (8192 rows per MoE grouped
 GEMM and per LM head).
 
@@ -32,15 +33,17 @@ from workload_common import (HostPerLayer, capture_buffers,
 
 pytestmark = pytest.mark.gpu
 
-WL = synth.WORKLOADS["stack30_fp8_b32_p2048"]
-SHAPE = WL.shape
 ORACLE_CANVASES = (0, 31)
 
 
-@pytest.fixture(scope="module")
-def batch32():
+@pytest.fixture(scope="module",
+                params=["stack30_fp8_b32_p2048", "stack30_w8a8_b32_p2048"])
+def batch32(request):
+    global WL, SHAPE
+    WL = synth.WORKLOADS[request.param]
+    SHAPE = WL.shape
     assert SHAPE.expert_dtype == "fp8_e4m3" and WL.batch == 32
-    log("fp8 batch 32: generating weights and 32 prefixes on the device")
+    log(f"{WL.name}: generating weights and 32 prefixes on the device")
     w = synth.make_weights(SHAPE, seed=1, device=DEV)
     n = WL.batch
     eng = dg.Engine(SHAPE, w, max_requests=n,
@@ -54,7 +57,7 @@ def batch32():
         del k, v
     torch.cuda.synchronize()
     log("fp8 batch 32: engine ready")
-    yield {"w": w, "eng": eng, "prefixes": prefixes}
+    yield {"w": w, "eng": eng, "prefixes": prefixes, "wl": WL}
     eng.close()
 
 
@@ -78,14 +81,14 @@ def test_fp8_batch32_step_lockstep_and_composition(batch32):
     assert np.all(e <= math.log(SHAPE.vocab) * (1 + 1e-5))
     assert np.all((a >= 0) & (a < SHAPE.vocab))
     log("  composition: all 32 canvases, all layers")
-    check_composition(eng, SHAPE, w, tok, req, plen, cap, "fp8 b32")
+    check_composition(eng, SHAPE, w, tok, req, plen, cap, WL.name)
     del cap
     sel = list(ORACLE_CANVASES)
     log(f"  lockstep: oracle canvases {sel}, all {SHAPE.n_layers} layers")
     pre = [(HostPerLayer(batch32["prefixes"][b][0]),
             HostPerLayer(batch32["prefixes"][b][1])) for b in sel]
     cap_o = []
-    ls = Lockstep(SHAPE, eng, w, n, req, plen, sel, cap_o, "fp8 b32", seed=1)
+    ls = Lockstep(SHAPE, eng, w, n, req, plen, sel, cap_o, WL.name, seed=1)
     ref = oracle.denoise_step(oshape(SHAPE), host_model(w, stop=ls),
                               cv["tokens"].numpy()[sel],
                               cv["committed"].numpy()[sel], pre, mirror=True,
@@ -93,10 +96,10 @@ def test_fp8_batch32_step_lockstep_and_composition(batch32):
     assert ls.finish() == SHAPE.n_layers
     ls.report()
     lockstep_head(SHAPE, eng, w, ref, ls.x_last, cv["committed"].numpy(), n,
-                  sel, "fp8 b32", seed=1)
+                  sel, WL.name, seed=1)
     lockstep_eb(ref["entropy"], ref["argmax"], cv["committed"].numpy()[sel],
                 cv["tokens"].numpy()[sel], cv["step"].numpy()[sel], WL.gamma,
-                WL.step_cap, "fp8 b32")
+                WL.step_cap, WL.name)
 
 
 def test_fp8_batch32_decode_until_every_block_is_committed(batch32):

@@ -941,3 +941,110 @@ def test_lm_head_sample_limits():
     su = oracle.lm_head_sample(np.zeros((2, 16)), emb, np.array([0.3, 2.0]),
                                ctr[:2], 7)
     np.testing.assert_allclose(su["entropy"], math.log(40), rtol=1e-12)
+
+
+# ----------------------------------------------------------------- FP8 activations
+
+def test_encode_e4m3_matches_torch_and_fixed_cases():
+    """encode_e4m3 (reading R13) against torch's float8_e4m3fn conversion on
+    values of every magnitude, the midpoints between E4M3 values and their
+    neighbours; and hand cases: ties go to the even code, saturation at
+    448, sign of zero kept, the subnormal step 2^-9."""
+    from oracle.numerics import encode_e4m3
+    rng = np.random.default_rng(3)
+    pos = np.sort(oracle.decode_e4m3(np.arange(127, dtype=np.uint8)))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([
+        (rng.standard_normal(100000) * 10.0 ** rng.uniform(-4, 2.6, 100000)),
+        mids, -mids, np.nextafter(mids, np.float32(0)),
+        np.nextafter(mids, np.float32(1e3))]).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = encode_e4m3(v)
+    nz = v != 0
+    np.testing.assert_array_equal(got[nz], ref[nz])
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (448.0, 0x7E), (500.0, 0x7E),
+             (-500.0, 0xFE), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02),
+             (2.0 ** -9, 0x01), (0.015625, 0x08), (-0.0, 0x80), (0.0, 0x00)]
+    for x, c in cases:
+        assert int(encode_e4m3(np.float32(x))) == c, (x, hex(c))
+
+
+def test_quantize_rows_closed_forms():
+    """Per-row quantisation (reading R13): a row of E4M3 values whose
+    largest magnitude is 448 has scale 1 and reproduces its codes; a zero
+    row has scale 1 and zero codes; scaling a row by 2^j scales s by 2^j
+    and keeps the codes; every value is recovered to E4M3's relative step
+    (2^-4) of the row's scale."""
+    from oracle.numerics import encode_e4m3, quantize_rows_e4m3
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 0x7F, (3, 64)).astype(np.uint8)
+    codes[:, 0] = 0x7E                       # 448 in every row
+    codes[:, 1:] |= rng.integers(0, 2, (3, 63)).astype(np.uint8) << 7
+    x = oracle.decode_e4m3(codes).astype(np.float32)
+    q, s = quantize_rows_e4m3(x)
+    np.testing.assert_array_equal(s, np.ones(3, np.float32))
+    np.testing.assert_array_equal(oracle.decode_e4m3(q), x)
+    q0, s0 = quantize_rows_e4m3(np.zeros((2, 16), np.float32))
+    assert np.all(s0 == 1.0) and np.all(q0 == 0)
+    y = rng.standard_normal((4, 256)).astype(np.float32)
+    qa, sa = quantize_rows_e4m3(y)
+    qb, sb = quantize_rows_e4m3(y * np.float32(2.0 ** 5))
+    np.testing.assert_array_equal(qa, qb)
+    np.testing.assert_array_equal(sb, sa * np.float32(2.0 ** 5))
+    back = oracle.decode_e4m3(qa) * sa[:, None]
+    assert np.all(np.abs(back - y) <= 2.0 ** -4 * np.abs(y) + 2.0 ** -9 * sa[:, None])
+    assert np.array_equal(qa, encode_e4m3(y / sa[:, None]))
+
+
+def _fp8_moe_model(seed=9, f=64):
+    from block_discrete_diffusion_tok_amd import synth
+    sh = synth.ModelShape(1, 128, 4, 2, 64, 8, 2, f, 64,
+                          expert_dtype="fp8_e4m3", act_dtype="fp8_e4m3")
+    w = synth.to_numpy_weights(synth.make_weights(sh, seed=seed))
+    osh = oracle.Shapes(sh.n_layers, sh.hidden, sh.n_q_heads, sh.n_kv_heads,
+                        sh.head_dim, sh.n_experts, sh.top_k, sh.expert_ffn,
+                        sh.vocab, sh.rms_eps, 0, True)
+    return sh, osh, w["layers"][0]
+
+
+def test_w8a8_equals_w8a16_when_rows_are_exactly_representable():
+    """With each token row already a scale times E4M3 values (largest 448
+    times the scale) and one-channel experts (a pair's SwiGLU row is one
+    value, which quantises to +-448 times its own scale), the FP8-activation
+    mixture equals the bf16-activation one to fp32 rounding of the scales:
+    the quantisation is then exact and the code products are the same
+    sums."""
+    import dataclasses
+    _, osh, lw = _fp8_moe_model(f=64)
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 0x7F, (16, 128)).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    scale = (2.0 ** rng.integers(-12, -6, 16)).astype(np.float32)
+    xh = oracle.decode_e4m3(codes) * scale[:, None]
+    # one SwiGLU channel per expert: keep the first gate and up rows only
+    f = 1
+    lw1 = dict(lw)
+    gu, gus = lw["w_gate_up"], lw["gate_up_scale"]
+    lw1["w_gate_up"] = np.concatenate([gu[:, :f], gu[:, 64:64 + f]], axis=1)
+    lw1["gate_up_scale"] = np.concatenate([gus[:, :f], gus[:, 64:64 + f]], axis=1)
+    lw1["w_down"] = lw["w_down"][:, :, :f].copy()
+    sh8 = dataclasses.replace(osh, expert_ffn=f)
+    sh16 = dataclasses.replace(sh8, act_fp8=False)
+    _, _, _, y8 = oracle.moe_layer(sh8, lw1, xh, mirror=False)
+    _, _, _, y16 = oracle.moe_layer(sh16, lw1, xh, mirror=False)
+    np.testing.assert_allclose(y8, y16, rtol=1e-6, atol=1e-6 * np.abs(y16).max())
+
+
+def test_w8a8_differs_from_w8a16_within_e4m3_precision():
+    """On general rows the FP8-activation mixture is not the bf16 one (the
+    setting is not ignored) and stays within E4M3's precision of it."""
+    import dataclasses
+    _, osh, lw = _fp8_moe_model()
+    rng = np.random.default_rng(6)
+    xh = oracle.round_bf16(rng.standard_normal((32, 128)))
+    _, _, _, y8 = oracle.moe_layer(osh, lw, xh, mirror=True)
+    _, _, _, y16 = oracle.moe_layer(dataclasses.replace(osh, act_fp8=False), lw,
+                                    xh, mirror=True)
+    err = np.max(np.abs(y8 - y16)) / np.max(np.abs(y16))
+    assert 1e-4 < err < 0.1, err
