@@ -352,8 +352,10 @@ std::string check_desc(const dg_model_desc* d) {
   if (d->act_dtype != DG_BF16 && d->act_dtype != DG_FP8_E4M3)
     return "act_dtype must be DG_BF16 or DG_FP8_E4M3";
   if (d->act_dtype == DG_FP8_E4M3 &&
-      (d->expert_dtype != DG_FP8_E4M3 || d->hidden % 128 || d->expert_ffn % 128))
-    return "E4M3 activations need E4M3 experts and hidden, expert_ffn multiples of 128";
+      (d->expert_dtype != DG_FP8_E4M3 || d->hidden % 128 || d->expert_ffn % 128 ||
+       d->hidden > 4096 || d->expert_ffn > 4096))
+    return "E4M3 activations need E4M3 experts and hidden, expert_ffn multiples of "
+           "128 up to 4096";
   if (d->n_shared_experts < 0 || d->n_shared_experts > 1 ||
       d->n_experts + d->n_shared_experts > 256)
     return "n_shared_experts must be 0 or 1 (and n_experts + shared <= 256)";
@@ -1383,7 +1385,8 @@ dg_status dg_op_quantize_rows(const void* x, int32_t rows, int32_t k,
                               void* stream) {
   if (!x || !scale || (!codes && !values))
     return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
-  if (rows < 0 || k < 8 || k % 8) return fail(nullptr, DG_ERR_SHAPE, "k must be a multiple of 8");
+  if (rows < 0 || k < 8 || k % 8 || k > 4096)
+    return fail(nullptr, DG_ERR_SHAPE, "k must be a multiple of 8 in 8..4096");
   HIPCHK(nullptr, launch_quant_rows((const uint16_t*)x, k, rows, k, nullptr, 0, codes,
                                     (uint16_t*)values, scale, (hipStream_t)stream));
   return DG_OK;

@@ -37,41 +37,6 @@ __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
-// OCP FP8 E4M3 code of an fp32 value: the nearest finite E4M3 value, ties
-// to the even code, saturating at +-448, sign bit from v.  Normal E4M3
-// values (|v| >= 2^-6) keep 3 of the 23 fp32 mantissa bits, rounded to
-// nearest even on the 20 dropped bits; below 2^-6 the step is 2^-9, so the
-// code is rint(|v| 2^9) (0..8, where 8 is the smallest normal's code).
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.f);
-  } else {
-    const uint32_t ab = __float_as_uint(a);
-    int ex = (int)(ab >> 23) - 127;
-    uint32_t keep = (ab >> 20) & 7u;
-    const uint32_t rem = ab & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-    if (keep == 8u) {
-      keep = 0;
-      ++ex;
-    }
-    code = ((uint32_t)(ex + 7) << 3) | keep;
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
-}
-// Value of an E4M3 code (not NaN) as fp32.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const int ex = (c >> 3) & 0xF, man = c & 7;
-  const float m = ex ? ldexpf((float)(8 + man), ex - 10) : ldexpf((float)man, -9);
-  return (c & 0x80u) ? -m : m;
-}
-
 // 16 OCP E4M3 bytes -> 16 bf16 (exact: 3 mantissa bits and exponents
 // 2^-9..2^8 all fit in bfloat16), by gfx950's packed conversion with unit
 // scale: each instruction widens the two bytes of one half-word, byte 0 of
@@ -383,8 +348,9 @@ hipError_t launch_unpermute_norm(const float* y, int T, int k, int H, float* x,
                                  uint16_t* xh, float* copy_f32,
                                  const int32_t* out_row, hipStream_t s);
 // Per-row E4M3 quantisation of bf16 rows x [rows, ldx] (K values each, K
-// a multiple of 8): scale[r] = max |x_r| / 448 (1 for a zero row), codes
-// e4m3(x / scale) into q8 [rows, K] and/or their values as bf16 into q16
+// a multiple of 8, at most 4096): scale[r] = max |x_r| / 448 (1 for a zero
+// row), codes e4m3(x * (448 / max |x_r|)) into q8 [rows, K] and/or their
+// values as bf16 into q16
 // [rows, K] (either may be null).  With count (groups of cap rows), row r
 // is skipped unless r % cap < count[r / cap].
 hipError_t launch_quant_rows(const uint16_t* x, int ldx, int rows, int K,

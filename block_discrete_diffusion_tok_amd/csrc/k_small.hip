@@ -1000,52 +1000,63 @@ hipError_t launch_permute(const int32_t* idx, int n_pairs, int E, int bm,
   return hipGetLastError();
 }
 
-// One workgroup per row: the row's max |x| by a block reduction, then each
-// 8-value run divided by the scale (fp32 division, correctly rounded) and
-// encoded.
+// One wave per row (4 rows per workgroup): the row's 16-byte runs of 8
+// values stay in registers (K <= 64 x 8 x kQuantRuns), the max |x| is a wave
+// reduction, then each value is multiplied by r = 448 / max (fp32), clamped
+// to +-448 and encoded by gfx950's packed fp32 -> E4M3 conversion (nearest,
+// ties to even: checked bit for bit against the format's definition for
+// every fp32 input of magnitude <= 448).
+constexpr int kQuantRuns = 8;
 __global__ __launch_bounds__(256) void quant_rows_kernel(
-    const uint16_t* x, int ldx, int K, const int32_t* count, int cap, uint8_t* q8,
-    uint16_t* q16, float* scale) {
-  __shared__ float red[4];
-  const int r = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* x, int ldx, int rows, int K, const int32_t* count, int cap,
+    uint8_t* q8, uint16_t* q16, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
   if (count && r % cap >= count[r / cap]) return;
   const uint16_t* xr = x + (long long)r * ldx;
+  const int runs = K >> 3;
+  uint4 v[kQuantRuns];
   float amax = 0.f;
-  for (int c = 8 * tid; c < K; c += 8 * 256) {
-    const uint4 v = *(const uint4*)(xr + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[i] & 0xFFFFu))));
-      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[i] >> 16))));
+  for (int i = 0; i < kQuantRuns; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < runs ? *(const uint4*)(xr + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[j] & 0xFFFFu))));
+      amax = fmaxf(amax, fabsf(bf2f((uint16_t)(w[j] >> 16))));
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, shfl_xor(amax, off));
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = amax > 0.f ? amax / 448.f : 1.f;
-  if (tid == 0) scale[r] = sc;
-  for (int c = 8 * tid; c < K; c += 8 * 256) {
-    const uint4 v = *(const uint4*)(xr + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t code[8];
+  const float mul = amax > 0.f ? 448.f / amax : 1.f;
+  if (lane == 0) scale[r] = sc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      code[2 * i] = e4m3_encode(bf2f((uint16_t)(w[i] & 0xFFFFu)) / sc);
-      code[2 * i + 1] = e4m3_encode(bf2f((uint16_t)(w[i] >> 16)) / sc);
+  for (int i = 0; i < kQuantRuns; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= runs) break;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t pk[2];   // 8 codes, byte j = value j
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float f[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f[2 * j] = fminf(fmaxf(bf2f((uint16_t)(w[2 * h + j] & 0xFFFFu)) * mul, -448.f), 448.f);
+        f[2 * j + 1] = fminf(fmaxf(bf2f((uint16_t)(w[2 * h + j] >> 16)) * mul, -448.f), 448.f);
+      }
+      int p = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      p = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p, true);
+      pk[h] = (uint32_t)p;
     }
-    if (q8)
-      *(uint2*)(q8 + (long long)r * K + c) =
-          make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
-                     code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
+    if (q8) *(uint2*)(q8 + (long long)r * K + 8 * c) = make_uint2(pk[0], pk[1]);
     if (q16) {
-      uint32_t h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        h[i] = pack_bf2(e4m3_value(code[2 * i]), e4m3_value(code[2 * i + 1]));
-      *(uint4*)(q16 + (long long)r * K + c) = make_uint4(h[0], h[1], h[2], h[3]);
+      u32x4_t lo, hi;
+      widen_e4m3x16(u32x4_t{pk[0], pk[1], 0u, 0u}, lo, hi);
+      *(uint4*)(q16 + (long long)r * K + 8 * c) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
   }
 }
@@ -1054,9 +1065,10 @@ hipError_t launch_quant_rows(const uint16_t* x, int ldx, int rows, int K,
                              const int32_t* count, int cap, uint8_t* q8,
                              uint16_t* q16, float* scale, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (K <= 0 || K % 8 || ldx % 8 || (count && cap <= 0)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(rows), dim3(256), 0, s, x, ldx, K, count,
-                     cap, q8, q16, scale);
+  if (K <= 0 || K % 8 || K > 64 * 8 * kQuantRuns || ldx % 8 || (count && cap <= 0))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, x, ldx,
+                     rows, K, count, cap, q8, q16, scale);
   return hipGetLastError();
 }
 

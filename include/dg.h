@@ -96,11 +96,11 @@ typedef struct {
                              write-up serves in FP8: Table 3 and Figure 11
                              captions).  DG_FP8_E4M3 (W8A8; needs E4M3
                              experts and hidden, expert_ffn multiples of
-                             128): each row (a token's FFN-norm output for
+                             128 up to 4096): each row (a token's FFN-norm output for
                              gate/up, a pair's SwiGLU output for down) is
                              quantised with scale s = max|row| / 448 (1 for
-                             a zero row), codes = E4M3(row / s) to nearest,
-                             ties to even, saturating (fp32 division); the
+                             a zero row), codes = E4M3(row x (448 / max|row|))
+                             to nearest, ties to even, saturating (fp32); the
                              product is s x w_scale[n] x sum q_row q_w,
                              on gfx950's FP8 MFMA where many rows share an
                              expert.  DG_BF16: bf16 rows. */

@@ -138,9 +138,10 @@ size_t dg_op_lmhead_sample_workspace_bytes(int32_t m, int32_t vocab);
 
 /* Per-row E4M3 quantisation of activations (the FP8 rows of the expert
  * GEMMs when act_dtype is DG_FP8_E4M3; write-up Table 3 caption, FP8):
- * x [rows, K] bf16 (K a multiple of 8) -> scale [rows] fp32 = max|x_r| /
- * 448 (1 for a zero row) and codes [rows, K] = E4M3(x / scale): nearest,
- * ties to even, saturating, fp32 division.  codes or values (their bf16
+ * x [rows, K] bf16 (K a multiple of 8, at most 4096) -> scale [rows] fp32 = max|x_r| /
+ * 448 (1 for a zero row) and codes [rows, K] = E4M3(x * (448 / max|x_r|)):
+ * nearest, ties to even, saturating; the divisions and the product in
+ * fp32.  codes or values (their bf16
  * values [rows, K]) may be NULL, not both. */
 dg_status dg_op_quantize_rows(const void* x, int32_t rows, int32_t k,
                               uint8_t* codes, void* values, float* scale,

@@ -69,9 +69,9 @@ R13 FP8 activations (write-up Table 3 and Figure 11 captions: served in
     FP8; the pages fix no scaling): with E4M3 experts and ``act_fp8`` the
     expert products take every row they multiply (a token's FFN-norm row
     for gate/up, a pair's SwiGLU row for down) as OCP E4M3 codes with one
-    scale per row: a = max |row|, s = a / 448 (1 for a zero row), codes =
-    E4M3(row / s) to nearest, ties to even, saturating, each step in fp32;
-    the product is s_row s_w[n] sum_k q_row[k] q_w[n][k].  Per-row dynamic
+    scale per row: a = max |row|, s = a / 448, r = 448 / a (both 1 for a
+    zero row), codes = E4M3(row * r) to nearest, ties to even, saturating,
+    each step in fp32; the product is s_row s_w[n] sum_k q_row[k] q_w[n][k].  Per-row dynamic
     scales are the plainest reading for activations that change every
     step.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in

@@ -76,13 +76,17 @@ def encode_e4m3(v):
 
 def quantize_rows_e4m3(x):
     """Per-row E4M3 quantisation of activations (reading R13), every step in
-    fp32 as the definition states: a = max |x_row|, s = a / 448 (fp32
-    division; s = 1 for an all-zero row), q = encode_e4m3(x / s) with x / s
-    an fp32 division.  x: [rows, K] values exactly representable in fp32
-    (bf16 activations).  Returns (codes uint8 [rows, K], scales float32
-    [rows])."""
+    fp32 as the definition states: a = max |x_row|; the row's scale s =
+    a / 448 and its multiplier r = 448 / a (fp32 divisions; both 1 for an
+    all-zero row); q = encode_e4m3(x * r) with x * r an fp32 product
+    (clamped to +-448, which the encoding's saturation gives anyway).
+    x: [rows, K] values exactly representable in fp32 (bf16 activations).
+    Returns (codes uint8 [rows, K], scales float32 [rows])."""
     x32 = np.asarray(x, dtype=np.float32)
     a = np.max(np.abs(x32), axis=1)
-    s = np.where(a > 0, a / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    v = (x32 / s[:, None]).astype(np.float32)
-    return encode_e4m3(v), s
+    pos = a > 0
+    safe = np.where(pos, a, np.float32(1.0)).astype(np.float32)
+    s = np.where(pos, safe / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    r = np.where(pos, np.float32(448.0) / safe, np.float32(1.0)).astype(np.float32)
+    v = (x32 * r[:, None]).astype(np.float32)
+    return encode_e4m3(np.clip(v, np.float32(-448.0), np.float32(448.0))), s
