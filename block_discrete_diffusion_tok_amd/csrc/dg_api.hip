@@ -114,8 +114,11 @@ struct dg_ctx {
   const float* final_norm;
   std::vector<dg_layer_weights> layers;
   int max_requests, max_kv_len, max_canvases;
-  uint16_t* k_cache;
+  uint16_t* k_cache;     // bf16 values, or E4M3 codes (kv8) at the same offsets
   uint16_t* v_cache;
+  bool kv8;              // E4M3 cache: codes, then one fp32 scale per row
+  float* k_scales;       // [L][R][Hkv][S] after the codes (kv8)
+  float* v_scales;
   char* ws;
   size_t ws_bytes;
   hipStream_t stream;
@@ -351,6 +354,8 @@ std::string check_desc(const dg_model_desc* d) {
     return "canvas_len must be in 0..256 (0: 256)";
   if (d->act_dtype != DG_BF16 && d->act_dtype != DG_FP8_E4M3)
     return "act_dtype must be DG_BF16 or DG_FP8_E4M3";
+  if (d->kv_dtype != DG_BF16 && d->kv_dtype != DG_FP8_E4M3)
+    return "kv_dtype must be DG_BF16 or DG_FP8_E4M3";
   if (d->act_dtype == DG_FP8_E4M3 &&
       (d->expert_dtype != DG_FP8_E4M3 || d->hidden % 128 || d->expert_ffn % 128 ||
        d->hidden > 4096 || d->expert_ffn > 4096))
@@ -685,17 +690,47 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   hipStream_t s = c->stream;
   GemmArgs g = gemm_dense(c->xh, T, H, w.w_qkv, qkvN, c->qkv, qkvN);
   KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
-  uint16_t* kc = c->k_cache + l * layer_stride;
-  uint16_t* vc = c->v_cache + l * layer_stride;
+  // layer l's cache: bf16 rows, or E4M3 codes (same offsets in bytes) and
+  // one scale per row
+  uint16_t* kc = c->kv8 ? (uint16_t*)((char*)c->k_cache + l * layer_stride)
+                        : c->k_cache + l * layer_stride;
+  uint16_t* vc = c->kv8 ? (uint16_t*)((char*)c->v_cache + l * layer_stride)
+                        : c->v_cache + l * layer_stride;
+  float* ks = c->kv8 ? c->k_scales + l * (layer_stride / D) : nullptr;
+  float* vs = c->kv8 ? c->v_scales + l * (layer_stride / D) : nullptr;
   int vis0[DG_MAX_BATCH];
   canvas_groups(n, req, vis0);   // (checked by the caller)
   if (commit) {
     // canvas b is appended after its request's earlier canvases of the batch
     int row0[DG_MAX_BATCH];
     for (int b = 0; b < n; ++b) row0[b] = plen[b] + (b - vis0[b]) * C;
-    KRUN(c, 15, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
-                               C, Hkv, D, kc, vc, req_stride,
-                               head_stride, req, row0, s));
+    if (c->kv8) {
+      KvQuantArgs q;
+      memset(&q, 0, sizeof(q));
+      q.src_k = c->qkv + Hq * D;
+      q.src_v = c->qkv + (Hq + Hkv) * D;
+      q.src_b_stride = (long long)C * qkvN;
+      q.src_row_stride = qkvN;
+      q.src_head_stride = D;
+      q.n = n;
+      q.rows = C;
+      q.Hkv = Hkv;
+      q.D = D;
+      q.S = c->max_kv_len;
+      q.kc = (uint8_t*)kc;
+      q.vc = (uint8_t*)vc;
+      q.ks = ks;
+      q.vs = vs;
+      for (int b = 0; b < n; ++b) {
+        q.req[b] = req[b];
+        q.row0[b] = row0[b];
+      }
+      KRUN(c, 15, launch_kv_quant(q, s));
+    } else {
+      KRUN(c, 15, launch_kv_append(c->qkv, qkvN, Hq * D, (Hq + Hkv) * D, n,
+                                 C, Hkv, D, kc, vc, req_stride,
+                                 head_stride, req, row0, s));
+    }
     if (l == d.n_layers - 1 && !full) return DG_OK;
   }
   AttnArgs aa;
@@ -708,6 +743,8 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   aa.D = D;
   aa.kc = kc;
   aa.vc = vc;
+  aa.ks = ks;
+  aa.vs = vs;
   aa.req_stride = req_stride;
   aa.head_stride = head_stride;
   for (int b = 0; b < n; ++b) {
@@ -790,8 +827,10 @@ size_t dg_workspace_bytes(const dg_model_desc* d, int32_t max_canvases) {
 size_t dg_kv_cache_bytes(const dg_model_desc* d, int32_t max_requests,
                          int32_t max_kv_len) {
   if (!check_desc(d).empty() || max_requests < 1 || max_kv_len < 1) return 0;
-  return (size_t)d->n_layers * max_requests * d->n_kv_heads * max_kv_len *
-         d->head_dim * 2;
+  const size_t rows = (size_t)d->n_layers * max_requests * d->n_kv_heads * max_kv_len;
+  // E4M3: one byte per value, then one fp32 scale per row
+  if (d->kv_dtype == DG_FP8_E4M3) return rows * d->head_dim + rows * 4;
+  return rows * d->head_dim * 2;
 }
 
 size_t dg_packed_bytes(int32_t groups, int32_t rows, int32_t cols, int32_t dtype) {
@@ -857,6 +896,16 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   c->max_canvases = max_canvases;
   c->k_cache = (uint16_t*)k_cache;
   c->v_cache = (uint16_t*)v_cache;
+  c->kv8 = desc->kv_dtype == DG_FP8_E4M3;
+  if (c->kv8) {
+    const size_t rows = (size_t)desc->n_layers * max_requests * desc->n_kv_heads * max_kv_len;
+    c->k_scales = (float*)((char*)k_cache + rows * desc->head_dim);
+    c->v_scales = (float*)((char*)v_cache + rows * desc->head_dim);
+    if (((uintptr_t)c->k_scales | (uintptr_t)c->v_scales) % 4) {
+      delete c;
+      return fail(nullptr, DG_ERR_INVALID_ARG, "caches must be 4-byte aligned");
+    }
+  }
   c->ws = (char*)workspace;
   c->ws_bytes = workspace_bytes;
   c->stream = (hipStream_t)stream;
@@ -953,6 +1002,26 @@ dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
   const long long layer_stride = (long long)c->max_requests * req_stride;
   const long long src_layer = (long long)d.n_kv_heads * n * d.head_dim;
   for (int l = 0; l < d.n_layers; ++l) {
+    if (c->kv8) {   // E4M3 cache: each row quantised on the way in
+      KvQuantArgs q;
+      memset(&q, 0, sizeof(q));
+      q.src_k = (const uint16_t*)k + l * src_layer;
+      q.src_v = (const uint16_t*)v + l * src_layer;
+      q.src_row_stride = d.head_dim;
+      q.src_head_stride = (long long)n * d.head_dim;
+      q.n = 1;
+      q.rows = n;
+      q.Hkv = d.n_kv_heads;
+      q.D = d.head_dim;
+      q.S = c->max_kv_len;
+      q.kc = (uint8_t*)c->k_cache + l * layer_stride;
+      q.vc = (uint8_t*)c->v_cache + l * layer_stride;
+      q.ks = c->k_scales + l * (layer_stride / d.head_dim);
+      q.vs = c->v_scales + l * (layer_stride / d.head_dim);
+      q.req[0] = req;
+      KRUN(c, 16, launch_kv_quant(q, c->stream));
+      continue;
+    }
     const long long dst = l * layer_stride + req * req_stride;
     KRUN(c, 16, launch_kv_install((const uint16_t*)k + l * src_layer,
                                 d.n_kv_heads, n, d.head_dim, c->k_cache + dst,
@@ -1137,13 +1206,16 @@ size_t dg_op_attention_workspace_bytes(int32_t n, int32_t canvas_len,
 dg_status dg_op_canvas_attention(const void* qkv, int32_t n, int32_t canvas_len,
                                  int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t head_dim, const void* k_cache,
-                                 const void* v_cache, int32_t max_requests,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, int32_t max_requests,
                                  int32_t max_kv_len, const int32_t* req,
                                  const int32_t* prefix_len, int32_t causal,
                                  int32_t kv_splits, void* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (!qkv || !k_cache || !v_cache || !req || !prefix_len || !out)
     return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (!k_scale != !v_scale)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "give both scale arrays or neither");
   if (n < 1 || n > DG_MAX_BATCH) return fail(nullptr, DG_ERR_CAPACITY, "n outside 1..64");
   if (canvas_len < 1 || canvas_len > DG_CANVAS)
     return fail(nullptr, DG_ERR_SHAPE, "canvas_len outside 1..256");
@@ -1177,6 +1249,8 @@ dg_status dg_op_canvas_attention(const void* qkv, int32_t n, int32_t canvas_len,
   aa.D = head_dim;
   aa.kc = (const uint16_t*)k_cache;
   aa.vc = (const uint16_t*)v_cache;
+  aa.ks = k_scale;
+  aa.vs = v_scale;
   aa.head_stride = (long long)max_kv_len * head_dim;
   aa.req_stride = (long long)n_kv_heads * aa.head_stride;
   for (int b = 0; b < n; ++b) {
@@ -1415,11 +1489,16 @@ dg_status dg_op_eb_select(int32_t n, int32_t canvas_len, const float* entropy,
 dg_status dg_op_kv_append(const void* qkv, int32_t n, int32_t canvas_len,
                           int32_t n_q_heads, int32_t n_kv_heads,
                           int32_t head_dim, void* k_cache, void* v_cache,
+                          float* k_scale, float* v_scale,
                           int32_t max_requests, int32_t max_kv_len,
                           const int32_t* req, const int32_t* row0,
                           void* stream) {
   if (!qkv || !k_cache || !v_cache || !req || !row0)
     return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (!k_scale != !v_scale)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "give both scale arrays or neither");
+  if (k_scale && head_dim != 64 && head_dim != 128)
+    return fail(nullptr, DG_ERR_SHAPE, "an E4M3 cache needs head_dim 64 or 128");
   if (n < 1 || n > DG_MAX_BATCH) return fail(nullptr, DG_ERR_CAPACITY, "n outside 1..64");
   if (canvas_len < 1 || canvas_len > DG_CANVAS || head_dim % 8 || head_dim < 8 ||
       n_kv_heads < 1 || n_q_heads < 1)
@@ -1431,6 +1510,31 @@ dg_status dg_op_kv_append(const void* qkv, int32_t n, int32_t canvas_len,
       return fail(nullptr, DG_ERR_CAPACITY, "rows beyond max_kv_len");
   }
   const long long head_stride = (long long)max_kv_len * head_dim;
+  if (k_scale) {
+    const int ld = (n_q_heads + 2 * n_kv_heads) * head_dim;
+    KvQuantArgs q;
+    memset(&q, 0, sizeof(q));
+    q.src_k = (const uint16_t*)qkv + n_q_heads * head_dim;
+    q.src_v = (const uint16_t*)qkv + (n_q_heads + n_kv_heads) * head_dim;
+    q.src_b_stride = (long long)canvas_len * ld;
+    q.src_row_stride = ld;
+    q.src_head_stride = head_dim;
+    q.n = n;
+    q.rows = canvas_len;
+    q.Hkv = n_kv_heads;
+    q.D = head_dim;
+    q.S = max_kv_len;
+    q.kc = (uint8_t*)k_cache;
+    q.vc = (uint8_t*)v_cache;
+    q.ks = k_scale;
+    q.vs = v_scale;
+    for (int b = 0; b < n; ++b) {
+      q.req[b] = req[b];
+      q.row0[b] = row0[b];
+    }
+    HIPCHK(nullptr, launch_kv_quant(q, (hipStream_t)stream));
+    return DG_OK;
+  }
   HIPCHK(nullptr, launch_kv_append((const uint16_t*)qkv,
                                    (n_q_heads + 2 * n_kv_heads) * head_dim,
                                    n_q_heads * head_dim,

@@ -292,6 +292,11 @@ struct AttnArgs {
   uint16_t* out;        // [n*C, Hq*D]
   float* opart;         // [splits][n*Hq*C][D]
   float* lpart;         // [splits][n*Hq*C]
+  // E4M3 cache (null: bf16): kc / vc then hold codes (one byte per value,
+  // same strides) and ks / vs the fp32 scale of each cached row, at the
+  // row's code offset / D
+  const float* ks;
+  const float* vs;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 // KV splits for n canvases; max_keys = longest prefix + C (0: the upper
@@ -388,5 +393,25 @@ hipError_t launch_kv_append(const uint16_t* qkv, int ldqkv, int col0_k,
 hipError_t launch_kv_install(const uint16_t* src, int Hkv, int n, int D,
                              uint16_t* dst, long long head_stride,
                              hipStream_t s);
+
+// Rows into an E4M3 cache (per-row quantisation as launch_quant_rows).
+// For canvas b < n and row j < rows, head g < Hkv: the bf16 K (V) row starts
+// at src_k (src_v) + b * src_b_stride + j * src_row_stride + g *
+// src_head_stride and goes to cache row row0[b] + j of slot req[b], head g:
+// codes at kc / vc + ((req * Hkv + g) * S + row) * D, scale at ks / vs +
+// (req * Hkv + g) * S + row.
+struct KvQuantArgs {
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  long long src_b_stride, src_row_stride, src_head_stride;
+  int n, rows, Hkv, D, S;
+  uint8_t* kc;
+  uint8_t* vc;
+  float* ks;
+  float* vs;
+  int req[DG_MAX_BATCH];
+  int row0[DG_MAX_BATCH];
+};
+hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t s);
 
 }  // namespace dg

@@ -74,7 +74,24 @@ __device__ __forceinline__ bool attn_tile(const AttnArgs& a, int n_chunks, AttnT
   return true;
 }
 
-template <int D, int QB>
+// 8 cached E4M3 codes of a K/V row -> the 8 bf16 values attention reads:
+// the code values (exact in bf16, by gfx950's conversion) times the row's
+// scale in fp32, rounded to the nearest bf16.
+__device__ __forceinline__ u32x4_t deq8(const uint2 q, float sc) {
+  uint32_t w[4];
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true));
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_bf2(bf2f((uint16_t)(w[i] & 0xFFFFu)) * sc, bf2f((uint16_t)(w[i] >> 16)) * sc);
+  return o;
+}
+
+// KV8: the cache holds E4M3 codes with a scale per row (a.ks / a.vs).
+template <int D, int QB, bool KV8>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks) {
   constexpr int KP = D + 16;     // padded K row (elements)
   constexpr int VQ = D * 4 + 8;  // padded key-quad stride (elements; 16-byte rows)
@@ -143,6 +160,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
     kk = min(kk, N - 1);
     return kk < P ? pre + (long long)kk * D : can + (long long)(kk - P) * a.ldqkv;
   };
+  // E4M3 cache: the slot and head's codes (bytes, same strides) and scales
+  const long long cbase = (long long)a.req[b] * a.req_stride + (long long)g * a.head_stride;
+  const uint8_t* k8 = (const uint8_t*)a.kc + cbase;
+  const uint8_t* v8 = (const uint8_t*)a.vc + cbase;
+  const float* ks8 = KV8 ? a.ks + cbase / D : nullptr;
+  const float* vs8 = KV8 ? a.vs + cbase / D : nullptr;
+  // 8 values of key kk from d0 on, as bf16
+  auto kload = [&](const uint16_t* pre, const uint16_t* can, const uint8_t* c8,
+                   const float* s8, int kk, int d0) -> u32x4_t {
+    if (KV8) {
+      const int kc = min(kk, N - 1);
+      if (kc < P) return deq8(*(const uint2*)(c8 + (long long)kc * D + d0), s8[kc]);
+    }
+    return *(const u32x4_t*)(krow(pre, can, kk) + d0);
+  };
 
   // ---- K/V tile staging: global -> registers (issued a tile ahead) ->
   // LDS.  V goes to key quads [key/4][d][4]: an item is 4 keys x 8 d (four
@@ -153,14 +185,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
     static_for<KCH>([&](auto j) {
       const int c = min(tid + kThreads * (int)j, KITEMS - 1);
       const int key = c / (D / 8), dc = c % (D / 8);
-      kr[j] = *(const u32x4_t*)(krow(kpre, kcan, key0 + key) + dc * 8);
+      kr[j] = kload(kpre, kcan, k8, ks8, key0 + key, dc * 8);
     });
     static_for<VIT>([&](auto j) {
       const int it = min(tid + kThreads * (int)j, VITEMS - 1);
       const int q = it / (D / 8), c8 = it % (D / 8);
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
-        vr[j][kq] = *(const u32x4_t*)(krow(vpre, vcan, key0 + 4 * q + kq) + c8 * 8);
+        vr[j][kq] = kload(vpre, vcan, v8, vs8, key0 + 4 * q + kq, c8 * 8);
     });
   };
   auto lstore = [&](int buf) {
@@ -432,17 +464,24 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int n_chunks = (G * a.C + 128 * qb - 1) / (128 * qb);
   const int n_groups = a.Hkv * a.n * a.splits;
   const dim3 grid((unsigned)(((n_groups + 7) / 8) * 8 * n_chunks));
+  const bool kv8 = a.ks != nullptr;
+  if (kv8 && !a.vs) return hipErrorInvalidValue;
+#define DG_ATTN(DD, QQ, K8) \
+  hipLaunchKernelGGL((attn_kernel<DD, QQ, K8>), grid, dim3(kThreads), 0, s, a, n_chunks)
   if (a.D == 128) {
-    if (qb == 2)
-      hipLaunchKernelGGL((attn_kernel<128, 2>), grid, dim3(kThreads), 0, s, a, n_chunks);
-    else
-      hipLaunchKernelGGL((attn_kernel<128, 1>), grid, dim3(kThreads), 0, s, a, n_chunks);
+    if (kv8) {
+      if (qb == 2) DG_ATTN(128, 2, true); else DG_ATTN(128, 1, true);
+    } else {
+      if (qb == 2) DG_ATTN(128, 2, false); else DG_ATTN(128, 1, false);
+    }
   } else {
-    if (qb == 2)
-      hipLaunchKernelGGL((attn_kernel<64, 2>), grid, dim3(kThreads), 0, s, a, n_chunks);
-    else
-      hipLaunchKernelGGL((attn_kernel<64, 1>), grid, dim3(kThreads), 0, s, a, n_chunks);
+    if (kv8) {
+      if (qb == 2) DG_ATTN(64, 2, true); else DG_ATTN(64, 1, true);
+    } else {
+      if (qb == 2) DG_ATTN(64, 2, false); else DG_ATTN(64, 1, false);
+    }
   }
+#undef DG_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int n_rows = a.n * a.Hq * a.C;

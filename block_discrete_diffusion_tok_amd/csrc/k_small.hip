@@ -1061,6 +1061,51 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   }
 }
 
+// One wave per (row, head) of a canvas: the K row, then the V row, each
+// quantised as in quant_rows_kernel (D <= 128: at most 2 values a lane).
+__global__ __launch_bounds__(256) void kv_quant_kernel(KvQuantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (item >= a.rows * a.Hkv) return;
+  const int j = item / a.Hkv, g = item % a.Hkv;
+  const long long off = (long long)b * a.src_b_stride + (long long)j * a.src_row_stride +
+                        (long long)g * a.src_head_stride;
+  const long long crow = ((long long)a.req[b] * a.Hkv + g) * a.S + a.row0[b] + j;
+  const int per = a.D >> 6;  // values per lane (1 or 2)
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* r = (kv ? a.src_v : a.src_k) + off;
+    float v0 = 0.f, v1 = 0.f;
+    if (per == 2) {
+      const uint32_t w = *(const uint32_t*)(r + 2 * lane);
+      v0 = bf2f((uint16_t)(w & 0xFFFFu));
+      v1 = bf2f((uint16_t)(w >> 16));
+    } else {
+      v0 = bf2f(r[lane]);
+    }
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, shfl_xor(amax, off));
+    const float sc = amax > 0.f ? amax / 448.f : 1.f;
+    const float mul = amax > 0.f ? 448.f / amax : 1.f;
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(v0 * mul, -448.f), 448.f),
+                                                   fminf(fmaxf(v1 * mul, -448.f), 448.f), 0,
+                                                   false);
+    uint8_t* codes = (kv ? a.vc : a.kc) + crow * a.D;
+    if (per == 2) *(uint16_t*)(codes + 2 * lane) = (uint16_t)(pk & 0xFFFF);
+    else codes[lane] = (uint8_t)(pk & 0xFF);
+    if (lane == 0) (kv ? a.vs : a.ks)[crow] = sc;
+  }
+}
+
+hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t s) {
+  if (a.n <= 0 || a.rows <= 0) return hipSuccess;
+  if ((a.D != 64 && a.D != 128) || a.n > DG_MAX_BATCH) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_quant_kernel, dim3((a.rows * a.Hkv + 3) / 4, a.n), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_rows(const uint16_t* x, int ldx, int rows, int K,
                              const int32_t* count, int cap, uint8_t* q8,
                              uint16_t* q16, float* scale, hipStream_t s) {

@@ -37,7 +37,8 @@ class ModelDesc(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("expert_ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("expert_dtype", ctypes.c_int32), ("canvas_len", ctypes.c_int32),
-                ("n_shared_experts", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+                ("n_shared_experts", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -102,7 +103,7 @@ _SIGS = {
     "dg_op_linear": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
     "dg_packed_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dg_pack_weights": (_I, [_P, _I, _I, _I, _I, _P, _P]),
-    "dg_op_canvas_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+    "dg_op_canvas_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
                                     ctypes.POINTER(_I), ctypes.POINTER(_I), _I,
                                     _I, _P, _P, ctypes.c_size_t, _P]),
     "dg_op_attention_workspace_bytes": (ctypes.c_size_t, [_I] * 6),
@@ -120,7 +121,7 @@ _SIGS = {
     "dg_op_lmhead_sample_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dg_op_eb_select": (_I, [_I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "dg_op_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P, _P]),
-    "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _I, _I,
+    "dg_op_kv_append": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
                              ctypes.POINTER(_I), ctypes.POINTER(_I), _P]),
 }
 EXPORTS = tuple(_SIGS)
@@ -166,6 +167,8 @@ def model_desc(shape):
                      getattr(shape, "canvas_len", CANVAS),
                      getattr(shape, "n_shared_experts", 0),
                      FP8_E4M3 if getattr(shape, "act_dtype", "bf16") == "fp8_e4m3"
+                     else BF16,
+                     FP8_E4M3 if getattr(shape, "kv_dtype", "bf16") == "fp8_e4m3"
                      else BF16)
 
 
@@ -253,10 +256,15 @@ class Engine:
         ws_bytes = L.dg_workspace_bytes(ctypes.byref(self.desc), max_canvases)
         if kv_bytes == 0 or ws_bytes == 0:
             raise DgError(2, "unsupported model shape")
-        self.k_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
-                                   device=device)
-        self.v_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
-                                   device=device)
+        self.kv8 = getattr(shape, "kv_dtype", "bf16") == "fp8_e4m3"
+        if self.kv8:   # E4M3 codes, then one fp32 scale per row
+            self.k_cache = torch.empty(kv_bytes, dtype=torch.uint8, device=device)
+            self.v_cache = torch.empty(kv_bytes, dtype=torch.uint8, device=device)
+        else:
+            self.k_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
+                                       device=device)
+            self.v_cache = torch.empty(kv_bytes // 2, dtype=torch.bfloat16,
+                                       device=device)
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8,
                                      device=device)
         self.max_requests, self.max_kv_len = max_requests, max_kv_len
@@ -280,10 +288,27 @@ class Engine:
             pass
 
     def cache_view(self, which="k"):
+        """[L, requests, Hkv, max_kv_len, D]: bf16 values, or E4M3 codes
+        (uint8) of an E4M3 cache."""
         s = self.shape
         t = self.k_cache if which == "k" else self.v_cache
-        return t.view(s.n_layers, self.max_requests, s.n_kv_heads,
-                      self.max_kv_len, s.head_dim)
+        shape = (s.n_layers, self.max_requests, s.n_kv_heads, self.max_kv_len,
+                 s.head_dim)
+        if self.kv8:
+            n = s.n_layers * self.max_requests * s.n_kv_heads * self.max_kv_len
+            return t[:n * s.head_dim].view(shape)
+        return t.view(shape)
+
+    def scale_view(self, which="k"):
+        """[L, requests, Hkv, max_kv_len] fp32 row scales of an E4M3 cache
+        (None for a bf16 cache)."""
+        if not self.kv8:
+            return None
+        s = self.shape
+        t = self.k_cache if which == "k" else self.v_cache
+        n = s.n_layers * self.max_requests * s.n_kv_heads * self.max_kv_len
+        return t[n * s.head_dim:].view(torch.float32).view(
+            s.n_layers, self.max_requests, s.n_kv_heads, self.max_kv_len)
 
     def prefill_kv(self, req, k, v):
         """Install mode. k, v: [L, Hkv, n, D] bf16 device tensors
@@ -389,14 +414,18 @@ def op_linear(x, w, out, mode):
 
 def op_canvas_attention(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,
                         k_cache, v_cache, max_requests, max_kv_len, req,
-                        prefix_len, causal, kv_splits, out):
+                        prefix_len, causal, kv_splits, out, k_scale=None,
+                        v_scale=None):
+    """k_scale / v_scale: the per-row scales of an E4M3 cache (k_cache /
+    v_cache then hold codes), or None for a bf16 cache."""
     L = lib()
     nb = L.dg_op_attention_workspace_bytes(n, canvas_len, n_q_heads,
                                            n_kv_heads, head_dim, kv_splits)
     ws = _ws(nb, qkv.device)
     _check(L.dg_op_canvas_attention(
         _ptr(qkv), n, canvas_len, n_q_heads, n_kv_heads, head_dim,
-        _ptr(k_cache), _ptr(v_cache), max_requests, max_kv_len,
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        max_requests, max_kv_len,
         _i32_array(req), _i32_array(prefix_len), int(causal), kv_splits,
         _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return ws
@@ -481,9 +510,11 @@ def op_eb_select(entropy, argmax, committed, tokens, step, gamma, step_cap,
 
 
 def op_kv_append(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,
-                 k_cache, v_cache, max_requests, max_kv_len, req, row0):
+                 k_cache, v_cache, max_requests, max_kv_len, req, row0,
+                 k_scale=None, v_scale=None):
     _check(lib().dg_op_kv_append(_ptr(qkv), n, canvas_len, n_q_heads,
                                  n_kv_heads, head_dim, _ptr(k_cache),
-                                 _ptr(v_cache), max_requests, max_kv_len,
+                                 _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                 max_requests, max_kv_len,
                                  _i32_array(req), _i32_array(row0),
                                  _stream()))

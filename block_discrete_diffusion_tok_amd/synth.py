@@ -39,6 +39,7 @@ class ModelShape:
     canvas_len: int = CANVAS    # positions per canvas (128 or 256)
     n_shared_experts: int = 0   # 0 or 1 shared expert (the last expert group)
     act_dtype: str = "bf16"     # expert GEMM token rows: "bf16" or "fp8_e4m3"
+    kv_dtype: str = "bf16"      # KV cache: "bf16" or "fp8_e4m3"
 
 
 @dataclass(frozen=True)
@@ -85,6 +86,11 @@ WORKLOADS = {
                  prefix_len=2048, batch=32, uncommitted=256, gamma=1.0,
                  step_cap=256,
                  notes="30 layers, E4M3 experts, 32 concurrent canvases"),
+        Workload("stack30_kv8_h2048_p131072",
+                 ModelShape(30, **_GEMMA_LAYER, kv_dtype="fp8_e4m3"),
+                 prefix_len=131072, batch=1, uncommitted=256, gamma=1.0,
+                 step_cap=256, steps=12,
+                 notes="the 131072-token prefix in an E4M3 KV cache"),
         Workload("stack30_w8a8_b32_p2048",
                  ModelShape(30, **_GEMMA_LAYER, expert_dtype="fp8_e4m3",
                             act_dtype="fp8_e4m3"),

@@ -104,6 +104,14 @@ typedef struct {
                              product is s x w_scale[n] x sum q_row q_w,
                              on gfx950's FP8 MFMA where many rows share an
                              expert.  DG_BF16: bf16 rows. */
+  int32_t kv_dtype;       /* dg_dtype of the KV cache.  DG_FP8_E4M3: every
+                             cached key / value row (one head, one position)
+                             is stored as E4M3 codes quantised like the
+                             activation rows above, with its fp32 scale, and
+                             attention reads it as bf16(code value x scale);
+                             keys and values of the canvases in a call are
+                             used as computed until they are committed.
+                             See dg_kv_cache_bytes for the layout. */
 } dg_model_desc;
 
 /* Packed weight layout.  Every weight matrix the kernels read (w_qkv, w_o,
@@ -154,7 +162,10 @@ typedef struct {
 size_t dg_workspace_bytes(const dg_model_desc* desc, int32_t max_canvases);
 
 /* Bytes of ONE of the two caches (K or V): layout
- * [n_layers][max_requests][n_kv_heads][max_kv_len][head_dim] bf16. */
+ * [n_layers][max_requests][n_kv_heads][max_kv_len][head_dim] bf16; with
+ * kv_dtype DG_FP8_E4M3 the same array of E4M3 codes (one byte each)
+ * followed by the fp32 scale of every row,
+ * [n_layers][max_requests][n_kv_heads][max_kv_len]. */
 size_t dg_kv_cache_bytes(const dg_model_desc* desc, int32_t max_requests,
                          int32_t max_kv_len);
 

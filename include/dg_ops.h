@@ -43,13 +43,18 @@ dg_status dg_op_linear(const void* x, int32_t m, int32_t k, const void* w,
  * DG_ERR_INVALID_ARG if equal req entries are not contiguous.
  * qkv [n*canvas_len, (Hq + 2 Hkv) D] bf16 (Q, K, V of the canvas rows as
  * written by the Q/K/V projection); k_cache / v_cache: one layer,
- * [max_requests][Hkv][max_kv_len][D] bf16; out [n*canvas_len, Hq D] bf16.
+ * [max_requests][Hkv][max_kv_len][D] bf16, or with k_scale / v_scale
+ * (both or neither) the E4M3 cache of the model's kv_dtype: codes at the
+ * same offsets in bytes and k_scale / v_scale [max_requests][Hkv]
+ * [max_kv_len] fp32, a cached row read as bf16(code value x scale) in
+ * fp32 (write-up Table 3 caption, FP8); out [n*canvas_len, Hq D] bf16.
  * kv_splits: number of key ranges processed by separate workgroups and
  * merged by log-sum-exp weights (0 = automatic, else 1..32). */
 dg_status dg_op_canvas_attention(const void* qkv, int32_t n,
                                  int32_t canvas_len, int32_t n_q_heads,
                                  int32_t n_kv_heads, int32_t head_dim,
                                  const void* k_cache, const void* v_cache,
+                                 const float* k_scale, const float* v_scale,
                                  int32_t max_requests, int32_t max_kv_len,
                                  const int32_t* req, const int32_t* prefix_len,
                                  int32_t causal, int32_t kv_splits, void* out,
@@ -161,10 +166,14 @@ dg_status dg_op_eb_select(int32_t n, int32_t canvas_len, const float* entropy,
 /* KV append (write-up Figure 4 stage 3): copy the K and V of canvas b's
  * canvas_len rows from qkv into cache rows [row0[b], row0[b] + canvas_len)
  * of slot req[b] in one layer's k_cache / v_cache
- * ([max_requests][Hkv][max_kv_len][D] bf16).  req, row0: (host) [n]. */
+ * ([max_requests][Hkv][max_kv_len][D] bf16; with k_scale / v_scale, both or
+ * neither, an E4M3 cache: each row quantised as dg_op_quantize_rows does,
+ * its codes at the same offsets in bytes and its scale in k_scale /
+ * v_scale [max_requests][Hkv][max_kv_len]).  req, row0: (host) [n]. */
 dg_status dg_op_kv_append(const void* qkv, int32_t n, int32_t canvas_len,
                           int32_t n_q_heads, int32_t n_kv_heads,
                           int32_t head_dim, void* k_cache, void* v_cache,
+                          float* k_scale, float* v_scale,
                           int32_t max_requests, int32_t max_kv_len,
                           const int32_t* req, const int32_t* row0,
                           void* stream);

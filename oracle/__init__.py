@@ -50,4 +50,4 @@ from .model import (  # noqa: F401
     expert_matrix,
 )
 from .numerics import (round_bf16, decode_e4m3, encode_e4m3,  # noqa: F401
-                       quantize_rows_e4m3)
+                       quantize_rows_e4m3, kv_cache_values)

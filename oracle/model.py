@@ -74,6 +74,14 @@ R13 FP8 activations (write-up Table 3 and Figure 11 captions: served in
     each step in fp32; the product is s_row s_w[n] sum_k q_row[k] q_w[n][k].  Per-row dynamic
     scales are the plainest reading for activations that change every
     step.
+R14 FP8 KV cache (write-up Table 3 caption, FP8 serving; the cache is
+    what long prompts move): with ``kv_fp8`` every cached key or value row
+    (one KV head, one position: D values) is stored as E4M3 codes with one
+    scale, quantised as in R13 when it enters the cache, and attention
+    reads bf16(fp32(code value x scale)) for it.  Keys and values of the
+    canvases in the same call (the canvas, the request's earlier canvases
+    of the batch) are used as computed; they enter the cache quantised when
+    committed.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -88,7 +96,8 @@ from dataclasses import dataclass
 import numpy as np
 from threadpoolctl import threadpool_limits
 
-from .numerics import round_bf16, decode_e4m3, quantize_rows_e4m3
+from .numerics import (round_bf16, decode_e4m3, quantize_rows_e4m3,
+                       kv_cache_values)
 from .philox import philox4x32_10, uniform24
 
 CANVAS = 256
@@ -108,6 +117,7 @@ class Shapes:
     rms_eps: float = 1e-6
     n_shared_experts: int = 0   # reading R10
     act_fp8: bool = False       # reading R13
+    kv_fp8: bool = False        # reading R14
 
 
 # The oracle's real type: fp64, so that every dot product, softmax sum and
@@ -508,7 +518,10 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
         for b in range(b_count):
             rows = slice(b * c_len, (b + 1) * c_len)
             kp, vp = prefix[b]
-            kp, vp = _real(kp[li]), _real(vp[li])
+            kp, vp = kp[li], vp[li]
+            if sh.kv_fp8:   # reading R14: the cache holds E4M3 rows
+                kp, vp = kv_cache_values(kp), kv_cache_values(vp)
+            kp, vp = _real(kp), _real(vp)
             if earlier[b]:   # the request's earlier canvases follow its prefix
                 sl = [slice(e * c_len, (e + 1) * c_len) for e in earlier[b]]
                 kp = np.concatenate([kp] + [k[:, r] for r in sl], axis=1)

@@ -90,3 +90,17 @@ def quantize_rows_e4m3(x):
     r = np.where(pos, np.float32(448.0) / safe, np.float32(1.0)).astype(np.float32)
     v = (x32 * r[:, None]).astype(np.float32)
     return encode_e4m3(np.clip(v, np.float32(-448.0), np.float32(448.0))), s
+
+
+def kv_cache_values(rows):
+    """The values attention reads from an E4M3 KV cache (reading R14) for
+    cached rows [..., D] (bf16 K or V rows as the cache received them):
+    each row quantised as quantize_rows_e4m3 does, then decoded as
+    bf16(fp32(code value x scale)) -- the fp32 product rounded to the
+    nearest bf16, ties to even."""
+    rows = np.asarray(rows)
+    shape = rows.shape
+    flat = rows.reshape(-1, shape[-1])
+    codes, scale = quantize_rows_e4m3(flat)
+    prod = (decode_e4m3(codes).astype(np.float32) * scale[:, None]).astype(np.float32)
+    return round_bf16(prod.astype(np.float64)).reshape(shape)

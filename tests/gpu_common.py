@@ -27,6 +27,13 @@ def fp8_act(shape):
     return getattr(shape, "act_dtype", "bf16") == "fp8_e4m3"
 
 
+def cache_scales(eng, li):
+    """Layer li's (K, V) row scales of an engine's E4M3 cache, or (None,
+    None) for a bf16 cache."""
+    ks, vs = eng.scale_view("k"), eng.scale_view("v")
+    return (None, None) if ks is None else (ks[li], vs[li])
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -37,7 +44,8 @@ def oshape(s):
                          s.head_dim, s.n_experts, s.top_k, s.expert_ffn,
                          s.vocab, s.rms_eps,
                          getattr(s, "n_shared_experts", 0),
-                         getattr(s, "act_dtype", "bf16") == "fp8_e4m3")
+                         getattr(s, "act_dtype", "bf16") == "fp8_e4m3",
+                         getattr(s, "kv_dtype", "bf16") == "fp8_e4m3")
 
 
 def to_dev(w, dev=DEV):

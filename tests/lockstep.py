@@ -31,7 +31,8 @@ import numpy as np
 import torch
 
 from block_discrete_diffusion_tok_amd import dg
-from gpu_common import (DEV, MARGIN, TOL, TOL_ROW_FP8_ACT, fp8_act, log,
+from gpu_common import (DEV, MARGIN, TOL, TOL_ROW_FP8_ACT, cache_scales,
+                        fp8_act, log,
                         np32, rel_err, row_err,
                         routing_margin, top2_margin)
 
@@ -135,10 +136,11 @@ class Lockstep:
         qkv_o = self._full(c["qkv"], qkv_n, torch.bfloat16)
         o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
         kc, vc = self.eng.cache_view("k"), self.eng.cache_view("v")
+        ks, vs = cache_scales(self.eng, li)
         dg.op_canvas_attention(qkv_o, self.n_full, self.C, Hq, Hkv, D, kc[li],
                                vc[li], self.eng.max_requests,
                                self.eng.max_kv_len, self.req, self.plen,
-                               self.causal, 0, o)
+                               self.causal, 0, o, ks, vs)
         self._cmp("attention", self._mine(o), c["attn"], li)
         # output projection added into the oracle's residual
         x = x_in.clone()

@@ -159,16 +159,24 @@ def test_sampler_and_ops_validation():
     assert L.dg_op_linear(f, 4, 128, f, 8, 7, f, None) == 1
     req = (ctypes.c_int32 * 1)(0)
     plen = (ctypes.c_int32 * 1)(5000)
-    assert L.dg_op_canvas_attention(f, 1, 256, 16, 8, 128, f, f, 1, 4096, req,
-                                    plen, 0, 0, f, f, 1 << 30, None) == 3
+    assert L.dg_op_canvas_attention(f, 1, 256, 16, 8, 128, f, f, None, None, 1,
+                                    4096, req, plen, 0, 0, f, f, 1 << 30,
+                                    None) == 3
     plen[0] = 10
-    assert L.dg_op_canvas_attention(f, 1, 256, 12, 8, 128, f, f, 1, 4096, req,
-                                    plen, 0, 0, f, f, 1 << 30, None) == 2
-    assert L.dg_op_canvas_attention(f, 1, 256, 16, 8, 128, f, f, 1, 4096, req,
-                                    plen, 0, 4, f, f, 16, None) == 3
+    assert L.dg_op_canvas_attention(f, 1, 256, 12, 8, 128, f, f, None, None, 1,
+                                    4096, req, plen, 0, 0, f, f, 1 << 30,
+                                    None) == 2
+    assert L.dg_op_canvas_attention(f, 1, 256, 16, 8, 128, f, f, None, None, 1,
+                                    4096, req, plen, 0, 4, f, f, 16, None) == 3
+    # an E4M3 cache needs both scale arrays
+    assert L.dg_op_canvas_attention(f, 1, 256, 16, 8, 128, f, f, f, None, 1,
+                                    4096, req, plen, 0, 0, f, f, 1 << 30,
+                                    None) == 1
     row0 = (ctypes.c_int32 * 1)(4000)
-    assert L.dg_op_kv_append(f, 1, 256, 16, 8, 128, f, f, 1, 4096, req, row0,
-                             None) == 3
+    assert L.dg_op_kv_append(f, 1, 256, 16, 8, 128, f, f, None, None, 1, 4096,
+                             req, row0, None) == 3
+    assert L.dg_op_kv_append(f, 1, 256, 16, 8, 96, f, f, f, f, 1, 4096,
+                             req, (ctypes.c_int32 * 1)(0), None) == 2
     assert L.dg_status_string(5) == b"DG_ERR_HIP"
 
 

@@ -1048,3 +1048,55 @@ def test_w8a8_differs_from_w8a16_within_e4m3_precision():
                                     xh, mirror=True)
     err = np.max(np.abs(y8 - y16)) / np.max(np.abs(y16))
     assert 1e-4 < err < 0.1, err
+
+
+# ----------------------------------------------------------------- FP8 KV cache
+
+def test_kv_cache_values_closed_forms():
+    """Reading R14: rows of E4M3 values times a power of two come back
+    exactly; the decode of a row is bf16 of the fp32 product of code value
+    and scale (hand case: the row (1.125, 448) x 3 has max 1344, scale
+    1344 / 448 = 3, multiplier 1/3 in fp32; 3.375 x 0.33333334 = 1.1250000
+    rounds to code 1.125 and back to 3.375); and every value is recovered to
+    E4M3's precision of its row's largest magnitude."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 0x7F, (5, 64)).astype(np.uint8)
+    codes[:, 3] = 0x7E
+    x = oracle.decode_e4m3(codes) * 2.0 ** -7
+    np.testing.assert_array_equal(oracle.kv_cache_values(x), x)
+    row = np.array([[3.375, 1344.0]])
+    np.testing.assert_array_equal(oracle.kv_cache_values(row), row)
+    y = oracle.round_bf16(rng.standard_normal((64, 128)))
+    back = oracle.kv_cache_values(y)
+    amax = np.max(np.abs(y), axis=1, keepdims=True)
+    assert np.all(np.abs(back - y) <= 2.0 ** -4 * np.abs(y) + 2.0 ** -9 * amax / 448 * 2
+                  + 2.0 ** -8 * np.abs(y))
+    assert not np.array_equal(back, y)
+
+
+def test_attention_with_fp8_cache_reduces_to_bf16_cache_on_exact_rows():
+    """A step whose cached prefix rows are already E4M3 values times powers
+    of two gives the same result with the E4M3 cache as with the bf16 one;
+    general prefixes differ, within E4M3 precision."""
+    import dataclasses
+    sh, osh, w = _tiny_model(l_count=1)
+    rng = np.random.default_rng(8)
+    tokens = RNG.integers(0, sh.vocab, (1, 12))
+    committed = np.zeros((1, 12), np.uint8)
+    kc = oracle.decode_e4m3(rng.integers(0, 0x7F, (1, sh.n_kv_heads, 6, sh.head_dim))
+                            .astype(np.uint8)) * 2.0 ** -8
+    kc[..., 0] = 448 * 2.0 ** -8
+    vc = oracle.decode_e4m3(rng.integers(0, 0x7F, kc.shape).astype(np.uint8)) * 2.0 ** -6
+    vc[..., 0] = 448 * 2.0 ** -6
+    a = oracle.denoise_step(osh, w, tokens, committed, [(kc, vc)], mirror=True,
+                            want_logits=True)
+    b = oracle.denoise_step(dataclasses.replace(osh, kv_fp8=True), w, tokens,
+                            committed, [(kc, vc)], mirror=True, want_logits=True)
+    np.testing.assert_array_equal(a["logits"], b["logits"])
+    pre = _prefix(sh, 6)
+    c = oracle.denoise_step(osh, w, tokens, committed, pre, mirror=False,
+                            want_logits=True)
+    d = oracle.denoise_step(dataclasses.replace(osh, kv_fp8=True), w, tokens,
+                            committed, pre, mirror=False, want_logits=True)
+    err = np.max(np.abs(c["logits"] - d["logits"])) / np.max(np.abs(c["logits"]))
+    assert 0 < err < 5e-2, err

@@ -6,7 +6,8 @@ import numpy as np
 import torch
 
 from block_discrete_diffusion_tok_amd import dg, synth
-from gpu_common import DEV, MARGIN, TOL, log, np32, rel_err, routing_margin
+from gpu_common import (DEV, MARGIN, TOL, cache_scales, log, np32, rel_err,
+                        routing_margin)
 
 
 class HostLayers:
@@ -98,9 +99,11 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
             qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
             dg.op_linear(xh, lw["w_qkv"], qkv, 0)
             o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
+            ks, vs = cache_scales(eng, li)
             dg.op_canvas_attention(qkv, n, T // n, Hq, Hkv, D, kc_all[li],
                                    vc_all[li], eng.max_requests,
-                                   eng.max_kv_len, req, plen, False, 0, o)
+                                   eng.max_kv_len, req, plen, False, 0, o,
+                                   ks, vs)
             e_att = rel_err(np32(o), np32(o_cap))
         dg.op_linear(o_cap, lw["w_o"], x, 2)   # the step's own kernel
         if li in layers:
@@ -159,6 +162,18 @@ def check_commit_composition(eng, shape, w, tokens, req, plen, tag, C=256):
             p = plen[b] + j * C
             k_op = qkv[rows, Hq * D:(Hq + Hkv) * D].reshape(C, Hkv, D).transpose(0, 1)
             v_op = qkv[rows, (Hq + Hkv) * D:].reshape(C, Hkv, D).transpose(0, 1)
+            if eng.kv8:
+                # an E4M3 cache: the appended codes and scales are those of
+                # the ops' K / V rows quantised, bit for bit
+                ks, vs = cache_scales(eng, li)
+                for cache, scl, rows_op in ((kc_all, ks, k_op), (vc_all, vs, v_op)):
+                    r = rows_op.reshape(-1, D).contiguous()
+                    q8 = torch.empty(r.shape, dtype=torch.uint8, device=DEV)
+                    sc = torch.empty(r.shape[0], dtype=torch.float32, device=DEV)
+                    dg.op_quantize_rows(r, q8, None, sc)
+                    assert torch.equal(cache[li, req[b], :, p:p + C].reshape(-1, D), q8)
+                    assert torch.equal(scl[req[b], :, p:p + C].reshape(-1), sc)
+                continue
             ek = rel_err(np32(kc_all[li, req[b], :, p:p + C]), np32(k_op))
             ev = rel_err(np32(vc_all[li, req[b], :, p:p + C]), np32(v_op))
             worst = max(worst, ek, ev)
@@ -167,9 +182,10 @@ def check_commit_composition(eng, shape, w, tokens, req, plen, tag, C=256):
         if li == s.n_layers - 1:
             break
         o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
+        ks, vs = cache_scales(eng, li)
         dg.op_canvas_attention(qkv, n, C, Hq, Hkv, D, kc_all[li], vc_all[li],
                                eng.max_requests, eng.max_kv_len, req, plen,
-                               True, 0, o)
+                               True, 0, o, ks, vs)
         dg.op_linear(o, lw["w_o"], x, 2)
         dg.op_rmsnorm(x, lw["ffn_norm"], s.rms_eps, xh)
         y = torch.empty((T, H), dtype=torch.float32, device=DEV)
