@@ -182,6 +182,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
   u32x4_t kr[KCH], vr[VIT][4];
   auto gload = [&](int kt) {
     const int key0 = kt * KT;
+    if (KV8 && key0 + KT <= P) {
+      // a tile of cached keys only (uniform over the workgroup): E4M3 rows,
+      // no canvas loads and no per-key branch
+      static_for<KCH>([&](auto j) {
+        const int c = min(tid + kThreads * (int)j, KITEMS - 1);
+        const int key = key0 + c / (D / 8), dc = c % (D / 8);
+        kr[j] = deq8(*(const uint2*)(k8 + (long long)key * D + dc * 8), ks8[key]);
+      });
+      static_for<VIT>([&](auto j) {
+        const int it = min(tid + kThreads * (int)j, VITEMS - 1);
+        const int q = it / (D / 8), c8 = it % (D / 8);
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          const int key = key0 + 4 * q + kq;
+          vr[j][kq] = deq8(*(const uint2*)(v8 + (long long)key * D + c8 * 8), vs8[key]);
+        }
+      });
+      return;
+    }
     static_for<KCH>([&](auto j) {
       const int c = min(tid + kThreads * (int)j, KITEMS - 1);
       const int key = c / (D / 8), dc = c % (D / 8);
