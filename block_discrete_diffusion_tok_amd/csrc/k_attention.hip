@@ -201,6 +201,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
       });
       return;
     }
+    if (!KV8 && key0 + KT <= P) {
+      // a tile of cached keys only: plain row addresses, no per-key choice
+      static_for<KCH>([&](auto j) {
+        const int c = min(tid + kThreads * (int)j, KITEMS - 1);
+        const int key = c / (D / 8), dc = c % (D / 8);
+        kr[j] = *(const u32x4_t*)(kpre + (long long)(key0 + key) * D + dc * 8);
+      });
+      static_for<VIT>([&](auto j) {
+        const int it = min(tid + kThreads * (int)j, VITEMS - 1);
+        const int q = it / (D / 8), c8 = it % (D / 8);
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          vr[j][kq] = *(const u32x4_t*)(vpre + (long long)(key0 + 4 * q + kq) * D + c8 * 8);
+      });
+      return;
+    }
     static_for<KCH>([&](auto j) {
       const int c = min(tid + kThreads * (int)j, KITEMS - 1);
       const int key = c / (D / 8), dc = c % (D / 8);
@@ -256,102 +272,111 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
     lstore(0);
   }
   __syncthreads();
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int key0 = kt * KT;
-    const int buf = (kt - kt_begin) & 1;
-    // next tile's loads (clamped: a redundant valid load on the last tile)
-    gload(min(kt + 1, kt_end - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* ks = Ks[buf];
-    const uint16_t* vq = Vq[buf];
+  // Two passes over the tiles: first those whose keys every query sees,
+  // then the rest (the last tile, or causal), which test each score.  The
+  // pass loop unrolls into two copies of the tile body, so the first copy
+  // carries no per-score test.
+  const int kt_split = min(max(klim_all / KT, kt_begin), kt_end);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool masked = pass == 1;
+    for (int kt = pass == 0 ? kt_begin : kt_split;
+         kt < (pass == 0 ? kt_split : kt_end); ++kt) {
+      const int key0 = kt * KT;
+      const int buf = (kt - kt_begin) & 1;
+      // next tile's loads (clamped: a redundant valid load on the last tile)
+      gload(min(kt + 1, kt_end - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* ks = Ks[buf];
+      const uint16_t* vq = Vq[buf];
 
-    // ---- S^T = K Q^T: lane holds its query column of each block, keys
-    // 16*t4 + 4*lg + e
-    f32x4_t sacc[QB][4];
+      // ---- S^T = K Q^T: lane holds its query column of each block, keys
+      // 16*t4 + 4*lg + e
+      f32x4_t sacc[QB][4];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+      for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const u32x4_t kf = *(const u32x4_t*)&ks[(t4 * 16 + l16) * KP + dc * 32 + lg * 8];
+        for (int dc = 0; dc < DC; ++dc) {
+          const u32x4_t kf = *(const u32x4_t*)&ks[(t4 * 16 + l16) * KP + dc * 32 + lg * 8];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = mfma_v(kf, qf[qb][dc], sacc[qb][t4]);
+          for (int qb = 0; qb < QB; ++qb) sacc[qb][t4] = mfma_v(kf, qf[qb][dc], sacc[qb][t4]);
+        }
       }
-    }
 
-    // ---- online softmax of each column (a column with no visible key so
-    // far keeps m = -inf, p = 0 and zero accumulators)
-    const bool full = key0 + KT <= klim_all;  // no key of the tile is masked
-    u32x4_t pf[QB][2];
+      // ---- online softmax of each column (a column with no visible key so
+      // far keeps m = -inf, p = 0 and zero accumulators)
+      u32x4_t pf[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mt = -INFINITY;
+      for (int qb = 0; qb < QB; ++qb) {
+        float mt = -INFINITY;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (!full) {
-            const int kk = key0 + t4 * 16 + lg * 4 + e;
-            if (kk >= klim[qb]) sacc[qb][t4][e] = -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            if (masked) {
+              const int kk = key0 + t4 * 16 + lg * 4 + e;
+              if (kk >= klim[qb]) sacc[qb][t4][e] = -INFINITY;
+            }
+            mt = fmaxf(mt, sacc[qb][t4][e]);
           }
-          mt = fmaxf(mt, sacc[qb][t4][e]);
-        }
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      mt *= sc;  // sc > 0: the max of the scaled scores
-      // raise the running max (and rescale) only when some column of the
-      // wave needs it
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kLazy) != 0) {
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float alpha =
-            m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        mt *= sc;  // sc > 0: the max of the scaled scores
+        // raise the running max (and rescale) only when some column of the
+        // wave needs it
+        if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kLazy) != 0) {
+          const float m_new = fmaxf(m_run[qb], mt);
+          const float alpha =
+              m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
-        m_run[qb] = m_new;
+          for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
+          m_run[qb] = m_new;
+        }
+        // exponents are <= kLazy; results below 2^-126 flush to 0 (negligible)
+        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        float p[4][4];
+        float ls = 0.f;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[t4][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t4][e], sc, -m_use));
+            ls += p[t4][e];
+          }
+        l_run[qb] += ls;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          pf[qb][kc] = u32x4_t{pack_bf2(p[2 * kc][0], p[2 * kc][1]),
+                               pack_bf2(p[2 * kc][2], p[2 * kc][3]),
+                               pack_bf2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
+                               pack_bf2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
       }
-      // exponents are <= kLazy; results below 2^-126 flush to 0 (negligible)
-      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-      float p[4][4];
-      float ls = 0.f;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[t4][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t4][e], sc, -m_use));
-          ls += p[t4][e];
-        }
-      l_run[qb] += ls;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        pf[qb][kc] = u32x4_t{pack_bf2(p[2 * kc][0], p[2 * kc][1]),
-                             pack_bf2(p[2 * kc][2], p[2 * kc][3]),
-                             pack_bf2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
-                             pack_bf2(p[2 * kc + 1][2], p[2 * kc + 1][3])};
-    }
 
-    // ---- O^T += V^T P^T.  k-slot 4 h + e of lane group lg is key
-    // 32 kc + 16 h + 4 lg + e (h = 0, 1), the order the S^T accumulators
-    // hold the probabilities in; the V operand reads the same keys (quads
-    // 8 kc + lg and 8 kc + 4 + lg at d)
+      // ---- O^T += V^T P^T.  k-slot 4 h + e of lane group lg is key
+      // 32 kc + 16 h + 4 lg + e (h = 0, 1), the order the S^T accumulators
+      // hold the probabilities in; the V operand reads the same keys (quads
+      // 8 kc + lg and 8 kc + 4 + lg at d)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int d = dt * 16 + l16;
-        const uint2 lo = *(const uint2*)&vq[(8 * kc + lg) * VQ + d * 4];
-        const uint2 hi = *(const uint2*)&vq[(8 * kc + 4 + lg) * VQ + d * 4];
-        const u32x4_t vf = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        for (int kc = 0; kc < 2; ++kc) {
+          const int d = dt * 16 + l16;
+          const uint2 lo = *(const uint2*)&vq[(8 * kc + lg) * VQ + d * 4];
+          const uint2 hi = *(const uint2*)&vq[(8 * kc + 4 + lg) * VQ + d * 4];
+          const u32x4_t vf = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma_v(vf, pf[qb][kc], oacc[qb][dt]);
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma_v(vf, pf[qb][kc], oacc[qb][dt]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // buffer buf ^ 1 was last read in the previous iteration, before the
+      // barrier that ended it
+      if (kt + 1 < kt_end) lstore(buf ^ 1);
+      __syncthreads();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // buffer buf ^ 1 was last read in the previous iteration, before the
-    // barrier that ended it
-    if (kt + 1 < kt_end) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- finalise: lane holds its query column, d = 16*dt + 4*lg + e
