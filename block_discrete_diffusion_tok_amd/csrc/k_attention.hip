@@ -21,10 +21,12 @@
 // Per wave: S^T = K Q^T with bf16 MFMA 16x16x32 (K tile rows as the A
 // operand, read from LDS once per tile and used for all QB query blocks),
 // so that every lane owns one query column per block and 4 keys of each
-// 16-key block: the running max / sum of the online softmax are per-lane
-// scalars.  P^T is taken straight from the S^T accumulators (bf16) as the B
-// operand of O^T = V^T P^T; V is stored in LDS as key quads ([key/4][d][4])
-// so that the matching A operand is two 8-byte reads.  Scores are scaled
+// 16-key block: the running max of the online softmax is a per-lane
+// scalar.  P^T is taken straight from the S^T accumulators (bf16) as the B
+// operand of O^T = V^T P^T; V is stored in LDS as key octets (for each d,
+// the 8 keys one lane's operand holds, adjacent) so that the matching A
+// operand is one 16-byte read.  The running sum of the probabilities comes
+// from the same product with an A operand of ones.  Scores are scaled
 // inside the exponent (exp2 of s * log2(e)/sqrt(D) - m).  The running max is
 // raised only when a tile's max exceeds it by more than 2^8 in the
 // exponential (or at the first tile): exact, since every probability and
@@ -94,7 +96,7 @@ __device__ __forceinline__ u32x4_t deq8(const uint2 q, float sc) {
 template <int D, int QB, bool KV8>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks) {
   constexpr int KP = D + 16;     // padded K row (elements)
-  constexpr int VQ = D * 4 + 8;  // padded key-quad stride (elements; 16-byte rows)
+  constexpr int VO = D * 8 + (D / 16) * 8;  // key-octet stride (elements)
   constexpr int DC = D / 32;     // 32-wide d chunks (MFMA k for S)
   constexpr int DT = D / 16;     // 16-wide d tiles (MFMA rows for O^T)
   constexpr int KITEMS = KT * (D / 8);           // K 16-byte chunks per tile
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
   constexpr int VIT = (VITEMS + kThreads - 1) / kThreads;
   constexpr int ROWS = 128 * QB;                 // query rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vq[2][(KT / 4) * VQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Vo[2][(KT / 8) * VO];
 
   AttnTile tl;
   if (!attn_tile(a, n_chunks, tl)) return;
@@ -177,8 +179,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
   };
 
   // ---- K/V tile staging: global -> registers (issued a tile ahead) ->
-  // LDS.  V goes to key quads [key/4][d][4]: an item is 4 keys x 8 d (four
-  // 16-byte loads) written as the 8 quads it forms.
+  // LDS.  V goes to key octets: octet o = 4 kc + lg holds, for each d, the
+  // 8 keys 32 kc + 16 h + 4 lg + e (h = 0, 1; e = 0..3) in the order the
+  // PV product's operand takes them, so that one 16-byte read forms it; an
+  // octet is 16-byte d entries with 16 bytes of padding after every 16 d.
+  // An item is a key quad q (keys 4q..4q+3, i.e. kc = q / 8, h = q / 4 % 2,
+  // lg = q % 4) x 8 d: four 16-byte loads, stored as 8 half entries.  Items
+  // are numbered so that the lanes of a wave that store the same d range
+  // hold quads of both halves (all 64 banks, no conflict).
+  static_assert(KT == 64, "the octet layout assumes 16 key quads");
+  auto vquad = [](int it) {
+    const int qi = it / (D / 8);
+    return ((qi & 3) << 2) | (qi >> 2);
+  };
   u32x4_t kr[KCH], vr[VIT][4];
   auto gload = [&](int kt) {
     const int key0 = kt * KT;
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
       });
       static_for<VIT>([&](auto j) {
         const int it = min(tid + kThreads * (int)j, VITEMS - 1);
-        const int q = it / (D / 8), c8 = it % (D / 8);
+        const int q = vquad(it), c8 = it % (D / 8);
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
           const int key = key0 + 4 * q + kq;
@@ -210,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
       });
       static_for<VIT>([&](auto j) {
         const int it = min(tid + kThreads * (int)j, VITEMS - 1);
-        const int q = it / (D / 8), c8 = it % (D / 8);
+        const int q = vquad(it), c8 = it % (D / 8);
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq)
           vr[j][kq] = *(const u32x4_t*)(vpre + (long long)(key0 + 4 * q + kq) * D + c8 * 8);
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
     });
     static_for<VIT>([&](auto j) {
       const int it = min(tid + kThreads * (int)j, VITEMS - 1);
-      const int q = it / (D / 8), c8 = it % (D / 8);
+      const int q = vquad(it), c8 = it % (D / 8);
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
         vr[j][kq] = kload(vpre, vcan, v8, vs8, key0 + 4 * q + kq, c8 * 8);
@@ -241,28 +254,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
     static_for<VIT>([&](auto j) {
       const int it = tid + kThreads * (int)j;
       if (VITEMS % kThreads == 0 || it < VITEMS) {
-        const int q = it / (D / 8), c8 = it % (D / 8);
-        uint16_t* dst = &Vq[buf][q * VQ + c8 * 8 * 4];
+        const int q = vquad(it), c8 = it % (D / 8);
+        uint16_t* dst = &Vo[buf][(4 * (q >> 3) + (q & 3)) * VO + 4 * ((q >> 2) & 1)];
 #pragma unroll
-        for (int dp = 0; dp < 4; ++dp) {  // d = 8 c8 + 2 dp, +1
-          const uint32_t w0 = vr[j][0][dp], w1 = vr[j][1][dp];
-          const uint32_t w2 = vr[j][2][dp], w3 = vr[j][3][dp];
-          // quad of d (low halves), then quad of d + 1 (high halves)
-          *(u32x4_t*)(dst + dp * 8) =
-              u32x4_t{(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16),
-                      (w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
+        for (int dd = 0; dd < 8; ++dd) {
+          // d = 8 c8 + dd: half dd % 2 of word dd / 2 of the quad's 4 keys
+          const int d = 8 * c8 + dd, w = dd >> 1;
+          const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+          *(uint2*)(dst + d * 8 + (d / 16) * 8) =
+              make_uint2(__builtin_amdgcn_perm(vr[j][1][w], vr[j][0][w], sel),
+                         __builtin_amdgcn_perm(vr[j][3][w], vr[j][2][w], sel));
         }
       }
     });
   };
 
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e)/sqrt(D)
-  float m_run[QB], l_run[QB];
-  f32x4_t oacc[QB][DT];
+  // m_run: running max of the scaled scores of the lane's column; lacc:
+  // the column's running sum of probabilities (as bf16, the values the PV
+  // product weights V by), every element alike, formed by the same MFMA
+  // with a V operand of ones
+  float m_run[QB];
+  f32x4_t oacc[QB][DT], lacc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    lacc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[qb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -288,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
       gload(min(kt + 1, kt_end - 1));
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t* ks = Ks[buf];
-      const uint16_t* vq = Vq[buf];
+      const uint16_t* vo = Vo[buf];
 
       // ---- S^T = K Q^T: lane holds its query column of each block, keys
       // 16*t4 + 4*lg + e
@@ -330,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
           const float m_new = fmaxf(m_run[qb], mt);
           const float alpha =
               m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_run[qb] *= alpha;
+          lacc[qb] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
           m_run[qb] = m_new;
@@ -338,15 +355,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
         // exponents are <= kLazy; results below 2^-126 flush to 0 (negligible)
         const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
         float p[4][4];
-        float ls = 0.f;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 4; ++e)
             p[t4][e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][t4][e], sc, -m_use));
-            ls += p[t4][e];
-          }
-        l_run[qb] += ls;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
           pf[qb][kc] = u32x4_t{pack_bf2(p[2 * kc][0], p[2 * kc][1]),
@@ -357,16 +370,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
 
       // ---- O^T += V^T P^T.  k-slot 4 h + e of lane group lg is key
       // 32 kc + 16 h + 4 lg + e (h = 0, 1), the order the S^T accumulators
-      // hold the probabilities in; the V operand reads the same keys (quads
-      // 8 kc + lg and 8 kc + 4 + lg at d)
+      // hold the probabilities in; the V operand is octet 4 kc + lg at d.
+      // The probability sums take a V operand of ones (bf16 1.0).
+      constexpr uint32_t kOne2 = 0x3F803F80u;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          lacc[qb] = mfma_v(u32x4_t{kOne2, kOne2, kOne2, kOne2}, pf[qb][kc], lacc[qb]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const int d = dt * 16 + l16;
-          const uint2 lo = *(const uint2*)&vq[(8 * kc + lg) * VQ + d * 4];
-          const uint2 hi = *(const uint2*)&vq[(8 * kc + 4 + lg) * VQ + d * 4];
-          const u32x4_t vf = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+          const u32x4_t vf = *(const u32x4_t*)&vo[(4 * kc + lg) * VO + d * 8 + dt * 8];
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma_v(vf, pf[qb][kc], oacc[qb][dt]);
         }
@@ -382,9 +399,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int n_chunks
   // ---- finalise: lane holds its query column, d = 16*dt + 4*lg + e
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float l = l_run[qb];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    const float l = lacc[qb][0];  // the whole column's sum in every lane
     if (!qvalid[qb]) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (a.splits == 1) {

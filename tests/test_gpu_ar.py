@@ -1,7 +1,13 @@
 """AR mode (write-up "What they did": the same weights decode left to right;
 model card "Model Overview") through dg_ar_step against the oracle's
 ar_step: next-token statistics and the K/V appended to the cache, step
-after step, both sides fed the oracle's greedy token."""
+after step, both sides fed the oracle's greedy token and the same cache
+(the oracle reads back the rows the device appended).
+
+A position whose oracle routing has a near tie in some layer (the k-th and
+(k+1)-th router logits closer than MARGIN) may be routed differently by the
+device: its statistics and the K/V of the layers after that one are
+reported, not asserted."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +38,16 @@ def _setup(shape, plens, max_kv=1024, seed=4):
     return eng, synth.to_numpy_weights(w), caches
 
 
+def _route_gaps(shape, cap):
+    """[n, L]: gap between the k-th and (k+1)-th router logits per layer."""
+    gaps = []
+    for c in cap:
+        srt = -np.sort(-np.asarray(c["router_logits"], np.float64), axis=1)
+        gaps.append(srt[:, shape.top_k - 1] - srt[:, shape.top_k]
+                    if shape.top_k < srt.shape[1] else np.full(len(srt), np.inf))
+    return np.stack(gaps, axis=1)
+
+
 def _ar_compare(shape, eng, wn, caches, req, tokens, tag):
     """One AR step on both sides; returns the oracle's greedy tokens."""
     n = len(req)
@@ -43,38 +59,51 @@ def _ar_compare(shape, eng, wn, caches, req, tokens, tag):
     eng.ar_step(req, torch.tensor(tokens, dtype=torch.int32, device=DEV),
                 ent, lse, am, logits)
     torch.cuda.synchronize()
+    cap = []
     ref = oracle.ar_step(oshape(shape), wn, np.asarray(tokens),
                          [tuple(caches[r]) for r in req], mirror=True,
-                         request=req, want_logits=True)
-    e_h = rel_err(ent.cpu().numpy(), ref["entropy"])
-    e_l = rel_err(lse.cpu().numpy(), ref["lse"])
-    e_z = rel_err(logits.cpu().numpy(), ref["logits"])
+                         request=req, want_logits=True, capture=cap)
+    gaps = _route_gaps(shape, cap)
+    tied = gaps < MARGIN                       # [n, L]
+    # first layer whose routing may differ (L when none)
+    first = np.where(tied.any(1), tied.argmax(1), shape.n_layers)
+    ok = first == shape.n_layers
+    e_h = rel_err(ent.cpu().numpy()[ok], ref["entropy"][ok])
+    e_l = rel_err(lse.cpu().numpy()[ok], ref["lse"][ok])
+    e_z = rel_err(logits.cpu().numpy()[ok], ref["logits"][ok])
     srt = np.sort(ref["logits"], axis=1)
     marg = srt[:, -1] - srt[:, -2]
     ga = am.cpu().numpy()
-    diff = ga != ref["argmax"]
+    diff = (ga != ref["argmax"]) & ok
     # K/V appended: position j of a sequence sits at its kv_len before the
-    # step plus j
-    e_kv, seen = 0.0, {}
+    # step plus j; layer l's K/V follow the routing of layers < l only
+    e_kv, seen, rows = 0.0, {}, []
     for b, r in enumerate(req):
         j = seen.get(r, 0)
         seen[r] = j + 1
         row = plen[b] + j
+        rows.append(row)
         for which, i in (("k", 0), ("v", 1)):
             got = eng.cache_view(which)[:, r, :, row, :].float().cpu().numpy()
-            e_kv = max(e_kv, rel_err(got, ref["kv"][b][i][:, :, 0]))
+            lim = first[b] + 1
+            e_kv = max(e_kv, rel_err(got[:lim], ref["kv"][b][i][:lim, :, 0]))
     log(f"  {tag}: entropy {e_h:.2e} lse {e_l:.2e} logits {e_z:.2e} K/V "
-        f"{e_kv:.2e}; argmax differs at {int(diff.sum())} of {n} (margins "
-        f"{np.sort(marg[diff]).tolist()})")
+        f"{e_kv:.2e}; argmax differs at {int(diff.sum())} of {int(ok.sum())} "
+        f"(margins {np.sort(marg[diff]).tolist()}); near-tied routing at "
+        f"positions {np.flatnonzero(~ok).tolist()} (gaps "
+        f"{[float(gaps[i].min()) for i in np.flatnonzero(~ok)]})")
     assert e_h < TOL and e_l < TOL and e_z < TOL and e_kv < TOL
     assert not (diff & (marg >= MARGIN)).any()
     for b, r in enumerate(req):
         assert eng.kv_len(r) == plen[b] + seen[r]
-    # the oracle's own caches grow by its K/V
+    # both sides continue from the device's cache: the oracle's prefix grows
+    # by the rows the device appended
     for b, r in enumerate(req):
-        for i in range(2):
-            caches[r][i] = np.concatenate([caches[r][i], ref["kv"][b][i]],
-                                          axis=2)
+        for which, i in (("k", 0), ("v", 1)):
+            got = eng.cache_view(which)[:, r, :, rows[b]:rows[b] + 1, :]
+            caches[r][i] = np.concatenate(
+                [caches[r][i], got.float().cpu().numpy().astype(np.float64)],
+                axis=2)
     return ref["argmax"]
 
 
