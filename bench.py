@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 WORKLOAD = "stack30_h2048_p4096"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 TPF_TARGET = 19.74             # tokens per forward, write-up Table 3
 
 
@@ -55,6 +56,11 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
     H, D, Hq, Hkv = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads
     E, k, F, V = s.n_experts, s.top_k, s.expert_ffn, s.vocab
     wb = 1 if s.expert_dtype == "fp8_e4m3" else 2     # expert weight bytes
+    # expert GEMM token rows: E4M3 codes plus one fp32 scale per row
+    ab = H + 4 if s.act_dtype == "fp8_e4m3" else 2 * H
+    fb = F + 4 if s.act_dtype == "fp8_e4m3" else 2 * F
+    # cached K / V rows: E4M3 codes plus one fp32 scale per row
+    kvb = D + 4 if s.kv_dtype == "fp8_e4m3" else 2 * D
     pairs = T * k
     touched = E * (1.0 - (1.0 - k / E) ** T)   # experts receiving a token
     qkvN = (Hq + 2 * Hkv) * D
@@ -63,14 +69,15 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
         return (V * H * 2 + mean_rows * H * 2 + mean_rows * 16,
                 2.0 * mean_rows * H * V)
     if kind == "moe_gate_up":
-        return (touched * 2 * F * H * wb + pairs * H * 2 + pairs * F * 2,
+        return (touched * 2 * F * H * wb + pairs * ab + pairs * F * 2,
                 2.0 * pairs * H * 2 * F)
     if kind == "moe_down":
-        return (touched * H * F * wb + pairs * F * 2 + pairs * H * 4,
+        return (touched * H * F * wb + pairs * fb + pairs * H * 4,
                 2.0 * pairs * F * H)
     if kind == "attention":
-        return (wl.batch * (P + 256) * Hkv * D * 2 * 2 + T * Hq * D * 2 * 2
-                + T * 2 * Hkv * D * 2, 4.0 * T * Hq * D * (P + 256))
+        return (wl.batch * P * Hkv * kvb * 2 + wl.batch * 256 * Hkv * D * 2 * 2
+                + T * Hq * D * 2 * 2 + T * 2 * Hkv * D * 2,
+                4.0 * T * Hq * D * (P + 256))
     if kind == "qkv_proj":
         return (qkvN * H * 2 + T * H * 2 + T * qkvN * 2, 2.0 * T * H * qkvN)
     if kind == "o_proj":
@@ -81,10 +88,18 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
     return None
 
 
-def roofline_of(kind, alg, t_avg_s):
+def mfma_peak(kind, s):
+    """Dense MFMA peak (TFLOP/s) of the type a kernel kind computes in:
+    the expert GEMMs run the fp8 MFMA when token rows are E4M3."""
+    if kind in ("moe_gate_up", "moe_down") and s.act_dtype == "fp8_e4m3":
+        return FP8_PEAK_TFLOPS
+    return BF16_PEAK_TFLOPS
+
+
+def roofline_of(kind, alg, t_avg_s, peak_tflops=BF16_PEAK_TFLOPS):
     nbytes, flops = alg
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    t_mfma = flops / (peak_tflops * 1e12)
     if t_hbm >= t_mfma:
         ach = nbytes / t_avg_s / 1e9
         return {"kernel": kind, "bound": "hbm", "achieved": round(ach, 1),
@@ -94,8 +109,8 @@ def roofline_of(kind, alg, t_avg_s):
                 "avg_launch_us": round(t_avg_s * 1e6, 2)}
     ach = flops / t_avg_s / 1e12
     return {"kernel": kind, "bound": "mfma", "achieved": round(ach, 2),
-            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+            "peak": peak_tflops, "unit": "TFLOP/s",
+            "frac": round(ach / peak_tflops, 4),
             "algorithmic_flops_per_launch": int(flops),
             "avg_launch_us": round(t_avg_s * 1e6, 2)}
 
@@ -574,7 +589,7 @@ def main():
                "avg_us": round(1000.0 * t / n, 2)}
         alg = algorithmic(name, s, wl, mean_rows, wl.prefix_len)
         if alg is not None:
-            rf = roofline_of(name, alg, t / n / 1000.0)
+            rf = roofline_of(name, alg, t / n / 1000.0, mfma_peak(name, s))
             ent["bound"] = rf["bound"]
             ent["frac"] = rf["frac"]
         kernels[name] = ent
@@ -583,7 +598,8 @@ def main():
               key=lambda k: prof[k][0])
     roofline = roofline_of(dom, algorithmic(dom, s, wl, mean_rows,
                                             wl.prefix_len),
-                           prof[dom][0] / prof[dom][1] / 1000.0)
+                           prof[dom][0] / prof[dom][1] / 1000.0,
+                           mfma_peak(dom, s))
     roofline["traffic"] = measured_traffic(args.workload, dom)
 
     tpf = None
