@@ -265,7 +265,7 @@ struct StreamArgs {
   const float* x_scale;    // SWIGLU / DOWN: X rows hold E4M3 values (as bf16);
                            //   the scale of each X row (null: none)
 };
-// Epilogues EPI_LMSTATS (up to 128 token columns per pass), EPI_SWIGLU (128)
+// Epilogues EPI_LMSTATS (up to 128 token columns per pass), EPI_SWIGLU (64)
 // and EPI_DOWN (64).  K must satisfy stream_lm_ok / stream_moe_ok.
 hipError_t launch_stream(int epi, bool w_e4m3, const StreamArgs& a, int groups,
                          hipStream_t s);

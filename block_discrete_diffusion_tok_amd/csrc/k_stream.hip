@@ -584,18 +584,19 @@ hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
 // LM head: 2 row tiles per wave (128 vocabulary rows per workgroup), up to
 // 128 token columns per pass, K chunks of 64, 3 chunks in flight (4 stages
 // of 16 KB, 4 weight register sets), 2 workgroups per CU.  Experts: 2 row
-// tiles per wave, K chunks of 64, 2 chunks in flight; gate/up one 8-wave
-// workgroup per CU with passes of 128 token columns, down 4-wave workgroups
-// (two per CU) with passes of 64.  Measured side by side in the step against
-// 4 waves, 32 token columns, 4 chunks in flight: gate/up 168 -> 144 us, down
-// 91.5 -> 88.7 us (an expert has ~16 tokens: the wider passes cost MFMAs on
-// clamped columns, and the 8 waves share one token stage over twice the
-// weight rows).  The down products have only K / 64 = 12 chunks per row
-// block: with two 4-wave workgroups per CU one fills its pipeline while the
-// other streams (89.0 -> 87.1 us against one 8-wave workgroup).
+// tiles per wave, K chunks of 64, 4-wave workgroups, two per CU, so that one
+// fills its pipeline while the other streams; gate/up with passes of 64
+// token columns and 3 chunks in flight, down with passes of 64 and 2 chunks
+// in flight (it has only K / 64 = 12 chunks per row block).  Side by side in
+// the 30-layer step at batch 1 (an expert has ~16 tokens), gate/up: one
+// 8-wave workgroup with 128-column passes and 2 chunks in flight 147 us, two
+// 4-wave workgroups with 64-column passes 142 us, with 3 chunks in flight
+// 140 us, with 32-column passes 151 us, 8 waves with 4 chunks in flight
+// 154 us.  Down: 89.0 -> 87.1 us against one 8-wave workgroup; 3 or 4 chunks
+// in flight or 32-column passes within noise.
 constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2, kLmWaves = 4;
-constexpr int kMoeRT = 2, kMoeKC = 64, kMoeOcc = 2, kMoeWaves = 8;
-constexpr int kGuNT = 8, kGuD = 2;  // gate/up
+constexpr int kMoeRT = 2, kMoeKC = 64, kMoeOcc = 2;
+constexpr int kGuNT = 4, kGuD = 3, kGuWaves = 4;  // gate/up
 constexpr int kDnNT = 4, kDnD = 2, kDnWaves = 4;  // down
 
 int stream_rows_per_wg() { return kLmWaves * kLmRT * 16; }
@@ -618,8 +619,8 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
       return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSAMPLE, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_SWIGLU:
       if (a.K % kMoeKC || a.K / kMoeKC < kGuD) return hipErrorInvalidValue;
-      return w8 ? launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, true, kMoeOcc, kMoeWaves>(a, groups, s)
-                : launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, false, kMoeOcc, kMoeWaves>(a, groups, s);
+      return w8 ? launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, true, kMoeOcc, kGuWaves>(a, groups, s)
+                : launch_s<kMoeRT, kGuNT, kMoeKC, kGuD, EPI_SWIGLU, false, kMoeOcc, kGuWaves>(a, groups, s);
     case EPI_DOWN:
       if (a.K % kMoeKC || a.K / kMoeKC < kDnD) return hipErrorInvalidValue;
       return w8 ? launch_s<kMoeRT, kDnNT, kMoeKC, kDnD, EPI_DOWN, true, kMoeOcc, kDnWaves>(a, groups, s)
