@@ -38,7 +38,7 @@ namespace {
 constexpr int kMmThreads = 512;
 constexpr int kMmBN = 256;   // weight rows per workgroup
 constexpr int kMmBM = 256;   // token rows per workgroup
-constexpr int kMmBK = 64;    // k per step
+constexpr int kMmBK = 64;    // k per step of the e4m3-weight path (32 bf16, 128 FP8)
 constexpr int kSwzM = 8;     // token tiles per block of the tile order
 
 __device__ __forceinline__ f32x4_t mfma_v(const u32x4_t a, const u32x4_t b, f32x4_t c) {
@@ -60,8 +60,10 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, DG_LDS_PTR(lds_wave_base), 16, 0, 0);
 }
 
-// s_waitcnt immediate: vmcnt(0), the other counters untouched
-constexpr int kVmWait0 = (0x7 << 4) | (0xF << 8);
+// s_waitcnt immediate: vmcnt(n), the other counters untouched
+constexpr int vm_wait_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
 
 // merge of two (max, sum e^(z-max), sum e^(z-max)(z-max), argmax) partials
 __device__ __forceinline__ void mm_stats_merge(float& m, float& s, float& t, int& am,
@@ -86,13 +88,20 @@ __device__ __forceinline__ float mm_silu(float v) { return v / (1.f + __expf(-v)
 template <int EPI, bool W8, bool A8 = false>
 __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   static_assert(!A8 || W8, "e4m3 tokens need e4m3 weights");
-  constexpr int BK = A8 ? 2 * kMmBK : kMmBK;      // k per step
+  // k per step: 32 (bf16: one 1 KB block per row tile and per token tile),
+  // 64 (e4m3 weights: one block per row tile, two per token tile), 128
+  // (e4m3 tokens: two of each)
+  constexpr int BK = A8 ? 2 * kMmBK : (W8 ? kMmBK : kMmBK / 2);
   constexpr int ESZ = W8 ? 1 : 2;
-  constexpr int WBLK = 16 * (BK * ESZ / 64);      // weight blocks per step (32 / 16 / 32)
-  constexpr int TBLK = 16 * 2;                    // token blocks per step (16 tiles x 2)
+  constexpr int WBLK = 16 * (BK * ESZ / 64);      // weight blocks per step (16 / 16 / 32)
+  constexpr int TBLK = 16 * (W8 ? 2 : 1);         // token blocks per step (16 tiles x 1 or 2)
   constexpr int WPW = WBLK / 8, TPW = TBLK / 8;   // DMA instructions per wave
-  constexpr int STAGE = (WBLK + TBLK) * 1024;     // bytes per LDS stage
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  constexpr int LOADS = WPW + TPW;
+  constexpr int STAGE = (WBLK + TBLK) * 1024;     // bytes per LDS stage (32 / 48 / 64 KB)
+  // LDS stages (128 / 144 / 128 KB): step s + NS - 1's DMA is issued when
+  // step s begins, so a stage's loads have NS - 1 steps of MFMAs to land
+  constexpr int NS = A8 ? 2 : (W8 ? 3 : 4);
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -158,7 +167,7 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   const char* tsrc[TPW];
   static_for<TPW>([&](auto j) {
     const int blk = wave * TPW + j;
-    const int tt = blk >> 1, h = blk & 1;
+    const int tt = TBLK == 16 ? blk : blk >> 1, h = TBLK == 16 ? 0 : blk & 1;
     const int row = min(row_begin + 16 * tt + l16, row_end - 1);
     const int src = a.a_map ? a.a_map[row] / a.a_map_div : row;
     if (A8) {
@@ -176,8 +185,8 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
   const int KB = a.K * ESZ / 64;   // packed blocks per row tile
   static_for<WPW>([&](auto j) {
     const int blk = wave * WPW + j;
-    const int rt = (W8 && !A8) ? blk : (blk >> 1);
-    const int kb = (W8 && !A8) ? 0 : (blk & 1);
+    const int rt = WBLK == 16 ? blk : (blk >> 1);
+    const int kb = WBLK == 16 ? 0 : (blk & 1);
     int rb;
     if (EPI == EPI_SWIGLU) {
       // 16 gate rows then the 16 matching up rows, per 32-row block
@@ -197,9 +206,9 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
     static_for<WPW>([&](auto j) {
       dma16(wsrc[j] + step * kWStep, st + (wave * WPW + j) * 1024);
     });
-    // (128 bytes of every token row per step: 64 bf16 or 128 e4m3 values)
+    // (BK values of every token row per step: 64 or 128 bytes)
     static_for<TPW>([&](auto j) {
-      dma16(tsrc[j] + (long long)step * 128, st + (WBLK + wave * TPW + j) * 1024);
+      dma16(tsrc[j] + (long long)step * (BK * (A8 ? 1 : 2)), st + (WBLK + wave * TPW + j) * 1024);
     });
   };
 
@@ -210,18 +219,25 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = a.K / BK;
-  issue(0, 0);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
   for (int ks = 0; ks < nk; ++ks) {
-    // this wave's DMA for step ks has landed; the barrier makes every
-    // wave's visible and ends every wave's reads of step ks - 1's stage
-    __builtin_amdgcn_s_waitcnt(kVmWait0);
+    // this wave's DMA for step ks has landed (its DMAs complete in issue
+    // order; those of the NS - 2 later steps may still be in flight); the
+    // barrier makes every wave's visible and ends every wave's reads of
+    // step ks - 1's stage, which step ks + NS - 1 then refills
+    if (ks + NS - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm((NS - 2) * LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < nk) issue(ks + 1, (ks + 1) & 1);
+    if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
     __builtin_amdgcn_sched_barrier(0);
-    const char* st = lds + (ks & 1) * STAGE;
+    const char* st = lds + (ks % NS) * STAGE;
     if (A8) {
       // one 128-k FP8 MFMA per tile pair: a lane's 32 bytes are k
       // 16 lg + [0, 16) (block 0) and 64 + 16 lg + [0, 16) (block 1) of
@@ -247,9 +263,10 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
       }
       continue;
     }
-    // two 32-k MFMA sub-steps
+    // 32-k MFMA sub-steps: one (bf16), two (e4m3 weights: the two halves
+    // of each widened block)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < BK / 32; ++h) {
       u32x4_t wf[8], tf[4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -260,13 +277,13 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
           widen_e4m3x16(q, lo, hi);
           wf[i] = h ? hi : lo;
         } else {
-          wf[i] = *(const u32x4_t*)(st + (rt * 2 + h) * 1024 + 16 * lane);
+          wf[i] = *(const u32x4_t*)(st + rt * 1024 + 16 * lane);
         }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tt = wt * 4 + j;
-        tf[j] = *(const u32x4_t*)(st + (WBLK + tt * 2 + h) * 1024 + 16 * lane);
+        tf[j] = *(const u32x4_t*)(st + (WBLK + tt * (TBLK / 16) + h) * 1024 + 16 * lane);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
