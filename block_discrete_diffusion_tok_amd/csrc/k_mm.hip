@@ -17,11 +17,12 @@
 //     token rows may be gathered (an expert's rows through the
 //     permutation), since each lane names its own address.
 // Every LDS read is a ds_read_b128 of 64 consecutive 16-byte pieces (no
-// bank conflicts, no padding).  K is walked in steps of 64 through two LDS
-// stages (64 KB each for bf16 weights, 48 KB for e4m3): step s + 1's DMA is
-// issued after the barrier that opens step s and lands while step s's
-// MFMAs run.  Each wave issues 64 MFMAs per step against 24 KB of LDS
-// reads (per CU ~94 B per clock at the MFMA issue rate).
+// bank conflicts, no padding).  K is walked through NS LDS stages (bf16:
+// 4 stages of 32 k, 32 KB each; e4m3 weights: 3 of 64 k, 48 KB; e4m3
+// tokens: 2 of 128 k, 64 KB): step s + NS - 1's DMA is issued after the
+// barrier that opens step s.  With bf16 weights the operand fragments of
+// step s + 1 are read from LDS while step s's MFMAs run.  Each wave issues
+// 32 MFMAs per 32 k against 12 KB of LDS reads.
 //
 // E4M3 weights: a packed e4m3 block holds 16 rows x 64 k; lane l's 16
 // bytes are k 16 (l/16) .. +15 of row l % 16, widened to bf16 in registers
@@ -222,6 +223,60 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s, s);
+  if constexpr (!W8) {
+    // bf16: step k + 1's fragments are read from LDS while step k's MFMAs
+    // run (two register sets, indexed by the step's parity; the loop takes
+    // steps in pairs so that the index is a constant).  Before the reads,
+    // this wave's DMA for step k + 1 has landed (issued NS - 2 steps
+    // earlier; those of the later steps may still be in flight) and the
+    // barrier makes every wave's visible; the stage refilled after it,
+    // step k - 1's, was read before the previous barrier.
+    u32x4_t wf[2][8], tf[2][4];
+    auto frags = [&](auto b, int k) {
+      const char* st = lds + (k % NS) * STAGE;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        wf[b][i] = *(const u32x4_t*)(st + (wn * 8 + i) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        tf[b][j] = *(const u32x4_t*)(st + (WBLK + wt * 4 + j) * 1024 + 16 * lane);
+    };
+    // step k's DMA visible to every wave, with the steps up to `last`
+    // issued: this wave's DMAs of the steps after k may stay in flight
+    static_assert(NS <= 4, "at most two later steps in flight");
+    auto sync = [&](int k, int last) {
+      const int later = min(last, nk - 1) - k;
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LOADS));
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(LOADS));
+      else
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    sync(0, NS - 2);
+    frags(std::integral_constant<int, 0>(), 0);
+    for (int ks = 0; ks < nk; ks += 2) {
+      static_for<2>([&](auto b) {
+        const int k = ks + (int)b;
+        if (k < nk) {
+          if (k + 1 < nk) {
+            __builtin_amdgcn_sched_barrier(0);
+            sync(k + 1, k + NS - 2);
+            if (k + NS - 1 < nk) issue(k + NS - 1, (k + NS - 1) % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            frags(std::integral_constant<int, 1 - decltype(b)::value>(), k + 1);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_v(wf[b][i], tf[b][j], acc[i][j]);
+        }
+      });
+    }
+  } else
   for (int ks = 0; ks < nk; ++ks) {
     // this wave's DMA for step ks has landed (its DMAs complete in issue
     // order; those of the NS - 2 later steps may still be in flight); the
