@@ -103,6 +103,9 @@ struct MoeBufs {
   uint8_t* aq8;         // [max(pairs, slots), F]
   uint16_t* aq16;       // [max(pairs, slots), F]
   float* as;            // [max(pairs, slots)]
+  // byte ranges (offset from the MoE base, length) that hold values, not
+  // indices or counts: what DG_POISON fills
+  std::vector<std::pair<size_t, size_t>> value_ranges;
 };
 // slot_tok is read up to one pass of 32 slots past an expert's last slot
 constexpr int kSlotPad = 64;
@@ -141,6 +144,9 @@ struct dg_ctx {
   float* smp_tau;         // [T] temperature of each LM-head row
   int32_t* smp_ctr;       // [T][3] Philox counter words of each LM-head row
   long long split_rows_cap;  // attention partial rows the workspace holds
+  // workspace byte ranges that hold values (activations, partials, router
+  // logits, gate weights, expert rows), not indices or counts
+  std::vector<std::pair<size_t, size_t>> value_ranges;
 };
 
 static dg_status fail(dg_ctx* c, dg_status s, const std::string& msg) {
@@ -160,6 +166,38 @@ bool debug_sync() {
     return v && v[0] == '1';
   }();
   return on;
+}
+
+// Debugging aids read once per process from the environment:
+//   DG_POISON=1  every engine call that runs layers first fills the
+//                workspace's value regions (activations, partials, router
+//                logits, expert rows; not its indices and counts) with
+//                0xFF bytes, NaN in fp32, bf16 and E4M3, so that a read of
+//                scratch no kernel of the call wrote shows up as NaN;
+//   DG_CHECK=1   dg_commit_block reads the committed flags back and refuses
+//                (DG_ERR_STATE) a canvas with an uncommitted position;
+//   DG_KV_SPLIT=s  the engine's attention uses s KV splits (1..32, at most
+//                what the workspace's partials hold) instead of its own
+//                choice.
+static bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] == '1' && v[1] == 0;
+}
+bool poison_on() {
+  static const bool on = env_flag("DG_POISON");
+  return on;
+}
+bool check_on() {
+  static const bool on = env_flag("DG_CHECK");
+  return on;
+}
+int kv_split_override() {
+  static const int s = [] {
+    const char* v = getenv("DG_KV_SPLIT");
+    const int x = v ? atoi(v) : 0;
+    return x >= 1 && x <= 32 ? x : 0;
+  }();
+  return s;
 }
 
 #define HIPCHK(ctx, expr)                                                    \
@@ -267,6 +305,8 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
   const size_t o_a16 = a8 ? cv.take((size_t)arows * d.expert_ffn * 2) : 0;
   const size_t o_as = a8 ? cv.take((size_t)arows * 4) : 0;
   if (b) {
+    b->value_ranges = {{o_rl, o_ri - o_rl}, {o_rw, o_cc - o_rw}, {o_ac, o_cn - o_ac}};
+    if (a8) b->value_ranges.push_back({o_x8, cv.off - o_x8});
     b->rlogits = (float*)(base + o_rl);
     b->ridx = (int32_t*)(base + o_ri);
     b->rw = (float*)(base + o_rw);
@@ -291,6 +331,16 @@ size_t moe_layout(const dg_model_desc& d, int T, char* base, MoeBufs* b) {
     b->slot_tok = (int32_t*)(base + o_st);
   }
   return cv.off;
+}
+
+size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c);
+
+// DG_POISON: the workspace's value regions to NaN (see env_flag above)
+static dg_status poison_workspace(dg_ctx* c) {
+  if (!poison_on()) return DG_OK;
+  for (const auto& r : c->value_ranges)
+    if (r.second) HIPCHK(c, hipMemsetAsync(c->ws + r.first, 0xFF, r.second, c->stream));
+  return DG_OK;
 }
 
 size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
@@ -329,6 +379,9 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->smp_ctr = (int32_t*)(w + o_ctr);
     c->split_rows_cap = split_rows;
     moe_layout(d, (int)T, w + o_moe, &c->moe);
+    c->value_ranges = {{o_x, o_rm - o_x}, {o_lm, o_ctr - o_lm}};
+    for (const auto& r : c->moe.value_ranges)
+      c->value_ranges.push_back({o_moe + r.first, r.second});
   }
   return cv.off;
 }
@@ -756,7 +809,8 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   int max_keys = 0;
   for (int b = 0; b < n; ++b)
     max_keys = std::max(max_keys, plen[b] + (b - vis0[b] + 1) * C);
-  aa.splits = attention_auto_splits(n, C, Hq, Hkv, max_keys);
+  aa.splits = kv_split_override() ? kv_split_override()
+                                  : attention_auto_splits(n, C, Hq, Hkv, max_keys);
   // (shorter canvases than the workspace was sized for may ask for more
   // splits than its partials hold)
   aa.splits = (int)std::max<long long>(
@@ -984,6 +1038,8 @@ dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
     // wrote and causally within itself, so the result is the causal encode
     // of the whole prompt
     int plen = 0;
+    const dg_status ps = poison_workspace(c);
+    if (ps != DG_OK) return ps;
     for (int off = 0; off < n; off += DG_CANVAS) {
       const int C = std::min(DG_CANVAS, n - off);
       KRUN(c, 0, launch_embed_norm(tokens + off, C, c->embed, d.vocab, d.hidden, c->x,
@@ -1057,6 +1113,7 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     plen[b] = c->kv_len[req[b]];
   }
   hipStream_t s = c->stream;
+  if ((st = poison_workspace(c)) != DG_OK) return st;
   KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, d.vocab, H, c->x,
                                c->layers[0].attn_norm, d.rms_eps, c->xh, s, bt->committed,
                                c->row_map, c->m_dev, c->pos_map));
@@ -1115,6 +1172,17 @@ dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
       return fail(c, DG_ERR_CAPACITY,
                   "KV cache full: kv_len + canvas_len x canvases > max_kv_len");
   }
+  if (check_on()) {
+    // DG_CHECK: every position of every canvas committed (host read-back)
+    std::vector<uint8_t> com((size_t)T);
+    HIPCHK(c, hipMemcpyAsync(com.data(), bt->committed, (size_t)T, hipMemcpyDeviceToHost,
+                             c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    for (int i = 0; i < T; ++i)
+      if (!com[i])
+        return fail(c, DG_ERR_STATE, "DG_CHECK: commit of a canvas with uncommitted positions");
+  }
+  if ((st = poison_workspace(c)) != DG_OK) return st;
   KRUN(c, 0, launch_embed_norm(bt->tokens, T, c->embed, c->d.vocab, c->d.hidden, c->x,
                                c->layers[0].attn_norm, c->d.rms_eps, c->xh, c->stream));
   for (int l = 0; l < c->d.n_layers; ++l) {
@@ -1149,6 +1217,8 @@ dg_status dg_ar_step(dg_ctx* c, int32_t n, const int32_t* req,
       return fail(c, DG_ERR_CAPACITY, "KV cache full");
   }
   hipStream_t s = c->stream;
+  const dg_status ps = poison_workspace(c);
+  if (ps != DG_OK) return ps;
   KRUN(c, 0, launch_embed_norm(tokens, n, c->embed, d.vocab, d.hidden, c->x,
                                c->layers[0].attn_norm, d.rms_eps, c->xh, s));
   for (int l = 0; l < d.n_layers; ++l) {

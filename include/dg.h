@@ -31,6 +31,19 @@
  *     call that launched the faulting kernel: every launch is then followed
  *     by a device synchronisation.  Nothing aborts, exits or throws across
  *     the ABI.
+ *   - Further debugging aids, also read once per process:
+ *     DG_POISON=1: dg_prefill_kv (token mode), dg_denoise_step,
+ *       dg_commit_block and dg_ar_step first fill the workspace's value
+ *       regions (activations, partials, router logits, expert rows; not its
+ *       indices and counts) with 0xFF bytes (NaN in fp32, bf16 and E4M3), so
+ *       a read of scratch that no kernel of the call wrote shows up as NaN
+ *       in the outputs;
+ *     DG_CHECK=1: dg_commit_block reads the committed flags back (a stream
+ *       synchronisation) and returns DG_ERR_STATE for a canvas with a
+ *       position still uncommitted;
+ *     DG_KV_SPLIT=s (1..32): the engine's attention splits every key range
+ *       into s parts (at most what the workspace's partials hold) instead of
+ *       choosing the count itself.
  *   - bf16 means IEEE bfloat16 stored as 16-bit words; e4m3 means OCP FP8
  *     E4M3 ("fn": no infinities, max 448) bytes.
  *   - Matrices are row-major [rows, cols] with cols contiguous; a weight
@@ -284,7 +297,8 @@ dg_status dg_eb_select(dg_ctx* ctx, const dg_canvas_batch* batch,
  * each layer's K/V of the 256 positions into cache rows [kv_len + 256 j,
  * kv_len + 256 (j + 1)) of the canvas's slot, j = the canvas's index among
  * its request's canvases; kv_len += 256 per canvas.
- * DG_ERR_CAPACITY if a request's kv_len + 256 x its canvases > max_kv_len. */
+ * DG_ERR_CAPACITY if a request's kv_len + 256 x its canvases > max_kv_len;
+ * with DG_CHECK=1, DG_ERR_STATE if a canvas has an uncommitted position. */
 dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
 
 /* AR mode (write-up "What they did": the same weights still decode left to
