@@ -11,6 +11,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "dg_internal.h"
 #include "dg_ops.h"
 
@@ -167,6 +169,15 @@ bool debug_sync() {
   }();
   return on;
 }
+
+// A roctx range (shown by rocprofv3 --marker-trace) for the lifetime of the
+// object: each engine call, and each layer inside one.
+struct RoctxRange {
+  explicit RoctxRange(const char* name) { roctxRangePushA(name); }
+  ~RoctxRange() { roctxRangePop(); }
+  RoctxRange(const RoctxRange&) = delete;
+  RoctxRange& operator=(const RoctxRange&) = delete;
+};
 
 // Debugging aids read once per process from the environment:
 //   DG_POISON=1  every engine call that runs layers first fills the
@@ -732,6 +743,7 @@ dg_status check_batch(dg_ctx* c, const dg_canvas_batch* bt) {
 dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
                     bool commit, const dg_capture* cap, int C = DG_CANVAS,
                     bool full = false) {
+  const RoctxRange range("dg layer");
   const dg_model_desc& d = c->d;
   const dg_layer_weights& w = c->layers[l];
   const int T = n * C, H = d.hidden, D = d.head_dim;
@@ -1024,6 +1036,7 @@ int32_t dg_kv_len(const dg_ctx* c, int32_t req) {
 
 dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
                         const int32_t* tokens, const void* k, const void* v) {
+  const RoctxRange range("dg_prefill_kv");
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   if (tokens && (k || v)) return fail(c, DG_ERR_INVALID_ARG, "give either tokens or k/v");
   if (!tokens && (!k || !v)) return fail(c, DG_ERR_INVALID_ARG, "k and v must not be NULL");
@@ -1092,6 +1105,7 @@ dg_status dg_prefill_kv(dg_ctx* c, int32_t req, int32_t n,
 
 dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
                           const dg_step_out* out) {
+  const RoctxRange range("dg_denoise_step");
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
@@ -1145,6 +1159,7 @@ dg_status dg_eb_select(dg_ctx* c, const dg_canvas_batch* bt,
                        const float* entropy, const int32_t* argmax,
                        const float* gamma, int32_t step_cap, int32_t refine,
                        int32_t* n_new, uint8_t* done) {
+  const RoctxRange range("dg_eb_select");
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
@@ -1159,6 +1174,7 @@ dg_status dg_eb_select(dg_ctx* c, const dg_canvas_batch* bt,
 }
 
 dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
+  const RoctxRange range("dg_commit_block");
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   dg_status st = check_batch(c, bt);
   if (st != DG_OK) return st;
@@ -1195,6 +1211,7 @@ dg_status dg_commit_block(dg_ctx* c, const dg_canvas_batch* bt) {
 
 dg_status dg_ar_step(dg_ctx* c, int32_t n, const int32_t* req,
                      const int32_t* tokens, const dg_step_out* out) {
+  const RoctxRange range("dg_ar_step");
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   if (!req || !tokens || !out || !out->entropy || !out->lse || !out->argmax)
     return fail(c, DG_ERR_INVALID_ARG, "NULL pointer");
