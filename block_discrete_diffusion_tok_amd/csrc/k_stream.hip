@@ -17,8 +17,8 @@
 //   * the group's token rows (an expert's fixed-capacity slots, whose token
 //     ids the top-k kernel wrote, or the rows of a dense operand) go
 //     HBM/L2 -> LDS directly (LDS-DMA loads, no registers) into a ring of
-//     D+1 chunk stages shared by the workgroup's waves (4 for the LM head,
-//     8 for the experts).  Each chunk's token DMA and weight loads are
+//     D+1 chunk stages shared by the workgroup's waves (4 waves per
+//     workgroup).  Each chunk's token DMA and weight loads are
 //     issued together D chunks ahead, so the wait for a
 //     chunk covers exactly the loads issued D chunks earlier (the load
 //     counter completes in issue order: a token load issued after younger
