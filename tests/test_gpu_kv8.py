@@ -161,3 +161,45 @@ def test_two_layer_steps_with_an_e4m3_cache():
     assert eng.kv_len(0) == 556 and eng.kv_len(1) == 333
     check_commit_composition(eng, shape, wd, tok, [0, 1], [300, 77], "kv8")
     eng.close()
+
+
+def test_thirty_layer_stack_with_an_e4m3_cache():
+    """The 30-layer stack (hidden 2048, 16/8 heads of 128, 128 experts, the
+    262144-token vocabulary) with its 4096-token prefix in an E4M3 cache: a
+    denoise step of an all-masked canvas in composition and in lockstep
+    through all 30 layers, the LM head and EB.  Checks the per-layer cache
+    and scale offsets at the model's full depth."""
+    from lockstep import Lockstep, lockstep_eb, lockstep_head
+    from workload_common import (HostPerLayer, capture_buffers,
+                                 check_composition, host_model)
+    from gpu_common import new_canvas_tensors, oshape
+    import dataclasses
+    wl = synth.WORKLOADS["stack30_h2048_p4096"]
+    shape = dataclasses.replace(wl.shape, kv_dtype="fp8_e4m3")
+    P = wl.prefix_len
+    log("30 layers, E4M3 cache, 4096-token prefix")
+    w = synth.make_weights(shape, seed=0, device=DEV)
+    eng = dg.Engine(shape, w, max_requests=1, max_kv_len=P + 256, max_canvases=1)
+    k, v = synth.make_prefix_kv(shape, P, 0, seed=0, device=DEV)
+    eng.prefill_kv(0, k.contiguous(), v.contiguous())
+    cv = synth.make_canvas(shape, 1, 256, seed=7)
+    tok, com, step = new_canvas_tensors(cv)
+    ent, lse, am, _ = step_outputs(1)
+    cap = capture_buffers(shape, 256, shape.n_layers)
+    eng.denoise_step([0], tok, com, step, ent, lse, am, None, cap)
+    torch.cuda.synchronize()
+    check_composition(eng, shape, w, tok, [0], [P], cap, "kv8-30")
+    del cap
+    cap_o = []
+    ls = Lockstep(shape, eng, w, 1, [0], [P], [0], cap_o, "kv8-30")
+    ref = oracle.denoise_step(oshape(shape), host_model(w, stop=ls),
+                              cv["tokens"].numpy(), cv["committed"].numpy(),
+                              [(HostPerLayer(k), HostPerLayer(v))],
+                              mirror=True, want_logits=True, capture=cap_o)
+    assert ls.finish() == shape.n_layers
+    ls.report()
+    lockstep_head(shape, eng, w, ref, ls.x_last, cv["committed"].numpy(), 1,
+                  [0], "kv8-30")
+    lockstep_eb(ref["entropy"], ref["argmax"], cv["committed"].numpy(),
+                cv["tokens"].numpy(), cv["step"].numpy(), wl.gamma, 64, "kv8-30")
+    eng.close()
