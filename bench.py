@@ -19,8 +19,9 @@ block decoded with the final-norm gain scaled so that EB commits ~19.74
 positions per step (the pages' tokens per forward) as a labelled variant;
 per-kernel times with their roofline fractions and the dominant kernel's
 roofline; labelled extras: AR decoding (greedy, one position per step) and
-token-mode prompt prefill on request 0; the CPU oracle timed on a bounded
-sample of the same workload.
+token-mode prompt prefill on request 0, and the same decoding with E4M3
+expert weights and token rows (W8A8, after the bf16 engine is freed); the
+CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
   python bench.py --denoise-only 3     # a few plain denoise steps, for profilers
@@ -487,6 +488,39 @@ def ar_and_prefill(b, n_tokens=64):
                                        "chunks of 256"}}
 
 
+def w8a8_variant(name, steps=2):
+    """Labelled extra: the same batch-1 decoding with E4M3 expert weights and
+    E4M3 expert token rows (per-row scales), one warm-up block and `steps`
+    consecutive timed blocks, hipEvents around each denoise step."""
+    import torch
+    from block_discrete_diffusion_tok_amd import synth
+    wl = synth.WORKLOADS[name]
+    b = Bench(wl, seed=0, max_blocks=steps)
+    b.block(blk=0)
+    torch.cuda.synchronize()
+    b.timing = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 0
+    for i in range(steps):
+        n += b.block(blk=i, kv_start=wl.prefix_len + 256 * i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    step_ms = [e[0].elapsed_time(e[1]) for e in b.timing]
+    med = percentile(step_ms, 50)
+    b.eng.close()
+    del b
+    torch.cuda.empty_cache()
+    return {"workload": name, "blocks": steps, "denoise_steps": n,
+            "canvas_tok_s": round(256.0 * n / (ms / 1000.0), 1),
+            "committed_tok_s": round(wl.uncommitted * steps / (ms / 1000.0), 1),
+            "denoise_step_ms_median": round(med, 4),
+            "note": "labelled extra: E4M3 experts and E4M3 expert token "
+                    "rows; attention, router and LM head in bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawTextHelpFormatter)
@@ -500,6 +534,8 @@ def main():
     ap.add_argument("--no-tpf-variant", action="store_true")
     ap.add_argument("--no-ar", action="store_true",
                     help="skip the AR-decoding and token-prefill extras")
+    ap.add_argument("--no-w8a8", action="store_true",
+                    help="skip the W8A8 batch-1 extra")
     ap.add_argument("--denoise-only", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -550,7 +586,8 @@ def main():
     eb_ms = [e[1].elapsed_time(e[2]) for e in b.timing]
     b.timing = None
     total_denoise = sum(steps)
-    value = 256.0 * b.n * total_denoise / (ms / 1000.0)
+    n_canvas = b.n
+    value = 256.0 * n_canvas * total_denoise / (ms / 1000.0)
     committed = (wl.uncommitted * b.n * args.steps / (ms / 1000.0)
                  if commits else None)
     med = percentile(step_ms, 50)
@@ -617,6 +654,13 @@ def main():
         log("[bench] timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(b)
 
+    if not args.no_w8a8 and args.workload == WORKLOAD:
+        log("[bench] W8A8 variant of the batch-1 stack")
+        b.eng.close()
+        del b
+        torch.cuda.empty_cache()
+        extras["w8a8"] = w8a8_variant("stack30_w8a8_h2048_p4096")
+
     out = {
         "metric": "canvas tokens/s per denoise step; committed output tok/s "
                   "at batch 1",
@@ -649,7 +693,8 @@ def main():
         "denoise_step_ms": {"median": round(med, 4), "p90": round(p90, 4),
                             "n": len(step_ms)},
         "denoise_plus_eb_ms_median": round(med_eb, 4),
-        "canvas_tok_s_median_step": round(256.0 * b.n / (med / 1000.0), 1),
+        "canvas_tok_s_median_step": round(256.0 * n_canvas / (med / 1000.0),
+                                          1),
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,

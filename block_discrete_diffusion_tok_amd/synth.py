@@ -98,6 +98,13 @@ WORKLOADS = {
                  step_cap=256,
                  notes="the 32-canvas batch with E4M3 expert activations "
                        "too (W8A8)"),
+        Workload("stack30_w8a8_h2048_p4096",
+                 ModelShape(30, **_GEMMA_LAYER, expert_dtype="fp8_e4m3",
+                            act_dtype="fp8_e4m3"),
+                 prefix_len=4096, batch=1, uncommitted=256, gamma=1.0,
+                 step_cap=64, blocks=4,
+                 notes="the batch-1 stack with E4M3 experts and E4M3 expert "
+                       "token rows (W8A8)"),
     ]
 }
 
