@@ -10,6 +10,8 @@ Value recipe (the pages publish no weights; every input is synthetic):
     stored as bfloat16 (round to nearest even of the float32 draw);
   * E4M3 expert weights: the same N(0, 0.02^2) draw quantised per output row,
     scale = max|row| / 448, code = RNE(w / scale) in OCP FP8 E4M3;
+  * E4M3 LM head (lm_dtype "fp8_e4m3"): the bf16 embedding table quantised
+    per vocabulary row the same way (the input lookup keeps the bf16 table);
   * RMSNorm gains 1 (or 1 + N(0, gain_std^2) when a test asks for it);
   * cached prefix K/V ~ N(0, 1) as bfloat16;
   * canvas tokens i.i.d. uniform over the vocabulary; a "masked" position is
@@ -40,6 +42,7 @@ class ModelShape:
     n_shared_experts: int = 0   # 0 or 1 shared expert (the last expert group)
     act_dtype: str = "bf16"     # expert GEMM token rows: "bf16" or "fp8_e4m3"
     kv_dtype: str = "bf16"      # KV cache: "bf16" or "fp8_e4m3"
+    lm_dtype: str = "bf16"      # LM head: "bf16" or "fp8_e4m3" (W8A8)
 
 
 @dataclass(frozen=True)
@@ -160,6 +163,9 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
 
     w = {"embed": normal((s.vocab, s.hidden), 0.02, seed, "embed", device, mdt),
          "final_norm": gain("final_norm"), "layers": []}
+    if s.lm_dtype != "bf16":
+        # the E4M3 LM head: per-vocabulary-row codes of the bf16 table
+        w["lm_head"], w["lm_head_scale"] = quantize_e4m3_rows(w["embed"])
     for li in range(s.n_layers):
         if layers is not None and li not in layers:
             w["layers"].append(None)
@@ -260,6 +266,9 @@ def to_numpy_weights(w):
 
     out = {"embed": cv(w["embed"]), "final_norm": cv(w["final_norm"]),
            "layers": []}
+    for k in ("lm_head", "lm_head_scale"):
+        if w.get(k) is not None:
+            out[k] = cv(w[k])
     for lw in w["layers"]:
         out["layers"].append(None if lw is None else
                              {k: cv(v) for k, v in lw.items()})

@@ -39,6 +39,7 @@ from .model import (  # noqa: F401
     moe_mixture,
     moe_layer,
     lm_head_stats,
+    lm_logits,
     lm_head_sample,
     gumbel,
     temperature,

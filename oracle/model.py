@@ -82,6 +82,13 @@ R14 FP8 KV cache (write-up Table 3 caption, FP8 serving; the cache is
     canvases in the same call (the canvas, the request's earlier canvases
     of the batch) are used as computed; they enter the cache quantised when
     committed.
+R15 FP8 LM head (the same captions: the model is served in FP8): with
+    ``lm_fp8`` the LM head reads the tied embedding as E4M3 codes with one
+    fp32 scale per vocabulary row (the row's max |value| / 448, as the
+    expert weights are stored) and takes each final-normed row as E4M3
+    codes with its row scale, quantised as in R13; the logit of vocabulary
+    id v is s_row s_v sum_k q_row[k] q_v[k].  The embedding lookup at the
+    input keeps the bf16 table.
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -118,6 +125,7 @@ class Shapes:
     n_shared_experts: int = 0   # reading R10
     act_fp8: bool = False       # reading R13
     kv_fp8: bool = False        # reading R14
+    lm_fp8: bool = False        # reading R15
 
 
 # The oracle's real type: fp64, so that every dot product, softmax sum and
@@ -318,14 +326,28 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
     return out
 
 
-def lm_head_stats(xhat, embed, want_logits=False):
+def lm_logits(xhat, embed, lm8=None):
+    """Logits of the tied LM head: z = xhat E^T.  With ``lm8`` = (codes
+    [V, H] uint8, scale [V]) the E4M3 head of reading R15: each row of
+    xhat is quantised as in R13 (codes q_row, scale s_row) and
+    z[r, v] = s_row s_v sum_k q_row[k] q_v[k]."""
+    if lm8 is None:
+        return _real(xhat) @ _real(embed).T
+    codes, scale = lm8
+    qx, sx = quantize_rows_e4m3(_real(xhat))
+    z = _real(decode_e4m3(qx)) @ _real(decode_e4m3(codes)).T
+    return z * _real(sx)[:, None] * _real(scale)[None, :]
+
+
+def lm_head_stats(xhat, embed, want_logits=False, lm8=None):
     """Vocabulary softmax statistics per row (reading R5), tied LM head.
 
-    z = xhat E^T;  lse = log sum_v exp(z_v);  p = exp(z - lse);
+    z = xhat E^T (or the E4M3 head of reading R15 with ``lm8``);
+    lse = log sum_v exp(z_v);  p = exp(z - lse);
     entropy = -sum_v p_v ln p_v (terms with p_v = 0 contribute 0), clamped
     at 0;  argmax = lowest v with the largest z_v.
     """
-    z = _real(xhat) @ _real(embed).T
+    z = lm_logits(xhat, embed, lm8)
     z_max = np.max(z, axis=1, keepdims=True)
     lse = z_max[:, 0] + np.log(np.sum(np.exp(z - z_max), axis=1))
     p = np.exp(z - lse[:, None])
@@ -358,12 +380,13 @@ def gumbel(v, pos, step, canvas, seed):
     return -np.log(-np.log(u))
 
 
-def lm_head_sample(xhat, embed, tau, ctr, seed):
+def lm_head_sample(xhat, embed, tau, ctr, seed, lm8=None):
     """Vocabulary statistics at the rows' temperatures and the sampled
     tokens (reading R11).  xhat [M, H]; tau [M]; ctr [M, 3] = (position,
-    step, canvas) of each row; seed: 64-bit key.  Returns dict with lse,
-    entropy (of softmax(z / tau)), argmax (of z) and sample per row."""
-    z = _real(xhat) @ _real(embed).T
+    step, canvas) of each row; seed: 64-bit key; ``lm8`` as in lm_logits.
+    Returns dict with lse, entropy (of softmax(z / tau)), argmax (of z) and
+    sample per row."""
+    z = lm_logits(xhat, embed, lm8)
     m_rows, v_count = z.shape
     lse = np.zeros(m_rows)
     ent = np.zeros(m_rows)
@@ -373,7 +396,7 @@ def lm_head_sample(xhat, embed, tau, ctr, seed):
     for r in range(m_rows):
         t = float(tau[r])
         if t <= 0.0:
-            st = lm_head_stats(xhat[r:r + 1], embed)
+            st = lm_head_stats(xhat[r:r + 1], embed, lm8=lm8)
             lse[r] = st["lse"][0]
             ent[r] = 0.0
             sample[r] = argmax[r]
@@ -548,6 +571,13 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
     return x
 
 
+def _lm8(sh, weights):
+    """The E4M3 LM head's (codes, scales) under reading R15, else None."""
+    if not sh.lm_fp8:
+        return None
+    return weights["lm_head"], weights["lm_head_scale"]
+
+
 def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
                  want_logits=False, capture=None, request=None, sampling=None,
                  step=None):
@@ -556,7 +586,8 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
     weights: {"embed" [V,H], "final_norm" [H], "layers": [per-layer dict with
     attn_norm, w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq D], ffn_norm, w_router [E, H],
     w_gate_up [E, 2F, H], w_down [E, H, F], optional gate_up_scale [E, 2F] and
-    down_scale [E, H] when the expert weights are E4M3 codes]}.
+    down_scale [E, H] when the expert weights are E4M3 codes]}, and with
+    ``sh.lm_fp8`` "lm_head" [V, H] E4M3 codes and "lm_head_scale" [V].
 
     Returns per-canvas arrays [B, C]: entropy, lse, argmax for the
     uncommitted positions (NaN / -1 at committed ones), plus "rows" (the
@@ -570,15 +601,17 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
                         request=request)
     rows = np.nonzero(committed.reshape(-1) == 0)[0]
     xf = _bf(rmsnorm(x[rows], weights["final_norm"], sh.rms_eps), mirror)
+    lm8 = _lm8(sh, weights)
     if sampling is None:
-        st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
+        st = lm_head_stats(xf, weights["embed"], want_logits=want_logits,
+                           lm8=lm8)
     else:   # reading R11: (tau_0, budget N, seed); step [B] of each canvas
         tau0, budget, seed = sampling
         steps = np.asarray(step, dtype=np.int64)
         canvas = rows // c_len
         tau = temperature(tau0, budget, steps[canvas])
         ctr = np.stack([rows % c_len, steps[canvas], canvas], axis=1)
-        st = lm_head_sample(xf, weights["embed"], tau, ctr, seed)
+        st = lm_head_sample(xf, weights["embed"], tau, ctr, seed, lm8=lm8)
     ent = np.full(b_count * c_len, np.nan)
     lse = np.full(b_count * c_len, np.nan)
     am = np.full(b_count * c_len, -1, dtype=np.int64)
@@ -615,7 +648,8 @@ def ar_step(sh, weights, tokens, prefix, mirror=True, request=None,
     x = _layers_forward(sh, weights, tokens, prefix, mirror, True, capture,
                         kv_out=kv, request=request, full=True)
     xf = _bf(rmsnorm(x, weights["final_norm"], sh.rms_eps), mirror)
-    st = lm_head_stats(xf, weights["embed"], want_logits=want_logits)
+    st = lm_head_stats(xf, weights["embed"], want_logits=want_logits,
+                       lm8=_lm8(sh, weights))
     out = {"entropy": st["entropy"], "lse": st["lse"], "argmax": st["argmax"],
            "final_xhat": xf}
     if want_logits:

@@ -45,14 +45,19 @@ def oshape(s):
                          s.vocab, s.rms_eps,
                          getattr(s, "n_shared_experts", 0),
                          getattr(s, "act_dtype", "bf16") == "fp8_e4m3",
-                         getattr(s, "kv_dtype", "bf16") == "fp8_e4m3")
+                         getattr(s, "kv_dtype", "bf16") == "fp8_e4m3",
+                         getattr(s, "lm_dtype", "bf16") == "fp8_e4m3")
 
 
 def to_dev(w, dev=DEV):
-    return {"embed": w["embed"].to(dev), "final_norm": w["final_norm"].to(dev),
-            "layers": [None if lw is None else
-                       {k: (v.to(dev).contiguous() if v is not None else None)
-                        for k, v in lw.items()} for lw in w["layers"]]}
+    out = {"embed": w["embed"].to(dev), "final_norm": w["final_norm"].to(dev),
+           "layers": [None if lw is None else
+                      {k: (v.to(dev).contiguous() if v is not None else None)
+                       for k, v in lw.items()} for lw in w["layers"]]}
+    for k in ("lm_head", "lm_head_scale"):
+        if w.get(k) is not None:
+            out[k] = w[k].to(dev).contiguous()
+    return out
 
 
 def np32(t):

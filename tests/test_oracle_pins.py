@@ -1050,6 +1050,75 @@ def test_w8a8_differs_from_w8a16_within_e4m3_precision():
     assert 1e-4 < err < 0.1, err
 
 
+# ----------------------------------------------------------------- FP8 LM head
+
+def _e4m3_rows(rng, rows, cols, lo, hi):
+    """Rows of E4M3 values (largest magnitude 448) times a power of two per
+    row: (codes, scales, values)."""
+    codes = rng.integers(0, 0x7F, (rows, cols)).astype(np.uint8)
+    codes |= rng.integers(0, 2, (rows, cols)).astype(np.uint8) << 7
+    codes[:, 0] = 0x7E
+    scale = (2.0 ** rng.integers(lo, hi, rows)).astype(np.float32)
+    return codes, scale, oracle.decode_e4m3(codes) * scale[:, None].astype(np.float64)
+
+
+def test_e4m3_lm_head_equals_the_plain_head_on_exact_operands():
+    """Reading R15: when the vocabulary rows and the final-normed rows are
+    already E4M3 values times a power of two, quantising the rows is exact
+    and the E4M3 head's logits, entropy, lse and argmax are those of the
+    plain product x E^T (each row and each vocabulary entry has its own
+    scale, so a dropped or swapped scale fails)."""
+    rng = np.random.default_rng(11)
+    ce, se, e = _e4m3_rows(rng, 40, 64, -14, -8)
+    _, _, x = _e4m3_rows(rng, 6, 64, -6, 0)
+    z8 = oracle.lm_logits(x, None, (ce, se))
+    z = x @ e.T
+    np.testing.assert_allclose(z8, z, rtol=1e-12, atol=0)
+    s8 = oracle.lm_head_stats(x, None, lm8=(ce, se))
+    s16 = oracle.lm_head_stats(x, e)
+    for k in ("entropy", "lse"):
+        np.testing.assert_allclose(s8[k], s16[k], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(s8["argmax"], s16["argmax"])
+
+
+def test_e4m3_lm_head_scales_act_per_vocabulary_entry_and_per_row():
+    """Doubling one vocabulary entry's scale doubles exactly that logit
+    column; doubling a final-normed row (a power-of-two change, which keeps
+    its codes) doubles exactly that logit row."""
+    rng = np.random.default_rng(12)
+    ce, se, _ = _e4m3_rows(rng, 33, 128, -12, -9)
+    x = oracle.round_bf16(rng.standard_normal((7, 128)))
+    z = oracle.lm_logits(x, None, (ce, se))
+    se2 = se.copy()
+    se2[5] *= 2
+    z2 = oracle.lm_logits(x, None, (ce, se2))
+    np.testing.assert_array_equal(z2[:, 5], 2 * z[:, 5])
+    np.testing.assert_array_equal(np.delete(z2, 5, axis=1), np.delete(z, 5, axis=1))
+    x2 = x.copy()
+    x2[3] *= 2
+    z3 = oracle.lm_logits(x2, None, (ce, se))
+    np.testing.assert_array_equal(z3[3], 2 * z[3])
+    np.testing.assert_array_equal(np.delete(z3, 3, axis=0), np.delete(z, 3, axis=0))
+
+
+def test_e4m3_lm_head_stays_within_e4m3_precision_of_the_bf16_head():
+    """On general rows and a quantised bf16 table the E4M3 head is not the
+    bf16 one (the setting is not ignored) and each logit stays within
+    E4M3's relative step of the operands' magnitudes: |z8 - z| <=
+    2^-3 sum_k |x_k| |E_vk| (both operands rounded to 2^-4 relative)."""
+    import torch
+    from block_discrete_diffusion_tok_amd import synth
+    rng = np.random.default_rng(13)
+    e = oracle.round_bf16(0.02 * rng.standard_normal((50, 256)))
+    codes, scale = synth.quantize_e4m3_rows(torch.from_numpy(e.astype(np.float32)))
+    x = oracle.round_bf16(rng.standard_normal((9, 256)))
+    z8 = oracle.lm_logits(x, None, (codes.numpy(), scale.numpy()))
+    z = x @ e.T
+    bound = 2.0 ** -3 * (np.abs(x) @ np.abs(e).T) + 1e-6
+    assert np.all(np.abs(z8 - z) <= bound)
+    assert np.max(np.abs(z8 - z)) > 1e-6
+
+
 # ----------------------------------------------------------------- FP8 KV cache
 
 def test_kv_cache_values_closed_forms():
