@@ -145,6 +145,14 @@ struct dg_ctx {
   float2* lm_spart;       // [T][V/128] sampled (score, id) per tile
   float* smp_tau;         // [T] temperature of each LM-head row
   int32_t* smp_ctr;       // [T][3] Philox counter words of each LM-head row
+  // E4M3 LM head (lm_dtype DG_FP8_E4M3): its weights and scales, and the
+  // LM rows as E4M3 codes (large-tile kernel), as the codes' bf16 values
+  // (streaming kernel) and their row scales
+  const void* lm8_w;
+  const float* lm8_scale;
+  uint8_t* lm_q8;
+  uint16_t* lm_q16;
+  float* lm_xs;
   long long split_rows_cap;  // attention partial rows the workspace holds
   // workspace byte ranges that hold values (activations, partials, router
   // logits, gate weights, expert rows), not indices or counts
@@ -372,6 +380,10 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
   const size_t o_sp = cv.take(T * lm_tiles(d.vocab) * 8);
   const size_t o_tau = cv.take(T * 4);
   const size_t o_ctr = cv.take(T * 12);
+  const bool lm8 = d.lm_dtype == DG_FP8_E4M3;
+  const size_t o_lq8 = lm8 ? cv.take(T * d.hidden) : 0;
+  const size_t o_lq16 = lm8 ? cv.take(T * d.hidden * 2) : 0;
+  const size_t o_lxs = lm8 ? cv.take(T * 4) : 0;
   const size_t o_moe = cv.take(moe_layout(d, (int)T, nullptr, nullptr));
   if (c) {
     char* w = c->ws;
@@ -388,9 +400,13 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->lm_spart = (float2*)(w + o_sp);
     c->smp_tau = (float*)(w + o_tau);
     c->smp_ctr = (int32_t*)(w + o_ctr);
+    c->lm_q8 = lm8 ? (uint8_t*)(w + o_lq8) : nullptr;
+    c->lm_q16 = lm8 ? (uint16_t*)(w + o_lq16) : nullptr;
+    c->lm_xs = lm8 ? (float*)(w + o_lxs) : nullptr;
     c->split_rows_cap = split_rows;
     moe_layout(d, (int)T, w + o_moe, &c->moe);
     c->value_ranges = {{o_x, o_rm - o_x}, {o_lm, o_ctr - o_lm}};
+    if (lm8) c->value_ranges.push_back({o_lq8, o_moe - o_lq8});
     for (const auto& r : c->moe.value_ranges)
       c->value_ranges.push_back({o_moe + r.first, r.second});
   }
@@ -425,6 +441,10 @@ std::string check_desc(const dg_model_desc* d) {
        d->hidden > 4096 || d->expert_ffn > 4096))
     return "E4M3 activations need E4M3 experts and hidden, expert_ffn multiples of "
            "128 up to 4096";
+  if (d->lm_dtype != DG_BF16 && d->lm_dtype != DG_FP8_E4M3)
+    return "lm_dtype must be DG_BF16 or DG_FP8_E4M3";
+  if (d->lm_dtype == DG_FP8_E4M3 && (d->hidden % 128 || d->hidden > 4096))
+    return "an E4M3 LM head needs hidden a multiple of 128 up to 4096";
   if (d->n_shared_experts < 0 || d->n_shared_experts > 1 ||
       d->n_experts + d->n_shared_experts > 256)
     return "n_shared_experts must be 0 or 1 (and n_experts + shared <= 256)";
@@ -469,22 +489,47 @@ int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi);
 // row counts it takes.
 constexpr int kLmStreamRows = 128;
 
+// The E4M3 LM head: weights [V, H] e4m3 packed with per-row scales, and
+// buffers for the rows' E4M3 codes [rows, H], their bf16 values [rows, H]
+// and row scales [rows].
+struct LmW8 {
+  const void* w;
+  const float* w_scale;
+  uint8_t* q8;
+  uint16_t* q16;
+  float* xs;
+};
+
 // smp: temperature sampling (EPI_LMSAMPLE, see LmSample) or nullptr.
+// w8: the E4M3 head (the rows are quantised first: only the live ones when
+// their count is on the device) or nullptr for the bf16 table.
 hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
                        int hidden, const void* embed, int vocab, float4* part,
                        float* logits, const int32_t* row_map, int* n_tiles,
-                       hipStream_t s, const LmSample* smp = nullptr) {
+                       hipStream_t s, const LmSample* smp = nullptr,
+                       const LmW8* w8 = nullptr) {
   *n_tiles = (vocab + 127) / 128;
   const int epi = smp ? EPI_LMSAMPLE : EPI_LMSTATS;
   const bool stream_ok = stream_lm_ok(hidden) && stream_rows_per_wg() == 128;
   const bool use_stream = stream_ok && (m_dev || rows_max <= kLmStreamRows);
   const bool use_mm = !stream_ok || rows_max > kLmStreamRows;
+  if (w8) {
+    const hipError_t e =
+        launch_quant_rows(xh, hidden, rows_max, hidden, m_dev, m_dev ? rows_max : 0,
+                          use_mm ? w8->q8 : nullptr, use_stream ? w8->q16 : nullptr,
+                          w8->xs, s);
+    if (e != hipSuccess) return e;
+  }
   if (use_stream) {
     StreamArgs a;
     memset(&a, 0, sizeof(a));
-    a.X = xh;
+    a.X = w8 ? w8->q16 : xh;
     a.ldx = hidden;
-    a.W = embed;
+    a.W = w8 ? w8->w : embed;
+    if (w8) {
+      a.w_scale = w8->w_scale;
+      a.x_scale = w8->xs;
+    }
     a.M = rows_max;
     a.M_dev = m_dev;
     a.N = vocab;
@@ -495,11 +540,16 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
     a.row_map = row_map;
     a.rows_le = use_mm ? kLmStreamRows : 0;
     if (smp) a.smp = *smp;
-    hipError_t e = launch_stream(epi, false, a, 1, s);
+    hipError_t e = launch_stream(epi, w8 != nullptr, a, 1, s);
     if (e != hipSuccess) return e;
   }
   if (!use_mm) return hipSuccess;
-  GemmArgs g = gemm_dense(xh, rows_max, hidden, embed, vocab, nullptr, 0);
+  GemmArgs g = gemm_dense(xh, rows_max, hidden, w8 ? w8->w : embed, vocab, nullptr, 0);
+  if (w8) {
+    g.A8 = w8->q8;
+    g.a_scale = w8->xs;
+    g.b_scale = w8->w_scale;
+  }
   g.M_dev = m_dev;
   g.rows_gt = use_stream ? kLmStreamRows : 0;
   g.part = part;
@@ -507,7 +557,7 @@ hipError_t run_lm_head(const uint16_t* xh, int rows_max, const int32_t* m_dev,
   g.logits = logits;
   g.row_map = row_map;
   if (smp) g.smp = *smp;
-  return launch_mm(epi, false, g, (rows_max + mm_bm() - 1) / mm_bm(), s);
+  return launch_mm(epi, w8 != nullptr, g, (rows_max + mm_bm() - 1) / mm_bm(), s);
 }
 
 // MoE FFN on xh [T, H] bf16: y mixture added into x (if x) and/or stored
@@ -932,6 +982,9 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   if (!de.empty()) return fail(nullptr, DG_ERR_SHAPE, de);
   if (!weights || !weights->embed || !weights->final_norm || !weights->layers)
     return fail(nullptr, DG_ERR_INVALID_ARG, "weights must not be NULL");
+  if (desc->lm_dtype == DG_FP8_E4M3 && (!weights->lm_head || !weights->lm_head_scale))
+    return fail(nullptr, DG_ERR_INVALID_ARG,
+                "an E4M3 LM head needs lm_head and lm_head_scale");
   for (int l = 0; l < desc->n_layers; ++l) {
     const std::string le = check_layer(*desc, weights->layers[l], false);
     if (!le.empty()) return fail(nullptr, DG_ERR_INVALID_ARG, le);
@@ -956,6 +1009,8 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   c->C = desc->canvas_len ? desc->canvas_len : DG_CANVAS;
   c->embed = (const uint16_t*)weights->embed;
   c->final_norm = weights->final_norm;
+  c->lm8_w = desc->lm_dtype == DG_FP8_E4M3 ? weights->lm_head : nullptr;
+  c->lm8_scale = desc->lm_dtype == DG_FP8_E4M3 ? weights->lm_head_scale : nullptr;
   c->layers.assign(weights->layers, weights->layers + desc->n_layers);
   c->max_requests = max_requests;
   c->max_kv_len = max_kv_len;
@@ -1146,8 +1201,10 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     ls.key1 = (uint32_t)(smp->seed >> 32);
     ls.spart = c->lm_spart;
   }
+  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->lm_q8, c->lm_q16, c->lm_xs};
   KRUN(c, 12, run_lm_head(c->xh, T, c->m_dev, H, c->embed, d.vocab, c->lm_part,
-                          out->logits, c->row_map, &n_tiles, s, smp ? &ls : nullptr));
+                          out->logits, c->row_map, &n_tiles, s, smp ? &ls : nullptr,
+                          c->lm8_w ? &lw8 : nullptr));
   KRUN(c, 13, launch_lm_merge(c->lm_part, n_tiles, c->m_dev, T, c->row_map,
                               out->entropy, out->lse, out->argmax, s,
                               smp ? c->smp_tau : nullptr, smp ? c->lm_spart : nullptr,
@@ -1243,8 +1300,10 @@ dg_status dg_ar_step(dg_ctx* c, int32_t n, const int32_t* req,
     if (st != DG_OK) return st;
   }
   int n_tiles = 0;
+  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->lm_q8, c->lm_q16, c->lm_xs};
   KRUN(c, 12, run_lm_head(c->xh, n, nullptr, d.hidden, c->embed, d.vocab, c->lm_part,
-                          out->logits, nullptr, &n_tiles, s));
+                          out->logits, nullptr, &n_tiles, s, nullptr,
+                          c->lm8_w ? &lw8 : nullptr));
   KRUN(c, 13, launch_lm_merge(c->lm_part, n_tiles, nullptr, n, nullptr, out->entropy,
                               out->lse, out->argmax, s));
   for (int b = 0; b < n; ++b) c->kv_len[req[b]] += 1;
@@ -1432,6 +1491,45 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                               vocab, (float4*)workspace, logits, nullptr,
                               &n_tiles, s));
   HIPCHK(nullptr, launch_lm_merge((const float4*)workspace, n_tiles, nullptr, m,
+                                  nullptr, entropy, lse, argmax, s));
+  return DG_OK;
+}
+
+size_t dg_op_lmhead_e4m3_workspace_bytes(int32_t m, int32_t hidden, int32_t vocab) {
+  if (m < 1 || vocab < 1 || hidden < 1) return 0;
+  return align_up((size_t)m * lm_tiles(vocab) * 16) + align_up((size_t)m * hidden) +
+         align_up((size_t)m * hidden * 2) + align_up((size_t)m * 4);
+}
+
+dg_status dg_op_lmhead_entropy_e4m3(const void* xhat, int32_t m, int32_t hidden,
+                                    const void* w8, const float* w_scale,
+                                    int32_t vocab, float* entropy, float* lse,
+                                    int32_t* argmax, float* logits,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!xhat || !w8 || !w_scale || !entropy || !lse || !argmax || !workspace)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (m < 1 || vocab < 1 || hidden < 128 || hidden % 128 || hidden > 4096)
+    return fail(nullptr, DG_ERR_SHAPE,
+                "need m >= 1, vocab >= 1, hidden a multiple of 128 up to 4096");
+  if (((uintptr_t)workspace % kAlign) != 0)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < dg_op_lmhead_e4m3_workspace_bytes(m, hidden, vocab))
+    return fail(nullptr, DG_ERR_CAPACITY, "workspace too small");
+  char* ws = (char*)workspace;
+  Carve cv;
+  const size_t o_part = cv.take((size_t)m * lm_tiles(vocab) * 16);
+  const size_t o_q8 = cv.take((size_t)m * hidden);
+  const size_t o_q16 = cv.take((size_t)m * hidden * 2);
+  const size_t o_xs = cv.take((size_t)m * 4);
+  const LmW8 lw8 = {w8, w_scale, (uint8_t*)(ws + o_q8), (uint16_t*)(ws + o_q16),
+                    (float*)(ws + o_xs)};
+  hipStream_t s = (hipStream_t)stream;
+  int n_tiles = 0;
+  HIPCHK(nullptr, run_lm_head((const uint16_t*)xhat, m, nullptr, hidden, nullptr, vocab,
+                              (float4*)(ws + o_part), logits, nullptr, &n_tiles, s,
+                              nullptr, &lw8));
+  HIPCHK(nullptr, launch_lm_merge((const float4*)(ws + o_part), n_tiles, nullptr, m,
                                   nullptr, entropy, lse, argmax, s));
   return DG_OK;
 }

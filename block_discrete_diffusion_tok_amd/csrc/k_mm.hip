@@ -356,10 +356,27 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
     // Gumbel-max token of the half (see LmSample).
     constexpr bool smp = EPI == EPI_LMSAMPLE;
     const int half = nt * 2 + wn;
+    // E4M3 head: each logit is scaled by its vocabulary row's scale and its
+    // token row's scale first (every statistic below is of the scaled z)
+    float wsc[8][4];
+    if (A8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          wsc[i][e] = a.b_scale[min(half * 128 + i * 16 + 4 * lg + e, a.N - 1)];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = row_begin + wt * 64 + j * 16 + l16;
       const int srow = min(row, row_end - 1);
+      if (A8) {
+        const float xs = a.a_scale[srow];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] *= wsc[i][e] * xs;
+      }
       float tau = 1.f;
       uint32_t c1 = 0, c2 = 0, c3 = 0;
       if (smp) {
@@ -553,8 +570,14 @@ hipError_t launch_mm(int epi, bool w8, const GemmArgs& a, int grid_m, hipStream_
                           : hipErrorInvalidValue;
       return w8 ? launch_mm_one<EPI_DOWN, true>(a, grid_m, s)
                 : launch_mm_one<EPI_DOWN, false>(a, grid_m, s);
-    case EPI_LMSTATS: return launch_mm_one<EPI_LMSTATS, false>(a, grid_m, s);
+    case EPI_LMSTATS:
+      // the E4M3 head takes E4M3 token rows (W8A8) only
+      if (w8) return a.A8 ? launch_mm_one<EPI_LMSTATS, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
+      return launch_mm_one<EPI_LMSTATS, false>(a, grid_m, s);
     case EPI_LMSAMPLE:
+      if (w8) return a.A8 && a.smp.tau ? launch_mm_one<EPI_LMSAMPLE, true, true>(a, grid_m, s)
+                                       : hipErrorInvalidValue;
       if (!a.smp.tau) return hipErrorInvalidValue;
       return launch_mm_one<EPI_LMSAMPLE, false>(a, grid_m, s);
   }

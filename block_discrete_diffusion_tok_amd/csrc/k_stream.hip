@@ -363,6 +363,25 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
       float2* red2 = (float2*)&red[WV * NT * 16];  // sampling: [WV waves][NT*16]
       static_assert(WV * NT * 16 * 24 <= S * STAGE * 2, "LDS reuse");
       constexpr bool smp = EPI == EPI_LMSAMPLE;
+      // E4M3 head (token rows given as their codes' bf16 values): each logit
+      // is scaled by its vocabulary row's scale and its token row's scale
+      // first (every statistic below is of the scaled z)
+      if (W8) {
+        float wsc[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wsc[rt][e] = a.w_scale[min(n_base + (wave * RT + rt) * 16 + 4 * lg + e, a.N - 1)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float xs = a.x_scale[min(t0 + nt * 16 + l16, t_end - 1)];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rt][nt][e] *= wsc[rt][e] * xs;
+        }
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         // temperature sampling: statistics of z / tau, Gumbel-max token
@@ -612,10 +631,20 @@ hipError_t launch_stream(int epi, bool w8, const StreamArgs& a, int groups,
                          hipStream_t s) {
   switch (epi) {
     case EPI_LMSTATS:
-      if (w8 || !stream_lm_ok(a.K)) return hipErrorInvalidValue;
+      if (!stream_lm_ok(a.K)) return hipErrorInvalidValue;
+      // the E4M3 head: E4M3 weights with per-row scales, token rows with
+      // their row scales
+      if (w8)
+        return a.w_scale && a.x_scale
+                   ? launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, true, kLmOcc, kLmWaves>(a, groups, s)
+                   : hipErrorInvalidValue;
       return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSTATS, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_LMSAMPLE:
-      if (w8 || !stream_lm_ok(a.K) || !a.smp.tau) return hipErrorInvalidValue;
+      if (!stream_lm_ok(a.K) || !a.smp.tau) return hipErrorInvalidValue;
+      if (w8)
+        return a.w_scale && a.x_scale
+                   ? launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSAMPLE, true, kLmOcc, kLmWaves>(a, groups, s)
+                   : hipErrorInvalidValue;
       return launch_s<kLmRT, 8, kLmKC, kLmD, EPI_LMSAMPLE, false, kLmOcc, kLmWaves>(a, groups, s);
     case EPI_SWIGLU:
       if (a.K % kMoeKC || a.K / kMoeKC < kGuD) return hipErrorInvalidValue;

@@ -38,7 +38,7 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("expert_dtype", ctypes.c_int32), ("canvas_len", ctypes.c_int32),
                 ("n_shared_experts", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("lm_dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -49,7 +49,8 @@ class LayerWeights(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(LayerWeights))]
+                ("layers", ctypes.POINTER(LayerWeights)),
+                ("lm_head", ctypes.c_void_p), ("lm_head_scale", ctypes.c_void_p)]
 
 
 class CanvasBatch(ctypes.Structure):
@@ -115,6 +116,9 @@ _SIGS = {
     "dg_op_lmhead_entropy": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P,
                                   ctypes.c_size_t, _P]),
     "dg_op_lmhead_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
+    "dg_op_lmhead_entropy_e4m3": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _P, _P,
+                                       _P, ctypes.c_size_t, _P]),
+    "dg_op_lmhead_e4m3_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "dg_op_lmhead_entropy_static": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P]),
     "dg_op_lmhead_sample": (_I, [_P, _I, _I, _P, _I, _P, _P, ctypes.c_uint64,
                                  _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -169,6 +173,8 @@ def model_desc(shape):
                      FP8_E4M3 if getattr(shape, "act_dtype", "bf16") == "fp8_e4m3"
                      else BF16,
                      FP8_E4M3 if getattr(shape, "kv_dtype", "bf16") == "fp8_e4m3"
+                     else BF16,
+                     FP8_E4M3 if getattr(shape, "lm_dtype", "bf16") == "fp8_e4m3"
                      else BF16)
 
 
@@ -216,6 +222,8 @@ def pack_weights(weights):
     embedding and every layer matrix packed; other entries are shared."""
     out = dict(weights)
     out["embed"] = pack(weights["embed"])
+    if weights.get("lm_head") is not None:
+        out["lm_head"] = pack(weights["lm_head"])
     out["layers"] = []
     for lw in weights["layers"]:
         if lw is None:
@@ -249,8 +257,12 @@ class Engine:
         self.desc = model_desc(shape)
         self._layers = (LayerWeights * shape.n_layers)(
             *[layer_weights(lw) for lw in weights["layers"]])
+        lm8 = weights.get("lm_head")
         self._w = Weights(weights["embed"].data_ptr(),
-                          weights["final_norm"].data_ptr(), self._layers)
+                          weights["final_norm"].data_ptr(), self._layers,
+                          lm8.data_ptr() if lm8 is not None else None,
+                          weights["lm_head_scale"].data_ptr()
+                          if lm8 is not None else None)
         kv_bytes = L.dg_kv_cache_bytes(ctypes.byref(self.desc), max_requests,
                                        max_kv_len)
         ws_bytes = L.dg_workspace_bytes(ctypes.byref(self.desc), max_canvases)
@@ -462,6 +474,22 @@ def op_lmhead_entropy(xhat, embed, entropy, lse, argmax, logits=None):
                                   _ptr(embed), embed.rows, _ptr(entropy),
                                   _ptr(lse), _ptr(argmax), _ptr(logits),
                                   _ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
+def op_lmhead_entropy_e4m3(xhat, w8, w_scale, entropy, lse, argmax,
+                           logits=None):
+    """The E4M3 head: w8 row-major [V, H] uint8 E4M3 codes (packed here) or
+    a Packed matrix, w_scale [V] fp32."""
+    L = lib()
+    w8 = pack(w8)
+    m, h = xhat.shape
+    nb = L.dg_op_lmhead_e4m3_workspace_bytes(m, h, w8.rows)
+    ws = _ws(nb, xhat.device)
+    _check(L.dg_op_lmhead_entropy_e4m3(_ptr(xhat), m, h, _ptr(w8),
+                                       _ptr(w_scale), w8.rows, _ptr(entropy),
+                                       _ptr(lse), _ptr(argmax), _ptr(logits),
+                                       _ptr(ws), ws.numel(), _stream()))
     return ws
 
 

@@ -125,6 +125,17 @@ typedef struct {
                              keys and values of the canvases in a call are
                              used as computed until they are committed.
                              See dg_kv_cache_bytes for the layout. */
+  int32_t lm_dtype;       /* dg_dtype of the LM head (the write-up serves in
+                             FP8: Table 3 and Figure 11 captions).
+                             DG_FP8_E4M3 (W8A8; hidden a multiple of 128 up
+                             to 4096): the head reads dg_weights.lm_head,
+                             E4M3 codes of the tied table with one fp32
+                             scale per vocabulary row, and takes each
+                             final-normed row as E4M3 codes with its row
+                             scale, quantised as the act_dtype rows above;
+                             logit v = s_row x lm_head_scale[v] x
+                             sum q_row q_v.  The embedding lookup keeps the
+                             bf16 table.  DG_BF16: the bf16 table. */
 } dg_model_desc;
 
 /* Packed weight layout.  Every weight matrix the kernels read (w_qkv, w_o,
@@ -168,6 +179,9 @@ typedef struct {
   const void* embed;               /* [V, H] bf16, packed; also the tied LM head */
   const float* final_norm;         /* [H] fp32 */
   const dg_layer_weights* layers;  /* (host) array of n_layers entries, copied */
+  const void* lm_head;             /* lm_dtype DG_FP8_E4M3: [V, H] e4m3, packed
+                                      (else NULL, unused) */
+  const float* lm_head_scale;      /* lm_dtype DG_FP8_E4M3: [V] fp32 per-row scale */
 } dg_weights;
 
 /* Bytes of device workspace a context needs for up to max_canvases canvases

@@ -104,6 +104,23 @@ dg_status dg_op_lmhead_entropy(const void* xhat, int32_t m, int32_t hidden,
                                size_t workspace_bytes, void* stream);
 size_t dg_op_lmhead_workspace_bytes(int32_t m, int32_t vocab);
 
+/* The E4M3 LM head (W8A8: the model's lm_dtype DG_FP8_E4M3, write-up
+ * Table 3 and Figure 11 captions, FP8 serving): as dg_op_lmhead_entropy,
+ * with the head's weights w8 [V, H] as E4M3 codes (packed,
+ * dg_pack_weights with DG_FP8_E4M3) and one fp32 scale per vocabulary row
+ * w_scale [V]; each row of xhat is quantised to E4M3 codes with its row
+ * scale as dg_op_quantize_rows does, and logit v = s_row x w_scale[v] x
+ * sum q_row q_v.  hidden a multiple of 128 up to 4096 (else DG_ERR_SHAPE);
+ * workspace of dg_op_lmhead_e4m3_workspace_bytes(m, hidden, vocab), device
+ * memory, 256-byte aligned. */
+dg_status dg_op_lmhead_entropy_e4m3(const void* xhat, int32_t m, int32_t hidden,
+                                    const void* w8, const float* w_scale,
+                                    int32_t vocab, float* entropy, float* lse,
+                                    int32_t* argmax, float* logits,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+size_t dg_op_lmhead_e4m3_workspace_bytes(int32_t m, int32_t hidden, int32_t vocab);
+
 /* Allocation-free variant of dg_op_lmhead_entropy, for callers that cannot
  * allocate device memory or pass a workspace: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation.  Same arguments and

@@ -32,6 +32,7 @@ import torch
 
 from block_discrete_diffusion_tok_amd import dg
 from gpu_common import (DEV, MARGIN, TOL, TOL_ROW_FP8_ACT, cache_scales,
+                        lm8_decision_bound,
                         fp8_act, log,
                         np32, rel_err, row_err,
                         routing_margin, top2_margin)
@@ -190,11 +191,13 @@ class Lockstep:
 
 
 def lockstep_head(shape, eng, w, ref, x_last, committed, n_full, sel, tag,
-                  seed=0):
+                  seed=0, lm8_host=None):
     """Final norm, LM head statistics and argmax on the oracle's final rows.
     x_last: oracle residual after the last layer [rows of sel canvases, H];
     ref: the oracle's denoise_step output for the sel canvases.  Returns the
-    device entropy / argmax of the oracle's rows."""
+    device entropy / argmax of the oracle's rows.  An E4M3 head (reading
+    R15) runs its own entry point; lm8_host = its row-major (codes, scales)
+    on the host, for the decision bound of its FP8 sums."""
     s = shape
     H = s.hidden
     rows_o = ref["rows"]                        # uncommitted rows, oracle order
@@ -221,7 +224,11 @@ def lockstep_head(shape, eng, w, ref, x_last, committed, n_full, sel, tag,
     ent = torch.empty(m_full, dtype=torch.float32, device=DEV)
     lse = torch.empty_like(ent)
     am = torch.empty(m_full, dtype=torch.int32, device=DEV)
-    dg.op_lmhead_entropy(xh, eng.weights["embed"], ent, lse, am)
+    if eng.weights.get("lm_head") is not None:
+        dg.op_lmhead_entropy_e4m3(xh, eng.weights["lm_head"],
+                                  eng.weights["lm_head_scale"], ent, lse, am)
+    else:
+        dg.op_lmhead_entropy(xh, eng.weights["embed"], ent, lse, am)
     g_ent = ent[idx].cpu().numpy()
     g_lse = lse[idx].cpu().numpy()
     g_am = am[idx].cpu().numpy()
@@ -242,7 +249,12 @@ def lockstep_head(shape, eng, w, ref, x_last, committed, n_full, sel, tag,
         # margins from the oracle's logits when it kept them
         assert "logits" in ref, "argmax differs and no oracle logits to judge"
         marg = top2_margin(ref["logits"], relative=False)
-        assert np.all(marg[g_am != o_am] < MARGIN), \
+        bound = np.full(len(marg), MARGIN)
+        if eng.weights.get("lm_head") is not None:
+            assert lm8_host is not None, "the E4M3 head's bound needs its codes"
+            bound = lm8_decision_bound(ref["final_xhat"], ref["logits"], *lm8_host)
+        d = g_am != o_am
+        assert np.all(marg[d] < bound[d]), \
             "argmax differs at a clear absolute margin"
     return g_ent, g_am
 

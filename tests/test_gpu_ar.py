@@ -107,7 +107,10 @@ def _ar_compare(shape, eng, wn, caches, req, tokens, tag):
     return ref["argmax"]
 
 
-@pytest.mark.parametrize("shape,name", [(TINY, "tiny"), (TWO, "two-layer")])
+@pytest.mark.parametrize("shape,name", [
+    (TINY, "tiny"), (TWO, "two-layer"),
+    (synth.ModelShape(**{**TWO.__dict__, "lm_dtype": "fp8_e4m3"}),
+     "two-layer, E4M3 head")])
 def test_ar_decode_steps_against_oracle(shape, name):
     """Two sequences (prefixes 300 and 77) decode five tokens each."""
     log(f"AR {name}")

@@ -96,7 +96,9 @@ def _compare_step(shape, eng, wn, prefix, cv, ent, lse, am, logits, cap, n,
     assert ls.finish() == shape.n_layers
     ls.report()
     lockstep_head(shape, eng, eng.weights, ref, ls.x_last,
-                  cv["committed"].numpy(), n, list(range(n)), "lockstep")
+                  cv["committed"].numpy(), n, list(range(n)), "lockstep",
+                  lm8_host=(wn["lm_head"], wn["lm_head_scale"])
+                  if wn.get("lm_head") is not None else None)
     lockstep_eb(ref["entropy"], ref["argmax"], cv["committed"].numpy(),
                 cv["tokens"].numpy(), cv["step"].numpy(), gamma, step_cap,
                 "lockstep")

@@ -45,8 +45,12 @@ class HostPerLayer:
 
 
 def host_model(w, count=None, stop=None):
-    return {"embed": np32(w["embed"]), "final_norm": np32(w["final_norm"]),
-            "layers": HostLayers(w["layers"], count, stop)}
+    out = {"embed": np32(w["embed"]), "final_norm": np32(w["final_norm"]),
+           "layers": HostLayers(w["layers"], count, stop)}
+    for k in ("lm_head", "lm_head_scale"):
+        if w.get(k) is not None:
+            out[k] = np32(w[k])
+    return out
 
 
 def capture_buffers(shape, T, L, final=True):
