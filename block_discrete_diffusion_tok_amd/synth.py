@@ -12,6 +12,8 @@ Value recipe (the pages publish no weights; every input is synthetic):
     scale = max|row| / 448, code = RNE(w / scale) in OCP FP8 E4M3;
   * E4M3 LM head (lm_dtype "fp8_e4m3"): the bf16 embedding table quantised
     per vocabulary row the same way (the input lookup keeps the bf16 table);
+  * E4M3 projections (proj_dtype "fp8_e4m3"): the bf16 Q/K/V and output
+    projection matrices quantised per output row the same way;
   * RMSNorm gains 1 (or 1 + N(0, gain_std^2) when a test asks for it);
   * cached prefix K/V ~ N(0, 1) as bfloat16;
   * canvas tokens i.i.d. uniform over the vocabulary; a "masked" position is
@@ -43,6 +45,7 @@ class ModelShape:
     act_dtype: str = "bf16"     # expert GEMM token rows: "bf16" or "fp8_e4m3"
     kv_dtype: str = "bf16"      # KV cache: "bf16" or "fp8_e4m3"
     lm_dtype: str = "bf16"      # LM head: "bf16" or "fp8_e4m3" (W8A8)
+    proj_dtype: str = "bf16"    # Q/K/V and output projections (W8A8)
 
 
 @dataclass(frozen=True)
@@ -150,8 +153,8 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
     rounding (bf16-expert shapes only); rounding them gives the default
     weights bit for bit."""
     s = shape
-    if masters and s.expert_dtype != "bf16":
-        raise ValueError("float32 masters exist for bf16-expert shapes only")
+    if masters and (s.expert_dtype != "bf16" or s.proj_dtype != "bf16"):
+        raise ValueError("float32 masters exist for bf16-weight shapes only")
     mdt = torch.float32 if masters else torch.bfloat16
     qkv_rows = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
 
@@ -201,6 +204,9 @@ def make_weights(shape: ModelShape, seed=0, device="cpu", gain_std=0.0,
             lw["w_gate_up"], lw["gate_up_scale"] = quantize_e4m3_rows(gu)
             lw["w_down"], lw["down_scale"] = quantize_e4m3_rows(dn)
             del gu, dn
+        if s.proj_dtype != "bf16":
+            for k, sk in (("w_qkv", "qkv_scale"), ("w_o", "o_scale")):
+                lw[k], lw[sk] = quantize_e4m3_rows(lw[k])
         w["layers"].append(lw)
     return w
 

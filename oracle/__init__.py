@@ -40,6 +40,8 @@ from .model import (  # noqa: F401
     moe_layer,
     lm_head_stats,
     lm_logits,
+    linear_w8a8,
+    projection,
     lm_head_sample,
     gumbel,
     temperature,

@@ -89,6 +89,15 @@ R15 FP8 LM head (the same captions: the model is served in FP8): with
     codes with its row scale, quantised as in R13; the logit of vocabulary
     id v is s_row s_v sum_k q_row[k] q_v[k].  The embedding lookup at the
     input keeps the bf16 table.
+R16 FP8 projections (the same captions): with ``proj_fp8`` the Q/K/V and
+    output projections read E4M3 weight codes with one fp32 scale per
+    output row (as the experts) and take their input rows (the attention
+    norm's rows, the attention output's rows) as E4M3 codes with one scale
+    per row, quantised as in R13: out[r, n] = s_r s_n sum_k q_r[k] q_n[k].
+    The router keeps bf16 weights and rows: its logits decide the routing,
+    and E4M3 rows would move them by whole E4M3 steps (the pages give no
+    detail; it is the plainer reading of an FP8 model whose gates keep
+    their precision).
 R8  Precision: the GPU stores GEMM operands in bfloat16 and accumulates in
     fp32.  With ``mirror=True`` the oracle rounds to bfloat16 exactly the
     activations the GPU stores as bfloat16 (norm outputs, Q/K/V, attention
@@ -126,6 +135,7 @@ class Shapes:
     act_fp8: bool = False       # reading R13
     kv_fp8: bool = False        # reading R14
     lm_fp8: bool = False        # reading R15
+    proj_fp8: bool = False      # reading R16
 
 
 # The oracle's real type: fp64, so that every dot product, softmax sum and
@@ -326,17 +336,33 @@ def moe_mixture(xhat, idx, w, w_gate_up, w_down, gate_up_scale=None,
     return out
 
 
-def lm_logits(xhat, embed, lm8=None):
-    """Logits of the tied LM head: z = xhat E^T.  With ``lm8`` = (codes
-    [V, H] uint8, scale [V]) the E4M3 head of reading R15: each row of
-    xhat is quantised as in R13 (codes q_row, scale s_row) and
-    z[r, v] = s_row s_v sum_k q_row[k] q_v[k]."""
-    if lm8 is None:
-        return _real(xhat) @ _real(embed).T
-    codes, scale = lm8
-    qx, sx = quantize_rows_e4m3(_real(xhat))
+def linear_w8a8(x, codes, scale):
+    """The product of E4M3 rows with E4M3 weight rows (readings R13, R15,
+    R16): each row of x is quantised as in R13 (codes q_r, scale s_r);
+    codes [N, K] uint8 and scale [N] are the weight rows;
+    out[r, n] = s_r scale[n] sum_k q_r[k] q_n[k]."""
+    qx, sx = quantize_rows_e4m3(_real(x))
     z = _real(decode_e4m3(qx)) @ _real(decode_e4m3(codes)).T
     return z * _real(sx)[:, None] * _real(scale)[None, :]
+
+
+def lm_logits(xhat, embed, lm8=None):
+    """Logits of the tied LM head: z = xhat E^T.  With ``lm8`` = (codes
+    [V, H] uint8, scale [V]) the E4M3 head of reading R15:
+    linear_w8a8(xhat, codes, scale)."""
+    if lm8 is None:
+        return _real(xhat) @ _real(embed).T
+    return linear_w8a8(xhat, *lm8)
+
+
+def projection(sh, x, lw, name):
+    """x W^T for the layer matrix ``name`` ("w_qkv" or "w_o"): bf16
+    weights, or under reading R16 E4M3 codes with the per-row scales
+    lw["qkv_scale"] / lw["o_scale"] and E4M3 rows of x."""
+    if sh.proj_fp8:
+        sc = lw["qkv_scale" if name == "w_qkv" else "o_scale"]
+        return linear_w8a8(x, lw[name], sc)
+    return _real(x) @ _real(lw[name]).T
 
 
 def lm_head_stats(xhat, embed, want_logits=False, lm8=None):
@@ -528,7 +554,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
     for li, lw in enumerate(weights["layers"]):
         x_in = x
         xh = _bf(rmsnorm(x, lw["attn_norm"], sh.rms_eps), mirror)
-        qkv = _bf(xh @ _real(lw["w_qkv"]).T, mirror)
+        qkv = _bf(projection(sh, xh, lw, "w_qkv"), mirror)
         q, k, v = _split_qkv(qkv, sh)
         if kv_out is not None:
             kv_out.append((k, v))
@@ -553,7 +579,7 @@ def _layers_forward(sh, weights, tokens, prefix, mirror, causal, capture,
                                   v[:, rows], causal=causal)
             o[rows] = ob.transpose(1, 0, 2).reshape(c_len, -1)
         o = _bf(o, mirror)
-        x = x + o @ _real(lw["w_o"]).T
+        x = x + projection(sh, o, lw, "w_o")
         x_mid = x
         xh_attn = xh
         xh = _bf(rmsnorm(x, lw["ffn_norm"], sh.rms_eps), mirror)
@@ -586,8 +612,10 @@ def denoise_step(sh, weights, tokens, committed, prefix, mirror=True,
     weights: {"embed" [V,H], "final_norm" [H], "layers": [per-layer dict with
     attn_norm, w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq D], ffn_norm, w_router [E, H],
     w_gate_up [E, 2F, H], w_down [E, H, F], optional gate_up_scale [E, 2F] and
-    down_scale [E, H] when the expert weights are E4M3 codes]}, and with
-    ``sh.lm_fp8`` "lm_head" [V, H] E4M3 codes and "lm_head_scale" [V].
+    down_scale [E, H] when the expert weights are E4M3 codes; with
+    ``sh.proj_fp8`` w_qkv and w_o as E4M3 codes with qkv_scale
+    [(Hq+2Hkv)D] and o_scale [H]]}, and with ``sh.lm_fp8`` "lm_head" [V, H]
+    E4M3 codes and "lm_head_scale" [V].
 
     Returns per-canvas arrays [B, C]: entropy, lse, argmax for the
     uncommitted positions (NaN / -1 at committed ones), plus "rows" (the

@@ -74,7 +74,8 @@ def oshape(s):
                          getattr(s, "n_shared_experts", 0),
                          getattr(s, "act_dtype", "bf16") == "fp8_e4m3",
                          getattr(s, "kv_dtype", "bf16") == "fp8_e4m3",
-                         getattr(s, "lm_dtype", "bf16") == "fp8_e4m3")
+                         getattr(s, "lm_dtype", "bf16") == "fp8_e4m3",
+                         getattr(s, "proj_dtype", "bf16") == "fp8_e4m3")
 
 
 def to_dev(w, dev=DEV):

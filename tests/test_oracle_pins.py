@@ -1119,6 +1119,79 @@ def test_e4m3_lm_head_stays_within_e4m3_precision_of_the_bf16_head():
     assert np.max(np.abs(z8 - z)) > 1e-6
 
 
+# ----------------------------------------------------------------- FP8 projections
+
+def _proj8_model(seed=21):
+    import dataclasses
+    from block_discrete_diffusion_tok_amd import synth
+    sh = synth.ModelShape(1, 128, 4, 2, 32, 8, 2, 64, 64,
+                          proj_dtype="fp8_e4m3")
+    w = synth.to_numpy_weights(synth.make_weights(sh, seed=seed, gain_std=0.1))
+    osh = dataclasses.replace(oracle.Shapes(
+        sh.n_layers, sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim,
+        sh.n_experts, sh.top_k, sh.expert_ffn, sh.vocab, sh.rms_eps),
+        proj_fp8=True)
+    rng = np.random.default_rng(seed)
+    tokens = rng.integers(0, sh.vocab, (1, 256))
+    prefix = [(rng.standard_normal((1, 2, 40, 32)),
+               rng.standard_normal((1, 2, 40, 32)))]
+    return osh, w, tokens, prefix
+
+
+def _first_layer(osh, w, tokens, prefix):
+    cap = []
+    oracle.model._layers_forward(osh, w, tokens, prefix, False, False, cap)
+    return cap[0]
+
+
+def test_fp8_projection_scales_are_wired_to_their_matrices():
+    """Reading R16: doubling the scale of one Q/K/V output row doubles
+    exactly that column of the layer's Q/K/V; doubling the scale of one
+    output-projection row doubles exactly that channel of the attention's
+    contribution to the residual (so each matrix is paired with its own
+    scales, by output row)."""
+    osh, w, tokens, prefix = _proj8_model()
+    base = _first_layer(osh, w, tokens, prefix)
+    lw = w["layers"][0]
+    col = 140                                   # a K row of w_qkv (Q: 0..127)
+    w2 = dict(w, layers=[dict(lw, qkv_scale=lw["qkv_scale"].copy())])
+    w2["layers"][0]["qkv_scale"][col] *= 2
+    c2 = _first_layer(osh, w2, tokens, prefix)
+    np.testing.assert_array_equal(c2["qkv"][:, col], 2 * base["qkv"][:, col])
+    np.testing.assert_array_equal(np.delete(c2["qkv"], col, 1),
+                                  np.delete(base["qkv"], col, 1))
+    ch = 9
+    w3 = dict(w, layers=[dict(lw, o_scale=lw["o_scale"].copy())])
+    w3["layers"][0]["o_scale"][ch] *= 2
+    c3 = _first_layer(osh, w3, tokens, prefix)
+    d0 = base["x_mid"] - base["x_in"]
+    d3 = c3["x_mid"] - c3["x_in"]
+    np.testing.assert_allclose(d3[:, ch], 2 * d0[:, ch], rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(np.delete(d3, ch, 1), np.delete(d0, ch, 1))
+
+
+def test_fp8_projections_stay_within_e4m3_precision_of_bf16_ones():
+    """The same layer with the E4M3 weights' values as bf16-free fp64
+    weights and bf16 activations (proj_fp8 off) differs from the W8A8 one
+    (the setting is not ignored) only by the rows' quantisation: Q/K/V
+    within E4M3's step of the operands' magnitudes (2^-4 of each row
+    value: |d| <= 2^-4 sum_k |x_k| |w_nk|)."""
+    import dataclasses
+    osh, w, tokens, prefix = _proj8_model(seed=22)
+    lw = w["layers"][0]
+    deq = dict(lw, w_qkv=oracle.decode_e4m3(lw["w_qkv"]) * lw["qkv_scale"][:, None],
+               w_o=oracle.decode_e4m3(lw["w_o"]) * lw["o_scale"][:, None])
+    c8 = _first_layer(osh, w, tokens, prefix)
+    c16 = _first_layer(dataclasses.replace(osh, proj_fp8=False),
+                       dict(w, layers=[deq]), tokens, prefix)
+    # identical inputs to the Q/K/V projection (embedding, norm)
+    np.testing.assert_array_equal(c8["xh_attn"], c16["xh_attn"])
+    d = np.abs(c8["qkv"] - c16["qkv"])
+    bound = 2.0 ** -4 * (np.abs(c8["xh_attn"]) @ np.abs(deq["w_qkv"]).T)
+    assert np.all(d <= bound + 1e-12)
+    assert np.max(d) > 0
+
+
 # ----------------------------------------------------------------- FP8 KV cache
 
 def test_kv_cache_values_closed_forms():
