@@ -145,14 +145,16 @@ struct dg_ctx {
   float2* lm_spart;       // [T][V/128] sampled (score, id) per tile
   float* smp_tau;         // [T] temperature of each LM-head row
   int32_t* smp_ctr;       // [T][3] Philox counter words of each LM-head row
-  // E4M3 LM head (lm_dtype DG_FP8_E4M3): its weights and scales, and the
-  // LM rows as E4M3 codes (large-tile kernel), as the codes' bf16 values
-  // (streaming kernel) and their row scales
+  // E4M3 LM head (lm_dtype DG_FP8_E4M3): its weights and scales
   const void* lm8_w;
   const float* lm8_scale;
-  uint8_t* lm_q8;
-  uint16_t* lm_q16;
-  float* lm_xs;
+  bool proj8;             // W8A8 Q/K/V and output projections (proj_dtype)
+  // rows quantised for an E4M3 product (the LM head's, a projection's
+  // input; one at a time on the stream): E4M3 codes (large-tile kernel),
+  // the codes' bf16 values (streaming and 64 x 64 tile kernels), scales
+  uint8_t* rq8;
+  uint16_t* rq16;
+  float* rqs;
   long long split_rows_cap;  // attention partial rows the workspace holds
   // workspace byte ranges that hold values (activations, partials, router
   // logits, gate weights, expert rows), not indices or counts
@@ -380,10 +382,11 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
   const size_t o_sp = cv.take(T * lm_tiles(d.vocab) * 8);
   const size_t o_tau = cv.take(T * 4);
   const size_t o_ctr = cv.take(T * 12);
-  const bool lm8 = d.lm_dtype == DG_FP8_E4M3;
-  const size_t o_lq8 = lm8 ? cv.take(T * d.hidden) : 0;
-  const size_t o_lq16 = lm8 ? cv.take(T * d.hidden * 2) : 0;
-  const size_t o_lxs = lm8 ? cv.take(T * 4) : 0;
+  const bool rq = d.lm_dtype == DG_FP8_E4M3 || d.proj_dtype == DG_FP8_E4M3;
+  const long long KQ = std::max(d.hidden, d.n_q_heads * d.head_dim);
+  const size_t o_lq8 = rq ? cv.take(T * KQ) : 0;
+  const size_t o_lq16 = rq ? cv.take(T * KQ * 2) : 0;
+  const size_t o_lxs = rq ? cv.take(T * 4) : 0;
   const size_t o_moe = cv.take(moe_layout(d, (int)T, nullptr, nullptr));
   if (c) {
     char* w = c->ws;
@@ -400,13 +403,13 @@ size_t ctx_layout(const dg_model_desc& d, int max_canvases, dg_ctx* c) {
     c->lm_spart = (float2*)(w + o_sp);
     c->smp_tau = (float*)(w + o_tau);
     c->smp_ctr = (int32_t*)(w + o_ctr);
-    c->lm_q8 = lm8 ? (uint8_t*)(w + o_lq8) : nullptr;
-    c->lm_q16 = lm8 ? (uint16_t*)(w + o_lq16) : nullptr;
-    c->lm_xs = lm8 ? (float*)(w + o_lxs) : nullptr;
+    c->rq8 = rq ? (uint8_t*)(w + o_lq8) : nullptr;
+    c->rq16 = rq ? (uint16_t*)(w + o_lq16) : nullptr;
+    c->rqs = rq ? (float*)(w + o_lxs) : nullptr;
     c->split_rows_cap = split_rows;
     moe_layout(d, (int)T, w + o_moe, &c->moe);
     c->value_ranges = {{o_x, o_rm - o_x}, {o_lm, o_ctr - o_lm}};
-    if (lm8) c->value_ranges.push_back({o_lq8, o_moe - o_lq8});
+    if (rq) c->value_ranges.push_back({o_lq8, o_moe - o_lq8});
     for (const auto& r : c->moe.value_ranges)
       c->value_ranges.push_back({o_moe + r.first, r.second});
   }
@@ -445,6 +448,13 @@ std::string check_desc(const dg_model_desc* d) {
     return "lm_dtype must be DG_BF16 or DG_FP8_E4M3";
   if (d->lm_dtype == DG_FP8_E4M3 && (d->hidden % 128 || d->hidden > 4096))
     return "an E4M3 LM head needs hidden a multiple of 128 up to 4096";
+  if (d->proj_dtype != DG_BF16 && d->proj_dtype != DG_FP8_E4M3)
+    return "proj_dtype must be DG_BF16 or DG_FP8_E4M3";
+  if (d->proj_dtype == DG_FP8_E4M3 &&
+      (d->hidden % 128 || d->hidden > 4096 || (d->n_q_heads * d->head_dim) % 128 ||
+       d->n_q_heads * d->head_dim > 4096))
+    return "E4M3 projections need hidden and n_q_heads*head_dim multiples of 128 up "
+           "to 4096";
   if (d->n_shared_experts < 0 || d->n_shared_experts > 1 ||
       d->n_experts + d->n_shared_experts > 256)
     return "n_shared_experts must be 0 or 1 (and n_experts + shared <= 256)";
@@ -457,6 +467,8 @@ std::string check_layer(const dg_model_desc& d, const dg_layer_weights& w,
     return "layer attention weights must not be NULL";
   if (!w.w_router || !w.w_gate_up || !w.w_down)
     return "layer MoE weights must not be NULL";
+  if (!moe_only && d.proj_dtype == DG_FP8_E4M3 && (!w.qkv_scale || !w.o_scale))
+    return "E4M3 projections need qkv_scale and o_scale";
   if (d.expert_dtype == DG_FP8_E4M3 && (!w.gate_up_scale || !w.down_scale))
     return "e4m3 experts need gate_up_scale and down_scale";
   return "";
@@ -480,6 +492,26 @@ GemmArgs gemm_dense(const uint16_t* A, int M, int K, const void* W, int N,
 
 int grid_m_dense(int M, int epi) { return (M + gemm_bm(epi) - 1) / gemm_bm(epi); }
 
+
+// A W8A8 projection (proj_dtype DG_FP8_E4M3): x's M rows [M, K] bf16 are
+// quantised per row, into E4M3 codes q8 for the large-tile kernel's FP8
+// MFMA (thousands of rows) or into the codes' bf16 values q16 for the
+// 64 x 64 tile kernel, with their scales xs; then epilogue epi of
+// out = s_row w_scale[n] sum q q.  q8 / q16: [M, K], xs: [M].
+hipError_t run_linear_e4m3(int epi, const uint16_t* x, int M, int K, const void* w8,
+                           const float* w_scale, int N, void* out, int ldc,
+                           uint8_t* q8, uint16_t* q16, float* xs, hipStream_t s) {
+  GemmArgs g = gemm_dense(x, M, K, w8, N, out, ldc);
+  const bool big = gemm_dense_on_mm(epi, g);
+  hipError_t e = launch_quant_rows(x, K, M, K, nullptr, 0, big ? q8 : nullptr,
+                                   big ? nullptr : q16, xs, s);
+  if (e != hipSuccess) return e;
+  if (big) g.A8 = q8;
+  else g.A = q16;
+  g.a_scale = xs;
+  g.b_scale = w_scale;
+  return launch_gemm(epi, true, g, grid_m_dense(M, epi), s);
+}
 
 // The LM head streams the tied embedding once per pass of up to 128 rows
 // (k_stream.hip); above 128 rows the large-tile kernel (k_mm.hip) reads it
@@ -803,8 +835,13 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
   const long long req_stride = (long long)Hkv * head_stride;
   const long long layer_stride = (long long)c->max_requests * req_stride;
   hipStream_t s = c->stream;
-  GemmArgs g = gemm_dense(c->xh, T, H, w.w_qkv, qkvN, c->qkv, qkvN);
-  KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
+  if (c->proj8) {
+    KRUN(c, 2, run_linear_e4m3(EPI_STORE_BF16, c->xh, T, H, w.w_qkv, w.qkv_scale, qkvN,
+                               c->qkv, qkvN, c->rq8, c->rq16, c->rqs, s));
+  } else {
+    GemmArgs g = gemm_dense(c->xh, T, H, w.w_qkv, qkvN, c->qkv, qkvN);
+    KRUN(c, 2, launch_gemm(EPI_STORE_BF16, false, g, grid_m_dense(T, EPI_STORE_BF16), s));
+  }
   // layer l's cache: bf16 rows, or E4M3 codes (same offsets in bytes) and
   // one scale per row
   uint16_t* kc = c->kv8 ? (uint16_t*)((char*)c->k_cache + l * layer_stride)
@@ -886,8 +923,13 @@ dg_status run_layer(dg_ctx* c, int l, int n, const int* req, const int* plen,
     HIPCHK(c, hipMemcpyAsync((char*)cap->attn_out + (size_t)l * T * Hq * D * 2,
                              c->attn, (size_t)T * Hq * D * 2,
                              hipMemcpyDeviceToDevice, s));
-  GemmArgs o = gemm_dense(c->attn, T, Hq * D, w.w_o, H, c->x, H);
-  KRUN(c, 4, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
+  if (c->proj8) {
+    KRUN(c, 4, run_linear_e4m3(EPI_ADD_F32, c->attn, T, Hq * D, w.w_o, w.o_scale, H, c->x,
+                               H, c->rq8, c->rq16, c->rqs, s));
+  } else {
+    GemmArgs o = gemm_dense(c->attn, T, Hq * D, w.w_o, H, c->x, H);
+    KRUN(c, 4, launch_gemm(EPI_ADD_F32, false, o, grid_m_dense(T, EPI_ADD_F32), s));
+  }
   const MoeBufs& mb = ctx_moe_bufs(c);
   KRUN(c, 1, launch_rmsnorm(c->x, T, H, w.ffn_norm, d.rms_eps, c->xh, nullptr,
                            nullptr, nullptr, s, mb.counts, expert_groups(d)));
@@ -1011,6 +1053,7 @@ dg_status dg_create(const dg_model_desc* desc, const dg_weights* weights,
   c->final_norm = weights->final_norm;
   c->lm8_w = desc->lm_dtype == DG_FP8_E4M3 ? weights->lm_head : nullptr;
   c->lm8_scale = desc->lm_dtype == DG_FP8_E4M3 ? weights->lm_head_scale : nullptr;
+  c->proj8 = desc->proj_dtype == DG_FP8_E4M3;
   c->layers.assign(weights->layers, weights->layers + desc->n_layers);
   c->max_requests = max_requests;
   c->max_kv_len = max_kv_len;
@@ -1201,7 +1244,7 @@ dg_status dg_denoise_step(dg_ctx* c, const dg_canvas_batch* bt,
     ls.key1 = (uint32_t)(smp->seed >> 32);
     ls.spart = c->lm_spart;
   }
-  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->lm_q8, c->lm_q16, c->lm_xs};
+  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->rq8, c->rq16, c->rqs};
   KRUN(c, 12, run_lm_head(c->xh, T, c->m_dev, H, c->embed, d.vocab, c->lm_part,
                           out->logits, c->row_map, &n_tiles, s, smp ? &ls : nullptr,
                           c->lm8_w ? &lw8 : nullptr));
@@ -1300,7 +1343,7 @@ dg_status dg_ar_step(dg_ctx* c, int32_t n, const int32_t* req,
     if (st != DG_OK) return st;
   }
   int n_tiles = 0;
-  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->lm_q8, c->lm_q16, c->lm_xs};
+  const LmW8 lw8 = {c->lm8_w, c->lm8_scale, c->rq8, c->rq16, c->rqs};
   KRUN(c, 12, run_lm_head(c->xh, n, nullptr, d.hidden, c->embed, d.vocab, c->lm_part,
                           out->logits, nullptr, &n_tiles, s, nullptr,
                           c->lm8_w ? &lw8 : nullptr));
@@ -1334,6 +1377,40 @@ dg_status dg_op_linear(const void* x, int32_t m, int32_t k, const void* w,
   else return fail(nullptr, DG_ERR_INVALID_ARG, "mode must be 0, 1 or 2");
   GemmArgs g = gemm_dense((const uint16_t*)x, m, k, w, n, out, n);
   HIPCHK(nullptr, launch_gemm(epi, false, g, grid_m_dense(m, epi), (hipStream_t)stream));
+  return DG_OK;
+}
+
+size_t dg_op_linear_e4m3_workspace_bytes(int32_t m, int32_t k) {
+  if (m < 1 || k < 1) return 0;
+  return align_up((size_t)m * k) + align_up((size_t)m * k * 2) + align_up((size_t)m * 4);
+}
+
+dg_status dg_op_linear_e4m3(const void* x, int32_t m, int32_t k, const void* w8,
+                            const float* w_scale, int32_t n, int32_t mode,
+                            void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!x || !w8 || !w_scale || !out || !workspace)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "NULL pointer");
+  if (m < 1 || n < 1 || k < 128 || k % 128 || k > 4096)
+    return fail(nullptr, DG_ERR_SHAPE,
+                "need m, n >= 1 and k a multiple of 128 up to 4096");
+  int epi;
+  if (mode == 0) epi = EPI_STORE_BF16;
+  else if (mode == 1) epi = EPI_STORE_F32;
+  else if (mode == 2) epi = EPI_ADD_F32;
+  else return fail(nullptr, DG_ERR_INVALID_ARG, "mode must be 0, 1 or 2");
+  if (((uintptr_t)workspace % kAlign) != 0)
+    return fail(nullptr, DG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < dg_op_linear_e4m3_workspace_bytes(m, k))
+    return fail(nullptr, DG_ERR_CAPACITY, "workspace too small");
+  char* ws = (char*)workspace;
+  Carve cv;
+  const size_t o_q8 = cv.take((size_t)m * k);
+  const size_t o_q16 = cv.take((size_t)m * k * 2);
+  const size_t o_xs = cv.take((size_t)m * 4);
+  HIPCHK(nullptr, run_linear_e4m3(epi, (const uint16_t*)x, m, k, w8, w_scale, n, out, n,
+                                  (uint8_t*)(ws + o_q8), (uint16_t*)(ws + o_q16),
+                                  (float*)(ws + o_xs), (hipStream_t)stream));
   return DG_OK;
 }
 

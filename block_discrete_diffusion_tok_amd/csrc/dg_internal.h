@@ -208,8 +208,11 @@ struct GemmArgs {
   int rows_gt;             // with M_dev: the launch does nothing unless
                            //   *M_dev > rows_gt (another kernel takes fewer rows)
   LmSample smp;            // EPI_LMSTATS: temperature sampling (smp.tau null: off)
-  const uint8_t* A8;       // large-tile SWIGLU / DOWN: E4M3 token rows [rows, lda]
+  const uint8_t* A8;       // large-tile kernel: E4M3 token rows [rows, lda]
   const float* a_scale;    //   bytes instead of A, and the scale of each A row
+                           //   (dense e4m3 products on the 64 x 64 tiles:
+                           //   A holds the codes' bf16 values, a_scale the
+                           //   row scales)
 };
 
 // Tile sizes of the grouped GEMMs (rows of one expert are tiled by this).
@@ -219,6 +222,9 @@ hipError_t launch_gemm(int epi, bool w_e4m3, const GemmArgs& a, int grid_m,
                        hipStream_t s);
 int gemm_bn(int epi);   // BN of the instance used for an epilogue
 int gemm_bm(int epi);   // BM of the instance used for an epilogue
+// Whether launch_gemm runs a dense product on the large-tile kernel (its
+// e4m3 form then takes E4M3 token rows, A8, on the FP8 MFMA).
+bool gemm_dense_on_mm(int epi, const GemmArgs& a);
 
 // Large-tile GEMM (k_mm.hip): 256 weight rows x 256 token rows per
 // workgroup, for thousands of token rows (dense) or hundreds per group.

@@ -314,7 +314,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) {
         const int n = nt * BN + wn * (BN / 2) + j * 16 + 4 * lg;
         if (n >= a.N) continue;
-        const f32x4_t v = acc[i][j];
+        f32x4_t v = acc[i][j];
+        if (W8 && EPI != EPI_DOWN) {
+          // dense e4m3 product: the weight rows' scales and the token
+          // row's (a_scale, when its values are E4M3 codes)
+          const float xs = a.a_scale ? a.a_scale[row] : 1.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= a.b_scale[min(n + e, a.N - 1)] * xs;
+        }
         if (EPI == EPI_DOWN) {
           // N (hidden) is a multiple of 64 on this path
           const int pair = a.c_map[row];
@@ -391,18 +398,30 @@ static bool use_mm_dense(int epi, const GemmArgs& a) {
          (epi == EPI_STORE_BF16 || epi == EPI_STORE_F32 || epi == EPI_ADD_F32);
 }
 
+bool gemm_dense_on_mm(int epi, const GemmArgs& a) { return use_mm_dense(epi, a); }
+
 hipError_t launch_gemm(int epi, bool w8, const GemmArgs& a, int grid_m,
                        hipStream_t s) {
   if (use_mm_dense(epi, a)) return launch_mm(epi, w8, a, (a.M + mm_bm() - 1) / mm_bm(), s);
   const int grid_m32 = (a.M + 31) / 32;
   switch (epi) {
+    // (dense e4m3 weights: scales from b_scale and, when given, a_scale)
     case EPI_STORE_BF16:
+      if (w8)
+        return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_BF16, true>(a, grid_m32, s)
+                                      : launch_one<64, 64, EPI_STORE_BF16, true>(a, grid_m, s);
       return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_BF16, false>(a, grid_m32, s)
                                     : launch_one<64, 64, EPI_STORE_BF16, false>(a, grid_m, s);
     case EPI_STORE_F32:
+      if (w8)
+        return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_F32, true>(a, grid_m32, s)
+                                      : launch_one<64, 64, EPI_STORE_F32, true>(a, grid_m, s);
       return small_dense(a, grid_m) ? launch_one<32, 64, EPI_STORE_F32, false>(a, grid_m32, s)
                                     : launch_one<64, 64, EPI_STORE_F32, false>(a, grid_m, s);
     case EPI_ADD_F32:
+      if (w8)
+        return small_dense(a, grid_m) ? launch_one<32, 64, EPI_ADD_F32, true>(a, grid_m32, s)
+                                      : launch_one<64, 64, EPI_ADD_F32, true>(a, grid_m, s);
       return small_dense(a, grid_m) ? launch_one<32, 64, EPI_ADD_F32, false>(a, grid_m32, s)
                                     : launch_one<64, 64, EPI_ADD_F32, false>(a, grid_m, s);
     case EPI_SWIGLU:

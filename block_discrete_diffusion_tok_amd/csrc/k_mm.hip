@@ -495,7 +495,12 @@ __global__ __launch_bounds__(kMmThreads) void mm_kernel(GemmArgs a) {
       for (int i = 0; i < 8; ++i) {
         const int n = nt * kMmBN + wn * 128 + i * 16 + 4 * lg;
         if (n >= a.N) continue;
-        const f32x4_t v = acc[i][j];
+        f32x4_t v = acc[i][j];
+        if (A8 && EPI != EPI_DOWN) {
+          // dense W8A8 product: the weight rows' scales and the token row's
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] *= a.b_scale[min(n + e, a.N - 1)] * xs;
+        }
         if (EPI == EPI_DOWN) {
           // N (hidden) is a multiple of 64 on this path
           const int pair = a.c_map[row];
@@ -557,9 +562,19 @@ int mm_bn() { return kMmBN; }
 hipError_t launch_mm(int epi, bool w8, const GemmArgs& a, int grid_m, hipStream_t s) {
   if (a.splits > 1) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_STORE_BF16: return launch_mm_one<EPI_STORE_BF16, false>(a, grid_m, s);
-    case EPI_STORE_F32: return launch_mm_one<EPI_STORE_F32, false>(a, grid_m, s);
-    case EPI_ADD_F32: return launch_mm_one<EPI_ADD_F32, false>(a, grid_m, s);
+    // (dense e4m3 weights take E4M3 token rows: W8A8 on the FP8 MFMA)
+    case EPI_STORE_BF16:
+      if (w8) return a.A8 ? launch_mm_one<EPI_STORE_BF16, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
+      return launch_mm_one<EPI_STORE_BF16, false>(a, grid_m, s);
+    case EPI_STORE_F32:
+      if (w8) return a.A8 ? launch_mm_one<EPI_STORE_F32, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
+      return launch_mm_one<EPI_STORE_F32, false>(a, grid_m, s);
+    case EPI_ADD_F32:
+      if (w8) return a.A8 ? launch_mm_one<EPI_ADD_F32, true, true>(a, grid_m, s)
+                          : hipErrorInvalidValue;
+      return launch_mm_one<EPI_ADD_F32, false>(a, grid_m, s);
     case EPI_SWIGLU:
       if (a.A8) return w8 ? launch_mm_one<EPI_SWIGLU, true, true>(a, grid_m, s)
                           : hipErrorInvalidValue;

@@ -38,13 +38,14 @@ class ModelDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("expert_dtype", ctypes.c_int32), ("canvas_len", ctypes.c_int32),
                 ("n_shared_experts", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("kv_dtype", ctypes.c_int32), ("lm_dtype", ctypes.c_int32)]
+                ("kv_dtype", ctypes.c_int32), ("lm_dtype", ctypes.c_int32),
+                ("proj_dtype", ctypes.c_int32)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "attn_norm", "w_qkv", "w_o", "ffn_norm", "w_router", "w_gate_up",
-        "w_down", "gate_up_scale", "down_scale")]
+        "w_down", "gate_up_scale", "down_scale", "qkv_scale", "o_scale")]
 
 
 class Weights(ctypes.Structure):
@@ -102,6 +103,9 @@ _SIGS = {
     "dg_kv_len": (_I, [_P, _I]),
     "dg_op_rmsnorm": (_I, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
     "dg_op_linear": (_I, [_P, _I, _I, _P, _I, _I, _P, _P]),
+    "dg_op_linear_e4m3": (_I, [_P, _I, _I, _P, _P, _I, _I, _P, _P,
+                               ctypes.c_size_t, _P]),
+    "dg_op_linear_e4m3_workspace_bytes": (ctypes.c_size_t, [_I, _I]),
     "dg_packed_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "dg_pack_weights": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "dg_op_canvas_attention": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I,
@@ -175,6 +179,8 @@ def model_desc(shape):
                      FP8_E4M3 if getattr(shape, "kv_dtype", "bf16") == "fp8_e4m3"
                      else BF16,
                      FP8_E4M3 if getattr(shape, "lm_dtype", "bf16") == "fp8_e4m3"
+                     else BF16,
+                     FP8_E4M3 if getattr(shape, "proj_dtype", "bf16") == "fp8_e4m3"
                      else BF16)
 
 
@@ -182,7 +188,8 @@ def layer_weights(lw):
     return LayerWeights(*[(lw[k].data_ptr() if lw.get(k) is not None else None)
                           for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm",
                                     "w_router", "w_gate_up", "w_down",
-                                    "gate_up_scale", "down_scale")])
+                                    "gate_up_scale", "down_scale",
+                                    "qkv_scale", "o_scale")])
 
 
 _PACKED_KEYS = ("w_qkv", "w_o", "w_router", "w_gate_up", "w_down")
@@ -422,6 +429,19 @@ def op_linear(x, w, out, mode):
     w = pack(w)
     _check(lib().dg_op_linear(_ptr(x), x.shape[0], x.shape[1], _ptr(w),
                               w.rows, mode, _ptr(out), _stream()))
+
+
+def op_linear_e4m3(x, w8, w_scale, out, mode):
+    """The W8A8 projection: w8 row-major [N, K] uint8 E4M3 codes (packed
+    here) or a Packed matrix, w_scale [N] fp32; x [M, K] bf16."""
+    L = lib()
+    w8 = pack(w8)
+    m, k = x.shape
+    ws = _ws(L.dg_op_linear_e4m3_workspace_bytes(m, k), x.device)
+    _check(L.dg_op_linear_e4m3(_ptr(x), m, k, _ptr(w8), _ptr(w_scale),
+                               w8.rows, mode, _ptr(out), _ptr(ws), ws.numel(),
+                               _stream()))
+    return ws
 
 
 def op_canvas_attention(qkv, n, canvas_len, n_q_heads, n_kv_heads, head_dim,

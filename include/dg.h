@@ -136,6 +136,17 @@ typedef struct {
                              logit v = s_row x lm_head_scale[v] x
                              sum q_row q_v.  The embedding lookup keeps the
                              bf16 table.  DG_BF16: the bf16 table. */
+  int32_t proj_dtype;     /* dg_dtype of the Q/K/V and output projections
+                             (the same FP8 serving).  DG_FP8_E4M3 (W8A8;
+                             hidden and n_q_heads*head_dim multiples of 128
+                             up to 4096): w_qkv and w_o are E4M3 codes with
+                             one fp32 scale per output row (qkv_scale,
+                             o_scale) and each input row (a token's
+                             attention-norm output, its attention output) is
+                             quantised as the act_dtype rows above; out[n] =
+                             s_row x scale[n] x sum q_row q_n, on gfx950's
+                             FP8 MFMA from 1024 rows.  The router keeps bf16
+                             weights and rows.  DG_BF16: bf16 projections. */
 } dg_model_desc;
 
 /* Packed weight layout.  Every weight matrix the kernels read (w_qkv, w_o,
@@ -164,8 +175,9 @@ dg_status dg_pack_weights(const void* src, int32_t groups, int32_t rows,
  * context).  Matrices are in the packed layout above. */
 typedef struct {
   const float* attn_norm;     /* [H] fp32 RMSNorm gain before attention */
-  const void* w_qkv;          /* [(Hq + 2 Hkv) D, H] bf16: Q rows, K rows, V rows */
-  const void* w_o;            /* [H, Hq D] bf16 */
+  const void* w_qkv;          /* [(Hq + 2 Hkv) D, H] bf16 (or e4m3, proj_dtype):
+                                 Q rows, K rows, V rows */
+  const void* w_o;            /* [H, Hq D] bf16 (or e4m3, proj_dtype) */
   const float* ffn_norm;      /* [H] fp32 RMSNorm gain before the MoE */
   const void* w_router;       /* [E, H] bf16 */
   const void* w_gate_up;      /* E + S groups of [2F, H] bf16 or e4m3: F gate rows, then
@@ -173,6 +185,9 @@ typedef struct {
   const void* w_down;         /* E + S groups of [H, F] bf16 or e4m3 */
   const float* gate_up_scale; /* [E + S, 2F] fp32 per-row scale (e4m3 only, else NULL) */
   const float* down_scale;    /* [E + S, H] fp32 per-row scale (e4m3 only, else NULL) */
+  const float* qkv_scale;     /* proj_dtype DG_FP8_E4M3: [(Hq + 2 Hkv) D] fp32 per-row
+                                 scale of w_qkv (then e4m3), else NULL */
+  const float* o_scale;       /* proj_dtype DG_FP8_E4M3: [H] fp32 per-row scale of w_o */
 } dg_layer_weights;
 
 typedef struct {

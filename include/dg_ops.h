@@ -31,6 +31,20 @@ dg_status dg_op_rmsnorm(const float* x, int32_t rows, int32_t hidden,
 dg_status dg_op_linear(const void* x, int32_t m, int32_t k, const void* w,
                        int32_t n, int32_t mode, void* out, void* stream);
 
+/* The W8A8 projection (proj_dtype DG_FP8_E4M3; write-up Table 3 and
+ * Figure 11 captions, FP8 serving): y[r, n] = s_r x w_scale[n] x
+ * sum_k q_r[k] q_n[k], with x's rows [M, K] bf16 quantised to E4M3 codes
+ * q_r and scales s_r as dg_op_quantize_rows does and w8 [N, K] E4M3 codes
+ * (packed, DG_FP8_E4M3) with per-row scales w_scale [N]; modes as
+ * dg_op_linear.  K a multiple of 128 up to 4096 (else DG_ERR_SHAPE); the
+ * FP8 MFMA from 1024 rows.  workspace of dg_op_linear_e4m3_workspace_bytes
+ * (m, k), device memory, 256-byte aligned. */
+dg_status dg_op_linear_e4m3(const void* x, int32_t m, int32_t k, const void* w8,
+                            const float* w_scale, int32_t n, int32_t mode,
+                            void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+size_t dg_op_linear_e4m3_workspace_bytes(int32_t m, int32_t k);
+
 /* Canvas attention of one layer (write-up Figure 4 stage 2: bidirectional
  * over the canvas plus attention to the cached context; model card "Model
  * Overview").  For canvas b, query head h, position i:

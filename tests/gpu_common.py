@@ -78,6 +78,17 @@ def oshape(s):
                          getattr(s, "proj_dtype", "bf16") == "fp8_e4m3")
 
 
+def op_proj(x, lw, name, out, mode):
+    """A layer's Q/K/V ("w_qkv") or output ("w_o") projection through the
+    entry point its weights need: the W8A8 one when they are E4M3 codes with
+    per-row scales (reading R16), else the bf16 one."""
+    sc = lw.get("qkv_scale" if name == "w_qkv" else "o_scale")
+    if sc is not None:
+        dg.op_linear_e4m3(x, lw[name], sc, out, mode)
+    else:
+        dg.op_linear(x, lw[name], out, mode)
+
+
 def to_dev(w, dev=DEV):
     out = {"embed": w["embed"].to(dev), "final_norm": w["final_norm"].to(dev),
            "layers": [None if lw is None else

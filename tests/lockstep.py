@@ -32,7 +32,7 @@ import torch
 
 from block_discrete_diffusion_tok_amd import dg
 from gpu_common import (DEV, MARGIN, TOL, TOL_ROW_FP8_ACT, cache_scales,
-                        lm8_decision_bound,
+                        lm8_decision_bound, op_proj,
                         fp8_act, log,
                         np32, rel_err, row_err,
                         routing_margin, top2_margin)
@@ -121,7 +121,7 @@ class Lockstep:
         # Q/K/V projection of the oracle's normed rows
         xh_o = self._full(c["xh_attn"], H, torch.bfloat16)
         qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
-        dg.op_linear(xh_o, lw["w_qkv"], qkv, 0)
+        op_proj(xh_o, lw, "w_qkv", qkv, 0)
         self._cmp("qkv", self._mine(qkv), c["qkv"], li)
         if self.kv_o is not None:     # commit: the appended K / V rows
             k_o, v_o = self.kv_o[li]
@@ -145,8 +145,7 @@ class Lockstep:
         self._cmp("attention", self._mine(o), c["attn"], li)
         # output projection added into the oracle's residual
         x = x_in.clone()
-        dg.op_linear(self._full(c["attn"], Hq * D, torch.bfloat16), lw["w_o"],
-                     x, 2)
+        op_proj(self._full(c["attn"], Hq * D, torch.bfloat16), lw, "w_o", x, 2)
         self._cmp("x after attention", self._mine(x), c["x_mid"], li)
         # FFN norm
         x_mid = self._full(c["x_mid"], H, torch.float32)

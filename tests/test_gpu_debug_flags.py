@@ -3,9 +3,9 @@ per process from the environment):
   DG_POISON=1 fills the workspace's value regions with NaN before every
     engine call that runs layers: a prefill from tokens, a denoise step, a
     commit and an AR step return the same outputs and caches bit for bit as
-    without it, for a bf16 model and for the E4M3 variants (W8A8 experts,
-    E4M3 cache, E4M3 LM head), so no kernel reads scratch its call did not
-    write;
+    without it, for a bf16 model and for the E4M3 variants (W8A8 experts
+    and projections, E4M3 cache, E4M3 LM head), so no kernel reads scratch
+    its call did not write;
   DG_CHECK=1 makes a commit of a canvas with uncommitted positions fail
     with DG_ERR_STATE;
   DG_KV_SPLIT=s changes only the attention's summation order."""
@@ -23,8 +23,8 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# The child: a two-layer model (bf16, or E4M3 experts with E4M3 token rows,
-# an E4M3 cache and an E4M3 LM head) with two requests, one prefilled from K/V and one from
+# The child: a two-layer model (bf16, or E4M3 experts and projections with
+# E4M3 token rows, an E4M3 cache and an E4M3 LM head) with two requests, one prefilled from K/V and one from
 # tokens; a denoise step over a canvas of each, their commit, an AR step.
 _CHILD = r'''
 import sys, torch
@@ -32,7 +32,7 @@ sys.path.insert(0, sys.argv[1])
 from block_discrete_diffusion_tok_amd import dg, synth
 fp8 = sys.argv[3] == "fp8"
 kw = dict(expert_dtype="fp8_e4m3", act_dtype="fp8_e4m3", kv_dtype="fp8_e4m3",
-          lm_dtype="fp8_e4m3") if fp8 else {}
+          lm_dtype="fp8_e4m3", proj_dtype="fp8_e4m3") if fp8 else {}
 shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096, **kw)
 w = synth.make_weights(shape, seed=31, gain_std=0.1, device="cuda")
 eng = dg.Engine(shape, w, max_requests=2, max_kv_len=1024, max_canvases=2)

@@ -253,8 +253,12 @@ def test_commit_block_two_layers_against_oracle():
     """Causal encode-and-append of two canvases: the appended K/V of both
     layers in lockstep with the oracle, and the cache rows dg_commit_block
     wrote against the op chain on the same tokens."""
-    shape = synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096)
-    log("commit: two layers, prefixes 300 / 512")
+    commit_case(synth.ModelShape(2, 256, 4, 2, 64, 16, 2, 512, 4096),
+                "two layers")
+
+
+def commit_case(shape, tag):
+    log(f"commit: {tag}, prefixes 300 / 512")
     eng, wn, prefix = _setup(shape, [300, 512], 2048, seed=4)
     cv = synth.make_canvas(shape, 2, 0, seed=9)
     tok, com, step = (t.to(DEV) for t in (cv["tokens"], cv["committed"],
@@ -263,8 +267,7 @@ def test_commit_block_two_layers_against_oracle():
     torch.cuda.synchronize()
     assert eng.kv_len(0) == 556 and eng.kv_len(1) == 768
     embed = {"embed": torch.as_tensor(wn["embed"], device=DEV).to(torch.bfloat16)}
-    check_commit_composition(eng, shape, embed, tok, [0, 1], [300, 512],
-                             "two layers")
+    check_commit_composition(eng, shape, embed, tok, [0, 1], [300, 512], tag)
     kv_o, cap_o = [], []
     ls = Lockstep(shape, eng, eng.weights, 2, [0, 1], [300, 512], [0, 1],
                   cap_o, "commit lockstep", causal=True, kv_o=kv_o)

@@ -6,8 +6,8 @@ import numpy as np
 import torch
 
 from block_discrete_diffusion_tok_amd import dg, synth
-from gpu_common import (DEV, MARGIN, TOL, cache_scales, log, np32, rel_err,
-                        routing_margin)
+from gpu_common import (DEV, MARGIN, TOL, cache_scales, log, np32, op_proj,
+                        rel_err, routing_margin)
 
 
 class HostLayers:
@@ -101,7 +101,7 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
             xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
             dg.op_rmsnorm(x, lw["attn_norm"], s.rms_eps, xh)
             qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
-            dg.op_linear(xh, lw["w_qkv"], qkv, 0)
+            op_proj(xh, lw, "w_qkv", qkv, 0)
             o = torch.empty((T, Hq * D), dtype=torch.bfloat16, device=DEV)
             ks, vs = cache_scales(eng, li)
             dg.op_canvas_attention(qkv, n, T // n, Hq, Hkv, D, kc_all[li],
@@ -109,7 +109,7 @@ def check_composition(eng, shape, w, tokens, req, plen, cap, tag, layers=None):
                                    eng.max_kv_len, req, plen, False, 0, o,
                                    ks, vs)
             e_att = rel_err(np32(o), np32(o_cap))
-        dg.op_linear(o_cap, lw["w_o"], x, 2)   # the step's own kernel
+        op_proj(o_cap, lw, "w_o", x, 2)   # the step's own kernel
         if li in layers:
             xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
             dg.op_rmsnorm(x, lw["ffn_norm"], s.rms_eps, xh)
@@ -156,7 +156,7 @@ def check_commit_composition(eng, shape, w, tokens, req, plen, tag, C=256):
         xh = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
         dg.op_rmsnorm(x, lw["attn_norm"], s.rms_eps, xh)
         qkv = torch.empty((T, qkv_n), dtype=torch.bfloat16, device=DEV)
-        dg.op_linear(xh, lw["w_qkv"], qkv, 0)
+        op_proj(xh, lw, "w_qkv", qkv, 0)
         for b in range(n):
             rows = slice(b * C, (b + 1) * C)
             # after the request's earlier canvases of the batch
@@ -190,7 +190,7 @@ def check_commit_composition(eng, shape, w, tokens, req, plen, tag, C=256):
         dg.op_canvas_attention(qkv, n, C, Hq, Hkv, D, kc_all[li], vc_all[li],
                                eng.max_requests, eng.max_kv_len, req, plen,
                                True, 0, o, ks, vs)
-        dg.op_linear(o, lw["w_o"], x, 2)
+        op_proj(o, lw, "w_o", x, 2)
         dg.op_rmsnorm(x, lw["ffn_norm"], s.rms_eps, xh)
         y = torch.empty((T, H), dtype=torch.float32, device=DEV)
         dg.op_moe(s, lw, xh, y)
