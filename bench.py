@@ -19,8 +19,8 @@ block decoded with the final-norm gain scaled so that EB commits ~19.74
 positions per step (the pages' tokens per forward) as a labelled variant;
 per-kernel times with their roofline fractions and the dominant kernel's
 roofline; labelled extras: AR decoding (greedy, one position per step) and
-token-mode prompt prefill on request 0, and the same decoding with E4M3
-expert weights and token rows (W8A8, after the bf16 engine is freed); the
+token-mode prompt prefill on request 0, and the same decoding in W8A8
+(E4M3 projections, experts and LM head; after the bf16 engine is freed); the
 CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
@@ -62,11 +62,18 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
     fb = F + 4 if s.act_dtype == "fp8_e4m3" else 2 * F
     # cached K / V rows: E4M3 codes plus one fp32 scale per row
     kvb = D + 4 if s.kv_dtype == "fp8_e4m3" else 2 * D
+    # E4M3 projections / LM head: 1-byte weights plus a scale per row, input
+    # rows as codes plus a scale
+    p8 = s.proj_dtype == "fp8_e4m3"
+    l8 = s.lm_dtype == "fp8_e4m3"
     pairs = T * k
     touched = E * (1.0 - (1.0 - k / E) ** T)   # experts receiving a token
     qkvN = (Hq + 2 * Hkv) * D
     P = prefix
     if kind == "lm_head":
+        if l8:
+            return (V * H + V * 4 + mean_rows * (H + 4) + mean_rows * 16,
+                    2.0 * mean_rows * H * V)
         return (V * H * 2 + mean_rows * H * 2 + mean_rows * 16,
                 2.0 * mean_rows * H * V)
     if kind == "moe_gate_up":
@@ -80,8 +87,14 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
                 + T * Hq * D * 2 * 2 + T * 2 * Hkv * D * 2,
                 4.0 * T * Hq * D * (P + 256))
     if kind == "qkv_proj":
+        if p8:
+            return (qkvN * (H + 4) + T * (H + 4) + T * qkvN * 2,
+                    2.0 * T * H * qkvN)
         return (qkvN * H * 2 + T * H * 2 + T * qkvN * 2, 2.0 * T * H * qkvN)
     if kind == "o_proj":
+        if p8:
+            return (H * (Hq * D + 4) + T * (Hq * D + 4) + T * H * 8,
+                    2.0 * T * Hq * D * H)
         return (H * Hq * D * 2 + T * Hq * D * 2 + T * H * 8,
                 2.0 * T * Hq * D * H)
     if kind == "router":
@@ -89,10 +102,19 @@ def algorithmic(kind, s, wl, mean_rows, prefix):
     return None
 
 
-def mfma_peak(kind, s):
+def mfma_peak(kind, s, rows=None):
     """Dense MFMA peak (TFLOP/s) of the type a kernel kind computes in:
-    the expert GEMMs run the fp8 MFMA when token rows are E4M3."""
+    the expert GEMMs run the fp8 MFMA when token rows are E4M3; E4M3
+    projections from 1024 rows and an E4M3 LM head above 128 rows take the
+    large-tile kernel's fp8 MFMA (fewer rows: E4M3 codes widened to bf16).
+    rows: token rows of a projection launch or mean LM-head rows."""
     if kind in ("moe_gate_up", "moe_down") and s.act_dtype == "fp8_e4m3":
+        return FP8_PEAK_TFLOPS
+    if kind in ("qkv_proj", "o_proj") and s.proj_dtype == "fp8_e4m3" and \
+            rows is not None and rows >= 1024:
+        return FP8_PEAK_TFLOPS
+    if kind == "lm_head" and s.lm_dtype == "fp8_e4m3" and rows is not None \
+            and rows > 128:
         return FP8_PEAK_TFLOPS
     return BF16_PEAK_TFLOPS
 
@@ -489,9 +511,10 @@ def ar_and_prefill(b, n_tokens=64):
 
 
 def w8a8_variant(name, steps=2):
-    """Labelled extra: the same batch-1 decoding with E4M3 expert weights and
-    E4M3 expert token rows (per-row scales), one warm-up block and `steps`
-    consecutive timed blocks, hipEvents around each denoise step."""
+    """Labelled extra: the same batch-1 decoding in W8A8 (E4M3 weights and
+    rows in the projections, the experts and the LM head), one warm-up
+    block and `steps` consecutive timed blocks, hipEvents around each
+    denoise step."""
     import torch
     from block_discrete_diffusion_tok_amd import synth
     wl = synth.WORKLOADS[name]
@@ -517,8 +540,10 @@ def w8a8_variant(name, steps=2):
             "canvas_tok_s": round(256.0 * n / (ms / 1000.0), 1),
             "committed_tok_s": round(wl.uncommitted * steps / (ms / 1000.0), 1),
             "denoise_step_ms_median": round(med, 4),
-            "note": "labelled extra: E4M3 experts and E4M3 expert token "
-                    "rows; attention, router and LM head in bf16"}
+            "note": "labelled extra: W8A8 -- E4M3 weights (per-row scales) "
+                    "and E4M3 rows in the Q/K/V and output projections, the "
+                    "experts and the LM head; attention, router and norms "
+                    "in bf16 / fp32, bf16 KV cache"}
 
 
 def main():
@@ -620,13 +645,17 @@ def main():
     b.eng.profile_enable(False)
     mean_rows = sum(rows_seen) / len(rows_seen)
 
+    def launch_rows(kind):
+        return mean_rows if kind == "lm_head" else wl.batch * 256
+
     kernels = {}
     for name, (t, n) in sorted(prof.items(), key=lambda x: -x[1][0]):
         ent = {"total_ms": round(t, 4), "launches": n,
                "avg_us": round(1000.0 * t / n, 2)}
         alg = algorithmic(name, s, wl, mean_rows, wl.prefix_len)
         if alg is not None:
-            rf = roofline_of(name, alg, t / n / 1000.0, mfma_peak(name, s))
+            rf = roofline_of(name, alg, t / n / 1000.0,
+                             mfma_peak(name, s, launch_rows(name)))
             ent["bound"] = rf["bound"]
             ent["frac"] = rf["frac"]
         kernels[name] = ent
@@ -636,7 +665,7 @@ def main():
     roofline = roofline_of(dom, algorithmic(dom, s, wl, mean_rows,
                                             wl.prefix_len),
                            prof[dom][0] / prof[dom][1] / 1000.0,
-                           mfma_peak(dom, s))
+                           mfma_peak(dom, s, launch_rows(dom)))
     roofline["traffic"] = measured_traffic(args.workload, dom)
 
     tpf = None
@@ -673,7 +702,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if s.expert_dtype == "bf16" else "bf16+e4m3 experts",
+        "dtype": ("bf16+e4m3 (w8a8)" if s.proj_dtype == "fp8_e4m3" else
+                  "bf16" if s.expert_dtype == "bf16" else "bf16+e4m3 experts"),
         "data": "synthetic: seeded N(0,0.02) bf16 weights, N(0,1) prefix K/V, "
                 "uniform canvas tokens",
         "config": {"workload": args.workload, "layers": s.n_layers,
@@ -681,7 +711,9 @@ def main():
                    "kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                    "experts": s.n_experts, "top_k": s.top_k,
                    "expert_ffn": s.expert_ffn, "vocab": s.vocab,
-                   "expert_dtype": s.expert_dtype,
+                   "expert_dtype": s.expert_dtype, "act_dtype": s.act_dtype,
+                   "proj_dtype": s.proj_dtype, "lm_dtype": s.lm_dtype,
+                   "kv_dtype": s.kv_dtype,
                    "prefix_len": wl.prefix_len, "batch": wl.batch,
                    "masked": wl.uncommitted, "gamma": wl.gamma,
                    "step_cap": wl.step_cap,

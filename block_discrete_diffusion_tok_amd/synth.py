@@ -64,6 +64,10 @@ class Workload:
 
 _GEMMA_LAYER = dict(hidden=2048, n_q_heads=16, n_kv_heads=8, head_dim=128,
                     n_experts=128, top_k=8, expert_ffn=768, vocab=262144)
+# FP8 serving: E4M3 weights and E4M3 rows in every dense product but the
+# router (attention, norms and the cache stay bf16 / fp32)
+_W8A8 = dict(expert_dtype="fp8_e4m3", act_dtype="fp8_e4m3",
+             lm_dtype="fp8_e4m3", proj_dtype="fp8_e4m3")
 
 WORKLOADS = {
     w.name: w for w in [
@@ -98,19 +102,17 @@ WORKLOADS = {
                  step_cap=256, steps=12,
                  notes="the 131072-token prefix in an E4M3 KV cache"),
         Workload("stack30_w8a8_b32_p2048",
-                 ModelShape(30, **_GEMMA_LAYER, expert_dtype="fp8_e4m3",
-                            act_dtype="fp8_e4m3"),
+                 ModelShape(30, **_GEMMA_LAYER, **_W8A8),
                  prefix_len=2048, batch=32, uncommitted=256, gamma=1.0,
                  step_cap=256,
-                 notes="the 32-canvas batch with E4M3 expert activations "
-                       "too (W8A8)"),
+                 notes="the 32-canvas batch in W8A8: E4M3 weights and rows "
+                       "in the projections, the experts and the LM head"),
         Workload("stack30_w8a8_h2048_p4096",
-                 ModelShape(30, **_GEMMA_LAYER, expert_dtype="fp8_e4m3",
-                            act_dtype="fp8_e4m3"),
+                 ModelShape(30, **_GEMMA_LAYER, **_W8A8),
                  prefix_len=4096, batch=1, uncommitted=256, gamma=1.0,
                  step_cap=64, blocks=4,
-                 notes="the batch-1 stack with E4M3 experts and E4M3 expert "
-                       "token rows (W8A8)"),
+                 notes="the batch-1 stack in W8A8: E4M3 weights and rows "
+                       "in the projections, the experts and the LM head"),
     ]
 }
 

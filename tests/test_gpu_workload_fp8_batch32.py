@@ -1,6 +1,7 @@
 """The concurrency workload at its full size: the 30-layer stack with E4M3
 expert weights (per-output-channel scales) -- and its W8A8 variant, whose
-expert GEMMs also take E4M3 token rows (reading R13) --, 32 requests with their own
+projections, expert GEMMs and LM head take E4M3 weights and E4M3 token rows
+(readings R13, R15, R16) --, 32 requests with their own
 2048-token prefixes, 32 canvases denoised together (8192 rows per MoE grouped
 GEMM and per LM head).
 
@@ -95,8 +96,11 @@ def test_fp8_batch32_step_lockstep_and_composition(batch32):
                               want_logits=True, capture=cap_o)
     assert ls.finish() == SHAPE.n_layers
     ls.report()
+    lm8 = None
+    if w.get("lm_head") is not None:
+        lm8 = (w["lm_head"].cpu().numpy(), w["lm_head_scale"].cpu().numpy())
     lockstep_head(SHAPE, eng, w, ref, ls.x_last, cv["committed"].numpy(), n,
-                  sel, WL.name, seed=1)
+                  sel, WL.name, seed=1, lm8_host=lm8)
     lockstep_eb(ref["entropy"], ref["argmax"], cv["committed"].numpy()[sel],
                 cv["tokens"].numpy()[sel], cv["step"].numpy()[sel], WL.gamma,
                 WL.step_cap, WL.name)
