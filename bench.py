@@ -19,7 +19,8 @@ block decoded with the final-norm gain scaled so that EB commits ~19.74
 positions per step (the pages' tokens per forward) as a labelled variant;
 per-kernel times with their roofline fractions and the dominant kernel's
 roofline; labelled extras: AR decoding (greedy, one position per step) and
-token-mode prompt prefill on request 0, and the same decoding in W8A8
+token-mode prompt prefill on request 0, the step replayed from a HIP graph
+against the same steps launched eagerly, and the same decoding in W8A8
 (E4M3 projections, experts and LM head; after the bf16 engine is freed); the
 CPU oracle timed on a bounded sample of the same workload.
 
@@ -510,6 +511,69 @@ def ar_and_prefill(b, n_tokens=64):
                                        "chunks of 256"}}
 
 
+def graph_variant(b, steps=32):
+    """Labelled extra: one denoise step + EB selection captured into a HIP
+    graph on a side stream (dg_set_stream) and replayed `steps` times from
+    the first block's initial canvas, against the same steps launched
+    eagerly on that stream; hipEvents around each run of steps."""
+    torch = b.torch
+    st = b.st
+    init = b.init[0][1]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    b.eng.set_stream(s)
+
+    def restore():
+        for kk in st:
+            st[kk].copy_(init[kk])
+        for r in b.req:
+            b.eng.set_kv_len(r, b.wl.prefix_len)
+
+    def one():
+        b.eng.denoise_step(b.req, st["tokens"], st["committed"], st["step"],
+                           b.ent, b.lse, b.am)
+        b.eng.eb_select(b.req, st["tokens"], st["committed"], st["step"],
+                        b.ent, b.am, b.gamma, b.wl.step_cap, True, b.n_new,
+                        b.done[0])
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        restore()
+        one()                                   # warm-up on the stream
+        restore()
+        e0.record()
+        for _ in range(steps):
+            one()
+        e1.record()
+    torch.cuda.synchronize()
+    eager = e0.elapsed_time(e1) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        one()
+    with torch.cuda.stream(s):
+        restore()
+        g.replay()                              # warm-up replay
+        restore()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    graph = e0.elapsed_time(e1) / steps
+    del g
+    b.eng.set_stream(None)
+    restore()
+    torch.cuda.synchronize()
+    return {"steps": steps, "eager_step_ms": round(eager, 4),
+            "graph_step_ms": round(graph, 4),
+            "note": "labelled extra: denoise step + EB selection replayed "
+                    "from a HIP graph vs launched eagerly, same stream"}
+
+
 def w8a8_variant(name, steps=2):
     """Labelled extra: the same batch-1 decoding in W8A8 (E4M3 weights and
     rows in the projections, the experts and the LM head), one warm-up
@@ -674,9 +738,11 @@ def main():
         tpf = tpf_matched(b, args.steps)
 
     extras = {}
+    log("[bench] HIP-graph replay of the step")
+    extras["hip_graph"] = graph_variant(b)
     if not args.no_ar:
         log("[bench] AR decoding and token-mode prefill")
-        extras = ar_and_prefill(b)
+        extras.update(ar_and_prefill(b))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1117,6 +1117,13 @@ const char* dg_profile_kind_name(int32_t kind) {
   return (kind >= 0 && kind < DG_PROF_KINDS) ? kKindNames[kind] : "";
 }
 
+dg_status dg_set_stream(dg_ctx* c, void* stream) {
+  if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
+  c->stream = (hipStream_t)stream;
+  c->prof.s = c->stream;
+  return DG_OK;
+}
+
 dg_status dg_set_kv_len(dg_ctx* c, int32_t req, int32_t len) {
   if (!c) return fail(nullptr, DG_ERR_INVALID_ARG, "ctx is NULL");
   if (req < 0 || req >= c->max_requests)

@@ -97,6 +97,7 @@ _SIGS = {
     "dg_commit_block": (_I, [_P, ctypes.POINTER(CanvasBatch)]),
     "dg_ar_step": (_I, [_P, _I, ctypes.POINTER(_I), _P, ctypes.POINTER(StepOut)]),
     "dg_set_kv_len": (_I, [_P, _I, _I]),
+    "dg_set_stream": (_I, [_P, _P]),
     "dg_profile_enable": (_I, [_P, _I]),
     "dg_profile_read": (_I, [_P, _P, _P]),
     "dg_profile_kind_name": (ctypes.c_char_p, [_I]),
@@ -353,6 +354,13 @@ class Engine:
             _check(5, self.ctx)
         return {L.dg_profile_kind_name(k).decode(): (ms[k], n[k])
                 for k in range(PROF_KINDS) if n[k] > 0}
+
+    def set_stream(self, stream=None):
+        """Enqueue the context's calls on ``stream`` (a torch.cuda.Stream;
+        None: torch's current stream), e.g. one captured into a HIP graph."""
+        h = (stream.cuda_stream if stream is not None
+             else torch.cuda.current_stream().cuda_stream)
+        _check(lib().dg_set_stream(self.ctx, ctypes.c_void_p(h)), self.ctx)
 
     def set_kv_len(self, req, n):
         _check(lib().dg_set_kv_len(self.ctx, req, n), self.ctx)

@@ -347,6 +347,19 @@ dg_status dg_commit_block(dg_ctx* ctx, const dg_canvas_batch* batch);
 dg_status dg_ar_step(dg_ctx* ctx, int32_t n, const int32_t* req,
                      const int32_t* tokens, const dg_step_out* out);
 
+/* The stream the context's calls enqueue on from now on (the one given to
+ * dg_create until then); the profiler's events are recorded on it too.
+ * HIP graphs: dg_denoise_step and dg_eb_select enqueue kernel launches
+ * only (no allocation, no host synchronisation, no memset unless
+ * DG_POISON; a capture adds device-to-device copies), so a caller may
+ * capture them on its own stream (set here first; capture cannot use the
+ * legacy null stream) and replay the graph.  A replay reuses the host-side
+ * values of the capture: the batch's request slots and kv_len (its key
+ * ranges), so a graph holds for the steps of one block; dg_commit_block
+ * and dg_ar_step advance kv_len on the host and are not for capture.
+ * DG_ERR_INVALID_ARG for a NULL ctx. */
+dg_status dg_set_stream(dg_ctx* ctx, void* stream);
+
 dg_status dg_set_kv_len(dg_ctx* ctx, int32_t req, int32_t len);
 int32_t dg_kv_len(const dg_ctx* ctx, int32_t req); /* -1 on a bad slot */
 
