@@ -743,6 +743,10 @@ def main():
     if not args.no_ar:
         log("[bench] AR decoding and token-mode prefill")
         extras.update(ar_and_prefill(b))
+        # the write-up's Figure 11 ratio: a 256-position denoise step against
+        # a one-position AR step, both at batch 1
+        extras["denoise_step_over_ar_step"] = round(
+            med / extras["ar_decode"]["ms_per_token"], 3)
 
     cpu = None
     if not args.no_cpu_baseline:
