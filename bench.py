@@ -26,6 +26,7 @@ CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
   python bench.py --denoise-only 3     # a few plain denoise steps, for profilers
+  python bench.py --prefill-only 32768 # token-mode prefill of a long prompt
   python bench.py --copy-calibration   # one plain copy of 1 GiB, for counters
 """
 import argparse
@@ -610,6 +611,39 @@ def w8a8_variant(name, steps=2):
                     "in bf16 / fp32, bf16 KV cache"}
 
 
+def prefill_only(wl, n_tokens):
+    """Token-mode prefill (dg_prefill_kv from tokens: the causal encode in
+    chunks of 256 through every layer, K/V written to the cache) of one
+    seeded prompt of n_tokens on the workload's model; a 512-token warm-up
+    first, then one timed prefill with hipEvents."""
+    import torch
+    from block_discrete_diffusion_tok_amd import dg, synth
+    s = wl.shape
+    w = synth.make_weights(s, seed=0, device="cuda")
+    eng = dg.Engine(s, w, max_requests=1, max_kv_len=n_tokens + 256,
+                    max_canvases=1)
+    g = torch.Generator(device="cpu").manual_seed(13)
+    prompt = torch.randint(0, s.vocab, (n_tokens,), generator=g,
+                           dtype=torch.int32).to("cuda")
+    eng.prefill_tokens(0, prompt[:512].contiguous())
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    eng.prefill_tokens(0, prompt)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert eng.kv_len(0) == n_tokens
+    eng.close()
+    return {"metric": "token-mode prefill tokens/s", "value": round(
+        n_tokens / (ms / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+            "ms": round(ms, 2), "tokens": n_tokens, "higher_is_better": True,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "layers": s.n_layers,
+                       "step": "causal encode in chunks of 256"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawTextHelpFormatter)
@@ -626,6 +660,9 @@ def main():
     ap.add_argument("--no-w8a8", action="store_true",
                     help="skip the W8A8 batch-1 extra")
     ap.add_argument("--denoise-only", type=int, default=0)
+    ap.add_argument("--prefill-only", type=int, default=0,
+                    help="time token-mode prefill of a prompt of this many "
+                         "tokens on the workload's model (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -640,6 +677,9 @@ def main():
     from block_discrete_diffusion_tok_amd import synth
     wl = synth.WORKLOADS[args.workload]
     s = wl.shape
+    if args.prefill_only:
+        print(json.dumps(prefill_only(wl, args.prefill_only)), flush=True)
+        return
     b = Bench(wl, max_blocks=max(args.steps, args.warmup))
 
     if args.denoise_only:
