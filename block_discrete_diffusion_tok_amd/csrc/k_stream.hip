@@ -70,11 +70,11 @@ __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); 
 // In the packed layout the q-th load of chunk kc is block kc * WREGS + q of
 // the row tile: one contiguous kilobyte per wave load, and the 4 tiles of a
 // tile group (2 waves) read one contiguous run per block column.
-// NTL: non-temporal loads (the weights are read once).  Measured per kernel:
-// the LM head streams faster with them; the expert kernels, whose token
-// rows are re-read through L2, do not (the down products slow down), so
-// they keep plain loads.
-template <int RT, int WREGS, int ESZ, int KC, bool NTL>
+// The loads are non-temporal: each weight byte is read once, and leaving it
+// out of the caches keeps them for the token rows that every pass re-reads.
+// Measured at 256 tokens of the 128-expert layer: gate/up 144.5 -> 125.4 us,
+// down 77.5 -> 69.5 us (the LM head streams faster with them too).
+template <int RT, int WREGS, int ESZ, int KC>
 __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
                                        const char* const (&src)[RT], int kc) {
 #pragma unroll
@@ -82,7 +82,7 @@ __device__ __forceinline__ void load_w(u32x4_t (&w)[RT][WREGS],
 #pragma unroll
     for (int q = 0; q < WREGS; ++q) {
       const u32x4_t* p = (const u32x4_t*)(src[rt] + ((long long)kc * WREGS + q) * kPackKStride);
-      w[rt][q] = NTL ? __builtin_nontemporal_load(p) : *p;
+      w[rt][q] = __builtin_nontemporal_load(p);
     }
 }
 
@@ -275,7 +275,7 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
   auto issue = [&](auto p, int k) {
     uint16_t* st = &Xs[(k % S) * STAGE + wave * IPW * 64 * 8];
     static_for<IPW>([&](auto i) { dma16(xsrc[i] + (long long)k * KC, st + i * 64 * 8); });
-    load_w<RT, WREGS, ESZ, KC, epi_is_lm(EPI)>(w[p], wsrc, k);
+    load_w<RT, WREGS, ESZ, KC>(w[p], wsrc, k);
   };
   auto prologue = [&]() {
     static_for<D>([&](auto p) {
