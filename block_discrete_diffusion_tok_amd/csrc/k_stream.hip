@@ -607,12 +607,14 @@ hipError_t launch_s(const StreamArgs& a, int groups, hipStream_t s) {
 // fills its pipeline while the other streams; gate/up with passes of 64
 // token columns and 3 chunks in flight, down with passes of 64 and 2 chunks
 // in flight (it has only K / 64 = 12 chunks per row block).  Side by side in
-// the 30-layer step at batch 1 (an expert has ~16 tokens), gate/up: one
-// 8-wave workgroup with 128-column passes and 2 chunks in flight 147 us, two
-// 4-wave workgroups with 64-column passes 142 us, with 3 chunks in flight
-// 140 us, with 32-column passes 151 us, 8 waves with 4 chunks in flight
-// 154 us.  Down: 89.0 -> 87.1 us against one 8-wave workgroup; 3 or 4 chunks
-// in flight or 32-column passes within noise.
+// the 30-layer step at batch 1 (an expert has ~16 tokens), with plain weight
+// loads, gate/up: one 8-wave workgroup with 128-column passes and 2 chunks in
+// flight 147 us, two 4-wave workgroups with 64-column passes 142 us, with 3
+// chunks in flight 140 us, with 32-column passes 151 us, 8 waves with 4
+// chunks in flight 154 us.  Down: 89.0 -> 87.1 us against one 8-wave
+// workgroup; 3 or 4 chunks in flight or 32-column passes within noise.  With
+// non-temporal weight loads (gate/up 125 us, down 70-72 us), 4 chunks in
+// flight for gate/up and 3 for down measured within noise.
 constexpr int kLmRT = 2, kLmKC = 64, kLmD = 3, kLmOcc = 2, kLmWaves = 4;
 constexpr int kMoeRT = 2, kMoeKC = 64, kMoeOcc = 2;
 constexpr int kGuNT = 4, kGuD = 3, kGuWaves = 4;  // gate/up
