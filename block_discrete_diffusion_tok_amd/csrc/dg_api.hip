@@ -658,6 +658,8 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     gu.C = b.act;
     gu.ldc = F;
     gu.ffn = F;
+    // fewer (token, rank) pairs than expert groups: most groups are empty
+    gu.count_first = pairs < EG ? 1 : 0;
     {
       ProfScope ps(prof, 8);
       if ((e = launch_stream(EPI_SWIGLU, w8, gu, EG, s)) != hipSuccess) return e;
@@ -685,6 +687,7 @@ hipError_t run_moe(const dg_model_desc& d, const dg_layer_weights& w,
     dn.ldc = H;
     dn.c_map = b.slot_pair;
     dn.row_scale = b.slot_w;
+    dn.count_first = gu.count_first;
     {
       ProfScope ps(prof, 9);
       if ((e = launch_stream(EPI_DOWN, w8, dn, EG, s)) != hipSuccess) return e;

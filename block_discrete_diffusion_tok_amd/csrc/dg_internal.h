@@ -270,6 +270,9 @@ struct StreamArgs {
   LmSample smp;            // EPI_LMSTATS: temperature sampling (smp.tau null: off)
   const float* x_scale;    // SWIGLU / DOWN: X rows hold E4M3 values (as bf16);
                            //   the scale of each X row (null: none)
+  int count_first;         // grouped: read a group's count before issuing any
+                           //   load, so that empty groups load nothing (for
+                           //   launches where most groups are empty)
 };
 // Epilogues EPI_LMSTATS (up to 128 token columns per pass), EPI_SWIGLU (64)
 // and EPI_DOWN (64).  K must satisfy stream_lm_ok / stream_moe_ok.

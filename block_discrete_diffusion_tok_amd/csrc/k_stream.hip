@@ -284,15 +284,22 @@ __device__ __forceinline__ void stream_run(const StreamArgs& a, uint16_t* Xs, in
     });
   };
 
+  // the count is read-only here (an earlier kernel wrote it): a scalar load
+  // through the constant address space, so its wait is not a vector-memory
+  // wait for every chunk in flight.  With few tokens (one decoded position:
+  // 8 of 128 experts hold a row) most groups are empty, and their first
+  // chunks would be loaded for nothing: the count is then read first.
+  if (GROUPED && a.count_first) {
+    t_end = min(*DG_CONST_PTR(int32_t, a.group_count + group), a.cap);
+    if (t_end <= 0) return;  // the whole workgroup: no load was issued
+  }
   load_ids(0);
   load_tok_ids(0);
   if (!GROUPED) t_end = dense_rows;
   set_rows(0);
   prologue();
-  // the count is read-only here (an earlier kernel wrote it): a scalar load
-  // through the constant address space, so its wait is not a vector-memory
-  // wait for every chunk in flight
-  if (GROUPED) t_end = min(*DG_CONST_PTR(int32_t, a.group_count + group), a.cap);
+  if (GROUPED && !a.count_first)
+    t_end = min(*DG_CONST_PTR(int32_t, a.group_count + group), a.cap);
   if (t_end <= 0) {  // an empty group: let the loads land before leaving
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     return;

@@ -311,6 +311,18 @@ def test_moe_large_tile_path_full_size_layer_shape():
     _moe_case(g8, 4096, "gemma_fp8_mm")
 
 
+@pytest.mark.parametrize("t", [1, 8, 15])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("shared", [0, 1])
+def test_moe_few_tokens_most_experts_empty(t, dtype, shared):
+    # fewer (token, rank) pairs than expert groups (one decoded position
+    # routes to 8 of 128 experts): the expert kernels read each group's
+    # count before any load, and the empty groups leave at once
+    g = synth.ModelShape(**{**GEMMA.__dict__, "expert_dtype": dtype,
+                            "n_shared_experts": shared})
+    _moe_case(g, t, f"few_{dtype}_{t}_{shared}")
+
+
 @pytest.mark.parametrize("t", [256, 1024, 4096])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
 def test_moe_with_shared_expert(t, dtype):
